@@ -1,0 +1,268 @@
+/*
+ * CPU oracle for the asymmetric-hashing (AH) search path -- TEST INFRASTRUCTURE.
+ *
+ * Plain, slow, deliberately unoptimised C.  Each function writes out the plain
+ * definition of one step of the query path described on the page "ScaNN:
+ * Anisotropic Vector Quantization for Maximum Inner Product Search", section
+ * "Three stages of a search" (partition scoring, per-block lookup table,
+ * sum of table entries, keep the best candidates, exact reorder).
+ *
+ * This file shares no code, header or constant with the GPU library: it is
+ * compiled on its own (oracle/build.py) and is used only by tests/, by the
+ * smoke check and by the benchmark's CPU-baseline leg.
+ *
+ * Conventions (readings of what the pages leave open):
+ *  - code of row i, block b: (codes[i*stride + b/2] >> (4*(b&1))) & 15, i.e. the
+ *    low nibble holds the even block;
+ *  - every ranking orders by score descending, then by id ascending, so the
+ *    kept set is unique;
+ *  - int8 table: per block the centre m_b = 0.5*(lo_b+hi_b), one per-query step
+ *    s = Rng/254 with Rng = max_b (hi_b - lo_b), entries rint((v - m_b)*254/Rng)
+ *    clamped to [-127,127] (rint = round half to even, as in the int8 lesson's
+ *    "ties go to the even mark"), bias = sum_b m_b accumulated in block order.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+typedef struct { int32_t score; int32_t id; } ISC;
+typedef struct { double score; int32_t id; } DSC;
+
+static int cmp_isc(const void* a, const void* b) {
+    const ISC* x = (const ISC*)a; const ISC* y = (const ISC*)b;
+    if (x->score != y->score) return x->score > y->score ? -1 : 1;
+    return (x->id > y->id) - (x->id < y->id);
+}
+static int cmp_dsc(const void* a, const void* b) {
+    const DSC* x = (const DSC*)a; const DSC* y = (const DSC*)b;
+    if (x->score != y->score) return x->score > y->score ? -1 : 1;
+    return (x->id > y->id) - (x->id < y->id);
+}
+
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+void oracle_set_threads(int t) { if (t > 0) omp_set_num_threads(t); }
+
+/* Nibble of block b in a row-major code row. */
+static inline int code_of(const uint8_t* row, int32_t b) {
+    return (row[b >> 1] >> (4 * (b & 1))) & 15;
+}
+
+/* Step 3 of the page: approximate score of one row = sum over blocks of that
+ * block's table entry at the row's code.  Integer, exact. */
+static inline int32_t adc_sum(const int8_t* lut_q, int32_t B, const uint8_t* row) {
+    int32_t s = 0;
+    for (int32_t b = 0; b < B; ++b) s += (int32_t)lut_q[b * 16 + code_of(row, b)];
+    return s;
+}
+
+/* All sums of every query against every row: out[q*n + i]. */
+void oracle_scan_sums(const int8_t* lut, int64_t nq, int32_t B, const uint8_t* codes,
+                      int64_t n, int32_t stride, int32_t* out) {
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t q = 0; q < nq; ++q)
+        for (int64_t i = 0; i < n; ++i)
+            out[q * n + i] = adc_sum(lut + q * (int64_t)B * 16, B, codes + i * (int64_t)stride);
+}
+
+/* Steps 3+4: for each query, score every row of the leaves it searches (all rows
+ * when leaves == NULL), sort all (sum, id) pairs by (sum desc, id asc) and keep
+ * the first R.  Missing slots are (-1, INT32_MIN). */
+void oracle_scan_topk(const int8_t* lut, int64_t nq, int32_t B, const uint8_t* codes, int64_t n,
+                      int32_t stride, const int32_t* ids, const int64_t* leaf_offsets, int32_t L,
+                      const int32_t* leaves, int32_t nl, int32_t R, int32_t* out_ids,
+                      int32_t* out_scores) {
+    (void)L;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t q = 0; q < nq; ++q) {
+        int64_t total = 0;
+        if (leaves) {
+            for (int32_t j = 0; j < nl; ++j) {
+                int32_t l = leaves[q * nl + j];
+                total += leaf_offsets[l + 1] - leaf_offsets[l];
+            }
+        } else {
+            total = n;
+        }
+        ISC* all = (ISC*)malloc(sizeof(ISC) * (size_t)(total > 0 ? total : 1));
+        int64_t m = 0;
+        const int8_t* lq = lut + q * (int64_t)B * 16;
+        if (leaves) {
+            for (int32_t j = 0; j < nl; ++j) {
+                int32_t l = leaves[q * nl + j];
+                for (int64_t i = leaf_offsets[l]; i < leaf_offsets[l + 1]; ++i) {
+                    all[m].score = adc_sum(lq, B, codes + i * (int64_t)stride);
+                    all[m].id = ids ? ids[i] : (int32_t)i;
+                    ++m;
+                }
+            }
+        } else {
+            for (int64_t i = 0; i < n; ++i) {
+                all[m].score = adc_sum(lq, B, codes + i * (int64_t)stride);
+                all[m].id = ids ? ids[i] : (int32_t)i;
+                ++m;
+            }
+        }
+        qsort(all, (size_t)m, sizeof(ISC), cmp_isc);
+        for (int32_t r = 0; r < R; ++r) {
+            out_ids[q * R + r] = r < m ? all[r].id : -1;
+            out_scores[q * R + r] = r < m ? all[r].score : INT32_MIN;
+        }
+        free(all);
+    }
+}
+
+/* Per-block lookup table of q . center in float64:
+ * lut[q][b][c] = sum_t q[b*dpb + t] * cb[b][c][t]. */
+void oracle_lut_f64(const float* qv, int64_t nq, int32_t d, const float* cb, int32_t B,
+                    int32_t dpb, double* out) {
+    (void)d;
+    #pragma omp parallel for schedule(static)
+    for (int64_t q = 0; q < nq; ++q)
+        for (int32_t b = 0; b < B; ++b)
+            for (int32_t c = 0; c < 16; ++c) {
+                double s = 0.0;
+                for (int32_t t = 0; t < dpb; ++t)
+                    s += (double)qv[q * d + b * dpb + t] * (double)cb[((int64_t)b * 16 + c) * dpb + t];
+                out[(q * B + b) * 16 + c] = s;
+            }
+}
+
+/* int8 quantisation of a given float32 table, all arithmetic in float32 in the
+ * order stated in the header comment. */
+void oracle_quantize_lut(const float* lut, int64_t nq, int32_t B, int8_t* out, float* scale,
+                         float* bias) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t q = 0; q < nq; ++q) {
+        const float* t = lut + q * (int64_t)B * 16;
+        float* mid = (float*)malloc(sizeof(float) * (size_t)(B > 0 ? B : 1));
+        float rng = 0.0f;
+        for (int32_t b = 0; b < B; ++b) {
+            float lo = t[b * 16], hi = t[b * 16];
+            for (int32_t c = 1; c < 16; ++c) {
+                if (t[b * 16 + c] < lo) lo = t[b * 16 + c];
+                if (t[b * 16 + c] > hi) hi = t[b * 16 + c];
+            }
+            float sum = lo + hi;
+            mid[b] = 0.5f * sum;
+            float w = hi - lo;
+            if (w > rng) rng = w;
+        }
+        float beta = 0.0f;
+        for (int32_t b = 0; b < B; ++b) beta = beta + mid[b];
+        int8_t* o = out + q * (int64_t)B * 16;
+        if (rng > 0.0f) {
+            float inv = 254.0f / rng;
+            for (int32_t b = 0; b < B; ++b)
+                for (int32_t c = 0; c < 16; ++c) {
+                    float diff = t[b * 16 + c] - mid[b];
+                    float v = rintf(diff * inv);
+                    if (v > 127.0f) v = 127.0f;
+                    if (v < -127.0f) v = -127.0f;
+                    o[b * 16 + c] = (int8_t)v;
+                }
+            scale[q] = rng / 254.0f;
+        } else {
+            memset(o, 0, (size_t)B * 16);
+            scale[q] = 0.0f;
+        }
+        bias[q] = beta;
+        free(mid);
+    }
+}
+
+static inline double load_row_elem(const void* base, int32_t dtype, int64_t idx) {
+    if (dtype == 0) return (double)((const float*)base)[idx];
+    uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;  /* bf16 -> f32, exact */
+    float f;
+    memcpy(&f, &bits, 4);
+    return (double)f;
+}
+
+/* Step 5: exact float64 dot products of each query with its candidates
+ * (id -1 = empty slot, skipped); keep the best k by (score desc, id asc).
+ * Missing slots are (-1, -inf). dtype 0 = float32 rows, 1 = bf16 rows. */
+void oracle_reorder(const float* qv, int64_t nq, int32_t d, const void* base, int32_t dtype,
+                    int64_t n, const int32_t* cand, int32_t R, int32_t k, int32_t* out_ids,
+                    double* out_scores) {
+    (void)n;
+    #pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t q = 0; q < nq; ++q) {
+        DSC* s = (DSC*)malloc(sizeof(DSC) * (size_t)(R > 0 ? R : 1));
+        int32_t m = 0;
+        for (int32_t r = 0; r < R; ++r) {
+            int32_t id = cand[q * R + r];
+            if (id < 0) continue;
+            double acc = 0.0;
+            for (int32_t j = 0; j < d; ++j)
+                acc += (double)qv[q * d + j] * load_row_elem(base, dtype, (int64_t)id * d + j);
+            s[m].score = acc;
+            s[m].id = id;
+            ++m;
+        }
+        qsort(s, (size_t)m, sizeof(DSC), cmp_dsc);
+        for (int32_t r = 0; r < k; ++r) {
+            out_ids[q * k + r] = r < m ? s[r].id : -1;
+            out_scores[q * k + r] = r < m ? s[r].score : -INFINITY;
+        }
+        free(s);
+    }
+}
+
+/* Step 1: score every centroid in float64 and keep the best nl leaves by
+ * (score desc, leaf id asc). */
+void oracle_partition(const float* qv, int64_t nq, int32_t d, const float* cent, int32_t L,
+                      int32_t nl, int32_t* out_leaves, double* out_scores) {
+    #pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t q = 0; q < nq; ++q) {
+        DSC* s = (DSC*)malloc(sizeof(DSC) * (size_t)(L > 0 ? L : 1));
+        for (int32_t l = 0; l < L; ++l) {
+            double acc = 0.0;
+            for (int32_t j = 0; j < d; ++j)
+                acc += (double)qv[q * d + j] * (double)cent[(int64_t)l * d + j];
+            s[l].score = acc;
+            s[l].id = l;
+        }
+        qsort(s, (size_t)L, sizeof(DSC), cmp_dsc);
+        for (int32_t r = 0; r < nl; ++r) {
+            out_leaves[q * nl + r] = s[r].id;
+            out_scores[q * nl + r] = s[r].score;
+        }
+        free(s);
+    }
+}
+
+/* Exact ground truth: float64 dot of every query with every row; the best k by
+ * (score desc, id asc) are kept in a small list maintained by insertion.
+ * dtype as in oracle_reorder. */
+static inline int dsc_better(double s, int32_t id, const DSC* o) {
+    return s > o->score || (s == o->score && id < o->id);
+}
+void oracle_brute_force(const float* qv, int64_t nq, int32_t d, const void* base, int32_t dtype,
+                        int64_t n, int32_t k, int32_t* out_ids, double* out_scores) {
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t q = 0; q < nq; ++q) {
+        DSC* best = (DSC*)malloc(sizeof(DSC) * (size_t)(k > 0 ? k : 1));
+        int32_t m = 0;
+        for (int64_t i = 0; i < n; ++i) {
+            double acc = 0.0;
+            for (int32_t j = 0; j < d; ++j)
+                acc += (double)qv[q * d + j] * load_row_elem(base, dtype, i * d + j);
+            if (m == k && !dsc_better(acc, (int32_t)i, &best[k - 1])) continue;
+            int32_t pos = m < k ? m : k - 1;
+            while (pos > 0 && dsc_better(acc, (int32_t)i, &best[pos - 1])) {
+                best[pos] = best[pos - 1];
+                --pos;
+            }
+            best[pos].score = acc;
+            best[pos].id = (int32_t)i;
+            if (m < k) ++m;
+        }
+        for (int32_t r = 0; r < k; ++r) {
+            out_ids[q * k + r] = r < m ? best[r].id : -1;
+            out_scores[q * k + r] = r < m ? best[r].score : -INFINITY;
+        }
+        free(best);
+    }
+}

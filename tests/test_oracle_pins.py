@@ -1,0 +1,328 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a golden
+example printed on the pages, a closed form, an independent formulation
+(one-hot matrix product, numpy lexsort), brute force on tiny inputs, or a
+special case that reduces to the textbook exact search.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    out = {}
+    with open(os.path.join(GOLD, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            out[key] = vals
+    return out
+
+
+def _decode_nibbles(codes, B):
+    lo = codes & 15
+    hi = codes >> 4
+    nib = np.empty((codes.shape[0], codes.shape[1] * 2), dtype=np.int64)
+    nib[:, 0::2] = lo
+    nib[:, 1::2] = hi
+    return nib[:, :B]
+
+
+def _onehot_sums(lut_i8, codes, B):
+    """Independent formulation: sums = onehot(codes) @ table^T in int64."""
+    nib = _decode_nibbles(codes, B)
+    n = codes.shape[0]
+    oh = np.zeros((n, B * 16), dtype=np.int64)
+    rows = np.repeat(np.arange(n), B)
+    cols = (np.tile(np.arange(B), n) * 16 + nib.reshape(-1))
+    oh[rows, cols] = 1
+    return (oh @ lut_i8.reshape(lut_i8.shape[0], -1).astype(np.int64).T).T
+
+
+# ---------------------------------------------------------------- code layout
+
+def test_nibble_layout_golden():
+    g = _golden("nibble_layout.txt")
+    row = np.array([[int(h, 16) for h in g["bytes"]]], dtype=np.uint8)
+    want = [int(c) for c in g["codes"]]
+    B = len(want)
+    # a table whose entry at (b, c) is 16*b + c reveals the code read for block b
+    lut = np.zeros((1, B, 16), dtype=np.int8)
+    for b in range(B):
+        lut[0, b, :] = 0
+    for b in range(B):
+        single = np.zeros((1, B, 16), dtype=np.int8)
+        single[0, b, :] = np.arange(16)
+        s = oracle.scan_sums(single, row)
+        assert int(s[0, 0]) == want[b], (b, int(s[0, 0]), want[b])
+
+
+# ---------------------------------------------------------------- table (ADC identity)
+
+@pytest.mark.parametrize("dpb,B", [(1, 5), (2, 8), (4, 6), (3, 3)])
+def test_adc_identity_float64(dpb, B):
+    """Sum of a row's table entries equals q . decode(codes) (ScaNN page,
+    "Three stages of a search": the approximate score is the sum of the
+    row's table entries, each table entry being q . center)."""
+    rng = np.random.default_rng(11 + dpb)
+    d = B * dpb
+    Q = rng.standard_normal((7, d)).astype(np.float32)
+    cb = rng.standard_normal((B, 16, dpb)).astype(np.float32)
+    codes = synth.random_codes(rng, 50, B)
+    lut = oracle.lut_f64(Q, cb)
+    nib = _decode_nibbles(codes, B)
+    decoded = np.concatenate([cb[b][nib[:, b]] for b in range(B)], axis=1).astype(np.float64)
+    direct = Q.astype(np.float64) @ decoded.T
+    via_table = np.zeros_like(direct)
+    for b in range(B):
+        via_table += lut[:, b, :][:, nib[:, b]]
+    assert np.allclose(via_table, direct, rtol=1e-12, atol=1e-12)
+
+
+def test_lut_transpose_would_fail():
+    """A transposed codebook (center/dim swapped) must not satisfy the identity."""
+    rng = np.random.default_rng(3)
+    Q = rng.standard_normal((2, 4)).astype(np.float32)
+    cb = rng.standard_normal((2, 16, 2)).astype(np.float32)
+    lut = oracle.lut_f64(Q, cb)
+    want = np.einsum("qbt,bct->qbc", Q.reshape(2, 2, 2).astype(np.float64), cb.astype(np.float64))
+    assert np.allclose(lut, want, rtol=1e-14)
+    wrong = np.einsum("qbt,bct->qbc", Q.reshape(2, 2, 2)[:, ::-1].astype(np.float64), cb.astype(np.float64))
+    assert not np.allclose(lut, wrong)
+
+
+# ---------------------------------------------------------------- int8 quantisation
+
+def test_round_half_even_golden():
+    """The int8 lesson's example: 127.5 marks rounds to 128 (ties to even)."""
+    g = _golden("int8_rounding_example.txt")
+    x, lo, hi, lev = (float(g[k][0]) for k in ("x", "lo", "hi", "levels"))
+    scaled = (x - lo) / (hi - lo) * lev
+    assert scaled == float(g["scaled"][0])
+    assert int(np.rint(scaled)) == int(g["code"][0])
+    dec = lo + int(g["code"][0]) / lev * (hi - lo)
+    assert round(dec, 5) == float(g["decoded"][0])
+
+
+def test_quantizer_ties_go_to_even():
+    """Build a table whose step makes (v - m_b) * 254/Rng land exactly on k + 0.5:
+    Rng = 254/128 gives an exact multiplier of 128, so diffs of (k+0.5)/128 are ties."""
+    rng_w = np.float32(254.0 / 128.0)
+    half = np.float32(rng_w / 2)
+    ks = np.array([0, 1, 2, 3, 10, 11, 62, 125, 126], dtype=np.float64)
+    lut = np.zeros((1, 2, 16), dtype=np.float32)
+    # block 0 spans [-half, +half] so m_0 = 0 and Rng = rng_w
+    lut[0, 0, 0] = -half
+    lut[0, 0, 1] = half
+    lut[0, 0, 2:2 + len(ks)] = ((ks + 0.5) / 128.0).astype(np.float32)
+    lut[0, 0, 2 + len(ks):] = 0
+    lut[0, 1, :] = 0.0
+    t8, s, beta = oracle.quantize_lut(lut)
+    assert s[0] == np.float32(rng_w / np.float32(254.0))
+    got = t8[0, 0, 2:2 + len(ks)].astype(int)
+    want = [int(k) if int(k) % 2 == 0 else int(k) + 1 for k in ks]
+    assert list(got) == want
+    assert t8[0, 0, 0] == -127 and t8[0, 0, 1] == 127
+
+
+def test_quantizer_error_bound_and_range():
+    """|beta + s * sum T8 - sum of float table entries| <= B*s/2 (+ float slack)."""
+    rng = np.random.default_rng(5)
+    nq, B = 6, 40
+    lut = (rng.standard_normal((nq, B, 16)) * rng.uniform(0.1, 3.0, size=(1, B, 1))).astype(np.float32)
+    t8, s, beta = oracle.quantize_lut(lut)
+    assert t8.min() >= -127 and t8.max() <= 127
+    assert (np.abs(t8).reshape(nq, -1).max(axis=1) == 127).all()
+    codes = synth.random_codes(rng, 300, B)
+    nib = _decode_nibbles(codes, B)
+    exact = np.zeros((nq, 300))
+    for b in range(B):
+        exact += lut[:, b, :].astype(np.float64)[:, nib[:, b]]
+    isums = _onehot_sums(t8, codes, B)
+    approx = beta[:, None].astype(np.float64) + s[:, None].astype(np.float64) * isums
+    bound = B * s[:, None] / 2 * (1 + 1e-4) + 1e-4 * np.abs(exact).max()
+    assert (np.abs(approx - exact) <= bound).all()
+    # a sign flip of the entries breaks the bound
+    flipped = beta[:, None] - s[:, None].astype(np.float64) * isums
+    assert (np.abs(flipped - exact) > bound).any()
+
+
+def test_quantizer_constant_table():
+    lut = np.full((2, 3, 16), 1.25, dtype=np.float32)
+    lut[1] = -0.5
+    t8, s, beta = oracle.quantize_lut(lut)
+    assert (t8 == 0).all() and (s == 0).all()
+    assert beta[0] == np.float32(3.75) and beta[1] == np.float32(-1.5)
+
+
+# ---------------------------------------------------------------- scan sums and top-R
+
+def test_scan_sums_match_onehot_product():
+    rng = np.random.default_rng(7)
+    for B in (1, 2, 5, 32, 33):
+        lut = synth.random_lut_i8(rng, 4, B)
+        codes = synth.random_codes(rng, 257, B)
+        got = oracle.scan_sums(lut, codes)
+        assert np.array_equal(got.astype(np.int64), _onehot_sums(lut, codes, B))
+
+
+def _lexsort_topr(sums_row, ids_row, R):
+    order = np.lexsort((ids_row, -sums_row.astype(np.int64)))
+    keep = order[:R]
+    ids = np.full(R, -1, dtype=np.int32)
+    sc = np.full(R, np.iinfo(np.int32).min, dtype=np.int32)
+    ids[: len(keep)] = ids_row[keep]
+    sc[: len(keep)] = sums_row[keep]
+    return ids, sc
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_scan_topk_brute_force_heavy_ties(seed):
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 20))
+    n = int(rng.integers(1, 900))
+    nq = 5
+    if seed % 2:
+        lut = rng.choice(np.array([-3, 4], dtype=np.int8), size=(nq, B, 16))
+    else:
+        lut = synth.random_lut_i8(rng, nq, B)
+    codes = synth.random_codes(rng, n, B)
+    R = int(rng.integers(1, n + 6))
+    ids, sc = oracle.scan_topk(lut, codes, R)
+    sums = _onehot_sums(lut, codes, B)
+    for q in range(nq):
+        wi, ws = _lexsort_topr(sums[q].astype(np.int32), np.arange(n, dtype=np.int32), R)
+        assert np.array_equal(ids[q], wi) and np.array_equal(sc[q], ws)
+
+
+def test_scan_topk_partitioned_with_ids_and_empty_leaves():
+    rng = np.random.default_rng(9)
+    B, n, nq, L, nl, R = 6, 700, 8, 20, 7, 40
+    lut = synth.random_lut_i8(rng, nq, B, -5, 5)
+    codes = synth.random_codes(rng, n, B)
+    sizes = synth.random_leaf_sizes(rng, n, L, skew=1.5)
+    sizes[3] = 0
+    sizes[4] += 0
+    sizes[-1] += n - sizes.sum()
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    perm = rng.permutation(n).astype(np.int32)
+    leaves = synth.random_probe_lists(rng, nq, L, nl)
+    leaves[0, 0] = 3  # an empty leaf is searched
+    ids, sc = oracle.scan_topk(lut, codes, R, ids=perm, leaf_offsets=offs, leaves=leaves)
+    sums = _onehot_sums(lut, codes, B)
+    for q in range(nq):
+        rows = np.concatenate([np.arange(offs[l], offs[l + 1]) for l in leaves[q]]).astype(np.int64)
+        wi, ws = _lexsort_topr(sums[q, rows].astype(np.int32), perm[rows], R)
+        assert np.array_equal(ids[q], wi) and np.array_equal(sc[q], ws)
+
+
+def test_scan_topk_empty_database():
+    lut = np.zeros((2, 3, 16), dtype=np.int8)
+    codes = np.zeros((0, 2), dtype=np.uint8)
+    ids, sc = oracle.scan_topk(lut, codes, 4)
+    assert (ids == -1).all() and (sc == np.iinfo(np.int32).min).all()
+
+
+# ---------------------------------------------------------------- reorder, partition, ground truth
+
+def test_reorder_exact_integer_rows_and_ties():
+    rng = np.random.default_rng(12)
+    X = rng.integers(-3, 4, size=(60, 9)).astype(np.float32)
+    X[17] = X[5]  # duplicate row: equal score, lower id must win
+    Q = rng.integers(-2, 3, size=(4, 9)).astype(np.float32)
+    cand = np.stack([rng.permutation(60)[:30] for _ in range(4)]).astype(np.int32)
+    cand[:, 0], cand[:, 1] = 17, 5
+    cand[2, 5:9] = -1
+    ids, sc = oracle.reorder(Q, X, cand, 8)
+    exact = Q.astype(np.int64) @ X.astype(np.int64).T
+    for q in range(4):
+        c = cand[q][cand[q] >= 0]
+        order = np.lexsort((c, -exact[q, c]))[:8]
+        assert np.array_equal(ids[q], c[order])
+        assert np.array_equal(sc[q], exact[q, c[order]].astype(np.float64))
+
+
+def test_reorder_bf16_rows_upcast_exactly():
+    rng = np.random.default_rng(13)
+    X = rng.standard_normal((40, 16)).astype(np.float32)
+    bits = synth.to_bf16_bits(X)
+    Xb = synth.bf16_bits_to_f32(bits).astype(np.float64)
+    Q = rng.standard_normal((3, 16)).astype(np.float32)
+    cand = np.tile(np.arange(40, dtype=np.int32), (3, 1))
+    ids, sc = oracle.reorder(Q, bits, cand, 5)
+    ref = Q.astype(np.float64) @ Xb.T
+    for q in range(3):
+        order = np.lexsort((np.arange(40), -ref[q]))[:5]
+        assert np.array_equal(ids[q], order)
+        assert np.allclose(sc[q], ref[q, order], rtol=1e-14, atol=1e-14)
+
+
+def test_reorder_pads_when_few_candidates():
+    X = np.eye(4, dtype=np.float32)
+    Q = np.ones((1, 4), dtype=np.float32)
+    ids, sc = oracle.reorder(Q, X, np.array([[2, -1, -1]], dtype=np.int32), 3)
+    assert list(ids[0]) == [2, -1, -1]
+    assert sc[0, 0] == 1.0 and np.isneginf(sc[0, 1:]).all()
+
+
+def test_partition_hand_case_with_tie():
+    Q = np.array([[1.0, 0.0]], dtype=np.float32)
+    Cn = np.array([[1, 0], [0, 1], [1, 0], [2, 0]], dtype=np.float32)
+    lv, sc = oracle.partition(Q, Cn, 3)
+    assert list(lv[0]) == [3, 0, 2]
+    assert list(sc[0]) == [2.0, 1.0, 1.0]
+
+
+def test_brute_force_against_full_sort():
+    rng = np.random.default_rng(14)
+    X = rng.standard_normal((300, 12)).astype(np.float32)
+    X /= np.linalg.norm(X, axis=1, keepdims=True)
+    X[200] = X[100]
+    Q = rng.standard_normal((6, 12)).astype(np.float32)
+    Q[0] = X[100]
+    ids, sc = oracle.brute_force(Q, X, 10)
+    S = Q.astype(np.float64) @ X.astype(np.float64).T
+    for q in range(6):
+        order = np.lexsort((np.arange(300), -S[q]))[:10]
+        assert np.array_equal(ids[q], order)
+    assert ids[0, 0] == 100 and ids[0, 1] == 200
+
+
+def test_full_reorder_reduces_to_exact_search():
+    """With R >= n every row reaches the exact reorder, so the result is the
+    textbook exact top-k (recall 1)."""
+    rng = np.random.default_rng(15)
+    w = synth.WORKLOADS["tiny"]
+    X = synth.rows(w, 0, 400)
+    Q = synth.rows(w, 0, 5, role=synth.ROLE_QUERY)
+    B = w.d // w.dpb
+    cb = rng.standard_normal((B, 16, w.dpb)).astype(np.float32)
+    codes = synth.random_codes(rng, 400, B)
+    res = oracle.search(Q, cb, codes, X, R=400, k=10)
+    gt, _ = oracle.brute_force(Q, X, 10)
+    assert np.array_equal(res["ids"], gt)
+    assert oracle.recall_at_k(res["ids"], gt) == 1.0
+
+
+# ---------------------------------------------------------------- recall
+
+def test_recall_golden_example():
+    g = _golden("recall_example.txt")
+    t = np.array([[int(x) for x in g["true"]]])
+    f = np.array([[int(x) for x in g["found"]]])
+    assert round(oracle.recall_at_k(f, t), 2) == float(g["recall"][0])
+
+
+def test_recall_ignores_empty_slots_and_averages():
+    t = np.array([[1, 2], [3, 4]])
+    f = np.array([[2, -1], [4, 3]])
+    assert oracle.recall_at_k(f, t) == pytest.approx(0.75)
