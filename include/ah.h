@@ -1,0 +1,154 @@
+/*
+ * ah.h -- C ABI of the MI355X (gfx950) asymmetric-hashing search path.
+ *
+ * The four calls follow the query path of the page "ScaNN: Anisotropic Vector
+ * Quantization for Maximum Inner Product Search", section "Three stages of a
+ * search": a query scores every partition centroid and descends into the best
+ * leaves (ah_partition_score); a lookup table of q.center per block of
+ * dimensions is built (ah_build_lut); a row's approximate score is the sum of
+ * its table entries, and the best candidates are kept (ah_scan_topk); the best
+ * few hundred candidates are rescored with exact dot products
+ * (ah_reorder_exact).  Codebooks, centroids and codes are trained on the host
+ * and passed in.
+ *
+ * Conventions shared by every call
+ *  - Every array pointer is a DEVICE pointer to row-major, contiguous memory
+ *    owned by the caller; the library keeps no pointer after a call returns and
+ *    holds no global mutable state, so calls on distinct streams are safe.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on that stream and returns; device faults surface at the
+ *    caller's next synchronisation.  The caller keeps inputs, outputs and
+ *    workspace alive until the stream has finished the work.
+ *  - Return value: AH_OK (0) or a negative AH_ERR_* code, checked on the host
+ *    before anything is enqueued (AH_ERR_HIP reports a failed launch).
+ *    ah_status_string() describes a code.  nq == 0 is a successful no-op.
+ *  - Rankings order by score descending, then by id ascending, so every kept
+ *    set is unique.
+ *  - Codes: row-major, `code_stride` bytes per row (>= ceil(B/2)); block b of a
+ *    row is the nibble (row[b/2] >> 4*(b%2)) & 15 (low nibble = even block).
+ */
+#ifndef AH_H
+#define AH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    AH_OK = 0,
+    AH_ERR_NULL = -1,        /* a required pointer is NULL */
+    AH_ERR_SHAPE = -2,       /* inconsistent or out-of-range sizes */
+    AH_ERR_UNSUPPORTED = -3, /* valid but not supported (dtype, limits below) */
+    AH_ERR_WORKSPACE = -4,   /* workspace pointer NULL or smaller than required */
+    AH_ERR_HIP = -5          /* a HIP launch failed */
+};
+
+enum { AH_F32 = 0, AH_BF16 = 1 };
+
+/* Limits (AH_ERR_UNSUPPORTED beyond them). */
+#define AH_MAX_BLOCKS 4096   /* B */
+#define AH_MAX_DPB 16        /* dimensions_per_block */
+#define AH_MAX_R 4096        /* pre-reorder candidates (also max nl and k) */
+#define AH_MAX_DIM 16384     /* d */
+
+const char* ah_status_string(int status);
+int ah_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Step 1: centroid scoring and leaf choice (ScaNN page, "Three stages of a
+ * search": a query scores every centroid and descends into the best
+ * num_leaves_to_search; cost on the worked example: 1,000 centroids x 128 dims).
+ *
+ *   q          float32 [nq][d]   queries
+ *   centroids  float32 [L][d]    partition centroids
+ *   leaves_out int32   [nq][nl]  best nl leaf ids, best first
+ *   leaf_scores_out float32 [nq][nl] their scores q.c (fp32 accumulation), or NULL
+ *   workspace  >= ah_partition_workspace_bytes(nq, L) bytes of device memory
+ * Errors: AH_ERR_NULL (q, centroids, leaves_out, workspace), AH_ERR_SHAPE
+ * (nq < 0, d < 1, L < 1, nl < 1 or nl > L), AH_ERR_UNSUPPORTED (d > AH_MAX_DIM,
+ * nl > AH_MAX_R), AH_ERR_WORKSPACE.
+ */
+size_t ah_partition_workspace_bytes(int64_t nq, int32_t L);
+int ah_partition_score(const float* q, int64_t nq, int32_t d, const float* centroids, int32_t L,
+                       int32_t nl, int32_t* leaves_out, float* leaf_scores_out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Step 2: per-query lookup table (ScaNN page, "Three stages of a search":
+ * a table of q.center per block; each vector is split into blocks of
+ * dimensions_per_block dims, each replaced by one of 16 centers).
+ *
+ *   q          float32 [nq][d]
+ *   codebooks  float32 [B][16][dpb]   (d == B*dpb)
+ *   lut_f32_out float32 [nq][B][16]   T[q][b][c] = sum_t q[b*dpb+t]*cb[b][c][t], or NULL
+ *   lut_i8_out  int8    [nq][B][16]   int8 table
+ *   scale_out   float32 [nq]          per-query step s
+ *   bias_out    float32 [nq]          per-query bias beta
+ * int8 table (fp32 arithmetic in this order): lo_b/hi_b = min/max over c of
+ * T[q][b][.]; m_b = 0.5f*(lo_b+hi_b); Rng = max_b(hi_b-lo_b); if Rng > 0:
+ * T8 = clamp(rint((T - m_b) * (254.0f/Rng)), -127, 127), s = Rng/254.0f, else
+ * T8 = 0, s = 0; beta = sum of m_b in block order.  The approximate score of a
+ * row is beta + s * sum_b T8[q][b][code_b].
+ * Errors: AH_ERR_NULL, AH_ERR_SHAPE (d != B*dpb, B < 1, dpb < 1, nq < 0),
+ * AH_ERR_UNSUPPORTED (B > AH_MAX_BLOCKS, dpb > AH_MAX_DPB).
+ */
+int ah_build_lut(const float* q, int64_t nq, int32_t d, const float* codebooks, int32_t B,
+                 int32_t dpb, float* lut_f32_out, int8_t* lut_i8_out, float* scale_out,
+                 float* bias_out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Steps 3+4: code scan and top-R (ScaNN page, "Three stages of a search": a
+ * row's approximate score is the sum of its table entries; "Using the library":
+ * the best pre_reorder_num_neighbors go on to reorder; worked example: the scan
+ * dominates the cost of a query).
+ *
+ *   lut_i8       int8 [nq][B][16]
+ *   codes        uint8 [n][code_stride]  (leaf-sorted when partitioned)
+ *   ids          int32 [n] original row id of each code row, or NULL (= row index)
+ *   leaf_offsets int64 [L+1] rows of leaf l are [leaf_offsets[l], leaf_offsets[l+1]),
+ *                or NULL when leaves == NULL
+ *   leaves       int32 [nq][nl] leaves each query scans (distinct per query), or
+ *                NULL = every query scans all n rows
+ *   cand_ids_out    int32 [nq][R]  original ids, best first
+ *   cand_scores_out int32 [nq][R]  their exact integer sums sum_b T8[q][b][code_b]
+ *   Slots beyond the number of scanned rows hold (-1, INT32_MIN).
+ *   workspace    >= ah_scan_workspace_bytes(nq, B, n, L, nl, R) bytes
+ * Sums are exact int32; the kept set is the unique top-R by (sum desc, id asc).
+ * Errors: AH_ERR_NULL, AH_ERR_SHAPE (nq < 0, n < 0, B < 1, code_stride <
+ * ceil(B/2), R < 1, leaves given with L < 1 or nl < 1 or nl > L or no
+ * leaf_offsets), AH_ERR_UNSUPPORTED (B > AH_MAX_BLOCKS, R > AH_MAX_R,
+ * n >= 2^31), AH_ERR_WORKSPACE.
+ */
+size_t ah_scan_workspace_bytes(int64_t nq, int32_t B, int64_t n, int32_t L, int32_t nl, int32_t R);
+int ah_scan_topk(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* codes,
+                 int32_t code_stride, int64_t n, const int32_t* ids, const int64_t* leaf_offsets,
+                 int32_t L, const int32_t* leaves, int32_t nl, int32_t R, int32_t* cand_ids_out,
+                 int32_t* cand_scores_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Step 5: exact reorder (ScaNN page, "Three stages of a search": the best few
+ * hundred candidates are rescored with exact dot products; "Failure modes":
+ * reorder must keep more than k).
+ *
+ *   q         float32 [nq][d]
+ *   base      [n][d] stored rows, float32 (AH_F32) or bf16 bits (AH_BF16)
+ *   cand_ids  int32 [nq][R]  candidate ids, -1 = empty slot (skipped)
+ *   ids_out   int32 [nq][k]  best k by exact score, best first
+ *   scores_out float32 [nq][k] exact q.x (bf16 rows widened exactly to fp32,
+ *             fp32 accumulation); empty slots (-1, -inf)
+ * Errors: AH_ERR_NULL, AH_ERR_SHAPE (nq < 0, d < 1, n < 0, R < 1, k < 1,
+ * k > R), AH_ERR_UNSUPPORTED (dtype, R > AH_MAX_R, d > AH_MAX_DIM).  Candidate
+ * ids must lie in [-1, n).
+ */
+int ah_reorder_exact(const float* q, int64_t nq, int32_t d, const void* base, int32_t base_dtype,
+                     int64_t n, const int32_t* cand_ids, int32_t R, int32_t k, int32_t* ids_out,
+                     float* scores_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AH_H */

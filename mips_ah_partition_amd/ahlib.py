@@ -1,0 +1,214 @@
+"""Thin Python binding of the C ABI in include/ah.h (libah.so, built in-tree).
+
+Argument marshalling only: every function takes torch CUDA (ROCm) tensors,
+checks dtype/shape/contiguity, passes raw device pointers and the current
+stream to the library and raises ``AHError`` on a non-zero status.  All work
+runs in the library's HIP kernels; there is no fallback path: if libah.so is
+missing or cannot be loaded, the import of this module's functions fails
+loudly.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libah.so")
+
+AH_OK, AH_ERR_NULL, AH_ERR_SHAPE, AH_ERR_UNSUPPORTED, AH_ERR_WORKSPACE, AH_ERR_HIP = 0, -1, -2, -3, -4, -5
+AH_F32, AH_BF16 = 0, 1
+
+# every symbol include/ah.h declares
+EXPORTS = (
+    "ah_status_string", "ah_version",
+    "ah_partition_workspace_bytes", "ah_partition_score",
+    "ah_build_lut",
+    "ah_scan_workspace_bytes", "ah_scan_topk",
+    "ah_reorder_exact",
+)
+
+_lib = None
+
+
+class AHError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+def lib() -> C.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+        L.ah_status_string.restype = C.c_char_p
+        L.ah_status_string.argtypes = [C.c_int]
+        L.ah_version.restype = C.c_int
+        L.ah_partition_workspace_bytes.restype = sz
+        L.ah_partition_workspace_bytes.argtypes = [i64, i32]
+        L.ah_partition_score.restype = C.c_int
+        L.ah_partition_score.argtypes = [vp, i64, i32, vp, i32, i32, vp, vp, vp, sz, vp]
+        L.ah_build_lut.restype = C.c_int
+        L.ah_build_lut.argtypes = [vp, i64, i32, vp, i32, i32, vp, vp, vp, vp, vp]
+        L.ah_scan_workspace_bytes.restype = sz
+        L.ah_scan_workspace_bytes.argtypes = [i64, i32, i64, i32, i32, i32]
+        L.ah_scan_topk.restype = C.c_int
+        L.ah_scan_topk.argtypes = [vp, i64, i32, vp, i32, i64, vp, vp, i32, vp, i32, i32, vp, vp, vp, sz, vp]
+        L.ah_reorder_exact.restype = C.c_int
+        L.ah_reorder_exact.argtypes = [vp, i64, i32, vp, i32, i64, vp, i32, i32, vp, vp, vp]
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().ah_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != AH_OK:
+        raise AHError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtype, name, ndim=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+    return t
+
+
+# ----------------------------------------------------------------------------- step 1
+def ah_partition_workspace_bytes(nq: int, L: int) -> int:
+    return int(lib().ah_partition_workspace_bytes(nq, L))
+
+
+def ah_partition_score(q, centroids, nl, leaves_out=None, leaf_scores_out=None, workspace=None, stream=None):
+    """Best nl leaves per query (and their fp32 scores)."""
+    q = _dev(q, torch.float32, "q", 2)
+    centroids = _dev(centroids, torch.float32, "centroids", 2)
+    nq, d = q.shape
+    L = centroids.shape[0]
+    if centroids.shape[1] != d:
+        raise ValueError("centroids dimension differs from queries")
+    if leaves_out is None:
+        leaves_out = torch.empty((nq, nl), dtype=torch.int32, device=q.device)
+    if leaf_scores_out is None:
+        leaf_scores_out = torch.empty((nq, nl), dtype=torch.float32, device=q.device)
+    _dev(leaves_out, torch.int32, "leaves_out")
+    _dev(leaf_scores_out, torch.float32, "leaf_scores_out")
+    need = ah_partition_workspace_bytes(nq, L)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().ah_partition_score(_ptr(q), nq, d, _ptr(centroids), L, nl, _ptr(leaves_out),
+                                    _ptr(leaf_scores_out), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "ah_partition_score")
+    return leaves_out, leaf_scores_out
+
+
+# ----------------------------------------------------------------------------- step 2
+def ah_build_lut(q, codebooks, lut_i8_out=None, scale_out=None, bias_out=None, lut_f32_out=None,
+                 want_f32=False, stream=None):
+    """int8 tables (and optionally the fp32 ones) for a query batch.
+    codebooks: float32 [B, 16, dpb]."""
+    q = _dev(q, torch.float32, "q", 2)
+    codebooks = _dev(codebooks, torch.float32, "codebooks", 3)
+    nq, d = q.shape
+    B, _, dpb = codebooks.shape
+    dev = q.device
+    if lut_i8_out is None:
+        lut_i8_out = torch.empty((nq, B, 16), dtype=torch.int8, device=dev)
+    if scale_out is None:
+        scale_out = torch.empty(nq, dtype=torch.float32, device=dev)
+    if bias_out is None:
+        bias_out = torch.empty(nq, dtype=torch.float32, device=dev)
+    if lut_f32_out is None and want_f32:
+        lut_f32_out = torch.empty((nq, B, 16), dtype=torch.float32, device=dev)
+    _dev(lut_i8_out, torch.int8, "lut_i8_out")
+    _dev(scale_out, torch.float32, "scale_out")
+    _dev(bias_out, torch.float32, "bias_out")
+    _dev(lut_f32_out, torch.float32, "lut_f32_out")
+    _check(lib().ah_build_lut(_ptr(q), nq, d, _ptr(codebooks), B, dpb, _ptr(lut_f32_out), _ptr(lut_i8_out),
+                              _ptr(scale_out), _ptr(bias_out), _stream(stream)), "ah_build_lut")
+    return lut_i8_out, scale_out, bias_out, lut_f32_out
+
+
+# ----------------------------------------------------------------------------- steps 3+4
+def ah_scan_workspace_bytes(nq: int, B: int, n: int, L: int, nl: int, R: int) -> int:
+    return int(lib().ah_scan_workspace_bytes(nq, B, n, L, nl, R))
+
+
+def ah_scan_topk(lut_i8, codes, R, ids=None, leaf_offsets=None, leaves=None, cand_ids_out=None,
+                 cand_scores_out=None, workspace=None, stream=None):
+    """Top-R rows per query by exact int32 sum of table entries.
+    codes: uint8 [n, stride]; leaves: int32 [nq, nl] or None (scan all rows)."""
+    lut_i8 = _dev(lut_i8, torch.int8, "lut_i8", 3)
+    codes = _dev(codes, torch.uint8, "codes", 2)
+    _dev(ids, torch.int32, "ids")
+    _dev(leaf_offsets, torch.int64, "leaf_offsets")
+    _dev(leaves, torch.int32, "leaves")
+    nq, B, _ = lut_i8.shape
+    n, stride = codes.shape
+    L = 0 if leaf_offsets is None else leaf_offsets.numel() - 1
+    nl = 0 if leaves is None else leaves.shape[1]
+    dev = lut_i8.device
+    if cand_ids_out is None:
+        cand_ids_out = torch.empty((nq, R), dtype=torch.int32, device=dev)
+    if cand_scores_out is None:
+        cand_scores_out = torch.empty((nq, R), dtype=torch.int32, device=dev)
+    _dev(cand_ids_out, torch.int32, "cand_ids_out")
+    _dev(cand_scores_out, torch.int32, "cand_scores_out")
+    Lw, nlw = (L, nl) if leaves is not None else (0, 0)
+    need = ah_scan_workspace_bytes(nq, B, n, Lw, nlw, R)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib().ah_scan_topk(_ptr(lut_i8), nq, B, _ptr(codes), stride, n, _ptr(ids), _ptr(leaf_offsets), L,
+                              _ptr(leaves), nl, R, _ptr(cand_ids_out), _ptr(cand_scores_out), _ptr(workspace),
+                              workspace.numel(), _stream(stream)), "ah_scan_topk")
+    return cand_ids_out, cand_scores_out
+
+
+# ----------------------------------------------------------------------------- step 5
+def ah_reorder_exact(q, base, cand_ids, k, ids_out=None, scores_out=None, stream=None):
+    """Exact rescoring of candidates; base is float32 [n, d] or bfloat16 [n, d]."""
+    q = _dev(q, torch.float32, "q", 2)
+    cand_ids = _dev(cand_ids, torch.int32, "cand_ids", 2)
+    if base.dtype == torch.float32:
+        dt = AH_F32
+    elif base.dtype == torch.bfloat16:
+        dt = AH_BF16
+    else:
+        raise TypeError("base must be float32 or bfloat16")
+    _dev(base, base.dtype, "base", 2)
+    nq, d = q.shape
+    n = base.shape[0]
+    R = cand_ids.shape[1]
+    dev = q.device
+    if ids_out is None:
+        ids_out = torch.empty((nq, k), dtype=torch.int32, device=dev)
+    if scores_out is None:
+        scores_out = torch.empty((nq, k), dtype=torch.float32, device=dev)
+    _dev(ids_out, torch.int32, "ids_out")
+    _dev(scores_out, torch.float32, "scores_out")
+    _check(lib().ah_reorder_exact(_ptr(q), nq, d, _ptr(base), dt, n, _ptr(cand_ids), R, k, _ptr(ids_out),
+                                  _ptr(scores_out), _stream(stream)), "ah_reorder_exact")
+    return ids_out, scores_out

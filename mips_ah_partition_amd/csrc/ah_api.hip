@@ -1,0 +1,92 @@
+// C ABI of the AH search path (declared in include/ah.h): argument checks on the
+// host, workspace sizing, and the kernel launches.  Nothing here allocates,
+// synchronises or keeps state between calls.
+#include "../../include/ah.h"
+#include "ah_kernels.hpp"
+
+namespace {
+
+inline bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? AH_OK : AH_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ah_status_string(int status) {
+    switch (status) {
+        case AH_OK: return "ok";
+        case AH_ERR_NULL: return "a required pointer is NULL";
+        case AH_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+        case AH_ERR_UNSUPPORTED: return "unsupported argument (dtype, alignment or a size above the library limits)";
+        case AH_ERR_WORKSPACE: return "workspace missing or smaller than required";
+        case AH_ERR_HIP: return "a HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int ah_version(void) { return 1; }
+
+size_t ah_partition_workspace_bytes(int64_t nq, int32_t L) {
+    if (nq < 0 || L < 0) return 0;
+    return ah::partition_workspace_bytes(nq, L);
+}
+
+int ah_partition_score(const float* q, int64_t nq, int32_t d, const float* centroids, int32_t L,
+                       int32_t nl, int32_t* leaves_out, float* leaf_scores_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (nq < 0 || d < 1 || L < 1 || nl < 1 || nl > L) return AH_ERR_SHAPE;
+    if (d > AH_MAX_DIM || nl > AH_MAX_R) return AH_ERR_UNSUPPORTED;
+    if (nq == 0) return AH_OK;
+    if (!q || !centroids || !leaves_out || !workspace) return AH_ERR_NULL;
+    if (workspace_bytes < ah::partition_workspace_bytes(nq, L)) return AH_ERR_WORKSPACE;
+    return hip_status(ah::launch_partition(q, nq, d, centroids, L, nl, leaves_out, leaf_scores_out,
+                                           workspace, static_cast<hipStream_t>(stream)));
+}
+
+int ah_build_lut(const float* q, int64_t nq, int32_t d, const float* codebooks, int32_t B,
+                 int32_t dpb, float* lut_f32_out, int8_t* lut_i8_out, float* scale_out,
+                 float* bias_out, void* stream) {
+    if (nq < 0 || B < 1 || dpb < 1 || (int64_t)B * dpb != d) return AH_ERR_SHAPE;
+    if (B > AH_MAX_BLOCKS || dpb > AH_MAX_DPB || B > AH_LUT_MAX_BLOCKS) return AH_ERR_UNSUPPORTED;
+    if (nq == 0) return AH_OK;
+    if (!q || !codebooks || !lut_i8_out || !scale_out || !bias_out) return AH_ERR_NULL;
+    return hip_status(ah::launch_build_lut(q, nq, d, codebooks, B, dpb, lut_f32_out, lut_i8_out,
+                                           scale_out, bias_out, static_cast<hipStream_t>(stream)));
+}
+
+size_t ah_scan_workspace_bytes(int64_t nq, int32_t B, int64_t n, int32_t L, int32_t nl, int32_t R) {
+    if (nq < 0 || n < 0 || B < 1 || R < 1) return 0;
+    return ah::scan_workspace_bytes(nq, B, n, L, nl, R);
+}
+
+int ah_scan_topk(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* codes,
+                 int32_t code_stride, int64_t n, const int32_t* ids, const int64_t* leaf_offsets,
+                 int32_t L, const int32_t* leaves, int32_t nl, int32_t R, int32_t* cand_ids_out,
+                 int32_t* cand_scores_out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (nq < 0 || n < 0 || B < 1 || R < 1 || code_stride < (B + 1) / 2) return AH_ERR_SHAPE;
+    if (leaves && (L < 1 || nl < 1 || nl > L || !leaf_offsets)) return AH_ERR_SHAPE;
+    if (B > AH_MAX_BLOCKS || R > AH_MAX_R || n >= ((int64_t)1 << 31)) return AH_ERR_UNSUPPORTED;
+    if (nq == 0) return AH_OK;
+    if (!lut_i8 || !cand_ids_out || !cand_scores_out || (n > 0 && !codes)) return AH_ERR_NULL;
+    if (!a16(lut_i8)) return AH_ERR_UNSUPPORTED;
+    const int32_t Lw = leaves ? L : 0, nlw = leaves ? nl : 0;
+    if (!workspace || workspace_bytes < ah::scan_workspace_bytes(nq, B, n, Lw, nlw, R)) return AH_ERR_WORKSPACE;
+    ah::ScanProblem sp{lut_i8, nq, B, codes, code_stride, n, ids, leaves ? leaf_offsets : nullptr, Lw,
+                       leaves, nlw, R, cand_ids_out, cand_scores_out};
+    return hip_status(ah::launch_scan(sp, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+int ah_reorder_exact(const float* q, int64_t nq, int32_t d, const void* base, int32_t base_dtype,
+                     int64_t n, const int32_t* cand_ids, int32_t R, int32_t k, int32_t* ids_out,
+                     float* scores_out, void* stream) {
+    if (nq < 0 || d < 1 || n < 0 || R < 1 || k < 1 || k > R) return AH_ERR_SHAPE;
+    if ((base_dtype != AH_F32 && base_dtype != AH_BF16) || R > AH_MAX_R || d > AH_MAX_DIM) return AH_ERR_UNSUPPORTED;
+    if (nq == 0) return AH_OK;
+    if (!q || !cand_ids || !ids_out || !scores_out || (n > 0 && !base)) return AH_ERR_NULL;
+    return hip_status(ah::launch_reorder(q, nq, d, base, base_dtype, n, cand_ids, R, k, ids_out,
+                                         scores_out, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

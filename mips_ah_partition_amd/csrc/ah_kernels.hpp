@@ -1,0 +1,44 @@
+// Host-side launch interface of the kernels behind the C ABI in include/ah.h.
+// The C-ABI layer (ah_api.hip) validates arguments, lays out workspaces and
+// calls these; each returns the launch status.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define AH_LUT_MAX_BLOCKS 4096
+
+namespace ah {
+
+hipError_t launch_build_lut(const float* q, int64_t nq, int32_t d, const float* cb, int32_t B,
+                            int32_t dpb, float* lut_f32, int8_t* lut_i8, float* scale, float* bias,
+                            hipStream_t stream);
+
+size_t partition_workspace_bytes(int64_t nq, int32_t L);
+hipError_t launch_partition(const float* q, int64_t nq, int32_t d, const float* cent, int32_t L,
+                            int32_t nl, int32_t* leaves, float* scores, void* ws, hipStream_t stream);
+
+struct ScanProblem {
+    const int8_t* lut;
+    int64_t nq;
+    int32_t B;
+    const uint8_t* codes;
+    int32_t stride;
+    int64_t n;
+    const int32_t* ids;
+    const int64_t* leaf_offsets;
+    int32_t L;
+    const int32_t* leaves;
+    int32_t nl;
+    int32_t R;
+    int32_t* out_ids;
+    int32_t* out_scores;
+};
+size_t scan_workspace_bytes(int64_t nq, int32_t B, int64_t n, int32_t L, int32_t nl, int32_t R);
+hipError_t launch_scan(const ScanProblem& p, void* ws, size_t ws_bytes, hipStream_t stream);
+
+hipError_t launch_reorder(const float* q, int64_t nq, int32_t d, const void* base, int32_t dtype,
+                          int64_t n, const int32_t* cand, int32_t R, int32_t k, int32_t* ids,
+                          float* scores, hipStream_t stream);
+
+}  // namespace ah

@@ -1,0 +1,736 @@
+// Code scan and top-R: for each query, the integer sum of its int8 table
+// entries at every scanned row's 4-bit codes, and the R best rows by
+// (sum desc, original id asc).
+//
+// Source: page "ScaNN: Anisotropic Vector Quantization for Maximum Inner
+// Product Search", section "Three stages of a search" (a row's approximate
+// score is the sum of its table entries), "Using the library"
+// (pre_reorder_num_neighbors candidates go on to reorder) and "Worked example:
+// cost of one query" (the scan dominates; batching queries improves reuse of
+// leaf data).
+//
+// gfx950 design
+//  * The sum over blocks of T8[q][b][code(i,b)] is the contraction
+//      sums[i][q] = sum_{b,c} onehot[i][(b,c)] * T8[q][(b,c)]
+//    with K = 16*B.  The scan runs it on the int8 matrix cores
+//    (v_mfma_i32_16x16x64_i8: exact int32 accumulation): the A operand is the
+//    one-hot expansion of 16 rows' codes, built in registers (one block per lane
+//    per k-step, 16 bytes with a single 1), the B operand is 16 queries' table
+//    rows, resident in LDS.  Each lane of a 16-lane group feeds its own block,
+//    and A and B use the same (lane group, byte) -> (block, center) map, so the
+//    hardware's internal k order does not matter.
+//  * A workgroup (8 waves) owns up to 64 queries and a run of rows (a leaf, or a
+//    chunk of the database); each wave takes 64 rows x 64 queries per tile
+//    (4 x 4 MFMA tiles), so every code byte fetched from HBM is used by all the
+//    workgroup's queries and every one-hot operand by 4 query tiles.  The
+//    tables stay in LDS (64 blocks x 64 queries = 64 KB per pass; more blocks
+//    are processed in 64-block chunks); codes are streamed into LDS with 16-byte
+//    loads, prefetched one step ahead.
+//  * Top-R without materialising sums: every query has a monotone threshold tau
+//    (a lower bound on its R-th best sum).  A warm-up kernel sets it from the
+//    query's first rows; rows at or above it are logged per wave in LDS and
+//    appended to the query's candidate list; a histogram of the appended sums
+//    lets each workgroup raise tau after every item (count(sum >= edge) >= R
+//    makes the edge a valid bound).  A final kernel selects each query's exact
+//    top-R from its list; a query whose list overflows is recomputed by a slow
+//    exact fallback, so the result never depends on timing.
+#include "ah_device.hpp"
+#include "ah_kernels.hpp"
+
+#include <limits.h>
+
+namespace ah {
+
+constexpr int kScanWaves = 8;
+constexpr int kScanThreads = kScanWaves * kWave;  // 512
+constexpr int kTilePts = 64 * kScanWaves;         // rows per tile
+constexpr int kQG = 64;                           // queries per item
+constexpr int kKC = 16;                           // k-steps (x4 blocks) per chunk
+constexpr int kCodeStride = 9;                    // LDS row stride (dwords) for a chunk's 8 code dwords
+constexpr int kNB = 1024;                         // histogram bins per query
+constexpr int kLogCap = 256;                      // logged hits per wave
+constexpr int kItemPts = 8192;                    // rows per item
+constexpr int kFbSlots = 4;                       // fallback workgroups
+constexpr int kSelThreads = 256;
+constexpr int kSelLds = 4096;                     // keys staged in LDS by the final select
+
+struct ScanLayout {
+    size_t tau, cnt, hmax, hist, cand, ctrl, ovf, fb, lcnt, lqoff, lcur, qlist, itemoff, total;
+    int64_t cap;
+};
+
+static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static ScanLayout scan_layout(int64_t nq, int32_t B, int64_t n, int32_t L, int32_t nl, int32_t R) {
+    (void)B;
+    ScanLayout s{};
+    int64_t cap = 16 * (int64_t)R;
+    if (cap < 32768) cap = 32768;
+    if (cap > n) cap = n > 0 ? n : 1;
+    s.cap = cap;
+    size_t o = 0;
+    s.tau = o;     o = align_up(o + (size_t)nq * 4);
+    s.cnt = o;     o = align_up(o + (size_t)nq * 4);
+    s.hmax = o;    o = align_up(o + (size_t)nq * 4);
+    s.hist = o;    o = align_up(o + (size_t)nq * kNB * 4);
+    s.cand = o;    o = align_up(o + (size_t)nq * (size_t)cap * 8);
+    s.ctrl = o;    o = align_up(o + 64);
+    s.ovf = o;     o = align_up(o + (size_t)nq * 4);
+    s.fb = o;      o = align_up(o + (size_t)kFbSlots * (size_t)(n > 0 ? n : 1) * 8);
+    const bool part = L > 0 && nl > 0;
+    s.lcnt = o;    o = align_up(o + (part ? (size_t)L * 4 : 0));
+    s.lqoff = o;   o = align_up(o + (part ? (size_t)(L + 1) * 4 : 0));
+    s.lcur = o;    o = align_up(o + (part ? (size_t)L * 4 : 0));
+    s.qlist = o;   o = align_up(o + (part ? (size_t)nq * nl * 4 : 0));
+    s.itemoff = o; o = align_up(o + (part ? (size_t)(L + 1) * 8 : 0));
+    s.total = o;
+    return s;
+}
+
+size_t scan_workspace_bytes(int64_t nq, int32_t B, int64_t n, int32_t L, int32_t nl, int32_t R) {
+    return scan_layout(nq, B, n, L, nl, R).total;
+}
+
+struct ScanState {
+    int32_t* tau;
+    uint32_t* cnt;
+    uint32_t* hmax;
+    uint32_t* hist;
+    uint64_t* cand;
+    uint32_t* ctrl;  // [0] work counter, [1] overflow count, [2] fallback cursor
+    int32_t* ovf;
+    uint64_t* fb;
+    int64_t cap;
+    int32_t hlo, hw;
+};
+
+struct Problem {
+    const int8_t* lut;
+    int64_t nq;
+    int32_t B;
+    const uint8_t* codes;
+    int32_t stride;
+    int64_t n;
+    const int32_t* ids;
+    const int64_t* leaf_offsets;
+    int32_t L;
+    const int32_t* leaves;
+    int32_t nl;
+    int32_t R;
+    int32_t* out_ids;
+    int32_t* out_scores;
+};
+
+__device__ __forceinline__ int hist_bin(int32_t s, int32_t hlo, int32_t hw) {
+    int64_t j = ((int64_t)s - hlo) / hw;
+    return (int)(j < 0 ? 0 : (j >= kNB ? kNB - 1 : j));
+}
+__device__ __forceinline__ int32_t ld_coherent(const int32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_coherent(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int nibble(const uint8_t* row, int b) { return (row[b >> 1] >> (4 * (b & 1))) & 15; }
+
+// Sum of one row's table entries; the table is int8 [B][16] in LDS.
+__device__ __forceinline__ int32_t row_sum(const int8_t* lut_s, int32_t B, const uint8_t* row, bool aligned4) {
+    int32_t s = 0;
+    if (aligned4) {
+        const uint32_t* r32 = reinterpret_cast<const uint32_t*>(row);
+        for (int b0 = 0; b0 < B; b0 += 8) {
+            const uint32_t wv = r32[b0 >> 3];
+            const int lim = B - b0 < 8 ? B - b0 : 8;
+            for (int t = 0; t < lim; ++t) s += lut_s[(b0 + t) * 16 + ((wv >> (4 * t)) & 15)];
+        }
+    } else {
+        for (int b = 0; b < B; ++b) s += lut_s[b * 16 + nibble(row, b)];
+    }
+    return s;
+}
+
+// ------------------------------------------------------------------ leaf -> query inversion
+__global__ void zero_u32_kernel(uint32_t* p, int64_t count) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+__global__ void leaf_count_kernel(const int32_t* __restrict__ leaves, int64_t pairs, int32_t L,
+                                  uint32_t* __restrict__ lcnt) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < pairs; i += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t l = leaves[i];
+        if (l >= 0 && l < L) atomicAdd(&lcnt[l], 1u);
+    }
+}
+
+// Single workgroup: query offsets per leaf and item offsets per leaf.
+__global__ __launch_bounds__(1024) void leaf_scan_kernel(const uint32_t* __restrict__ lcnt,
+                                                         const int64_t* __restrict__ leaf_offsets, int32_t L,
+                                                         int32_t* __restrict__ lqoff, int64_t* __restrict__ itemoff) {
+    __shared__ int64_t part_q[1024], part_i[1024];
+    const int tid = threadIdx.x;
+    const int64_t per = (L + 1023) / 1024;
+    const int64_t a = tid * per, b = (a + per < L) ? a + per : L;
+    int64_t sq = 0, si = 0;
+    for (int64_t l = a; l < b; ++l) {
+        const int64_t nqL = lcnt[l];
+        const int64_t rows = leaf_offsets[l + 1] - leaf_offsets[l];
+        sq += nqL;
+        si += (nqL > 0 && rows > 0) ? ((nqL + kQG - 1) / kQG) * ((rows + kItemPts - 1) / kItemPts) : 0;
+    }
+    part_q[tid] = sq;
+    part_i[tid] = si;
+    __syncthreads();
+    if (tid == 0) {
+        int64_t cq = 0, ci = 0;
+        for (int t = 0; t < 1024; ++t) {
+            const int64_t x = part_q[t], y = part_i[t];
+            part_q[t] = cq;
+            part_i[t] = ci;
+            cq += x;
+            ci += y;
+        }
+        lqoff[L] = (int32_t)cq;
+        itemoff[L] = ci;
+    }
+    __syncthreads();
+    int64_t cq = part_q[tid], ci = part_i[tid];
+    for (int64_t l = a; l < b; ++l) {
+        lqoff[l] = (int32_t)cq;
+        itemoff[l] = ci;
+        const int64_t nqL = lcnt[l];
+        const int64_t rows = leaf_offsets[l + 1] - leaf_offsets[l];
+        cq += nqL;
+        ci += (nqL > 0 && rows > 0) ? ((nqL + kQG - 1) / kQG) * ((rows + kItemPts - 1) / kItemPts) : 0;
+    }
+}
+
+__global__ void leaf_scatter_kernel(const int32_t* __restrict__ leaves, int64_t nq, int32_t nl, int32_t L,
+                                    const int32_t* __restrict__ lqoff, uint32_t* __restrict__ lcur,
+                                    int32_t* __restrict__ qlist) {
+    const int64_t pairs = nq * nl;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < pairs; i += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t l = leaves[i];
+        if (l < 0 || l >= L) continue;
+        const uint32_t pos = atomicAdd(&lcur[l], 1u);
+        qlist[lqoff[l] + pos] = (int32_t)(i / nl);
+    }
+}
+
+// ------------------------------------------------------------------ warm-up threshold
+// One workgroup per query: sum the first W rows of the query's scan order (its
+// leaves in probe order, or rows 0..W-1), set tau to the R-th best of them
+// (a valid lower bound on the R-th best over all scanned rows), and clear the
+// query's candidate count and histogram.
+__global__ __launch_bounds__(kSelThreads) void warmup_kernel(Problem p, ScanState st, int32_t W) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ SelectShared sh;
+    __shared__ int64_t got_s;
+    const int64_t q = blockIdx.x;
+    const int tid = threadIdx.x;
+    int8_t* lut_s = reinterpret_cast<int8_t*>(smem);
+    uint64_t* keys = reinterpret_cast<uint64_t*>(smem + (((size_t)p.B * 16 + 15) & ~(size_t)15));
+    for (int e = tid; e < p.B * 16; e += kSelThreads) lut_s[e] = p.lut[q * p.B * 16 + e];
+    for (int j = tid; j < kNB; j += kSelThreads) st.hist[q * kNB + j] = 0;
+    if (tid == 0) {
+        st.cnt[q] = 0;
+        st.hmax[q] = 0;
+        got_s = 0;
+    }
+    for (int j = tid; j < W; j += kSelThreads) keys[j] = 0;
+    __syncthreads();
+    const bool al4 = (p.stride & 3) == 0 && (reinterpret_cast<uintptr_t>(p.codes) & 3) == 0;
+    const int nsrc = p.leaves ? p.nl : 1;
+    for (int j = 0; j < nsrc; ++j) {
+        const int64_t got = got_s;
+        if (got >= W) break;
+        int64_t a, b;
+        if (p.leaves) {
+            const int32_t l = p.leaves[q * p.nl + j];
+            const bool okl = l >= 0 && l < p.L;
+            a = okl ? p.leaf_offsets[l] : 0;
+            b = okl ? p.leaf_offsets[l + 1] : 0;
+        } else {
+            a = 0;
+            b = p.n;
+        }
+        int64_t take = b - a;
+        if (take > W - got) take = W - got;
+        for (int64_t t = tid; t < take; t += kSelThreads) {
+            const int64_t row = a + t;
+            const int32_t s = row_sum(lut_s, p.B, p.codes + row * p.stride, al4);
+            keys[got + t] = int_key(s, p.ids ? p.ids[row] : (int32_t)row);
+        }
+        __syncthreads();
+        if (tid == 0) got_s = got + take;
+        __syncthreads();
+    }
+    int nvalid = 0;
+    const uint64_t kth = wg_kth_largest<kSelThreads>(LdsKeys{keys}, W, p.R, sh, &nvalid);
+    if (tid == 0) st.tau[q] = nvalid >= p.R ? key_int_score(kth) : INT_MIN;
+    if (q == 0 && tid < 16) st.ctrl[tid] = 0;
+}
+
+// ------------------------------------------------------------------ main scan
+struct MainArgs {
+    Problem p;
+    ScanState st;
+    int32_t nkstep;   // k-steps of 4 blocks (blocks rounded up to 8)
+    int32_t nchunk;   // 64-block chunks
+    int32_t nqg;      // query groups (full scan)
+    int64_t n_items;  // items (full scan); partitioned: itemoff[L]
+    const int32_t* lqoff;
+    const int32_t* qlist;
+    const int64_t* itemoff;
+    int fast_codes;   // rows 16-byte aligned (stride % 16 == 0)
+};
+
+__device__ __forceinline__ v4i onehot16(uint32_t x) {
+    // x & 15 = center index; returns 16 bytes with a single 1 at that index
+    const uint32_t sh8 = (x & 7u) << 3;
+    const uint64_t t = 1ull << sh8;
+    const uint32_t m = 0u - ((x >> 3) & 1u);
+    const uint32_t tl = (uint32_t)t, th = (uint32_t)(t >> 32);
+    v4i r;
+    r.x = (int)(tl & ~m);
+    r.y = (int)(th & ~m);
+    r.z = (int)(tl & m);
+    r.w = (int)(th & m);
+    return r;
+}
+
+// Appends a wave's logged hits to the queries' candidate lists and histograms.
+// Log entry: sum (high 32 bits) | local query (bits 16..21) | row - p0 (low 16).
+__device__ __forceinline__ void flush_log(const Problem& p, const ScanState& st, const uint64_t* log,
+                                          int log_n, const int32_t* qid_s, uint32_t* qapp_s, int64_t p0) {
+    const int lane = lane_id();
+    for (int base = 0; base < log_n; base += 4 * kWave) {
+        uint64_t ent[4];
+        uint32_t slot[4];
+        int32_t idv[4];
+        int qq[4];
+        bool ok[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = base + u * kWave + lane;
+            ok[u] = e < log_n;
+            ent[u] = ok[u] ? log[e] : 0;
+            qq[u] = qid_s[(ent[u] >> 16) & 63];
+            const int64_t row = p0 + (int64_t)(ent[u] & 0xFFFF);
+            if (ok[u]) {
+                slot[u] = atomicAdd(&st.cnt[qq[u]], 1u);
+                idv[u] = p.ids ? p.ids[row] : (int32_t)row;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (!ok[u]) continue;
+            const int32_t s = (int32_t)(uint32_t)(ent[u] >> 32);
+            if ((int64_t)slot[u] < st.cap) st.cand[(int64_t)qq[u] * st.cap + slot[u]] = int_key(s, idv[u]);
+            const int bin = hist_bin(s, st.hlo, st.hw);
+            atomicAdd(&st.hist[(int64_t)qq[u] * kNB + bin], 1u);
+            atomicMax(&st.hmax[qq[u]], (uint32_t)bin);
+            atomicAdd(&qapp_s[(ent[u] >> 16) & 63], 1u);
+        }
+    }
+}
+
+// Raises tau of query q to the highest histogram edge with at least R appended
+// sums at or above it (one wave).
+__device__ __forceinline__ void refresh_tau(const ScanState& st, int q, int R) {
+    const int lane = lane_id();
+    const int32_t tcur = ld_coherent(st.tau + q);
+    const int jt = tcur == INT_MIN ? 0 : hist_bin(tcur, st.hlo, st.hw);
+    const int jm = (int)ld_coherent(st.hmax + q);
+    int cum = 0;
+    for (int top = jm; top >= jt; top -= kWave) {
+        const int j = top - lane;
+        const int v = j >= jt ? (int)ld_coherent(st.hist + (int64_t)q * kNB + j) : 0;
+        const int incl = wave_inclusive_sum(v);
+        const uint64_t mk = __ballot(cum + incl >= R);
+        if (mk) {
+            const int l = __ffsll((unsigned long long)mk) - 1;
+            if (lane == 0) atomicMax(st.tau + q, (int32_t)(st.hlo + (int64_t)(top - l) * st.hw));
+            return;
+        }
+        cum += __shfl(incl, kWave - 1, kWave);
+    }
+}
+
+__global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) {
+    __shared__ __align__(16) int8_t lut_s[kKC * 4 * kWave * 16];  // [kstep][ntile][lane][16]
+    __shared__ __align__(16) uint32_t code_s[kTilePts * kCodeStride];
+    __shared__ uint64_t log_s[kScanWaves * kLogCap];
+    __shared__ int32_t qid_s[kQG];
+    __shared__ uint32_t qapp_s[kQG];
+    __shared__ int64_t item_s, p0_s, p1_s, qbase_s;
+    __shared__ int32_t qn_s;
+
+    const Problem& p = a.p;
+    const ScanState& st = a.st;
+    const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int64_t n_items = p.leaves ? a.itemoff[p.L] : a.n_items;
+    uint64_t* mylog = log_s + w * kLogCap;
+
+    for (;;) {
+        if (tid == 0) {
+            const int64_t item = (int64_t)atomicAdd(&st.ctrl[0], 1u);
+            item_s = item;
+            if (item < n_items) {
+                int64_t p0, p1, qbase;
+                int qn;
+                if (!p.leaves) {
+                    const int64_t chunk = item / a.nqg, grp = item % a.nqg;
+                    p0 = chunk * kItemPts;
+                    p1 = p0 + kItemPts < p.n ? p0 + kItemPts : p.n;
+                    qbase = grp * kQG;
+                    qn = (int)(p.nq - qbase < kQG ? p.nq - qbase : kQG);
+                } else {
+                    int lo = 0, hi = p.L;  // largest l with itemoff[l] <= item
+                    while (hi - lo > 1) {
+                        const int mid = (lo + hi) >> 1;
+                        if (a.itemoff[mid] <= item) lo = mid; else hi = mid;
+                    }
+                    const int l = lo;
+                    const int64_t nqL = a.lqoff[l + 1] - a.lqoff[l];
+                    const int64_t ng = (nqL + kQG - 1) / kQG;
+                    const int64_t loc = item - a.itemoff[l];
+                    const int64_t chunk = loc / ng, grp = loc % ng;
+                    const int64_t ra = p.leaf_offsets[l], rb = p.leaf_offsets[l + 1];
+                    p0 = ra + chunk * kItemPts;
+                    p1 = p0 + kItemPts < rb ? p0 + kItemPts : rb;
+                    qbase = a.lqoff[l] + grp * kQG;
+                    qn = (int)(nqL - grp * kQG < kQG ? nqL - grp * kQG : kQG);
+                }
+                p0_s = p0;
+                p1_s = p1;
+                qbase_s = qbase;
+                qn_s = qn;
+            }
+        }
+        __syncthreads();
+        const int64_t item = item_s;
+        if (item >= n_items) break;
+        const int64_t p0 = p0_s, p1 = p1_s;
+        const int qn = qn_s;
+        if (tid < kQG) {
+            int32_t qq = 0;
+            if (tid < qn) qq = p.leaves ? a.qlist[qbase_s + tid] : (int32_t)(qbase_s + tid);
+            qid_s[tid] = qq;
+            qapp_s[tid] = 0;
+        }
+        __syncthreads();
+
+        // table staging: B operand layout [kstep][ntile][lane][16 bytes]
+        auto stage_lut = [&](int c) {
+            for (int e = tid; e < kKC * 4 * kWave; e += kScanThreads) {
+                const int s = e >> 8, nt = (e >> 6) & 3, ln = e & 63;
+                const int ql = 16 * nt + (ln & 15);
+                const int blk = c * 64 + 4 * s + (ln >> 4);
+                v4i v = {0, 0, 0, 0};
+                if (ql < qn && blk < p.B)
+                    v = *reinterpret_cast<const v4i*>(p.lut + ((int64_t)qid_s[ql] * p.B + blk) * 16);
+                *reinterpret_cast<v4i*>(lut_s + e * 16) = v;
+            }
+        };
+        // code staging: thread t owns row tile0 + t, code bytes [32c, 32c+32)
+        auto load_codes = [&](int64_t tile0, int c, uint4& x0, uint4& x1) {
+            x0 = make_uint4(0, 0, 0, 0);
+            x1 = make_uint4(0, 0, 0, 0);
+            const int64_t row = tile0 + tid;
+            if (row >= p1) return;
+            const uint8_t* src = p.codes + row * p.stride + 32 * c;
+            if (a.fast_codes) {
+                const int avail = p.stride - 32 * c;
+                if (avail >= 16) x0 = *reinterpret_cast<const uint4*>(src);
+                if (avail >= 32) x1 = *reinterpret_cast<const uint4*>(src + 16);
+            } else {
+                const int cb = (p.B + 1) / 2 - 32 * c;
+                uint32_t wd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                for (int i = 0; i < 32 && i < cb; ++i) wd[i >> 2] |= (uint32_t)src[i] << (8 * (i & 3));
+                x0 = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                x1 = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+            }
+        };
+
+        if (a.nchunk == 1) stage_lut(0);
+
+        const int64_t ntiles = (p1 - p0 + kTilePts - 1) / kTilePts;
+        const int64_t nsteps = ntiles * a.nchunk;
+        uint4 px0, px1;
+        load_codes(p0, 0, px0, px1);
+        v4i acc[4][4];
+        int32_t tq[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+        int log_n = 0;
+
+        for (int64_t step = 0; step < nsteps; ++step) {
+            const int64_t t = step / a.nchunk;
+            const int c = (int)(step % a.nchunk);
+            const int64_t tile0 = p0 + t * kTilePts;
+            if (c == 0) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt) acc[m][nt] = v4i{0, 0, 0, 0};
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    const int ql = 16 * nt + r16;
+                    tq[nt] = ql < qn ? ld_coherent(st.tau + qid_s[ql]) : INT_MAX;
+                }
+            }
+            if (a.nchunk > 1) stage_lut(c);
+            {
+                uint32_t* d = code_s + tid * kCodeStride;
+                d[0] = px0.x; d[1] = px0.y; d[2] = px0.z; d[3] = px0.w;
+                d[4] = px1.x; d[5] = px1.y; d[6] = px1.z; d[7] = px1.w;
+            }
+            __syncthreads();
+            if (step + 1 < nsteps) {
+                const int64_t t2 = (step + 1) / a.nchunk;
+                load_codes(p0 + t2 * kTilePts, (int)((step + 1) % a.nchunk), px0, px1);
+            }
+            const int ks = a.nkstep - c * kKC < kKC ? a.nkstep - c * kKC : kKC;
+            const uint32_t* crow = code_s + (w * 64 + r16) * kCodeStride;
+            for (int j = 0; j < (ks >> 1); ++j) {
+                uint32_t cw[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) cw[m] = crow[m * 16 * kCodeStride + j];
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int s = 2 * j + s2;
+                    v4i bf[4];
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt)
+                        bf[nt] = *reinterpret_cast<const v4i*>(lut_s + ((s * 4 + nt) * kWave + lane) * 16);
+                    const uint32_t shf = 16 * s2 + 4 * g;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const v4i af = onehot16(cw[m] >> shf);
+#pragma unroll
+                        for (int nt = 0; nt < 4; ++nt)
+                            acc[m][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[nt], acc[m][nt], 0, 0, 0);
+                    }
+                }
+            }
+            __syncthreads();
+            if (c != a.nchunk - 1) continue;
+
+            // filter: tile (m, nt) holds, in register i, the sum of row
+            // 16m + 4g + i (of this wave's 64) for query 16nt + r16
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int ql = 16 * nt + r16;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int64_t row = tile0 + w * 64 + m * 16 + 4 * g + i;
+                        const int32_t s = acc[m][nt][i];
+                        const bool hit = row < p1 && s >= tq[nt];
+                        const uint64_t mk = __ballot(hit);
+                        if (mk) {
+                            if (hit)
+                                mylog[log_n + __popcll(mk & lanemask_lt())] =
+                                    ((uint64_t)(uint32_t)s << 32) | ((uint64_t)ql << 16) | (uint64_t)(row - p0);
+                            log_n += __popcll(mk);
+                            if (log_n > kLogCap - kWave) {
+                                flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0);
+                                log_n = 0;
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        if (log_n > 0) flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0);
+        __syncthreads();
+        for (int ql = w; ql < qn; ql += kScanWaves)
+            if (qapp_s[ql] > 0) refresh_tau(st, qid_s[ql], p.R);
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------ final selection
+__global__ __launch_bounds__(kSelThreads) void final_select_kernel(Problem p, ScanState st) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ SelectShared sh;
+    __shared__ uint32_t nst;
+    const int64_t q = blockIdx.x;
+    const int tid = threadIdx.x;
+    const uint32_t total = st.cnt[q];
+    if ((int64_t)total > st.cap) {
+        if (tid == 0) {
+            const uint32_t k = atomicAdd(&st.ctrl[1], 1u);
+            st.ovf[k] = (int32_t)q;
+        }
+        return;
+    }
+    const int32_t tau = st.tau[q];
+    const uint64_t* list = st.cand + q * st.cap;
+    uint64_t* stage = reinterpret_cast<uint64_t*>(smem);
+    uint64_t* sel = stage + kSelLds;
+    if (tid == 0) nst = 0;
+    __syncthreads();
+    uint32_t mine = 0;
+    for (uint32_t i = tid; i < total; i += kSelThreads) mine += key_int_score(list[i]) >= tau;
+    atomicAdd(&nst, mine);
+    __syncthreads();
+    const uint32_t above = nst;
+    int m;
+    if (above <= (uint32_t)kSelLds) {
+        __syncthreads();
+        if (tid == 0) nst = 0;
+        __syncthreads();
+        for (uint32_t i = tid; i < total; i += kSelThreads) {
+            const uint64_t k = list[i];
+            if (key_int_score(k) >= tau) stage[atomicAdd(&nst, 1u)] = k;
+        }
+        __syncthreads();
+        m = wg_select_topk<kSelThreads>(LdsKeys{stage}, above, p.R, sh, sel);
+    } else {
+        m = wg_select_topk<kSelThreads>(GlobalKeysAbove{list, tau}, total, p.R, sh, sel);
+    }
+    for (int r = tid; r < p.R; r += kSelThreads) {
+        p.out_ids[q * p.R + r] = r < m ? key_id(sel[r]) : -1;
+        p.out_scores[q * p.R + r] = r < m ? key_int_score(sel[r]) : INT_MIN;
+    }
+}
+
+// ------------------------------------------------------------------ overflow fallback
+// A query whose candidate list overflowed is recomputed exactly: every scanned
+// row's key into a private scratch slot, then the exact selection.  Persistent
+// workgroups take overflowed queries from the list until it is exhausted.
+__global__ __launch_bounds__(kSelThreads) void fallback_kernel(Problem p, ScanState st) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ SelectShared sh;
+    __shared__ uint32_t item;
+    const int tid = threadIdx.x;
+    uint64_t* sel = reinterpret_cast<uint64_t*>(smem);
+    int8_t* lut_s = reinterpret_cast<int8_t*>(sel + next_pow2(p.R));
+    uint64_t* scratch = st.fb + (int64_t)blockIdx.x * (p.n > 0 ? p.n : 1);
+    const bool al4 = (p.stride & 3) == 0 && (reinterpret_cast<uintptr_t>(p.codes) & 3) == 0;
+    for (;;) {
+        if (tid == 0) item = atomicAdd(&st.ctrl[2], 1u);
+        __syncthreads();
+        const uint32_t it = item;
+        if (it >= ld_coherent(&st.ctrl[1])) break;
+        const int64_t q = st.ovf[it];
+        for (int e = tid; e < p.B * 16; e += kSelThreads) lut_s[e] = p.lut[q * p.B * 16 + e];
+        __syncthreads();
+        int64_t m = 0;
+        const int nsrc = p.leaves ? p.nl : 1;
+        for (int j = 0; j < nsrc; ++j) {
+            int64_t a, b;
+            if (p.leaves) {
+                const int32_t l = p.leaves[q * p.nl + j];
+                const bool okl = l >= 0 && l < p.L;
+                a = okl ? p.leaf_offsets[l] : 0;
+                b = okl ? p.leaf_offsets[l + 1] : 0;
+            } else {
+                a = 0;
+                b = p.n;
+            }
+            if (b - a > p.n - m) b = a + (p.n - m);
+            for (int64_t t = tid; t < b - a; t += kSelThreads) {
+                const int64_t row = a + t;
+                scratch[m + t] = int_key(row_sum(lut_s, p.B, p.codes + row * p.stride, al4),
+                                         p.ids ? p.ids[row] : (int32_t)row);
+            }
+            m += b - a;
+        }
+        __syncthreads();
+        const int k = wg_select_topk<kSelThreads>(LdsKeys{scratch}, m, p.R, sh, sel);
+        for (int r = tid; r < p.R; r += kSelThreads) {
+            p.out_ids[q * p.R + r] = r < k ? key_id(sel[r]) : -1;
+            p.out_scores[q * p.R + r] = r < k ? key_int_score(sel[r]) : INT_MIN;
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------ host side
+template <typename K>
+static void allow_lds(K kernel, size_t bytes) {
+    if (bytes > 48 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+static int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+    return cus;
+}
+
+hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStream_t stream) {
+    (void)ws_bytes;
+    if (sp.nq == 0) return hipSuccess;
+    const ScanLayout lay = scan_layout(sp.nq, sp.B, sp.n, sp.L, sp.nl, sp.R);
+    char* base = reinterpret_cast<char*>(ws);
+    Problem p{sp.lut, sp.nq, sp.B, sp.codes, sp.stride, sp.n, sp.ids, sp.leaf_offsets, sp.L,
+              sp.leaves, sp.nl, sp.R, sp.out_ids, sp.out_scores};
+    ScanState st{};
+    st.tau = reinterpret_cast<int32_t*>(base + lay.tau);
+    st.cnt = reinterpret_cast<uint32_t*>(base + lay.cnt);
+    st.hmax = reinterpret_cast<uint32_t*>(base + lay.hmax);
+    st.hist = reinterpret_cast<uint32_t*>(base + lay.hist);
+    st.cand = reinterpret_cast<uint64_t*>(base + lay.cand);
+    st.ctrl = reinterpret_cast<uint32_t*>(base + lay.ctrl);
+    st.ovf = reinterpret_cast<int32_t*>(base + lay.ovf);
+    st.fb = reinterpret_cast<uint64_t*>(base + lay.fb);
+    st.cap = lay.cap;
+    st.hlo = -127 * sp.B;
+    st.hw = (int32_t)((254LL * sp.B + 1 + kNB - 1) / kNB);
+    const bool part = sp.leaves != nullptr;
+    hipError_t e;
+
+    MainArgs ma{};
+    ma.p = p;
+    ma.st = st;
+    const int32_t B8 = (sp.B + 7) & ~7;
+    ma.nkstep = B8 / 4;
+    ma.nchunk = (ma.nkstep + kKC - 1) / kKC;
+    ma.nqg = (int32_t)((sp.nq + kQG - 1) / kQG);
+    ma.n_items = (int64_t)ma.nqg * ((sp.n + kItemPts - 1) / kItemPts);
+    ma.fast_codes = (sp.stride % 16) == 0 && (reinterpret_cast<uintptr_t>(sp.codes) & 15) == 0;
+    if (part) {
+        uint32_t* lcnt = reinterpret_cast<uint32_t*>(base + lay.lcnt);
+        uint32_t* lcur = reinterpret_cast<uint32_t*>(base + lay.lcur);
+        int32_t* lqoff = reinterpret_cast<int32_t*>(base + lay.lqoff);
+        int32_t* qlist = reinterpret_cast<int32_t*>(base + lay.qlist);
+        int64_t* itemoff = reinterpret_cast<int64_t*>(base + lay.itemoff);
+        hipLaunchKernelGGL(zero_u32_kernel, dim3(64), dim3(256), 0, stream, lcnt, (int64_t)sp.L);
+        hipLaunchKernelGGL(zero_u32_kernel, dim3(64), dim3(256), 0, stream, lcur, (int64_t)sp.L);
+        const int64_t pairs = sp.nq * sp.nl;
+        const unsigned gb = (unsigned)((pairs + 255) / 256 < 4096 ? (pairs + 255) / 256 : 4096);
+        hipLaunchKernelGGL(leaf_count_kernel, dim3(gb), dim3(256), 0, stream, sp.leaves, pairs, sp.L, lcnt);
+        hipLaunchKernelGGL(leaf_scan_kernel, dim3(1), dim3(1024), 0, stream, lcnt, sp.leaf_offsets, sp.L, lqoff, itemoff);
+        hipLaunchKernelGGL(leaf_scatter_kernel, dim3(gb), dim3(256), 0, stream, sp.leaves, sp.nq, sp.nl, sp.L, lqoff, lcur, qlist);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        ma.lqoff = lqoff;
+        ma.qlist = qlist;
+        ma.itemoff = itemoff;
+    }
+    int32_t W = 4 * sp.R;
+    if (W < 2048) W = 2048;
+    if (W > 8192) W = 8192;
+    const size_t lut_bytes = ((size_t)sp.B * 16 + 15) & ~(size_t)15;
+    allow_lds(warmup_kernel, lut_bytes + (size_t)W * 8);
+    hipLaunchKernelGGL(warmup_kernel, dim3((unsigned)sp.nq), dim3(kSelThreads), lut_bytes + (size_t)W * 8, stream, p, st, W);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t max_items = part ? (int64_t)sp.nq * sp.nl + sp.L : ma.n_items;
+    int grid = device_cus();
+    if (max_items < grid) grid = (int)(max_items > 0 ? max_items : 1);
+    hipLaunchKernelGGL(scan_main_kernel, dim3(grid), dim3(kScanThreads), 0, stream, ma);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    int Rp = 1;
+    while (Rp < sp.R) Rp <<= 1;
+    allow_lds(final_select_kernel, (size_t)(kSelLds + Rp) * 8);
+    hipLaunchKernelGGL(final_select_kernel, dim3((unsigned)sp.nq), dim3(kSelThreads), (size_t)(kSelLds + Rp) * 8, stream, p, st);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    allow_lds(fallback_kernel, (size_t)Rp * 8 + lut_bytes);
+    hipLaunchKernelGGL(fallback_kernel, dim3(kFbSlots), dim3(kSelThreads), (size_t)Rp * 8 + lut_bytes, stream, p, st);
+    return hipGetLastError();
+}
+
+}  // namespace ah

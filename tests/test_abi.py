@@ -1,0 +1,79 @@
+"""The C-ABI library loads, exports every symbol include/ah.h declares, and
+rejects bad arguments on the host before enqueueing anything (no GPU needed:
+these calls return before any HIP API is touched)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ah.h")
+LIB = os.path.join(ROOT, "mips_ah_partition_amd", "libah.so")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:const char\*|int|size_t)\s+(ah_\w+)\(", txt, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from mips_ah_partition_amd import build
+        build.build()
+    return C.CDLL(LIB)
+
+
+def test_header_declares_the_four_path_calls():
+    names = _declared()
+    for n in ("ah_partition_score", "ah_build_lut", "ah_scan_topk", "ah_reorder_exact"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from mips_ah_partition_amd import ahlib
+    names = _declared()
+    assert sorted(ahlib.EXPORTS) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    lib.ah_status_string.restype = C.c_char_p
+    for s in (0, -1, -2, -3, -4, -5):
+        assert lib.ah_status_string(s)
+    assert lib.ah_version() >= 1
+
+
+def test_host_side_validation(lib):
+    vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    lib.ah_scan_topk.argtypes = [vp, i64, i32, vp, i32, i64, vp, vp, i32, vp, i32, i32, vp, vp, vp, sz, vp]
+    lib.ah_build_lut.argtypes = [vp, i64, i32, vp, i32, i32, vp, vp, vp, vp, vp]
+    lib.ah_reorder_exact.argtypes = [vp, i64, i32, vp, i32, i64, vp, i32, i32, vp, vp, vp]
+    lib.ah_partition_score.argtypes = [vp, i64, i32, vp, i32, i32, vp, vp, vp, sz, vp]
+    lib.ah_scan_workspace_bytes.restype = sz
+    lib.ah_scan_workspace_bytes.argtypes = [i64, i32, i64, i32, i32, i32]
+    fake = vp(4096)  # never dereferenced: every case below fails validation first
+    # scan: stride too small, R < 1, nl > L, missing pointers, R too large, no workspace
+    assert lib.ah_scan_topk(fake, 2, 8, fake, 3, 10, None, None, 0, None, 0, 5, fake, fake, fake, 1 << 30, None) == -2
+    assert lib.ah_scan_topk(fake, 2, 8, fake, 4, 10, None, None, 0, None, 0, 0, fake, fake, fake, 1 << 30, None) == -2
+    assert lib.ah_scan_topk(fake, 2, 8, fake, 4, 10, None, fake, 3, fake, 4, 5, fake, fake, fake, 1 << 30, None) == -2
+    assert lib.ah_scan_topk(None, 2, 8, fake, 4, 10, None, None, 0, None, 0, 5, fake, fake, fake, 1 << 30, None) == -1
+    assert lib.ah_scan_topk(fake, 2, 8, fake, 4, 10, None, None, 0, None, 0, 5000, fake, fake, fake, 1 << 30, None) == -3
+    assert lib.ah_scan_topk(fake, 2, 8, fake, 4, 10, None, None, 0, None, 0, 5, fake, fake, None, 0, None) == -4
+    need = lib.ah_scan_workspace_bytes(2, 8, 10, 0, 0, 5)
+    assert need > 0
+    assert lib.ah_scan_topk(fake, 2, 8, fake, 4, 10, None, None, 0, None, 0, 5, fake, fake, fake, need - 1, None) == -4
+    # nq == 0 is a no-op even with NULL pointers
+    assert lib.ah_scan_topk(None, 0, 8, None, 4, 10, None, None, 0, None, 0, 5, None, None, None, 0, None) == 0
+    # LUT: d != B*dpb, dpb too large, NULL output
+    assert lib.ah_build_lut(fake, 3, 10, fake, 4, 2, None, fake, fake, fake, None) == -2
+    assert lib.ah_build_lut(fake, 3, 64, fake, 2, 32, None, fake, fake, fake, None) == -3
+    assert lib.ah_build_lut(fake, 3, 8, fake, 4, 2, None, None, fake, fake, None) == -1
+    # reorder: k > R (the page's "reorder not above k" failure mode), bad dtype
+    assert lib.ah_reorder_exact(fake, 3, 8, fake, 0, 10, fake, 5, 6, fake, fake, None) == -2
+    assert lib.ah_reorder_exact(fake, 3, 8, fake, 7, 10, fake, 5, 5, fake, fake, None) == -3
+    # partition: nl > L, workspace too small
+    assert lib.ah_partition_score(fake, 3, 8, fake, 4, 5, fake, None, fake, 1 << 30, None) == -2
+    assert lib.ah_partition_score(fake, 3, 8, fake, 4, 2, fake, None, fake, 8, None) == -4

@@ -1,0 +1,218 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Stage-chained: every GPU stage is compared with the oracle run on the same
+inputs that stage received.  Integer results (int8 tables, scan sums, top-R id
+sets) must match bit for bit; floating-point results (fp32 tables, centroid
+scores, reorder scores) within 1e-4 relative, relative to
+max(|ref|, sum_j |a_j b_j|) with the float64 oracle as reference.  Where two
+items' float64 scores lie within that tolerance, either order is accepted.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mips_ah_partition_amd import ahlib
+    ahlib.lib()
+    return torch, ahlib
+
+
+def _t(torch, a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+# ----------------------------------------------------------------------------- LUT
+@pytest.mark.parametrize("dpb,B,nq", [(1, 5, 3), (2, 64, 37), (4, 32, 100), (2, 200, 17), (2, 768, 5), (3, 7, 66)])
+def test_build_lut_parity(gpu, dpb, B, nq):
+    torch, ah = gpu
+    rng = np.random.default_rng(1000 + B * 10 + dpb)
+    Q = rng.standard_normal((nq, B * dpb)).astype(np.float32)
+    cb = rng.standard_normal((B, 16, dpb)).astype(np.float32)
+    t8, s, beta, l32 = ah.ah_build_lut(_t(torch, Q), _t(torch, cb), want_f32=True)
+    torch.cuda.synchronize()
+    l32 = _np(l32)
+    ref = oracle.lut_f64(Q, cb)
+    denom = np.maximum(np.abs(ref), np.einsum("qbt,bct->qbc", np.abs(Q.reshape(nq, B, dpb)).astype(np.float64),
+                                               np.abs(cb).astype(np.float64)))
+    assert (np.abs(l32 - ref) <= TOL * denom + 1e-30).all()
+    o8, os_, ob = oracle.quantize_lut(l32)
+    assert np.array_equal(_np(t8), o8)
+    assert np.array_equal(_np(s), os_)
+    assert np.array_equal(_np(beta), ob)
+
+
+def test_build_lut_constant_table(gpu):
+    torch, ah = gpu
+    Q = np.zeros((4, 8), dtype=np.float32)
+    cb = np.random.default_rng(2).standard_normal((4, 16, 2)).astype(np.float32)
+    t8, s, beta, _ = ah.ah_build_lut(_t(torch, Q), _t(torch, cb))
+    torch.cuda.synchronize()
+    assert (_np(t8) == 0).all() and (_np(s) == 0).all() and (_np(beta) == 0).all()
+
+
+# ----------------------------------------------------------------------------- scan
+def _scan_check(torch, ah, lut, codes, R, ids=None, offs=None, leaves=None):
+    g_ids, g_sc = ah.ah_scan_topk(_t(torch, lut), _t(torch, codes), R,
+                                  ids=None if ids is None else _t(torch, ids),
+                                  leaf_offsets=None if offs is None else _t(torch, offs),
+                                  leaves=None if leaves is None else _t(torch, leaves))
+    torch.cuda.synchronize()
+    o_ids, o_sc = oracle.scan_topk(lut, codes, R, ids=ids, leaf_offsets=offs, leaves=leaves)
+    g_ids, g_sc = _np(g_ids), _np(g_sc)
+    bad = np.nonzero((g_ids != o_ids).any(axis=1) | (g_sc != o_sc).any(axis=1))[0]
+    assert len(bad) == 0, f"{len(bad)} queries differ, first {bad[:5]}: gpu {g_ids[bad[0], :8]} {g_sc[bad[0], :8]} oracle {o_ids[bad[0], :8]} {o_sc[bad[0], :8]}"
+    return g_ids, g_sc
+
+
+@pytest.mark.parametrize("B,n,nq,R,stride_pad", [
+    (32, 10000, 100, 100, 0),   # tiny workload shape: 32 blocks, 16 B rows
+    (64, 5000, 70, 200, 0),     # 64 blocks, ragged query group
+    (50, 3001, 65, 37, 0),      # 25 B rows (unaligned path), ragged rows
+    (8, 700, 9, 1000, 0),       # R > n: pads
+    (200, 2000, 20, 300, 0),    # several 64-block chunks
+    (768, 1500, 8, 400, 0),     # 768 blocks
+    (33, 1234, 5, 10, 7),       # odd B, padded rows
+])
+def test_scan_full_parity(gpu, B, n, nq, R, stride_pad):
+    torch, ah = gpu
+    rng = np.random.default_rng(B * 7 + n)
+    lut = synth.random_lut_i8(rng, nq, B)
+    codes = synth.random_codes(rng, n, B)
+    if stride_pad:
+        codes = np.concatenate([codes, rng.integers(0, 256, size=(n, stride_pad), dtype=np.uint8)], axis=1)
+    _scan_check(torch, ah, lut, codes, R)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_scan_heavy_ties(gpu, seed):
+    torch, ah = gpu
+    rng = np.random.default_rng(50 + seed)
+    B, n, nq, R = 16, 6000, 40, 150
+    lut = rng.choice(np.array([-1, 1], dtype=np.int8), size=(nq, B, 16))
+    codes = synth.random_codes(rng, n, B)
+    _scan_check(torch, ah, lut, codes, R)
+
+
+def test_scan_empty_database(gpu):
+    torch, ah = gpu
+    lut = np.ones((3, 4, 16), dtype=np.int8)
+    codes = np.zeros((0, 2), dtype=np.uint8)
+    ids, sc = ah.ah_scan_topk(_t(torch, lut), _t(torch, codes), 5)
+    torch.cuda.synchronize()
+    assert (_np(ids) == -1).all() and (_np(sc) == np.iinfo(np.int32).min).all()
+
+
+def test_scan_partitioned_parity(gpu):
+    torch, ah = gpu
+    rng = np.random.default_rng(77)
+    B, n, nq, L, nl, R = 64, 30000, 150, 40, 6, 120
+    sizes = np.concatenate([[20000], synth.random_leaf_sizes(rng, n - 20000, L - 1, skew=1.0)])
+    sizes[6] += sizes[5]
+    sizes[5] = 0  # an empty leaf; leaf 0 spans several 8192-row items
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    lut = synth.random_lut_i8(rng, nq, B)
+    codes = synth.random_codes(rng, n, B)
+    perm = rng.permutation(n).astype(np.int32)
+    leaves = synth.random_probe_lists(rng, nq, L, nl)
+    leaves[:, 0] = 0
+    leaves[1, 1] = 5
+    _scan_check(torch, ah, lut, codes, R, ids=perm, offs=offs, leaves=leaves)
+
+
+def test_scan_overflow_fallback(gpu):
+    """All sums equal: the threshold cannot rise, candidate lists overflow and the
+    exact fallback must return the R lowest ids."""
+    torch, ah = gpu
+    B, n, nq, R = 4, 40000, 3, 50
+    lut = np.zeros((nq, B, 16), dtype=np.int8)
+    codes = synth.random_codes(np.random.default_rng(1), n, B)
+    ids, sc = _scan_check(torch, ah, lut, codes, R)
+    assert (ids == np.arange(R)).all() and (sc == 0).all()
+
+
+def test_scan_deterministic(gpu):
+    torch, ah = gpu
+    rng = np.random.default_rng(5)
+    lut = synth.random_lut_i8(rng, 64, 32, -3, 3)
+    codes = synth.random_codes(rng, 20000, 32)
+    a = [_np(x) for x in ah.ah_scan_topk(_t(torch, lut), _t(torch, codes), 64)]
+    b = [_np(x) for x in ah.ah_scan_topk(_t(torch, lut), _t(torch, codes), 64)]
+    torch.cuda.synchronize()
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ----------------------------------------------------------------------------- reorder
+def _check_ranked(g_ids, g_sc, o_ids, o_sc, ref_fn, denom_fn):
+    """GPU picks a valid best-k up to near-ties: its float64 scores match the
+    oracle's ranked scores within tolerance, and its own scores are accurate."""
+    for q in range(g_ids.shape[0]):
+        valid = o_ids[q] >= 0
+        assert ((g_ids[q] >= 0) == valid).all()
+        gi = g_ids[q][valid]
+        ref = ref_fn(q, gi)
+        den = np.maximum(np.abs(ref), denom_fn(q, gi))
+        assert (np.abs(g_sc[q][valid] - ref) <= TOL * den).all(), q
+        assert (np.abs(ref - o_sc[q][valid]) <= 2 * TOL * den).all(), q
+        assert len(set(gi.tolist())) == len(gi)
+
+
+@pytest.mark.parametrize("dtype,d,R,k", [("f32", 128, 200, 10), ("f32", 100, 37, 37), ("bf16", 384, 300, 10),
+                                         ("bf16", 1536, 64, 10), ("f32", 7, 10, 3)])
+def test_reorder_parity(gpu, dtype, d, R, k):
+    torch, ah = gpu
+    rng = np.random.default_rng(d + R)
+    n, nq = 3000, 45
+    X = rng.standard_normal((n, d)).astype(np.float32)
+    Q = rng.standard_normal((nq, d)).astype(np.float32)
+    cand = np.stack([rng.permutation(n)[:R] for _ in range(nq)]).astype(np.int32)
+    cand[3, R // 2:] = -1
+    cand[4, :] = -1
+    if dtype == "f32":
+        base_np, base_t, Xr = X, _t(torch, X), X.astype(np.float64)
+    else:
+        bits = synth.to_bf16_bits(X)
+        base_np = bits
+        base_t = _t(torch, bits.view(np.int16)).view(torch.bfloat16)
+        Xr = synth.bf16_bits_to_f32(bits).astype(np.float64)
+    g_ids, g_sc = ah.ah_reorder_exact(_t(torch, Q), base_t, _t(torch, cand), k)
+    torch.cuda.synchronize()
+    o_ids, o_sc = oracle.reorder(Q, base_np, cand, k)
+    Qd = Q.astype(np.float64)
+    _check_ranked(_np(g_ids), _np(g_sc), o_ids, o_sc,
+                  lambda q, ids: Xr[ids] @ Qd[q], lambda q, ids: np.abs(Xr[ids]) @ np.abs(Qd[q]))
+    assert (_np(g_ids)[4] == -1).all() and np.isneginf(_np(g_sc)[4]).all()
+
+
+# ----------------------------------------------------------------------------- partition
+@pytest.mark.parametrize("nq,d,L,nl", [(100, 100, 1000, 50), (67, 128, 300, 7), (5, 1536, 130, 100), (3, 9, 5, 5)])
+def test_partition_parity(gpu, nq, d, L, nl):
+    torch, ah = gpu
+    rng = np.random.default_rng(nq + L)
+    Q = rng.standard_normal((nq, d)).astype(np.float32)
+    Cn = rng.standard_normal((L, d)).astype(np.float32)
+    lv, sc = ah.ah_partition_score(_t(torch, Q), _t(torch, Cn), nl)
+    torch.cuda.synchronize()
+    o_lv, o_sc = oracle.partition(Q, Cn, nl)
+    Qd, Cd = Q.astype(np.float64), Cn.astype(np.float64)
+    _check_ranked(_np(lv), _np(sc), o_lv, o_sc,
+                  lambda q, ids: Cd[ids] @ Qd[q], lambda q, ids: np.abs(Cd[ids]) @ np.abs(Qd[q]))
+    agree = (_np(lv) == o_lv).mean()
+    assert agree > 0.99
