@@ -128,6 +128,18 @@ int ah_scan_topk(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* cod
                  int32_t L, const int32_t* leaves, int32_t nl, int32_t R, int32_t* cand_ids_out,
                  int32_t* cand_scores_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Same as ah_scan_topk.  When main_start_event / main_stop_event are non-NULL
+ * hipEvent_t handles (created by the caller), they are recorded on `stream`
+ * immediately before and after the main scan kernel, so the caller can time
+ * that kernel alone (the leaf inversion, threshold warm-up and final selection
+ * run outside the pair). */
+int ah_scan_topk_timed(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* codes,
+                       int32_t code_stride, int64_t n, const int32_t* ids,
+                       const int64_t* leaf_offsets, int32_t L, const int32_t* leaves, int32_t nl,
+                       int32_t R, int32_t* cand_ids_out, int32_t* cand_scores_out, void* workspace,
+                       size_t workspace_bytes, void* stream, void* main_start_event,
+                       void* main_stop_event);
+
 /* ---------------------------------------------------------------------------
  * Step 5: exact reorder (ScaNN page, "Three stages of a search": the best few
  * hundred candidates are rescored with exact dot products; "Failure modes":

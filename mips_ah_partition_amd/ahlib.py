@@ -25,7 +25,7 @@ EXPORTS = (
     "ah_status_string", "ah_version",
     "ah_partition_workspace_bytes", "ah_partition_score",
     "ah_build_lut",
-    "ah_scan_workspace_bytes", "ah_scan_topk",
+    "ah_scan_workspace_bytes", "ah_scan_topk", "ah_scan_topk_timed",
     "ah_reorder_exact",
 )
 
@@ -58,6 +58,9 @@ def lib() -> C.CDLL:
         L.ah_scan_workspace_bytes.argtypes = [i64, i32, i64, i32, i32, i32]
         L.ah_scan_topk.restype = C.c_int
         L.ah_scan_topk.argtypes = [vp, i64, i32, vp, i32, i64, vp, vp, i32, vp, i32, i32, vp, vp, vp, sz, vp]
+        L.ah_scan_topk_timed.restype = C.c_int
+        L.ah_scan_topk_timed.argtypes = [vp, i64, i32, vp, i32, i64, vp, vp, i32, vp, i32, i32, vp, vp, vp, sz, vp,
+                                         vp, vp]
         L.ah_reorder_exact.restype = C.c_int
         L.ah_reorder_exact.argtypes = [vp, i64, i32, vp, i32, i64, vp, i32, i32, vp, vp, vp]
         _lib = L
@@ -158,7 +161,7 @@ def ah_scan_workspace_bytes(nq: int, B: int, n: int, L: int, nl: int, R: int) ->
 
 
 def ah_scan_topk(lut_i8, codes, R, ids=None, leaf_offsets=None, leaves=None, cand_ids_out=None,
-                 cand_scores_out=None, workspace=None, stream=None):
+                 cand_scores_out=None, workspace=None, stream=None, main_events=None):
     """Top-R rows per query by exact int32 sum of table entries.
     codes: uint8 [n, stride]; leaves: int32 [nq, nl] or None (scan all rows)."""
     lut_i8 = _dev(lut_i8, torch.int8, "lut_i8", 3)
@@ -181,9 +184,13 @@ def ah_scan_topk(lut_i8, codes, R, ids=None, leaf_offsets=None, leaves=None, can
     need = ah_scan_workspace_bytes(nq, B, n, Lw, nlw, R)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    _check(lib().ah_scan_topk(_ptr(lut_i8), nq, B, _ptr(codes), stride, n, _ptr(ids), _ptr(leaf_offsets), L,
-                              _ptr(leaves), nl, R, _ptr(cand_ids_out), _ptr(cand_scores_out), _ptr(workspace),
-                              workspace.numel(), _stream(stream)), "ah_scan_topk")
+    args = (_ptr(lut_i8), nq, B, _ptr(codes), stride, n, _ptr(ids), _ptr(leaf_offsets), L, _ptr(leaves), nl, R,
+            _ptr(cand_ids_out), _ptr(cand_scores_out), _ptr(workspace), workspace.numel(), _stream(stream))
+    if main_events is None:
+        _check(lib().ah_scan_topk(*args), "ah_scan_topk")
+    else:  # (start, stop) raw hipEvent_t handles bracketing the main scan kernel
+        _check(lib().ah_scan_topk_timed(*args, C.c_void_p(main_events[0]), C.c_void_p(main_events[1])),
+               "ah_scan_topk_timed")
     return cand_ids_out, cand_scores_out
 
 

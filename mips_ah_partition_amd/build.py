@@ -1,4 +1,5 @@
-"""Build the gfx950 HIP library behind include/ah.h (libah.so, in-tree).
+"""Build the gfx950 HIP library behind include/ah.h (libah.so, in-tree) and the
+host index builder behind include/ah_index.h (libah_index.so).
 
 One hipcc invocation compiles every source under csrc/ for gfx950 only.  Device
 code is built without fast-math (IEEE division and rint are part of the int8
@@ -14,6 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libah.so")
+HOST_LIB = os.path.join(HERE, "libah_index.so")
 ARCH = "gfx950"
 
 
@@ -38,7 +40,20 @@ def build(verbose: bool = False) -> str:
     if verbose and out.strip():
         print(out)
     os.replace(tmp, LIB)
+    build_host(verbose)
     return LIB
+
+
+def build_host(verbose: bool = False) -> str:
+    """Host-only index builder (include/ah_index.h): g++ with OpenMP."""
+    tmp = HOST_LIB + ".tmp"
+    cmd = ["g++", "-O3", "-std=c++17", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-Wall",
+           "-o", tmp, os.path.join(CSRC, "host", "ah_index.cpp")]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, HOST_LIB)
+    return HOST_LIB
 
 
 if __name__ == "__main__":

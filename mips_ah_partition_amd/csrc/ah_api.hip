@@ -61,10 +61,11 @@ size_t ah_scan_workspace_bytes(int64_t nq, int32_t B, int64_t n, int32_t L, int3
     return ah::scan_workspace_bytes(nq, B, n, L, nl, R);
 }
 
-int ah_scan_topk(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* codes,
-                 int32_t code_stride, int64_t n, const int32_t* ids, const int64_t* leaf_offsets,
-                 int32_t L, const int32_t* leaves, int32_t nl, int32_t R, int32_t* cand_ids_out,
-                 int32_t* cand_scores_out, void* workspace, size_t workspace_bytes, void* stream) {
+int ah_scan_topk_timed(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* codes,
+                       int32_t code_stride, int64_t n, const int32_t* ids, const int64_t* leaf_offsets,
+                       int32_t L, const int32_t* leaves, int32_t nl, int32_t R, int32_t* cand_ids_out,
+                       int32_t* cand_scores_out, void* workspace, size_t workspace_bytes, void* stream,
+                       void* main_start_event, void* main_stop_event) {
     if (nq < 0 || n < 0 || B < 1 || R < 1 || code_stride < (B + 1) / 2) return AH_ERR_SHAPE;
     if (leaves && (L < 1 || nl < 1 || nl > L || !leaf_offsets)) return AH_ERR_SHAPE;
     if (B > AH_MAX_BLOCKS || R > AH_MAX_R || n >= ((int64_t)1 << 31)) return AH_ERR_UNSUPPORTED;
@@ -75,7 +76,17 @@ int ah_scan_topk(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* cod
     if (!workspace || workspace_bytes < ah::scan_workspace_bytes(nq, B, n, Lw, nlw, R)) return AH_ERR_WORKSPACE;
     ah::ScanProblem sp{lut_i8, nq, B, codes, code_stride, n, ids, leaves ? leaf_offsets : nullptr, Lw,
                        leaves, nlw, R, cand_ids_out, cand_scores_out};
-    return hip_status(ah::launch_scan(sp, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+    return hip_status(ah::launch_scan(sp, workspace, workspace_bytes, static_cast<hipStream_t>(stream),
+                                      static_cast<hipEvent_t>(main_start_event),
+                                      static_cast<hipEvent_t>(main_stop_event)));
+}
+
+int ah_scan_topk(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* codes,
+                 int32_t code_stride, int64_t n, const int32_t* ids, const int64_t* leaf_offsets,
+                 int32_t L, const int32_t* leaves, int32_t nl, int32_t R, int32_t* cand_ids_out,
+                 int32_t* cand_scores_out, void* workspace, size_t workspace_bytes, void* stream) {
+    return ah_scan_topk_timed(lut_i8, nq, B, codes, code_stride, n, ids, leaf_offsets, L, leaves, nl, R,
+                              cand_ids_out, cand_scores_out, workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
 int ah_reorder_exact(const float* q, int64_t nq, int32_t d, const void* base, int32_t base_dtype,

@@ -35,7 +35,8 @@ struct ScanProblem {
     int32_t* out_scores;
 };
 size_t scan_workspace_bytes(int64_t nq, int32_t B, int64_t n, int32_t L, int32_t nl, int32_t R);
-hipError_t launch_scan(const ScanProblem& p, void* ws, size_t ws_bytes, hipStream_t stream);
+hipError_t launch_scan(const ScanProblem& p, void* ws, size_t ws_bytes, hipStream_t stream,
+                       hipEvent_t main_start = nullptr, hipEvent_t main_stop = nullptr);
 
 hipError_t launch_reorder(const float* q, int64_t nq, int32_t d, const void* base, int32_t dtype,
                           int64_t n, const int32_t* cand, int32_t R, int32_t k, int32_t* ids,

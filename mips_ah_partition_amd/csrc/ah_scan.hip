@@ -662,7 +662,8 @@ static int device_cus() {
     return cus;
 }
 
-hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStream_t stream) {
+hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t main_start,
+                       hipEvent_t main_stop) {
     (void)ws_bytes;
     if (sp.nq == 0) return hipSuccess;
     const ScanLayout lay = scan_layout(sp.nq, sp.B, sp.n, sp.L, sp.nl, sp.R);
@@ -721,8 +722,10 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     const int64_t max_items = part ? (int64_t)sp.nq * sp.nl + sp.L : ma.n_items;
     int grid = device_cus();
     if (max_items < grid) grid = (int)(max_items > 0 ? max_items : 1);
+    if (main_start && (e = hipEventRecord(main_start, stream)) != hipSuccess) return e;
     hipLaunchKernelGGL(scan_main_kernel, dim3(grid), dim3(kScanThreads), 0, stream, ma);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (main_stop && (e = hipEventRecord(main_stop, stream)) != hipSuccess) return e;
     int Rp = 1;
     while (Rp < sp.R) Rp <<= 1;
     allow_lds(final_select_kernel, (size_t)(kSelLds + Rp) * 8);

@@ -1,0 +1,191 @@
+"""Host-side index build: partition k-means, anisotropic PQ codebooks, coupled
+encoding, leaf sort.
+
+Source: page "ScaNN: Anisotropic Vector Quantization for Maximum Inner
+Product Search": "The loss in one paragraph" (eta and its large-d limit),
+"Training an anisotropic codebook yourself" (the trainer), "Three stages of a
+search" (partition into leaves; blocks of dimensions_per_block dims, 16 centers
+each) and "Using the library" (training on a sample of up to 250,000 rows).
+
+The codebook training and encoding run in the C++ host library
+(include/ah_index.h, libah_index.so); the partition k-means uses numpy BLAS.
+Nothing here runs on the GPU: the index is built once on the host and its
+arrays are passed to the C ABI of include/ah.h.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import dataclasses
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+HOST_LIB = os.path.join(_HERE, "libah_index.so")
+_hl = None
+
+SAMPLE_ROWS = 250_000
+ITERS = 10
+
+
+def _host():
+    global _hl
+    if _hl is None:
+        if not os.path.exists(HOST_LIB):
+            from . import build
+            build.build_host()
+        L = C.CDLL(HOST_LIB)
+        f32 = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+        i64 = np.ctypeslib.ndpointer(np.int64, flags="C_CONTIGUOUS")
+        u8 = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
+        L.ahx_train_pq.restype = C.c_int
+        L.ahx_train_pq.argtypes = [f32, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_double, C.c_int32,
+                                   i64, f32, C.c_void_p]
+        L.ahx_encode.restype = C.c_int
+        L.ahx_encode.argtypes = [f32, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_double, f32, C.c_int32,
+                                 u8, C.c_int32]
+        L.ahx_loss.restype = C.c_double
+        L.ahx_loss.argtypes = [f32, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_double, f32, u8, C.c_int32]
+        _hl = L
+    return _hl
+
+
+# ------------------------------------------------------------------------- eta
+def eta_for(d: int, T: float, norms) -> np.ndarray:
+    """Large-dimension limit of h_par/h_perp for the threshold weight (ScaNN page,
+    "The loss in one paragraph"): (d-1) r / (1-r), r = (T/|x|)^2."""
+    r = (T / np.asarray(norms, dtype=np.float64)) ** 2
+    if np.any(r >= 1):
+        raise ValueError("T must be below every row norm")
+    return (d - 1) * r / (1 - r)
+
+
+def relative_threshold_for_eta(d: int, eta: float) -> float:
+    """T/|x| that gives weight ratio eta in dimension d (inverse of eta_for)."""
+    return float(np.sqrt(eta / (d - 1 + eta)))
+
+
+# ------------------------------------------------------------------------- PQ
+def train_codebooks(X: np.ndarray, dpb: int, eta: float, iters: int = ITERS, seed=0, init_rows=None,
+                    return_loss: bool = False):
+    """Anisotropic PQ codebooks float32 [B, 16, dpb] trained on rows X."""
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    m, d = X.shape
+    B = d // dpb
+    if init_rows is None:
+        init_rows = np.random.default_rng(seed).choice(m, 16, replace=False)
+    init_rows = np.ascontiguousarray(init_rows, dtype=np.int64)
+    cb = np.empty((B, 16, dpb), dtype=np.float32)
+    loss = np.empty(iters + 1, dtype=np.float64)
+    rc = _host().ahx_train_pq(X, m, d, B, dpb, float(eta), iters, init_rows, cb, loss.ctypes.data_as(C.c_void_p))
+    if rc != 0:
+        raise ValueError("ahx_train_pq: bad arguments")
+    return (cb, loss) if return_loss else cb
+
+
+def encode(X: np.ndarray, codebooks: np.ndarray, eta: float, sweeps: int = 2, stride: int | None = None) -> np.ndarray:
+    """Row-major nibble codes uint8 [n, stride] (low nibble = even block)."""
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    cb = np.ascontiguousarray(codebooks, dtype=np.float32)
+    B, _, dpb = cb.shape
+    stride = (B + 1) // 2 if stride is None else stride
+    out = np.empty((X.shape[0], stride), dtype=np.uint8)
+    rc = _host().ahx_encode(X, X.shape[0], X.shape[1], B, dpb, float(eta), cb, sweeps, out, stride)
+    if rc != 0:
+        raise ValueError("ahx_encode: bad arguments")
+    return out
+
+
+def pq_loss(X, codebooks, codes, eta) -> float:
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    cb = np.ascontiguousarray(codebooks, dtype=np.float32)
+    B, _, dpb = cb.shape
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    return float(_host().ahx_loss(X, X.shape[0], X.shape[1], B, dpb, float(eta), cb, codes, codes.shape[1]))
+
+
+# ------------------------------------------------------------------------- partition
+def nearest_centroid(X: np.ndarray, Cn: np.ndarray, chunk: int = 32768) -> np.ndarray:
+    """Index of the L2-nearest centroid of every row (lowest index on ties)."""
+    Cd = Cn.astype(np.float64)
+    cn2 = np.einsum("ij,ij->i", Cd, Cd)
+    out = np.empty(X.shape[0], dtype=np.int32)
+    for a in range(0, X.shape[0], chunk):
+        xb = X[a:a + chunk].astype(np.float64)
+        dist = cn2[None, :] - 2.0 * (xb @ Cd.T)
+        out[a:a + chunk] = np.argmin(dist, axis=1)
+    return out
+
+
+def kmeans(X: np.ndarray, k: int, iters: int = ITERS, seed=0, init_rows=None):
+    """Lloyd k-means (squared L2), init = k distinct rows, empty clusters keep
+    their center.  Returns (centroids float32 [k, d], assignment)."""
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    if init_rows is None:
+        init_rows = np.random.default_rng(seed).choice(X.shape[0], k, replace=False)
+    Cn = X[np.asarray(init_rows)].astype(np.float32).copy()
+    assign = nearest_centroid(X, Cn)
+    for _ in range(iters):
+        sums = np.zeros((k, X.shape[1]), dtype=np.float64)
+        np.add.at(sums, assign, X.astype(np.float64))
+        cnt = np.bincount(assign, minlength=k)
+        nz = cnt > 0
+        Cn[nz] = (sums[nz] / cnt[nz, None]).astype(np.float32)
+        assign = nearest_centroid(X, Cn)
+    return Cn, assign
+
+
+def leaf_sort(assign: np.ndarray, num_leaves: int):
+    """Rows grouped by leaf, ascending id inside each leaf.
+    Returns (ids int32 [n] original row of each position, leaf_offsets int64 [L+1])."""
+    ids = np.argsort(assign, kind="stable").astype(np.int32)
+    cnt = np.bincount(assign, minlength=num_leaves)
+    offs = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int64)
+    return ids, offs
+
+
+# ------------------------------------------------------------------------- whole index
+@dataclasses.dataclass
+class HostIndex:
+    codebooks: np.ndarray            # float32 [B, 16, dpb]
+    codes: np.ndarray                # uint8 [n, stride], leaf-sorted when partitioned
+    ids: np.ndarray | None           # int32 [n] original row of each code row (None = identity)
+    centroids: np.ndarray | None     # float32 [L, d]
+    leaf_offsets: np.ndarray | None  # int64 [L+1]
+    eta: float
+
+
+def build(X: np.ndarray, dpb: int, eta: float, num_leaves: int = 0, seed: int = 0, sample_rows: int = SAMPLE_ROWS,
+          iters: int = ITERS, sweeps: int = 2) -> HostIndex:
+    """Train and encode an index over rows X (float32 [n, d])."""
+    n = X.shape[0]
+    rng = np.random.default_rng(seed)
+    sample = np.sort(rng.choice(n, min(n, sample_rows), replace=False)) if n > sample_rows else np.arange(n)
+    Xs = X[sample]
+    centroids = leaf_offsets = ids = None
+    if num_leaves > 0:
+        centroids, _ = kmeans(Xs, num_leaves, iters, seed=rng)
+        assign = nearest_centroid(X, centroids)
+        ids, leaf_offsets = leaf_sort(assign, num_leaves)
+    cb = train_codebooks(Xs, dpb, eta, iters, seed=rng)
+    codes = encode(X, cb, eta, sweeps)
+    if ids is not None:
+        codes = np.ascontiguousarray(codes[ids])
+    return HostIndex(cb, codes, ids, centroids, leaf_offsets, eta)
+
+
+def save(path: str, ix: HostIndex) -> None:
+    arrs = {"codebooks": ix.codebooks, "codes": ix.codes, "eta": np.array(ix.eta)}
+    for k in ("ids", "centroids", "leaf_offsets"):
+        v = getattr(ix, k)
+        if v is not None:
+            arrs[k] = v
+    tmp = path + ".tmp.npz"
+    np.savez(tmp, **arrs)
+    os.replace(tmp, path)
+
+
+def load(path: str) -> HostIndex:
+    z = np.load(path, allow_pickle=False)
+    g = lambda k: z[k] if k in z.files else None  # noqa: E731
+    return HostIndex(z["codebooks"], z["codes"], g("ids"), g("centroids"), g("leaf_offsets"), float(z["eta"]))

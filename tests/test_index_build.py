@@ -1,0 +1,124 @@
+"""Pins of the host index builder (anisotropic PQ training, coupled encoding,
+partition k-means) against the ScaNN page's closed forms and special cases."""
+import numpy as np
+import pytest
+
+from mips_ah_partition_amd import index as ix
+
+
+def test_eta_closed_form_values():
+    """eta = (d-1) T^2/(1-T^2) for unit norm (page, "The loss in one paragraph")."""
+    assert ix.eta_for(128, 0.2, [1.0])[0] == pytest.approx(127 * 0.04 / 0.96)
+    assert ix.eta_for(128, 0.2, [1.0])[0] == pytest.approx(5.2917, abs=1e-4)
+    assert ix.eta_for(768, 0.2, [1.0])[0] == pytest.approx(31.958, abs=1e-3)
+    with pytest.raises(ValueError):
+        ix.eta_for(10, 2.0, [1.0])
+    for d, eta in ((128, 4.0), (100, 4.0), (1536, 4.0)):
+        t = ix.relative_threshold_for_eta(d, eta)
+        assert ix.eta_for(d, t, [1.0])[0] == pytest.approx(eta)
+
+
+def _lloyd_blocks(X, B, dpb, init_rows, iters):
+    """Plain per-block Lloyd k-means (numpy, float64 means)."""
+    n = X.shape[0]
+    Xb = X.reshape(n, B, dpb).astype(np.float64)
+    C = X[init_rows].reshape(16, B, dpb).transpose(1, 0, 2).astype(np.float32).copy()
+    for _ in range(iters + 1):
+        d2 = ((Xb[:, :, None, :] - C[None].astype(np.float64)) ** 2).sum(-1)  # n, B, 16
+        a = d2.argmin(-1)
+        if _ == iters:
+            break
+        for b in range(B):
+            for c in range(16):
+                m = a[:, b] == c
+                if m.any():
+                    C[b, c] = (Xb[m, b].sum(0) / m.sum()).astype(np.float32)
+    return C, a
+
+
+def test_eta_one_is_kmeans():
+    """With eta = 1 the update is the cluster mean: training must equal plain
+    per-block Lloyd k-means from the same initial rows (page's sanity test)."""
+    rng = np.random.default_rng(0)
+    X = rng.standard_normal((3000, 12)).astype(np.float32)
+    init = rng.choice(3000, 16, replace=False)
+    cb = ix.train_codebooks(X, 3, 1.0, iters=6, init_rows=init)
+    ref, a = _lloyd_blocks(X, 4, 3, init, 6)
+    assert np.allclose(cb, ref, rtol=1e-6, atol=1e-6)
+    codes = ix.encode(X, cb, 1.0, sweeps=2)
+    nib = np.stack([(codes[:, b // 2] >> (4 * (b % 2))) & 15 for b in range(4)], axis=1)
+    assert (nib == a).mean() > 0.999
+
+
+def _loss_grad(X, c, eta):
+    """Gradient of sum_i (eta-1)(u_i.(x_i-c))^2 + |x_i-c|^2 in c."""
+    U = X / np.linalg.norm(X, axis=1, keepdims=True)
+    R = X - c
+    par = (U * R).sum(1)
+    return (-2 * (eta - 1) * par[:, None] * U - 2 * R).sum(0)
+
+
+def test_vq_update_is_stationary_and_page_rhs_is_not():
+    """One block (plain VQ): the trained center solves
+    (sum (eta-1) u u^T + m I) c = sum eta x, a stationary point of the loss;
+    the right-hand side sum x printed with the page's toy trainer is not
+    (it agrees only at eta = 1)."""
+    rng = np.random.default_rng(1)
+    d, eta = 6, 4.0
+    X = rng.standard_normal((500, d)).astype(np.float32) + 1.0
+    init = rng.choice(500, 16, replace=False)
+    cb = ix.train_codebooks(X, d, eta, iters=1, init_rows=init)
+    # the assignment the iteration used: nearest, then one loss-minimising pass
+    C0 = X[init].astype(np.float64)
+    U = X / np.linalg.norm(X, axis=1, keepdims=True)
+    R = X[:, None, :] - C0[None]
+    L = (eta - 1) * np.einsum("nkd,nd->nk", R, U) ** 2 + (R ** 2).sum(-1)
+    a = L.argmin(1)
+    for j in range(16):
+        m = a == j
+        if not m.any():
+            assert np.allclose(cb[0, j], X[init[j]])
+            continue
+        Xm = X[m].astype(np.float64)
+        g = _loss_grad(Xm, cb[0, j].astype(np.float64), eta)
+        assert np.abs(g).max() < 1e-3 * max(1.0, np.abs(Xm).sum())
+        Um = U[m].astype(np.float64)
+        A = m.sum() * np.eye(d) + (eta - 1) * Um.T @ Um
+        c_page = np.linalg.solve(A, Xm.sum(0))
+        assert np.abs(_loss_grad(Xm, c_page, eta)).max() > 1.0
+
+
+def test_training_loss_never_increases():
+    rng = np.random.default_rng(2)
+    X = rng.integers(0, 256, size=(4000, 16)).astype(np.float32)
+    cb, loss = ix.train_codebooks(X, 2, 4.0, iters=8, seed=3, return_loss=True)
+    assert (np.diff(loss) <= 1e-9 * loss[0]).all()
+    assert loss[-1] < loss[0]
+
+
+def test_encode_sweeps_lower_the_loss_and_zero_sweeps_is_nearest():
+    rng = np.random.default_rng(4)
+    X = rng.standard_normal((2000, 10)).astype(np.float32)
+    cb = ix.train_codebooks(X, 2, 3.0, iters=3, seed=5)
+    c0 = ix.encode(X, cb, 3.0, sweeps=0)
+    c2 = ix.encode(X, cb, 3.0, sweeps=2, stride=4)
+    assert c2.shape == (2000, 4) and (c2[:, 3] == 0).all()
+    Xb = X.reshape(2000, 5, 2)
+    near = ((Xb[:, :, None, :] - cb[None]) ** 2).sum(-1).argmin(-1)
+    nib0 = np.stack([(c0[:, b // 2] >> (4 * (b % 2))) & 15 for b in range(5)], axis=1)
+    assert (nib0 == near).all()
+    assert ix.pq_loss(X, cb, c2, 3.0) <= ix.pq_loss(X, cb, c0, 3.0)
+
+
+def test_kmeans_and_leaf_sort():
+    rng = np.random.default_rng(6)
+    centers = rng.standard_normal((5, 4)) * 10
+    X = (centers[rng.integers(0, 5, 1000)] + rng.standard_normal((1000, 4))).astype(np.float32)
+    Cn, a = ix.kmeans(X, 5, iters=10, seed=7)
+    d2 = ((X[:, None, :].astype(np.float64) - Cn[None]) ** 2).sum(-1)
+    assert (a == d2.argmin(1)).all()
+    ids, offs = ix.leaf_sort(a, 5)
+    assert offs[0] == 0 and offs[-1] == 1000
+    for l in range(5):
+        seg = ids[offs[l]:offs[l + 1]]
+        assert (a[seg] == l).all() and (np.diff(seg) > 0).all()
