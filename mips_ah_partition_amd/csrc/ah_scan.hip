@@ -48,7 +48,7 @@ constexpr int kQG = 64;                           // queries per item
 constexpr int kKC = 16;                           // k-steps (x4 blocks) per chunk
 constexpr int kCodeStride = 9;                    // LDS row stride (dwords) for a chunk's 8 code dwords
 constexpr int kNB = 1024;                         // histogram bins per query
-constexpr int kLogCap = 256;                      // logged hits per wave
+constexpr int kLogCap = 1152;                     // logged hits per wave (one query tile = 1024 max)
 constexpr int kItemPts = 8192;                    // rows per item
 constexpr int kFbSlots = 4;                       // fallback workgroups
 constexpr int kSelThreads = 256;
@@ -445,9 +445,16 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                 if (avail >= 16) x0 = *reinterpret_cast<const uint4*>(src);
                 if (avail >= 32) x1 = *reinterpret_cast<const uint4*>(src + 16);
             } else {
-                const int cb = (p.B + 1) / 2 - 32 * c;
-                uint32_t wd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                for (int i = 0; i < 32 && i < cb; ++i) wd[i >> 2] |= (uint32_t)src[i] << (8 * (i & 3));
+                const int cb = (p.B + 1) / 2 - 32 * c;  // code bytes of this row from the chunk start
+                uint32_t wd[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    uint32_t v = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * k + e < cb) v |= (uint32_t)src[4 * k + e] << (8 * e);
+                    wd[k] = v;
+                }
                 x0 = make_uint4(wd[0], wd[1], wd[2], wd[3]);
                 x1 = make_uint4(wd[4], wd[5], wd[6], wd[7]);
             }
@@ -516,30 +523,39 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
             if (c != a.nchunk - 1) continue;
 
             // filter: tile (m, nt) holds, in register i, the sum of row
-            // 16m + 4g + i (of this wave's 64) for query 16nt + r16
+            // 16m + 4g + i (of this wave's 64) for query 16nt + r16.  All
+            // accumulator indices are compile-time constants (no dynamic
+            // indexing, so the accumulators stay in registers); the log is
+            // flushed only between query tiles and always has room for one.
+            const int64_t wrow = tile0 + w * 64 + 4 * g;
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
-                const int ql = 16 * nt + r16;
+                if (log_n > kLogCap - 16 * kWave) {
+                    flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0);
+                    log_n = 0;
+                }
+                uint32_t hits = 0;
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        hits |= (uint32_t)(wrow + m * 16 + i < p1 && acc[m][nt][i] >= tq[nt]) << (4 * m + i);
+                if (__ballot(hits != 0) == 0) continue;
+                const uint64_t qbits = (uint64_t)(16 * nt + r16) << 16;
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int64_t row = tile0 + w * 64 + m * 16 + 4 * g + i;
-                        const int32_t s = acc[m][nt][i];
-                        const bool hit = row < p1 && s >= tq[nt];
+                        const bool hit = (hits >> (4 * m + i)) & 1u;
                         const uint64_t mk = __ballot(hit);
                         if (mk) {
                             if (hit)
                                 mylog[log_n + __popcll(mk & lanemask_lt())] =
-                                    ((uint64_t)(uint32_t)s << 32) | ((uint64_t)ql << 16) | (uint64_t)(row - p0);
+                                    ((uint64_t)(uint32_t)acc[m][nt][i] << 32) | qbits |
+                                    (uint64_t)(wrow + m * 16 + i - p0);
                             log_n += __popcll(mk);
-                            if (log_n > kLogCap - kWave) {
-                                flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0);
-                                log_n = 0;
-                            }
                         }
                     }
-                }
             }
         }
         if (log_n > 0) flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0);
