@@ -48,8 +48,8 @@ constexpr int kQG = 64;                           // queries per item
 constexpr int kKC = 16;                           // k-steps (x4 blocks) per chunk
 constexpr int kCodeStride = 9;                    // LDS row stride (dwords) for a chunk's 8 code dwords
 constexpr int kNB = 1024;                         // histogram bins per query
-constexpr int kLogCap = 1152;                     // logged hits per wave (one query tile = 1024 max)
-constexpr int kItemPts = 8192;                    // rows per item
+constexpr int kLogCap = 384;                      // logged hits per wave (one row tile of a query tile: 256 max)
+constexpr int kItemPts = 16384;                   // rows per item (row offsets fit the log's 16 bits)
 constexpr int kFbSlots = 4;                       // fallback workgroups
 constexpr int kSelThreads = 256;
 constexpr int kSelLds = 4096;                     // keys staged in LDS by the final select
@@ -131,6 +131,13 @@ __device__ __forceinline__ int32_t ld_coherent(const int32_t* p) {
 __device__ __forceinline__ uint32_t ld_coherent(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Orders this wave's LDS accesses across lanes (the hardware executes one
+// wave's LDS operations in order; this keeps the compiler from moving them).
+__device__ __forceinline__ void wave_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
 __device__ __forceinline__ int nibble(const uint8_t* row, int b) { return (row[b >> 1] >> (4 * (b & 1))) & 15; }
 
 // Sum of one row's table entries; the table is int8 [B][16] in LDS.
@@ -335,7 +342,7 @@ __device__ __forceinline__ void flush_log(const Problem& p, const ScanState& st,
 }
 
 // Raises tau of query q to the highest histogram edge with at least R appended
-// sums at or above it (one wave).
+// sums at or above it (one wave; general case, any window).
 __device__ __forceinline__ void refresh_tau(const ScanState& st, int q, int R) {
     const int lane = lane_id();
     const int32_t tcur = ld_coherent(st.tau + q);
@@ -356,10 +363,53 @@ __device__ __forceinline__ void refresh_tau(const ScanState& st, int q, int R) {
     }
 }
 
+// refresh_tau for the (up to 8) queries ql = w, w+8, ... of one wave that got
+// appends in this item, with every load of all of them issued together (one
+// round trip for thresholds and histogram tops, one for the 64-bin windows).
+__device__ __forceinline__ void refresh_tau_wave(const ScanState& st, const int32_t* qid_s, const uint32_t* qapp_s,
+                                                 int qn, int w, int R) {
+    const int lane = lane_id();
+    int qk = -1;
+    if (lane < 8) {
+        const int ql = w + kScanWaves * lane;
+        if (ql < qn && qapp_s[ql] > 0) qk = qid_s[ql];
+    }
+    if (__ballot(qk >= 0) == 0) return;
+    int32_t tc = INT_MIN;
+    int jm = 0;
+    if (qk >= 0) {
+        tc = ld_coherent(st.tau + qk);
+        jm = (int)ld_coherent(st.hmax + qk);
+    }
+    int qs[8], top[8], jt[8], v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        qs[k] = __shfl(qk, k, kWave);
+        top[k] = __shfl(jm, k, kWave);
+        const int32_t t = __shfl(tc, k, kWave);
+        jt[k] = t == INT_MIN ? 0 : hist_bin(t, st.hlo, st.hw);
+        const int j = top[k] - lane;
+        v[k] = (qs[k] >= 0 && j >= jt[k]) ? (int)ld_coherent(st.hist + (int64_t)qs[k] * kNB + j) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        if (qs[k] < 0) continue;
+        const int incl = wave_inclusive_sum(v[k]);
+        const uint64_t mk = __ballot(incl >= R);
+        if (mk) {
+            const int l = __ffsll((unsigned long long)mk) - 1;
+            if (lane == 0) atomicMax(st.tau + qs[k], (int32_t)(st.hlo + (int64_t)(top[k] - l) * st.hw));
+        } else if (top[k] - kWave >= jt[k]) {
+            refresh_tau(st, qs[k], R);  // the R-th best lies below the first window
+        }
+    }
+}
+
 __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) {
     __shared__ __align__(16) int8_t lut_s[kKC * 4 * kWave * 16];  // [kstep][ntile][lane][16]
-    __shared__ __align__(16) uint32_t code_s[kTilePts * kCodeStride];
+    __shared__ __align__(16) uint32_t code_s[2][kTilePts * kCodeStride];
     __shared__ uint64_t log_s[kScanWaves * kLogCap];
+    __shared__ __align__(16) uint32_t onehot_s[16 * 4];           // onehot_s[c] = 16 bytes, byte c = 1
     __shared__ int32_t qid_s[kQG];
     __shared__ uint32_t qapp_s[kQG];
     __shared__ int64_t item_s, p0_s, p1_s, qbase_s;
@@ -371,10 +421,17 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
     const int r16 = lane & 15, g = lane >> 4;
     const int64_t n_items = p.leaves ? a.itemoff[p.L] : a.n_items;
     uint64_t* mylog = log_s + w * kLogCap;
+    if (tid < 16) {
+        // center c: dword c/4 holds 1 << 8*(c%4), the other three dwords are 0
+#pragma unroll
+        for (int j = 0; j < 4; ++j) onehot_s[tid * 4 + j] = (tid >> 2) == j ? 1u << (8 * (tid & 3)) : 0u;
+    }
 
+    int64_t claimed = 0;  // thread 0: the next item, claimed while the current one computes
+    if (tid == 0) claimed = (int64_t)atomicAdd(&st.ctrl[0], 1u);
     for (;;) {
         if (tid == 0) {
-            const int64_t item = (int64_t)atomicAdd(&st.ctrl[0], 1u);
+            const int64_t item = claimed;
             item_s = item;
             if (item < n_items) {
                 int64_t p0, p1, qbase;
@@ -406,6 +463,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                 p1_s = p1;
                 qbase_s = qbase;
                 qn_s = qn;
+                claimed = (int64_t)atomicAdd(&st.ctrl[0], 1u);
             }
         }
         __syncthreads();
@@ -434,17 +492,28 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
             }
         };
         // code staging: thread t owns row tile0 + t, code bytes [32c, 32c+32)
-        auto load_codes = [&](int64_t tile0, int c, uint4& x0, uint4& x1) {
-            x0 = make_uint4(0, 0, 0, 0);
-            x1 = make_uint4(0, 0, 0, 0);
+        auto load_codes = [&](int64_t step, uint4& x0, uint4& x1) {
+            const int64_t tile0 = p0 + (step / a.nchunk) * kTilePts;
+            const int c = (int)(step % a.nchunk);
             const int64_t row = tile0 + tid;
-            if (row >= p1) return;
-            const uint8_t* src = p.codes + row * p.stride + 32 * c;
+            const bool live = row < p1;
             if (a.fast_codes) {
+                // always exactly two 16-byte loads from an in-bounds address (the
+                // row itself, or the item's last row), so the number of loads in
+                // flight is static; bytes outside the row's codes are zeroed after
+                const int64_t r = live ? row : p1 - 1;
+                const uint8_t* base = p.codes + r * p.stride;
                 const int avail = p.stride - 32 * c;
-                if (avail >= 16) x0 = *reinterpret_cast<const uint4*>(src);
-                if (avail >= 32) x1 = *reinterpret_cast<const uint4*>(src + 16);
+                const uint4 y0 = *reinterpret_cast<const uint4*>(base + (avail >= 16 ? 32 * c : 0));
+                const uint4 y1 = *reinterpret_cast<const uint4*>(base + (avail >= 32 ? 32 * c + 16 : 0));
+                const uint4 z = make_uint4(0, 0, 0, 0);
+                x0 = live && avail >= 16 ? y0 : z;
+                x1 = live && avail >= 32 ? y1 : z;
             } else {
+                x0 = make_uint4(0, 0, 0, 0);
+                x1 = make_uint4(0, 0, 0, 0);
+                if (!live) return;
+                const uint8_t* src = p.codes + row * p.stride + 32 * c;
                 const int cb = (p.B + 1) / 2 - 32 * c;  // code bytes of this row from the chunk start
                 uint32_t wd[8];
 #pragma unroll
@@ -459,94 +528,138 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                 x1 = make_uint4(wd[4], wd[5], wd[6], wd[7]);
             }
         };
-
-        if (a.nchunk == 1) stage_lut(0);
+        auto store_codes = [&](int buf, const uint4& x0, const uint4& x1) {
+            uint32_t* d = code_s[buf] + tid * kCodeStride;
+            d[0] = x0.x; d[1] = x0.y; d[2] = x0.z; d[3] = x0.w;
+            d[4] = x1.x; d[5] = x1.y; d[6] = x1.z; d[7] = x1.w;
+        };
 
         const int64_t ntiles = (p1 - p0 + kTilePts - 1) / kTilePts;
         const int64_t nsteps = ntiles * a.nchunk;
         uint4 px0, px1;
-        load_codes(p0, 0, px0, px1);
+        load_codes(0, px0, px1);
+        store_codes(0, px0, px1);
+        if (nsteps > 1) load_codes(1, px0, px1);
+        if (a.nchunk == 1) stage_lut(0);
+        __syncthreads();  // lut_s and qid_s for this item are complete
+
         v4i acc[4][4];
         int32_t tq[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
         int log_n = 0;
 
         for (int64_t step = 0; step < nsteps; ++step) {
-            const int64_t t = step / a.nchunk;
+            const int buf = (int)(step & 1);
+            const int64_t tile0 = p0 + (step / a.nchunk) * kTilePts;
             const int c = (int)(step % a.nchunk);
-            const int64_t tile0 = p0 + t * kTilePts;
             if (c == 0) {
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt) acc[m][nt] = v4i{0, 0, 0, 0};
+            }
+            // thresholds for this tile's filter (every step, so the number of
+            // loads in flight stays static); padded query slots read query 0
+            // and are disabled below
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
-                    const int ql = 16 * nt + r16;
-                    tq[nt] = ql < qn ? ld_coherent(st.tau + qid_s[ql]) : INT_MAX;
-                }
+            for (int nt = 0; nt < 4; ++nt) tq[nt] = ld_coherent(st.tau + qid_s[16 * nt + r16]);
+            if (a.nchunk > 1) {  // every wave is past the previous step's reads of lut_s
+                if (step > 0) __syncthreads();
+                stage_lut(c);
+                __syncthreads();
             }
-            if (a.nchunk > 1) stage_lut(c);
-            {
-                uint32_t* d = code_s + tid * kCodeStride;
-                d[0] = px0.x; d[1] = px0.y; d[2] = px0.z; d[3] = px0.w;
-                d[4] = px1.x; d[5] = px1.y; d[6] = px1.z; d[7] = px1.w;
-            }
-            __syncthreads();
-            if (step + 1 < nsteps) {
-                const int64_t t2 = (step + 1) / a.nchunk;
-                load_codes(p0 + t2 * kTilePts, (int)((step + 1) % a.nchunk), px0, px1);
-            }
-            const int ks = a.nkstep - c * kKC < kKC ? a.nkstep - c * kKC : kKC;
-            const uint32_t* crow = code_s + (w * 64 + r16) * kCodeStride;
+            const int ks = a.nkstep - c * kKC < kKC ? a.nkstep - c * kKC : kKC;  // even
+            const uint32_t* crow = code_s[buf] + (w * 64 + r16) * kCodeStride;
+            const int8_t* lutw = lut_s + lane * 16;
+            // k-steps go in pairs sharing one code dword per row tile (blocks
+            // 8j..8j+7); each step's A and B fragments are fetched from LDS one
+            // step ahead into alternating registers.
+            v4i aA[4], aB[4], bA[4], bB[4];
+            uint32_t cw[4], cwn[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) cw[m] = crow[m * 16 * kCodeStride];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) bA[nt] = *reinterpret_cast<const v4i*>(lutw + nt * kWave * 16);
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                aA[m] = *reinterpret_cast<const v4i*>(onehot_s + __builtin_amdgcn_ubfe(cw[m], 4 * g, 4) * 4);
             for (int j = 0; j < (ks >> 1); ++j) {
-                uint32_t cw[4];
+                const int s1 = 2 * j + 1;
 #pragma unroll
-                for (int m = 0; m < 4; ++m) cw[m] = crow[m * 16 * kCodeStride + j];
+                for (int nt = 0; nt < 4; ++nt)
+                    bB[nt] = *reinterpret_cast<const v4i*>(lutw + (s1 * 4 + nt) * kWave * 16);
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int s = 2 * j + s2;
-                    v4i bf[4];
+                for (int m = 0; m < 4; ++m)
+                    aB[m] = *reinterpret_cast<const v4i*>(onehot_s + __builtin_amdgcn_ubfe(cw[m], 16 + 4 * g, 4) * 4);
+                const bool more = j + 1 < (ks >> 1);
+                if (more) {
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) cwn[m] = crow[m * 16 * kCodeStride + j + 1];
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt)
-                        bf[nt] = *reinterpret_cast<const v4i*>(lut_s + ((s * 4 + nt) * kWave + lane) * 16);
-                    const uint32_t shf = 16 * s2 + 4 * g;
+                        acc[m][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aA[m], bA[nt], acc[m][nt], 0, 0, 0);
+                if (more) {
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt)
+                        bA[nt] = *reinterpret_cast<const v4i*>(lutw + ((s1 + 1) * 4 + nt) * kWave * 16);
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
-                        const v4i af = onehot16(cw[m] >> shf);
-#pragma unroll
-                        for (int nt = 0; nt < 4; ++nt)
-                            acc[m][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[nt], acc[m][nt], 0, 0, 0);
+                        cw[m] = cwn[m];
+                        aA[m] = *reinterpret_cast<const v4i*>(onehot_s + __builtin_amdgcn_ubfe(cw[m], 4 * g, 4) * 4);
                     }
                 }
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt)
+                        acc[m][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aB[m], bB[nt], acc[m][nt], 0, 0, 0);
             }
-            __syncthreads();
+            // Each wave stages and reads only its own 64 code rows, so with one
+            // 64-block chunk the waves need no workgroup barrier inside an item:
+            // a wave-scope fence orders this wave's reads of buf^1 (one step
+            // ago) before its new writes, and the waves drift apart, so one
+            // wave's filter overlaps the other wave's MFMAs on the same SIMD.
+            // Several chunks share lut_s, which is restaged every step.
+            if (a.nchunk > 1) __syncthreads();
+            wave_fence();
+            if (step + 1 < nsteps) store_codes(buf ^ 1, px0, px1);  // buf^1 was last read one step ago
+            if (step + 2 < nsteps) load_codes(step + 2, px0, px1);
+            wave_fence();
             if (c != a.nchunk - 1) continue;
 
             // filter: tile (m, nt) holds, in register i, the sum of row
             // 16m + 4g + i (of this wave's 64) for query 16nt + r16.  All
-            // accumulator indices are compile-time constants (no dynamic
-            // indexing, so the accumulators stay in registers); the log is
-            // flushed only between query tiles and always has room for one.
+            // accumulator indices are compile-time constants, so the
+            // accumulators stay in registers.  A full tile first tests each
+            // query tile's maximum against the thresholds; the log is flushed
+            // between row tiles and always has room for one (16 x 64 hits).
             const int64_t wrow = tile0 + w * 64 + 4 * g;
+            const bool full = tile0 + kTilePts <= p1;
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                if (16 * nt + r16 >= qn) tq[nt] = INT_MAX;
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
-                if (log_n > kLogCap - 16 * kWave) {
-                    flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0);
-                    log_n = 0;
+                if (full) {
+                    int32_t mx = acc[0][nt][0];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) mx = max(mx, acc[m][nt][i]);
+                    if (__ballot(mx >= tq[nt]) == 0) continue;
                 }
-                uint32_t hits = 0;
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        hits |= (uint32_t)(wrow + m * 16 + i < p1 && acc[m][nt][i] >= tq[nt]) << (4 * m + i);
-                if (__ballot(hits != 0) == 0) continue;
                 const uint64_t qbits = (uint64_t)(16 * nt + r16) << 16;
 #pragma unroll
-                for (int m = 0; m < 4; ++m)
+                for (int m = 0; m < 4; ++m) {
+                    if (log_n > kLogCap - 4 * kWave) {
+                        flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0);
+                        log_n = 0;
+                    }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const bool hit = (hits >> (4 * m + i)) & 1u;
+                        const bool hit = wrow + m * 16 + i < p1 && acc[m][nt][i] >= tq[nt];
                         const uint64_t mk = __ballot(hit);
                         if (mk) {
                             if (hit)
@@ -556,12 +669,12 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                             log_n += __popcll(mk);
                         }
                     }
+                }
             }
         }
         if (log_n > 0) flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0);
         __syncthreads();
-        for (int ql = w; ql < qn; ql += kScanWaves)
-            if (qapp_s[ql] > 0) refresh_tau(st, qid_s[ql], p.R);
+        refresh_tau_wave(st, qid_s, qapp_s, qn, w, p.R);
         __syncthreads();
     }
 }
