@@ -110,6 +110,26 @@ def ground_truth(w, X, Q, torch, k=10, shortlist=64):
     return gt
 
 
+def profiled_traffic(workload):
+    """HBM bytes per launch of the main scan kernel from the committed rocprofv3
+    summary (profiles/scan_main_<workload>.txt), or None when the kernel source
+    has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"scan_main_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "mips_ah_partition_amd", "csrc", "ah_scan.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("kernel_source", "").split()[-1:] != [sha]:
+        return None
+    return float(fields["scan_main_traffic_bytes"])
+
+
 def recall(found, truth):
     hit = 0
     for f, t in zip(found, truth):
@@ -153,11 +173,23 @@ def main():
     ap.add_argument("--workload", default="sift1m", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 1 GiB device-to-device 5 times (calibrates FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(the multi-GPU sharding is a design note, not a code path)"}))
         sys.exit(2)
+
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": src.numel() * 4, "launches": 5}))
+        return
 
     w = synth.WORKLOADS[args.workload]
     t0 = time.time()
@@ -236,7 +268,7 @@ def main():
         "reorder_gather_GBps": reorder_gbps,
         "roofline": {"kernel": "scan_main_kernel", "bound": "mfma", "achieved": achieved_tops,
                      "peak": PEAK_INT8_TOPS, "unit": "TOP/s", "frac": achieved_tops / PEAK_INT8_TOPS,
-                     "traffic": None},
+                     "traffic": profiled_traffic(w.name)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, ix, X, Q, gt, gpu_ids, args.cpu_budget)
