@@ -1,0 +1,194 @@
+"""Parity at the workloads' full sizes, in the launch configuration the benchmark
+uses, checked on sampled queries that the oracle computes one by one.
+
+Stage-chained like tests/test_gpu_parity.py: the oracle receives, for each sampled
+query, the same int8 table, leaves and candidates the GPU stage received.  Integer
+results must match exactly; float scores within 1e-4 relative (float64 reference,
+denominator max(|ref|, sum |a_j b_j|)).
+"""
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mips_ah_partition_amd import ahlib
+    ahlib.lib()
+    return torch, ahlib
+
+
+def _log(msg):
+    print(f"[fullsize {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+def _sample(nq, k=6):
+    return sorted(set([0, 1, nq // 3, nq // 2, nq - 2, nq - 1][:k]))
+
+
+def _check_scan(lut_q, codes, R, gpu_ids, gpu_sc, ids=None, offs=None, leaves_q=None):
+    o_ids, o_sc = oracle.scan_topk(lut_q, codes, R, ids=ids, leaf_offsets=offs, leaves=leaves_q)
+    assert np.array_equal(gpu_ids, o_ids), "top-R ids differ"
+    assert np.array_equal(gpu_sc, o_sc), "top-R sums differ"
+
+
+def _check_reorder(Qs, rows_of, cand, k, g_ids, g_sc):
+    """rows_of(ids) -> float64 rows; the oracle reorders the same candidates."""
+    for i in range(Qs.shape[0]):
+        c = cand[i][cand[i] >= 0]
+        Xr = rows_of(c)
+        ref = Xr @ Qs[i].astype(np.float64)
+        den = np.abs(Xr) @ np.abs(Qs[i].astype(np.float64))
+        order = np.lexsort((c, -ref))[:k]
+        gi = g_ids[i][g_ids[i] >= 0]
+        pos = {int(x): j for j, x in enumerate(c)}
+        gref = np.array([ref[pos[int(x)]] for x in gi])
+        gden = np.array([den[pos[int(x)]] for x in gi])
+        assert len(gi) == len(order)
+        assert (np.abs(g_sc[i][:len(gi)] - gref) <= TOL * np.maximum(np.abs(gref), gden)).all()
+        assert (np.abs(gref - ref[order]) <= 2 * TOL * np.maximum(np.abs(gref), gden)).all()
+
+
+def test_sift1m_bench_configuration(gpu):
+    """1,000,000 x 128 integer rows, 64 blocks x 2 dims, 10,000 queries, R=200,
+    k=10: the benchmark's configuration with its trained index."""
+    torch, ah = gpu
+    import bench
+    from mips_ah_partition_amd.search import AHIndex
+    w = synth.WORKLOADS["sift1m"]
+    X, Q = bench.workload_arrays(w)
+    ix = bench.load_index(w, X)
+    _log("index ready")
+    index = AHIndex(ix, X, reorder=w.reorder, final_num_neighbors=w.k)
+    Qd = torch.from_numpy(Q).cuda()
+    t8, s, beta, l32 = ah.ah_build_lut(Qd, index.codebooks, want_f32=True)
+    cand, csum = ah.ah_scan_topk(t8, index.codes, w.reorder)
+    fid, fsc = ah.ah_reorder_exact(Qd, index.base, cand, w.k)
+    torch.cuda.synchronize()
+    _log("gpu path done")
+    S = _sample(w.nq)
+    l32s, t8s = l32[S].cpu().numpy(), t8[S].cpu().numpy()
+    o8, os_, ob = oracle.quantize_lut(l32s)
+    assert np.array_equal(t8s, o8)
+    assert np.array_equal(s[S].cpu().numpy(), os_) and np.array_equal(beta[S].cpu().numpy(), ob)
+    ref = oracle.lut_f64(Q[S], ix.codebooks)
+    B, dpb = ix.codebooks.shape[0], ix.codebooks.shape[2]
+    den = np.einsum("qbt,bct->qbc", np.abs(Q[S].reshape(len(S), B, dpb)).astype(np.float64),
+                    np.abs(ix.codebooks).astype(np.float64))
+    assert (np.abs(l32s - ref) <= TOL * np.maximum(np.abs(ref), den)).all()
+    _check_scan(t8s, ix.codes, w.reorder, cand[S].cpu().numpy(), csum[S].cpu().numpy())
+    _log("scan sampled parity ok")
+    _check_reorder(Q[S], lambda c: X[c].astype(np.float64), cand[S].cpu().numpy(), w.k,
+                   fid[S].cpu().numpy(), fsc[S].cpu().numpy())
+    # property over every query: candidate sums are non-increasing, ids unique
+    c_all, s_all = cand.cpu().numpy(), csum.cpu().numpy()
+    assert (np.diff(s_all, axis=1) <= 0).all()
+    assert all(len(set(r.tolist())) == w.reorder for r in c_all[:: max(1, w.nq // 500)])
+
+
+def test_tiny_whole_path_every_query(gpu):
+    """10,000 x 128 unit rows, 32 blocks x 4 dims (eta = 1), 100 queries, R=100:
+    every query through every stage, against the oracle on the GPU's inputs."""
+    torch, ah = gpu
+    from mips_ah_partition_amd import index as ixm
+    w = synth.WORKLOADS["tiny"]
+    X = synth.database(w)
+    Q = synth.queries(w)
+    ix = ixm.build(X, w.dpb, w.eta, seed=1000 * w.index + synth.ROLE_CODEBOOK)
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    Qd = T(Q)
+    t8, s, beta, l32 = ah.ah_build_lut(Qd, T(ix.codebooks), want_f32=True)
+    cand, csum = ah.ah_scan_topk(t8, T(ix.codes), w.reorder)
+    fid, fsc = ah.ah_reorder_exact(Qd, T(X), cand, w.k)
+    torch.cuda.synchronize()
+    l32, t8 = l32.cpu().numpy(), t8.cpu().numpy()
+    assert np.array_equal(t8, oracle.quantize_lut(l32)[0])
+    _check_scan(t8, ix.codes, w.reorder, cand.cpu().numpy(), csum.cpu().numpy())
+    _check_reorder(Q, lambda c: X[c].astype(np.float64), cand.cpu().numpy(), w.k, fid.cpu().numpy(),
+                   fsc.cpu().numpy())
+    gt, _ = oracle.brute_force(Q, X, w.k)
+    res = oracle.search(Q, ix.codebooks, ix.codes, X, w.reorder, w.k)
+    assert oracle.recall_at_k(fid.cpu().numpy(), gt) >= oracle.recall_at_k(res["ids"], gt) - 0.01
+
+
+def _partitioned_case(gpu, name, generate_originals_on_gpu):
+    """Full-size partitioned shapes with synthetic structure: lognormal leaf sizes,
+    random codes and id permutation, random centroids; real mixture queries."""
+    torch, ah = gpu
+    w = synth.WORKLOADS[name]
+    rng = np.random.default_rng(7000 + w.index)
+    B, n, L = w.blocks, w.n, w.num_leaves
+    _log(f"{name}: generating {n} x {w.code_bytes} B codes")
+    codes = np.empty((n, w.code_bytes), dtype=np.uint8)
+    step = 1 << 21
+    for a in range(0, n, step):
+        codes[a:a + step] = rng.integers(0, 256, size=(min(step, n - a), w.code_bytes), dtype=np.uint8)
+    sizes = synth.random_leaf_sizes(rng, n, L, skew=0.7)
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    perm = rng.permutation(n).astype(np.int32)
+    Q = synth.queries(w)
+    cent = rng.standard_normal((L, w.d)).astype(np.float32)
+    cb = (rng.standard_normal((B, 16, w.dpb)) * 0.1).astype(np.float32)
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    Qd = T(Q)
+    codes_d, offs_d, perm_d = T(codes), T(offs), T(perm)
+    _log(f"{name}: running the path")
+    leaves, lsc = ah.ah_partition_score(Qd, T(cent), w.leaves_to_search)
+    t8, s, beta, l32 = ah.ah_build_lut(Qd, T(cb), want_f32=True)
+    cand, csum = ah.ah_scan_topk(t8, codes_d, w.reorder, ids=perm_d, leaf_offsets=offs_d, leaves=leaves)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9000 + w.index)
+    if generate_originals_on_gpu:
+        base = torch.randn((n, w.d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    else:
+        base = torch.randn((n, w.d), generator=g, device="cuda", dtype=torch.float32)
+    fid, fsc = ah.ah_reorder_exact(Qd, base, cand, w.k)
+    torch.cuda.synchronize()
+    _log(f"{name}: gpu path done")
+    S = _sample(w.nq, 4)
+    lv = leaves[S].cpu().numpy()
+    o_lv, o_ls = oracle.partition(Q[S], cent, w.leaves_to_search)
+    gls = lsc[S].cpu().numpy()
+    Cd, Qs = cent.astype(np.float64), Q[S].astype(np.float64)
+    for i in range(len(S)):
+        ref = Cd[lv[i]] @ Qs[i]
+        den = np.abs(Cd[lv[i]]) @ np.abs(Qs[i])
+        assert (np.abs(gls[i] - ref) <= TOL * np.maximum(np.abs(ref), den)).all()
+        assert (np.abs(ref - o_ls[i]) <= 2 * TOL * np.maximum(np.abs(ref), den)).all()
+    t8s = t8[S].cpu().numpy()
+    assert np.array_equal(t8s, oracle.quantize_lut(l32[S].cpu().numpy())[0])
+    _check_scan(t8s, codes, w.reorder, cand[S].cpu().numpy(), csum[S].cpu().numpy(), ids=perm, offs=offs,
+                leaves_q=lv)
+    _log(f"{name}: scan sampled parity ok")
+    cs = cand[S].cpu().numpy()
+    rows = {}
+    for i in range(len(S)):
+        c = cs[i][cs[i] >= 0]
+        r = base[torch.from_numpy(c.astype(np.int64)).cuda()].float().cpu().numpy().astype(np.float64)
+        rows.update({int(x): r[j] for j, x in enumerate(c)})
+    _check_reorder(Q[S], lambda c: np.stack([rows[int(x)] for x in c]), cs, w.k, fid[S].cpu().numpy(),
+                   fsc[S].cpu().numpy())
+    s_all = csum.cpu().numpy()
+    assert (np.diff(s_all, axis=1) <= 0).all()
+
+
+def test_glove1m_partitioned_shape(gpu):
+    _partitioned_case(gpu, "glove1m", False)
+
+
+def test_openai2m_partitioned_shape(gpu):
+    _partitioned_case(gpu, "openai2m", True)
+
+
+def test_wiki20m_partitioned_shape(gpu):
+    _partitioned_case(gpu, "wiki20m", True)
