@@ -14,26 +14,30 @@
 //      sums[i][q] = sum_{b,c} onehot[i][(b,c)] * T8[q][(b,c)]
 //    with K = 16*B.  The scan runs it on the int8 matrix cores
 //    (v_mfma_i32_16x16x64_i8: exact int32 accumulation): the A operand is the
-//    one-hot expansion of 16 rows' codes, built in registers (one block per lane
-//    per k-step, 16 bytes with a single 1), the B operand is 16 queries' table
-//    rows, resident in LDS.  Each lane of a 16-lane group feeds its own block,
-//    and A and B use the same (lane group, byte) -> (block, center) map, so the
-//    hardware's internal k order does not matter.
+//    one-hot expansion of 16 rows' codes, read from a 16-entry LDS table (one
+//    block per lane per k-step, 16 bytes with a single 1), the B operand is 16
+//    queries' table rows, resident in LDS.  Each lane of a 16-lane group feeds
+//    its own block, and A and B use the same (lane group, byte) -> (block,
+//    center) map, so the hardware's internal k order does not matter.
 //  * A workgroup (8 waves) owns up to 64 queries and a run of rows (a leaf, or a
-//    chunk of the database); each wave takes 64 rows x 64 queries per tile
+//    chunk of the database); each wave takes 64 rows x 64 queries per step
 //    (4 x 4 MFMA tiles), so every code byte fetched from HBM is used by all the
 //    workgroup's queries and every one-hot operand by 4 query tiles.  The
 //    tables stay in LDS (64 blocks x 64 queries = 64 KB per pass; more blocks
-//    are processed in 64-block chunks); codes are streamed into LDS with 16-byte
-//    loads, prefetched one step ahead.
+//    are processed in 64-block chunks).  With one chunk, the waves claim 64-row
+//    slabs from an LDS counter and need no barrier until the item ends; each
+//    wave streams its slab's codes into its own LDS buffer with 16-byte loads
+//    issued a step ahead.
 //  * Top-R without materialising sums: every query has a monotone threshold tau
 //    (a lower bound on its R-th best sum).  A warm-up kernel sets it from the
-//    query's first rows; rows at or above it are logged per wave in LDS and
-//    appended to the query's candidate list; a histogram of the appended sums
-//    lets each workgroup raise tau after every item (count(sum >= edge) >= R
-//    makes the edge a valid bound).  A final kernel selects each query's exact
-//    top-R from its list; a query whose list overflows is recomputed by a slow
-//    exact fallback, so the result never depends on timing.
+//    query's first rows; a step's sums are tested against it per query tile,
+//    then per row tile, then per element, and rows at or above it are logged
+//    per wave in LDS and appended to the query's candidate list (one slot
+//    reservation per query and flush); a histogram of the appended sums lets
+//    each workgroup raise tau after every item (count(sum >= edge) >= R makes
+//    the edge a valid bound).  A final kernel selects each query's exact top-R
+//    from its list; a query whose list overflows is recomputed by a slow exact
+//    fallback, so the result never depends on timing.
 #include "ah_device.hpp"
 #include "ah_kernels.hpp"
 
@@ -307,37 +311,64 @@ __device__ __forceinline__ v4i onehot16(uint32_t x) {
 
 // Appends a wave's logged hits to the queries' candidate lists and histograms.
 // Log entry: sum (high 32 bits) | local query (bits 16..21) | row - p0 (low 16).
+// Each lane takes four entries per pass.  The pass first counts its entries
+// per local query in the wave's LDS scratch (wq: 64 counters, wm: 64 bin
+// maxima), then reserves each query's list slots with one global atomic per
+// query, so the per-query counters see one atomic per pass instead of one per
+// hit and no two lanes of an atomic share an address.
 __device__ __forceinline__ void flush_log(const Problem& p, const ScanState& st, const uint64_t* log,
-                                          int log_n, const int32_t* qid_s, uint32_t* qapp_s, int64_t p0) {
+                                          int log_n, const int32_t* qid_s, uint32_t* qapp_s, int64_t p0,
+                                          uint32_t* wq, uint32_t* wm) {
     const int lane = lane_id();
     for (int base = 0; base < log_n; base += 4 * kWave) {
+        wq[lane] = 0;
+        wm[lane] = 0;
+        wave_fence();
         uint64_t ent[4];
-        uint32_t slot[4];
-        int32_t idv[4];
-        int qq[4];
         bool ok[4];
+        int ql[4];
+        uint32_t li[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int e = base + u * kWave + lane;
             ok[u] = e < log_n;
-            ent[u] = ok[u] ? log[e] : 0;
-            qq[u] = qid_s[(ent[u] >> 16) & 63];
-            const int64_t row = p0 + (int64_t)(ent[u] & 0xFFFF);
-            if (ok[u]) {
-                slot[u] = atomicAdd(&st.cnt[qq[u]], 1u);
-                idv[u] = p.ids ? p.ids[row] : (int32_t)row;
-            }
+            ent[u] = log[ok[u] ? e : 0];
+            ql[u] = (int)((ent[u] >> 16) & 63);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {  // lanes without an entry add 0 to their own counter
+            li[u] = atomicAdd(&wq[ok[u] ? ql[u] : lane], ok[u] ? 1u : 0u);
+            if (ok[u]) atomicMax(&wm[ql[u]], (uint32_t)hist_bin((int32_t)(uint32_t)(ent[u] >> 32), st.hlo, st.hw));
+        }
+        wave_fence();
+        const uint32_t c = wq[lane];
+        const int q = qid_s[lane];
+        uint32_t gb = 0;
+        if (c) {
+            gb = atomicAdd(&st.cnt[q], c);
+            atomicMax(&st.hmax[q], wm[lane]);
+            atomicAdd(&qapp_s[lane], c);
+        }
+        wq[lane] = gb;
+        wave_fence();
+        int32_t idv[4];
+        if (p.ids) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) idv[u] = p.ids[ok[u] ? p0 + (int64_t)(ent[u] & 0xFFFF) : p0];
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) idv[u] = (int32_t)(p0 + (int64_t)(ent[u] & 0xFFFF));
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             if (!ok[u]) continue;
-            const int32_t s = (int32_t)(uint32_t)(ent[u] >> 32);
-            if ((int64_t)slot[u] < st.cap) st.cand[(int64_t)qq[u] * st.cap + slot[u]] = int_key(s, idv[u]);
-            const int bin = hist_bin(s, st.hlo, st.hw);
-            atomicAdd(&st.hist[(int64_t)qq[u] * kNB + bin], 1u);
-            atomicMax(&st.hmax[qq[u]], (uint32_t)bin);
-            atomicAdd(&qapp_s[(ent[u] >> 16) & 63], 1u);
+            const int32_t sv = (int32_t)(uint32_t)(ent[u] >> 32);
+            const int qq = qid_s[ql[u]];
+            const uint32_t slot = wq[ql[u]] + li[u];
+            if ((int64_t)slot < st.cap) st.cand[(int64_t)qq * st.cap + slot] = int_key(sv, idv[u]);
+            atomicAdd(&st.hist[(int64_t)qq * kNB + hist_bin(sv, st.hlo, st.hw)], 1u);
         }
+        wave_fence();
     }
 }
 
@@ -412,7 +443,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
     __shared__ __align__(16) uint32_t onehot_s[16 * 4];           // onehot_s[c] = 16 bytes, byte c = 1
     __shared__ int32_t qid_s[kQG];
     __shared__ uint32_t qapp_s[kQG];
+    __shared__ uint32_t fl_s[kScanWaves * 2 * kWave];  // per-wave flush scratch
     __shared__ int64_t item_s, p0_s, p1_s, qbase_s;
+    __shared__ uint32_t slab_s;  // next 64-row slab of the item (one 64-block chunk)
     __shared__ int32_t qn_s;
 
     const Problem& p = a.p;
@@ -421,6 +454,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
     const int r16 = lane & 15, g = lane >> 4;
     const int64_t n_items = p.leaves ? a.itemoff[p.L] : a.n_items;
     uint64_t* mylog = log_s + w * kLogCap;
+    uint32_t* mywq = fl_s + w * 2 * kWave;
     if (tid < 16) {
         // center c: dword c/4 holds 1 << 8*(c%4), the other three dwords are 0
 #pragma unroll
@@ -463,6 +497,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                 p1_s = p1;
                 qbase_s = qbase;
                 qn_s = qn;
+                slab_s = 0;
                 claimed = (int64_t)atomicAdd(&st.ctrl[0], 1u);
             }
         }
@@ -491,25 +526,25 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                 *reinterpret_cast<v4i*>(lut_s + e * 16) = v;
             }
         };
-        // code staging: thread t owns row tile0 + t, code bytes [32c, 32c+32)
-        auto load_codes = [&](int64_t step, uint4& x0, uint4& x1) {
-            const int64_t tile0 = p0 + (step / a.nchunk) * kTilePts;
-            const int c = (int)(step % a.nchunk);
-            const int64_t row = tile0 + tid;
+        // code staging: lane l of a wave owns row rowbase + l, code bytes
+        // [32c, 32c+32).  A staged pair of 16-byte words carries a keep mask
+        // (bit 0: first word, bit 1: second); the words are zeroed by the mask
+        // only when they are stored, so the loads stay in flight for a step.
+        auto load_codes = [&](int64_t rowbase, int c, uint4& x0, uint4& x1, uint32_t& keep) {
+            const int64_t row = rowbase + lane;
             const bool live = row < p1;
             if (a.fast_codes) {
                 // always exactly two 16-byte loads from an in-bounds address (the
                 // row itself, or the item's last row), so the number of loads in
-                // flight is static; bytes outside the row's codes are zeroed after
+                // flight is static
                 const int64_t r = live ? row : p1 - 1;
                 const uint8_t* base = p.codes + r * p.stride;
                 const int avail = p.stride - 32 * c;
-                const uint4 y0 = *reinterpret_cast<const uint4*>(base + (avail >= 16 ? 32 * c : 0));
-                const uint4 y1 = *reinterpret_cast<const uint4*>(base + (avail >= 32 ? 32 * c + 16 : 0));
-                const uint4 z = make_uint4(0, 0, 0, 0);
-                x0 = live && avail >= 16 ? y0 : z;
-                x1 = live && avail >= 32 ? y1 : z;
+                x0 = *reinterpret_cast<const uint4*>(base + (avail >= 16 ? 32 * c : 0));
+                x1 = *reinterpret_cast<const uint4*>(base + (avail >= 32 ? 32 * c + 16 : 0));
+                keep = (live && avail >= 16 ? 1u : 0u) | (live && avail >= 32 ? 2u : 0u);
             } else {
+                keep = 3u;
                 x0 = make_uint4(0, 0, 0, 0);
                 x1 = make_uint4(0, 0, 0, 0);
                 if (!live) return;
@@ -528,42 +563,66 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                 x1 = make_uint4(wd[4], wd[5], wd[6], wd[7]);
             }
         };
-        auto store_codes = [&](int buf, const uint4& x0, const uint4& x1) {
+        auto store_codes = [&](int buf, const uint4& x0, const uint4& x1, uint32_t keep) {
             uint32_t* d = code_s[buf] + tid * kCodeStride;
-            d[0] = x0.x; d[1] = x0.y; d[2] = x0.z; d[3] = x0.w;
-            d[4] = x1.x; d[5] = x1.y; d[6] = x1.z; d[7] = x1.w;
+            const uint32_t k0 = (keep & 1u) ? 0xFFFFFFFFu : 0u, k1 = (keep & 2u) ? 0xFFFFFFFFu : 0u;
+            d[0] = x0.x & k0; d[1] = x0.y & k0; d[2] = x0.z & k0; d[3] = x0.w & k0;
+            d[4] = x1.x & k1; d[5] = x1.y & k1; d[6] = x1.z & k1; d[7] = x1.w & k1;
         };
 
-        const int64_t ntiles = (p1 - p0 + kTilePts - 1) / kTilePts;
-        const int64_t nsteps = ntiles * a.nchunk;
+        // A wave's steps.  With one 64-block chunk, each step is a 64-row slab
+        // that the wave claims from the item's LDS counter, so the waves of an
+        // item finish within one slab of each other.  With several chunks, the
+        // waves share each chunk's table and step through the 512-row tiles in
+        // lockstep: step = tile * nchunk + c, rows tile * 512 + 64 w onwards.
+        const bool dyn = a.nchunk == 1;
+        const int64_t nslabs = (p1 - p0 + 63) / 64;
+        const int64_t nsteps = ((p1 - p0 + kTilePts - 1) / kTilePts) * a.nchunk;
+        auto claim = [&]() -> int64_t {
+            uint32_t v = 0;
+            if (lane == 0) v = atomicAdd(&slab_s, 1u);
+            return (int64_t)__builtin_amdgcn_readfirstlane(v);
+        };
+        // (u, c): unit (slab, or tile) and chunk of a step; valid while u < nunits
+        const int64_t nunits = dyn ? nslabs : nsteps / a.nchunk;
+        auto rowbase_of = [&](int64_t u) { return dyn ? p0 + 64 * u : p0 + u * kTilePts + 64 * w; };
+        int64_t cu = 0, nu = 0;  // current and next unit
+        int cc = 0, nc = 0;      // their chunks
+        auto step_after = [&](int64_t& u, int& c) {
+            if (dyn) { u = claim(); return; }
+            if (++c == a.nchunk) { c = 0; ++u; }
+        };
+        if (dyn) cu = claim();
+        nu = cu; nc = cc;
+        step_after(nu, nc);
         uint4 px0, px1;
-        load_codes(0, px0, px1);
-        store_codes(0, px0, px1);
-        if (nsteps > 1) load_codes(1, px0, px1);
+        uint32_t pkeep;
+        if (cu < nunits) {
+            load_codes(rowbase_of(cu), cc, px0, px1, pkeep);
+            store_codes(0, px0, px1, pkeep);
+        }
+        if (nu < nunits) load_codes(rowbase_of(nu), nc, px0, px1, pkeep);
         if (a.nchunk == 1) stage_lut(0);
-        __syncthreads();  // lut_s and qid_s for this item are complete
+        __syncthreads();  // lut_s, qid_s and the first codes for this item are complete
 
         v4i acc[4][4];
         int32_t tq[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
         int log_n = 0;
 
-        for (int64_t step = 0; step < nsteps; ++step) {
-            const int buf = (int)(step & 1);
-            const int64_t tile0 = p0 + (step / a.nchunk) * kTilePts;
-            const int c = (int)(step % a.nchunk);
+        for (int buf = 0; cu < nunits; buf ^= 1) {
+            const int c = cc;
             if (c == 0) {
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt) acc[m][nt] = v4i{0, 0, 0, 0};
             }
-            // thresholds for this tile's filter (every step, so the number of
-            // loads in flight stays static); padded query slots read query 0
-            // and are disabled below
+            // thresholds for this step's filter, loaded every step (padded
+            // query slots read query 0 and are disabled in the filter)
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) tq[nt] = ld_coherent(st.tau + qid_s[16 * nt + r16]);
-            if (a.nchunk > 1) {  // every wave is past the previous step's reads of lut_s
-                if (step > 0) __syncthreads();
+            if (!dyn) {  // every wave is past the previous step's reads of lut_s
+                if (c > 0 || cu > 0) __syncthreads();
                 stage_lut(c);
                 __syncthreads();
             }
@@ -616,63 +675,69 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                     for (int nt = 0; nt < 4; ++nt)
                         acc[m][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aB[m], bB[nt], acc[m][nt], 0, 0, 0);
             }
-            // Each wave stages and reads only its own 64 code rows, so with one
-            // 64-block chunk the waves need no workgroup barrier inside an item:
-            // a wave-scope fence orders this wave's reads of buf^1 (one step
-            // ago) before its new writes, and the waves drift apart, so one
-            // wave's filter overlaps the other wave's MFMAs on the same SIMD.
-            // Several chunks share lut_s, which is restaged every step.
-            if (a.nchunk > 1) __syncthreads();
-            wave_fence();
-            if (step + 1 < nsteps) store_codes(buf ^ 1, px0, px1);  // buf^1 was last read one step ago
-            if (step + 2 < nsteps) load_codes(step + 2, px0, px1);
-            wave_fence();
-            if (c != a.nchunk - 1) continue;
-
-            // filter: tile (m, nt) holds, in register i, the sum of row
-            // 16m + 4g + i (of this wave's 64) for query 16nt + r16.  All
-            // accumulator indices are compile-time constants, so the
-            // accumulators stay in registers.  A full tile first tests each
-            // query tile's maximum against the thresholds; the log is flushed
-            // between row tiles and always has room for one (16 x 64 hits).
-            const int64_t wrow = tile0 + w * 64 + 4 * g;
-            const bool full = tile0 + kTilePts <= p1;
+            if (c == a.nchunk - 1) {
+                // filter: tile (m, nt) holds, in register i, the sum of row
+                // 16m + 4g + i (of this wave's 64) for query 16nt + r16.  All
+                // accumulator indices are compile-time constants, so the
+                // accumulators stay in registers.  A query tile is tested by
+                // its maximum, then each row tile by its own, and only row
+                // tiles holding a sum at or above a threshold are tested
+                // element by element; rows past the item's end (a partial
+                // slab) are dropped there.  The log is flushed between row
+                // tiles and always has room for one (4 x 64 hits).
+                const int32_t lrow0 = (int32_t)(rowbase_of(cu) - p0) + 4 * g;  // item-local row of (m, i) = (0, 0)
+                const int32_t nloc = (int32_t)(p1 - p0);
+                const bool full = rowbase_of(cu) + 64 <= p1;
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-                if (16 * nt + r16 >= qn) tq[nt] = INT_MAX;
+                for (int nt = 0; nt < 4; ++nt)
+                    if (16 * nt + r16 >= qn) tq[nt] = INT_MAX;
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                if (full) {
-                    int32_t mx = acc[0][nt][0];
+                for (int nt = 0; nt < 4; ++nt) {
+                    int32_t mm[4];
 #pragma unroll
                     for (int m = 0; m < 4; ++m)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) mx = max(mx, acc[m][nt][i]);
+                        mm[m] = max(max(acc[m][nt][0], acc[m][nt][1]), max(acc[m][nt][2], acc[m][nt][3]));
+                    const int32_t mx = max(max(mm[0], mm[1]), max(mm[2], mm[3]));
                     if (__ballot(mx >= tq[nt]) == 0) continue;
-                }
-                const uint64_t qbits = (uint64_t)(16 * nt + r16) << 16;
+                    const uint64_t qbits = (uint64_t)(16 * nt + r16) << 16;
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    if (log_n > kLogCap - 4 * kWave) {
-                        flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0);
-                        log_n = 0;
-                    }
+                    for (int m = 0; m < 4; ++m) {
+                        if (__ballot(mm[m] >= tq[nt]) == 0) continue;
+                        if (log_n > kLogCap - 4 * kWave) {
+                            flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave);
+                            log_n = 0;
+                        }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const bool hit = wrow + m * 16 + i < p1 && acc[m][nt][i] >= tq[nt];
-                        const uint64_t mk = __ballot(hit);
-                        if (mk) {
-                            if (hit)
-                                mylog[log_n + __popcll(mk & lanemask_lt())] =
-                                    ((uint64_t)(uint32_t)acc[m][nt][i] << 32) | qbits |
-                                    (uint64_t)(wrow + m * 16 + i - p0);
-                            log_n += __popcll(mk);
+                        for (int i = 0; i < 4; ++i) {
+                            const int32_t lr = lrow0 + 16 * m + i;
+                            const bool hit = acc[m][nt][i] >= tq[nt] && (full || lr < nloc);
+                            const uint64_t mk = __ballot(hit);
+                            if (mk) {
+                                if (hit)
+                                    mylog[log_n + __popcll(mk & lanemask_lt())] =
+                                        ((uint64_t)(uint32_t)acc[m][nt][i] << 32) | qbits | (uint64_t)(uint32_t)lr;
+                                log_n += __popcll(mk);
+                            }
                         }
                     }
                 }
             }
+            // Each wave stages and reads only its own 64 code rows, so with one
+            // chunk the waves need no workgroup barrier inside an item: a
+            // wave-scope fence orders this wave's reads of buf^1 (one step ago)
+            // before its new writes.  Several chunks share lut_s, which is
+            // restaged every step.  The next step's loads are issued after the
+            // filter, whose wait for the thresholds would otherwise wait for them.
+            if (!dyn) __syncthreads();
+            wave_fence();
+            if (nu < nunits) store_codes(buf ^ 1, px0, px1, pkeep);  // buf^1 was last read one step ago
+            cu = nu;
+            cc = nc;
+            step_after(nu, nc);
+            if (nu < nunits) load_codes(rowbase_of(nu), nc, px0, px1, pkeep);
+            wave_fence();
         }
-        if (log_n > 0) flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0);
+        if (log_n > 0) flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave);
         __syncthreads();
         refresh_tau_wave(st, qid_s, qapp_s, qn, w, p.R);
         __syncthreads();
