@@ -52,6 +52,7 @@ constexpr int kQG = 64;                           // queries per item
 constexpr int kKC = 16;                           // k-steps (x4 blocks) per chunk
 constexpr int kCodeStride = 9;                    // LDS row stride (dwords) for a chunk's 8 code dwords
 constexpr int kNB = 1024;                         // histogram bins per query
+constexpr int kLB = 64;                           // an item's LDS histogram bins per query
 constexpr int kLogCap = 384;                      // logged hits per wave (one row tile of a query tile: 256 max)
 constexpr int kItemPts = 16384;                   // rows per item (row offsets fit the log's 16 bits)
 constexpr int kFbSlots = 4;                       // fallback workgroups
@@ -105,7 +106,7 @@ struct ScanState {
     int32_t* ovf;
     uint64_t* fb;
     int64_t cap;
-    int32_t hlo, hw;
+    int32_t hlo, hw, hsh;  // bin b covers sums [hlo + b*hw, hlo + (b+1)*hw), hw = 1 << hsh
 };
 
 struct Problem {
@@ -125,9 +126,10 @@ struct Problem {
     int32_t* out_scores;
 };
 
-__device__ __forceinline__ int hist_bin(int32_t s, int32_t hlo, int32_t hw) {
-    int64_t j = ((int64_t)s - hlo) / hw;
-    return (int)(j < 0 ? 0 : (j >= kNB ? kNB - 1 : j));
+__device__ __forceinline__ int hist_bin(int32_t s, int32_t hlo, int32_t hsh) {
+    const int64_t d = (int64_t)s - hlo;
+    const int64_t j = d < 0 ? 0 : d >> hsh;
+    return (int)(j >= kNB ? kNB - 1 : j);
 }
 __device__ __forceinline__ int32_t ld_coherent(const int32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -309,16 +311,18 @@ __device__ __forceinline__ v4i onehot16(uint32_t x) {
     return r;
 }
 
-// Appends a wave's logged hits to the queries' candidate lists and histograms.
-// Log entry: sum (high 32 bits) | local query (bits 16..21) | row - p0 (low 16).
-// Each lane takes four entries per pass.  The pass first counts its entries
-// per local query in the wave's LDS scratch (wq: 64 counters, wm: 64 bin
-// maxima), then reserves each query's list slots with one global atomic per
-// query, so the per-query counters see one atomic per pass instead of one per
-// hit and no two lanes of an atomic share an address.
+// Appends a wave's logged hits to the queries' candidate lists and counts them
+// in the item's LDS histogram (lh: kLB bins per local query, starting at the
+// query's global bin jb_s at item start; the top bin also takes everything
+// above it).  Log entry: sum (high 32 bits) | local query (bits 16..21) |
+// row - p0 (low 16).  Each lane takes four entries per pass.  The pass first
+// counts its entries per local query in the wave's LDS scratch (wq), then
+// reserves each query's list slots with one global atomic per query, so the
+// per-query counters see one atomic per pass instead of one per hit and no
+// two lanes of an atomic share an address.
 __device__ __forceinline__ void flush_log(const Problem& p, const ScanState& st, const uint64_t* log,
                                           int log_n, const int32_t* qid_s, uint32_t* qapp_s, int64_t p0,
-                                          uint32_t* wq, uint32_t* wm) {
+                                          uint32_t* wq, uint32_t* wm, uint32_t* lh, const int32_t* jb_s) {
     const int lane = lane_id();
     for (int base = 0; base < log_n; base += 4 * kWave) {
         wq[lane] = 0;
@@ -338,7 +342,15 @@ __device__ __forceinline__ void flush_log(const Problem& p, const ScanState& st,
 #pragma unroll
         for (int u = 0; u < 4; ++u) {  // lanes without an entry add 0 to their own counter
             li[u] = atomicAdd(&wq[ok[u] ? ql[u] : lane], ok[u] ? 1u : 0u);
-            if (ok[u]) atomicMax(&wm[ql[u]], (uint32_t)hist_bin((int32_t)(uint32_t)(ent[u] >> 32), st.hlo, st.hw));
+            if (ok[u]) {
+                // a logged sum is at or above the threshold the item started
+                // with, so its bin is at least jb_s; anything lower would be
+                // dropped (never counted where it could overstate a bound)
+                const int gbin = hist_bin((int32_t)(uint32_t)(ent[u] >> 32), st.hlo, st.hsh);
+                const int bl = gbin - jb_s[ql[u]];
+                if (bl >= 0) atomicAdd(&lh[ql[u] * kLB + (bl < kLB ? bl : kLB - 1)], 1u);
+                atomicMax(&wm[ql[u]], (uint32_t)gbin);
+            }
         }
         wave_fence();
         const uint32_t c = wq[lane];
@@ -363,13 +375,39 @@ __device__ __forceinline__ void flush_log(const Problem& p, const ScanState& st,
         for (int u = 0; u < 4; ++u) {
             if (!ok[u]) continue;
             const int32_t sv = (int32_t)(uint32_t)(ent[u] >> 32);
-            const int qq = qid_s[ql[u]];
             const uint32_t slot = wq[ql[u]] + li[u];
+            const int qq = qid_s[ql[u]];
             if ((int64_t)slot < st.cap) st.cand[(int64_t)qq * st.cap + slot] = int_key(sv, idv[u]);
-            atomicAdd(&st.hist[(int64_t)qq * kNB + hist_bin(sv, st.hlo, st.hw)], 1u);
+            atomicAdd(&st.hist[(int64_t)qq * kNB + hist_bin(sv, st.hlo, st.hsh)], 1u);
         }
         wave_fence();
     }
+}
+
+// Raises the item-local thresholds of one wave's queries (ql = w, w+8, ...) to
+// the highest LDS-histogram edge with at least R of this item's appended sums
+// at or above it: those are real rows, so the edge is a valid lower bound.
+__device__ __forceinline__ void local_refresh(const uint32_t* lh, int32_t* tau_s, const int32_t* jb_s, int qn, int w,
+                                              int R, int32_t hlo, int32_t hsh) {
+    const int lane = lane_id();
+    const int b = kLB - 1 - lane;  // lane 0 owns the highest bin
+#pragma unroll 1
+    for (int k = 0; k < kQG / kScanWaves; ++k) {
+        const int ql = w + kScanWaves * k;
+        if (ql >= qn) break;
+        const int incl = wave_inclusive_sum((int)lh[ql * kLB + b]);
+        const uint64_t mk = __ballot(incl >= R);
+        if (mk && lane == __ffsll((unsigned long long)mk) - 1)
+            atomicMax(&tau_s[ql], (int32_t)(hlo + ((int64_t)(jb_s[ql] + b) << hsh)));
+    }
+}
+
+// Publishes one wave's queries' item-local thresholds (ql = w, w+8, ...).
+__device__ __forceinline__ void publish_item(const ScanState& st, const int32_t* tau_s, const int32_t* qid_s, int qn,
+                                             int w) {
+    const int lane = lane_id();
+    const int ql = w + kScanWaves * lane;
+    if (lane < kQG / kScanWaves && ql < qn) atomicMax(st.tau + qid_s[ql], tau_s[ql]);
 }
 
 // Raises tau of query q to the highest histogram edge with at least R appended
@@ -377,7 +415,7 @@ __device__ __forceinline__ void flush_log(const Problem& p, const ScanState& st,
 __device__ __forceinline__ void refresh_tau(const ScanState& st, int q, int R) {
     const int lane = lane_id();
     const int32_t tcur = ld_coherent(st.tau + q);
-    const int jt = tcur == INT_MIN ? 0 : hist_bin(tcur, st.hlo, st.hw);
+    const int jt = tcur == INT_MIN ? 0 : hist_bin(tcur, st.hlo, st.hsh);
     const int jm = (int)ld_coherent(st.hmax + q);
     int cum = 0;
     for (int top = jm; top >= jt; top -= kWave) {
@@ -387,7 +425,7 @@ __device__ __forceinline__ void refresh_tau(const ScanState& st, int q, int R) {
         const uint64_t mk = __ballot(cum + incl >= R);
         if (mk) {
             const int l = __ffsll((unsigned long long)mk) - 1;
-            if (lane == 0) atomicMax(st.tau + q, (int32_t)(st.hlo + (int64_t)(top - l) * st.hw));
+            if (lane == 0) atomicMax(st.tau + q, (int32_t)(st.hlo + ((int64_t)(top - l) << st.hsh)));
             return;
         }
         cum += __shfl(incl, kWave - 1, kWave);
@@ -418,7 +456,7 @@ __device__ __forceinline__ void refresh_tau_wave(const ScanState& st, const int3
         qs[k] = __shfl(qk, k, kWave);
         top[k] = __shfl(jm, k, kWave);
         const int32_t t = __shfl(tc, k, kWave);
-        jt[k] = t == INT_MIN ? 0 : hist_bin(t, st.hlo, st.hw);
+        jt[k] = t == INT_MIN ? 0 : hist_bin(t, st.hlo, st.hsh);
         const int j = top[k] - lane;
         v[k] = (qs[k] >= 0 && j >= jt[k]) ? (int)ld_coherent(st.hist + (int64_t)qs[k] * kNB + j) : 0;
     }
@@ -429,7 +467,7 @@ __device__ __forceinline__ void refresh_tau_wave(const ScanState& st, const int3
         const uint64_t mk = __ballot(incl >= R);
         if (mk) {
             const int l = __ffsll((unsigned long long)mk) - 1;
-            if (lane == 0) atomicMax(st.tau + qs[k], (int32_t)(st.hlo + (int64_t)(top[k] - l) * st.hw));
+            if (lane == 0) atomicMax(st.tau + qs[k], (int32_t)(st.hlo + ((int64_t)(top[k] - l) << st.hsh)));
         } else if (top[k] - kWave >= jt[k]) {
             refresh_tau(st, qs[k], R);  // the R-th best lies below the first window
         }
@@ -443,6 +481,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
     __shared__ __align__(16) uint32_t onehot_s[16 * 4];           // onehot_s[c] = 16 bytes, byte c = 1
     __shared__ int32_t qid_s[kQG];
     __shared__ uint32_t qapp_s[kQG];
+    __shared__ uint32_t lh[kQG * kLB];  // this item's appended sums per query, bins from jb_s
+    __shared__ int32_t tau_s[kQG];     // item-local thresholds (raised from lh)
+    __shared__ int32_t jb_s[kQG];      // global bin of the threshold at item start
     __shared__ uint32_t fl_s[kScanWaves * 2 * kWave];  // per-wave flush scratch
     __shared__ int64_t item_s, p0_s, p1_s, qbase_s;
     __shared__ uint32_t slab_s;  // next 64-row slab of the item (one 64-block chunk)
@@ -511,7 +552,11 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
             if (tid < qn) qq = p.leaves ? a.qlist[qbase_s + tid] : (int32_t)(qbase_s + tid);
             qid_s[tid] = qq;
             qapp_s[tid] = 0;
+            const int32_t t = tid < qn ? ld_coherent(st.tau + qq) : INT_MAX;
+            tau_s[tid] = t;
+            jb_s[tid] = (t == INT_MIN || t == INT_MAX) ? 0 : hist_bin(t, st.hlo, st.hsh);
         }
+        for (int e = tid; e < kQG * kLB; e += kScanThreads) lh[e] = 0;
         __syncthreads();
 
         // table staging: B operand layout [kstep][ntile][lane][16 bytes]
@@ -689,8 +734,10 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                 const int32_t nloc = (int32_t)(p1 - p0);
                 const bool full = rowbase_of(cu) + 64 <= p1;
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
+                for (int nt = 0; nt < 4; ++nt) {
+                    tq[nt] = max(tq[nt], tau_s[16 * nt + r16]);
                     if (16 * nt + r16 >= qn) tq[nt] = INT_MAX;
+                }
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) {
                     int32_t mm[4];
@@ -704,8 +751,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                     for (int m = 0; m < 4; ++m) {
                         if (__ballot(mm[m] >= tq[nt]) == 0) continue;
                         if (log_n > kLogCap - 4 * kWave) {
-                            flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave);
+                            flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave, lh, jb_s);
                             log_n = 0;
+                            local_refresh(lh, tau_s, jb_s, qn, w, p.R, st.hlo, st.hsh);
                         }
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
@@ -737,8 +785,10 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
             if (nu < nunits) load_codes(rowbase_of(nu), nc, px0, px1, pkeep);
             wave_fence();
         }
-        if (log_n > 0) flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave);
+        if (log_n > 0) flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave, lh, jb_s);
         __syncthreads();
+        local_refresh(lh, tau_s, jb_s, qn, w, p.R, st.hlo, st.hsh);
+        publish_item(st, tau_s, qid_s, qn, w);
         refresh_tau_wave(st, qid_s, qapp_s, qn, w, p.R);
         __syncthreads();
     }
@@ -875,7 +925,13 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     st.fb = reinterpret_cast<uint64_t*>(base + lay.fb);
     st.cap = lay.cap;
     st.hlo = -127 * sp.B;
-    st.hw = (int32_t)((254LL * sp.B + 1 + kNB - 1) / kNB);
+    {
+        const int64_t need = (254LL * sp.B + 1 + kNB - 1) / kNB;  // every sum lies in [-127 B, 127 B]
+        int32_t sh = 0;
+        while ((1LL << sh) < need) ++sh;
+        st.hsh = sh;
+        st.hw = 1 << sh;
+    }
     const bool part = sp.leaves != nullptr;
     hipError_t e;
 
