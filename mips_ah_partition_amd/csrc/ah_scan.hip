@@ -962,8 +962,10 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
         ma.qlist = qlist;
         ma.itemoff = itemoff;
     }
-    int32_t W = 4 * sp.R;
-    if (W < 2048) W = 2048;
+    // warm-up rows per query: enough for a first bound; the item-local
+    // thresholds tighten it within the first items
+    int32_t W = 2 * sp.R;
+    if (W < 512) W = 512;
     if (W > 8192) W = 8192;
     const size_t lut_bytes = ((size_t)sp.B * 16 + 15) & ~(size_t)15;
     allow_lds(warmup_kernel, lut_bytes + (size_t)W * 8);
