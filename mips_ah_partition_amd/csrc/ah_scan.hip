@@ -178,7 +178,8 @@ __global__ void leaf_count_kernel(const int32_t* __restrict__ leaves, int64_t pa
 // Single workgroup: query offsets per leaf and item offsets per leaf.
 __global__ __launch_bounds__(1024) void leaf_scan_kernel(const uint32_t* __restrict__ lcnt,
                                                          const int64_t* __restrict__ leaf_offsets, int32_t L,
-                                                         int32_t* __restrict__ lqoff, int64_t* __restrict__ itemoff) {
+                                                         int32_t qg, int32_t* __restrict__ lqoff,
+                                                         int64_t* __restrict__ itemoff) {
     __shared__ int64_t part_q[1024], part_i[1024];
     const int tid = threadIdx.x;
     const int64_t per = (L + 1023) / 1024;
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(1024) void leaf_scan_kernel(const uint32_t* __restr
         const int64_t nqL = lcnt[l];
         const int64_t rows = leaf_offsets[l + 1] - leaf_offsets[l];
         sq += nqL;
-        si += (nqL > 0 && rows > 0) ? ((nqL + kQG - 1) / kQG) * ((rows + kItemPts - 1) / kItemPts) : 0;
+        si += (nqL > 0 && rows > 0) ? ((nqL + qg - 1) / qg) * ((rows + kItemPts - 1) / kItemPts) : 0;
     }
     part_q[tid] = sq;
     part_i[tid] = si;
@@ -289,6 +290,7 @@ struct MainArgs {
     ScanState st;
     int32_t nkstep;   // k-steps of 4 blocks (blocks rounded up to 8)
     int32_t nchunk;   // 64-block chunks
+    int32_t qg;       // queries per item
     int32_t nqg;      // query groups (full scan)
     int64_t n_items;  // items (full scan); partitioned: itemoff[L]
     const int32_t* lqoff;
@@ -296,6 +298,38 @@ struct MainArgs {
     const int64_t* itemoff;
     int fast_codes;   // rows 16-byte aligned (stride % 16 == 0)
 };
+
+// Item -> (rows [p0, p1), first entry qbase of its query list, qn queries).
+// Full scan: item = chunk * nqg + group.  Partitioned: items are numbered leaf
+// by leaf (itemoff), and within a leaf chunk-major over its query groups.
+__device__ __forceinline__ void decode_item(const MainArgs& a, int64_t item, int64_t& p0, int64_t& p1,
+                                            int64_t& qbase, int& qn) {
+    const Problem& p = a.p;
+    const int64_t G = a.qg;
+    if (!p.leaves) {
+        const int64_t chunk = item / a.nqg, grp = item % a.nqg;
+        p0 = chunk * kItemPts;
+        p1 = p0 + kItemPts < p.n ? p0 + kItemPts : p.n;
+        qbase = grp * G;
+        qn = (int)(p.nq - qbase < G ? p.nq - qbase : G);
+    } else {
+        int lo = 0, hi = p.L;  // largest l with itemoff[l] <= item
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (a.itemoff[mid] <= item) lo = mid; else hi = mid;
+        }
+        const int l = lo;
+        const int64_t nqL = a.lqoff[l + 1] - a.lqoff[l];
+        const int64_t ng = (nqL + G - 1) / G;
+        const int64_t loc = item - a.itemoff[l];
+        const int64_t chunk = loc / ng, grp = loc % ng;
+        const int64_t ra = p.leaf_offsets[l], rb = p.leaf_offsets[l + 1];
+        p0 = ra + chunk * kItemPts;
+        p1 = p0 + kItemPts < rb ? p0 + kItemPts : rb;
+        qbase = a.lqoff[l] + grp * G;
+        qn = (int)(nqL - grp * G < G ? nqL - grp * G : G);
+    }
+}
 
 __device__ __forceinline__ v4i onehot16(uint32_t x) {
     // x & 15 = center index; returns 16 bytes with a single 1 at that index
@@ -511,29 +545,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
             if (item < n_items) {
                 int64_t p0, p1, qbase;
                 int qn;
-                if (!p.leaves) {
-                    const int64_t chunk = item / a.nqg, grp = item % a.nqg;
-                    p0 = chunk * kItemPts;
-                    p1 = p0 + kItemPts < p.n ? p0 + kItemPts : p.n;
-                    qbase = grp * kQG;
-                    qn = (int)(p.nq - qbase < kQG ? p.nq - qbase : kQG);
-                } else {
-                    int lo = 0, hi = p.L;  // largest l with itemoff[l] <= item
-                    while (hi - lo > 1) {
-                        const int mid = (lo + hi) >> 1;
-                        if (a.itemoff[mid] <= item) lo = mid; else hi = mid;
-                    }
-                    const int l = lo;
-                    const int64_t nqL = a.lqoff[l + 1] - a.lqoff[l];
-                    const int64_t ng = (nqL + kQG - 1) / kQG;
-                    const int64_t loc = item - a.itemoff[l];
-                    const int64_t chunk = loc / ng, grp = loc % ng;
-                    const int64_t ra = p.leaf_offsets[l], rb = p.leaf_offsets[l + 1];
-                    p0 = ra + chunk * kItemPts;
-                    p1 = p0 + kItemPts < rb ? p0 + kItemPts : rb;
-                    qbase = a.lqoff[l] + grp * kQG;
-                    qn = (int)(nqL - grp * kQG < kQG ? nqL - grp * kQG : kQG);
-                }
+                decode_item(a, item, p0, p1, qbase, qn);
                 p0_s = p0;
                 p1_s = p1;
                 qbase_s = qbase;
@@ -794,6 +806,218 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
     }
 }
 
+// ------------------------------------------------------------------ small-batch streaming scan
+// For a handful of queries (at most kStreamMaxQ) the one-hot contraction would
+// leave most of every 16-query MFMA tile empty and the scan is bound by
+// streaming the codes from HBM.  Each thread then sums one row's table entries
+// itself, by LDS lookups, while its next 16 code bytes load:
+//  * G = 1: the table is the query's int8 entries, [block][center];
+//  * G = 4: entry (b, c) is a dword holding the four queries' entries + 128
+//    (bytes 0..3); the even and odd bytes are accumulated as two pairs of
+//    16-bit fields (at most 256 blocks between folds into int32, so no field
+//    overflows), and 128 B is subtracted at the end.  Absent queries hold 128.
+// Items, thresholds, hit logs and flushes are those of the main kernel, with
+// G queries per item.
+constexpr int kStreamMaxQ = 4;
+constexpr size_t kStreamMaxTable = 96 * 1024;  // LDS bytes for the table
+
+// 16 code bytes of a row from src; nbytes (1..16) of them are the row's own.
+// Aligned rows (stride a multiple of 16 bytes) read the whole 16 bytes, which
+// stay inside the row's stride; others read byte by byte and zero the rest.
+__device__ __forceinline__ uint4 load_code16(const uint8_t* src, int nbytes, bool fast) {
+    if (fast) return *reinterpret_cast<const uint4*>(src);
+    uint32_t wd[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (4 * k + e < nbytes) v |= (uint32_t)src[4 * k + e] << (8 * e);
+        wd[k] = v;
+    }
+    return make_uint4(wd[0], wd[1], wd[2], wd[3]);
+}
+
+// Raises the item-local thresholds of all of an item's qn queries (one wave).
+__device__ __forceinline__ void local_refresh_all(const uint32_t* lh, int32_t* tau_s, const int32_t* jb_s, int qn,
+                                                  int R, int32_t hlo, int32_t hsh) {
+    const int lane = lane_id();
+    const int b = kLB - 1 - lane;
+#pragma unroll 1
+    for (int ql = 0; ql < qn; ++ql) {
+        const int incl = wave_inclusive_sum((int)lh[ql * kLB + b]);
+        const uint64_t mk = __ballot(incl >= R);
+        if (mk && lane == __ffsll((unsigned long long)mk) - 1)
+            atomicMax(&tau_s[ql], (int32_t)(hlo + ((int64_t)(jb_s[ql] + b) << hsh)));
+    }
+}
+
+// Adds the table entries of the 32 blocks [32 j0, 32 j0 + nb) coded in v
+// (byte k holds blocks 32 j0 + 2k (low nibble) and + 2k + 1 (high)).
+template <int G>
+__device__ __forceinline__ void stream_accumulate(const unsigned char* tbl, int j0, uint4 v, int nb, int32_t& s1,
+                                                  uint32_t& ae, uint32_t& ao) {
+    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int bl = 8 * k + e;  // block within the segment
+            if (bl >= nb) break;
+            const uint32_t c = (wd[k] >> (4 * e)) & 15u;
+            const int b = 32 * j0 + bl;
+            if (G == 1) {
+                s1 += (int32_t)reinterpret_cast<const int8_t*>(tbl)[b * 16 + (int)c];
+            } else {
+                const uint32_t x = reinterpret_cast<const uint32_t*>(tbl)[b * 16 + (int)c];
+                ae += x & 0x00FF00FFu;
+                ao += __builtin_amdgcn_perm(x, x, 0x0c030c01u);  // bytes 1 and 3 -> 16-bit fields
+            }
+        }
+    }
+}
+
+template <int G>
+__global__ __launch_bounds__(kScanThreads, 2) void scan_stream_kernel(MainArgs a) {
+    extern __shared__ __align__(16) unsigned char tbl[];  // B * 16 entries of G == 1 ? 1 : 4 bytes
+    __shared__ uint64_t log_s[kScanWaves * kLogCap];
+    __shared__ int32_t qid_s[kQG];  // flushes read kQG entries
+    __shared__ uint32_t qapp_s[kQG];
+    __shared__ uint32_t fl_s[kScanWaves * 2 * kWave];
+    __shared__ uint32_t lh[G * kLB];
+    __shared__ int32_t tau_s[kQG];
+    __shared__ int32_t jb_s[kQG];
+    __shared__ int64_t item_s, p0_s, p1_s, qbase_s;
+    __shared__ int32_t qn_s;
+
+    const Problem& p = a.p;
+    const ScanState& st = a.st;
+    const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+    const int64_t n_items = p.leaves ? a.itemoff[p.L] : a.n_items;
+    uint64_t* mylog = log_s + w * kLogCap;
+    uint32_t* mywq = fl_s + w * 2 * kWave;
+    const int cb = (p.B + 1) / 2;     // code bytes per row
+    const int nseg = (cb + 15) / 16;  // 16-byte segments per row (the last may be partial)
+    const bool fast = a.fast_codes != 0;
+
+    int64_t claimed = 0;
+    if (tid == 0) claimed = (int64_t)atomicAdd(&st.ctrl[0], 1u);
+    for (;;) {
+        if (tid == 0) {
+            const int64_t item = claimed;
+            item_s = item;
+            if (item < n_items) {
+                int64_t p0, p1, qbase;
+                int qn;
+                decode_item(a, item, p0, p1, qbase, qn);
+                p0_s = p0;
+                p1_s = p1;
+                qbase_s = qbase;
+                qn_s = qn;
+                claimed = (int64_t)atomicAdd(&st.ctrl[0], 1u);
+            }
+        }
+        __syncthreads();
+        const int64_t item = item_s;
+        if (item >= n_items) break;
+        const int64_t p0 = p0_s, p1 = p1_s;
+        const int qn = qn_s;
+        if (tid < kQG) {
+            int32_t qq = 0;
+            if (tid < qn) qq = p.leaves ? a.qlist[qbase_s + tid] : (int32_t)(qbase_s + tid);
+            qid_s[tid] = qq;
+            qapp_s[tid] = 0;
+            const int32_t t = tid < qn ? ld_coherent(st.tau + qq) : INT_MAX;
+            tau_s[tid] = t;
+            jb_s[tid] = (t == INT_MIN || t == INT_MAX) ? 0 : hist_bin(t, st.hlo, st.hsh);
+        }
+        for (int e = tid; e < G * kLB; e += kScanThreads) lh[e] = 0;
+        __syncthreads();
+        // table staging
+        if (G == 1) {
+            const int8_t* src = p.lut + (int64_t)qid_s[0] * p.B * 16;
+            if ((reinterpret_cast<uintptr_t>(p.lut) & 15) == 0) {
+                for (int e = tid; e < p.B; e += kScanThreads)
+                    reinterpret_cast<uint4*>(tbl)[e] = reinterpret_cast<const uint4*>(src)[e];
+            } else {
+                for (int e = tid; e < p.B * 16; e += kScanThreads) tbl[e] = (unsigned char)src[e];
+            }
+        } else {
+            for (int e = tid; e < p.B * 16; e += kScanThreads) {
+                uint32_t x = 0;
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const int32_t t = g < qn ? (int32_t)p.lut[(int64_t)qid_s[g] * p.B * 16 + e] : 0;
+                    x |= (uint32_t)(t + 128) << (8 * g);
+                }
+                reinterpret_cast<uint32_t*>(tbl)[e] = x;
+            }
+        }
+        __syncthreads();
+
+        int log_n = 0;
+        for (int64_t rb = p0 + w * kWave; rb < p1; rb += kScanThreads) {
+            const int64_t row = rb + lane;
+            const bool valid = row < p1;
+            const uint8_t* src = p.codes + (valid ? row : p1 - 1) * p.stride;
+            int32_t tq[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) tq[g] = g < qn ? tau_s[g] : INT_MAX;
+            int32_t s1 = 0;
+            int32_t sg[4] = {0, 0, 0, 0};
+            uint32_t ae = 0, ao = 0;
+            // segments j < nseg - 1 are full (32 blocks); the next one is
+            // loaded while the current one is summed
+            const int lastb = cb - 16 * (nseg - 1);  // code bytes in the last segment
+            uint4 cur = load_code16(src, nseg == 1 ? lastb : 16, fast);
+            for (int j = 0; j < nseg - 1; ++j) {
+                const int jn = j + 1;
+                const uint4 nxt = load_code16(src + 16 * jn, jn < nseg - 1 ? 16 : lastb, fast);
+                stream_accumulate<G>(tbl, j, cur, 32, s1, ae, ao);
+                if (G != 1 && (j & 7) == 7) {  // 256 blocks: fold the 16-bit fields
+                    sg[0] += (int32_t)(ae & 0xFFFFu); sg[2] += (int32_t)(ae >> 16);
+                    sg[1] += (int32_t)(ao & 0xFFFFu); sg[3] += (int32_t)(ao >> 16);
+                    ae = ao = 0;
+                }
+                cur = nxt;
+            }
+            stream_accumulate<G>(tbl, nseg - 1, cur, p.B - 32 * (nseg - 1), s1, ae, ao);  // 1..32 blocks
+            int32_t sum[G];
+            if (G == 1) {
+                sum[0] = s1;
+            } else {
+                sg[0] += (int32_t)(ae & 0xFFFFu); sg[2] += (int32_t)(ae >> 16);
+                sg[1] += (int32_t)(ao & 0xFFFFu); sg[3] += (int32_t)(ao >> 16);
+#pragma unroll
+                for (int g = 0; g < G; ++g) sum[g] = sg[g] - 128 * p.B;
+            }
+            if (log_n > kLogCap - G * kWave) {
+                flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave, lh, jb_s);
+                log_n = 0;
+                local_refresh_all(lh, tau_s, jb_s, qn, p.R, st.hlo, st.hsh);
+            }
+            const uint32_t lr = (uint32_t)(row - p0);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const bool hit = valid && sum[g] >= tq[g];
+                const uint64_t mk = __ballot(hit);
+                if (mk) {
+                    if (hit)
+                        mylog[log_n + __popcll(mk & lanemask_lt())] =
+                            ((uint64_t)(uint32_t)sum[g] << 32) | ((uint64_t)g << 16) | (uint64_t)lr;
+                    log_n += __popcll(mk);
+                }
+            }
+        }
+        if (log_n > 0) flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave, lh, jb_s);
+        __syncthreads();
+        local_refresh(lh, tau_s, jb_s, qn, w, p.R, st.hlo, st.hsh);
+        publish_item(st, tau_s, qid_s, qn, w);
+        refresh_tau_wave(st, qid_s, qapp_s, qn, w, p.R);
+        __syncthreads();
+    }
+}
+
 // ------------------------------------------------------------------ final selection
 __global__ __launch_bounds__(kSelThreads) void final_select_kernel(Problem p, ScanState st) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -924,9 +1148,9 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     st.ovf = reinterpret_cast<int32_t*>(base + lay.ovf);
     st.fb = reinterpret_cast<uint64_t*>(base + lay.fb);
     st.cap = lay.cap;
-    st.hlo = -127 * sp.B;
+    st.hlo = -128 * sp.B;  // every sum lies in [-128 B, 127 B], so no sum falls below bin 0's edge
     {
-        const int64_t need = (254LL * sp.B + 1 + kNB - 1) / kNB;  // every sum lies in [-127 B, 127 B]
+        const int64_t need = (255LL * sp.B + 1 + kNB - 1) / kNB;
         int32_t sh = 0;
         while ((1LL << sh) < need) ++sh;
         st.hsh = sh;
@@ -941,7 +1165,13 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     const int32_t B8 = (sp.B + 7) & ~7;
     ma.nkstep = B8 / 4;
     ma.nchunk = (ma.nkstep + kKC - 1) / kKC;
-    ma.nqg = (int32_t)((sp.nq + kQG - 1) / kQG);
+    // small batches stream the codes through VALU lookups (G = 1 or 4 queries
+    // per item); larger ones use the MFMA kernel with 64 queries per item
+    const int sg = sp.nq <= 1 ? 1 : 4;
+    const size_t stbl = (size_t)sp.B * 16 * (sg == 1 ? 1 : 4);
+    const bool streaming = sp.nq <= kStreamMaxQ && stbl <= kStreamMaxTable;
+    ma.qg = streaming ? sg : kQG;
+    ma.nqg = (int32_t)((sp.nq + ma.qg - 1) / ma.qg);
     ma.n_items = (int64_t)ma.nqg * ((sp.n + kItemPts - 1) / kItemPts);
     ma.fast_codes = (sp.stride % 16) == 0 && (reinterpret_cast<uintptr_t>(sp.codes) & 15) == 0;
     if (part) {
@@ -955,7 +1185,8 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
         const int64_t pairs = sp.nq * sp.nl;
         const unsigned gb = (unsigned)((pairs + 255) / 256 < 4096 ? (pairs + 255) / 256 : 4096);
         hipLaunchKernelGGL(leaf_count_kernel, dim3(gb), dim3(256), 0, stream, sp.leaves, pairs, sp.L, lcnt);
-        hipLaunchKernelGGL(leaf_scan_kernel, dim3(1), dim3(1024), 0, stream, lcnt, sp.leaf_offsets, sp.L, lqoff, itemoff);
+        hipLaunchKernelGGL(leaf_scan_kernel, dim3(1), dim3(1024), 0, stream, lcnt, sp.leaf_offsets, sp.L, ma.qg, lqoff,
+                           itemoff);
         hipLaunchKernelGGL(leaf_scatter_kernel, dim3(gb), dim3(256), 0, stream, sp.leaves, sp.nq, sp.nl, sp.L, lqoff, lcur, qlist);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         ma.lqoff = lqoff;
@@ -972,10 +1203,18 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     hipLaunchKernelGGL(warmup_kernel, dim3((unsigned)sp.nq), dim3(kSelThreads), lut_bytes + (size_t)W * 8, stream, p, st, W);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t max_items = part ? (int64_t)sp.nq * sp.nl + sp.L : ma.n_items;
-    int grid = device_cus();
+    int grid = device_cus() * (streaming ? 2 : 1);
     if (max_items < grid) grid = (int)(max_items > 0 ? max_items : 1);
     if (main_start && (e = hipEventRecord(main_start, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL(scan_main_kernel, dim3(grid), dim3(kScanThreads), 0, stream, ma);
+    if (!streaming) {
+        hipLaunchKernelGGL(scan_main_kernel, dim3(grid), dim3(kScanThreads), 0, stream, ma);
+    } else if (sg == 1) {
+        allow_lds(scan_stream_kernel<1>, stbl);
+        hipLaunchKernelGGL(scan_stream_kernel<1>, dim3(grid), dim3(kScanThreads), stbl, stream, ma);
+    } else {
+        allow_lds(scan_stream_kernel<4>, stbl);
+        hipLaunchKernelGGL(scan_stream_kernel<4>, dim3(grid), dim3(kScanThreads), stbl, stream, ma);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (main_stop && (e = hipEventRecord(main_stop, stream)) != hipSuccess) return e;
     int Rp = 1;

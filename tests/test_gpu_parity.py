@@ -137,6 +137,60 @@ def test_scan_partitioned_parity(gpu):
     _scan_check(torch, ah, lut, codes, R, ids=perm, offs=offs, leaves=leaves)
 
 
+# Small batches (at most four queries) take the streaming kernel: one query, or
+# four queries packed per table entry.  Cases cover segment folds past 256
+# blocks, partial last segments, unaligned rows, R > n and a 64 KB table.
+@pytest.mark.parametrize("B,n,nq,R,stride_pad", [
+    (32, 10000, 1, 100, 0),
+    (64, 50000, 4, 200, 0),
+    (50, 3001, 2, 37, 0),       # 25 B rows: byte loads
+    (8, 700, 3, 1000, 0),       # R > n
+    (200, 20000, 1, 300, 0),    # 100 B rows: partial last segment
+    (300, 4000, 4, 50, 0),      # 300 blocks: packed fields folded mid-row
+    (768, 5000, 4, 400, 0),     # 48 KB packed table
+    (33, 1234, 1, 10, 7),       # odd B, 24 B stride
+    (1, 999, 4, 5, 0),          # one block
+    (4096, 600, 1, 20, 0),      # 64 KB single-query table
+])
+def test_scan_stream_parity(gpu, B, n, nq, R, stride_pad):
+    torch, ah = gpu
+    rng = np.random.default_rng(B * 13 + n + nq)
+    lut = synth.random_lut_i8(rng, nq, B)
+    codes = synth.random_codes(rng, n, B)
+    if stride_pad:
+        codes = np.concatenate([codes, rng.integers(0, 256, size=(n, stride_pad), dtype=np.uint8)], axis=1)
+    _scan_check(torch, ah, lut, codes, R)
+
+
+@pytest.mark.parametrize("nq", [4, 70])
+def test_scan_extreme_tables(gpu, nq):
+    """Entries of -128 and 127 only (streaming: packed fields at both ends of
+    their range), one query all 127 and one all -128 (every sum -128 B, the
+    lowest possible: a threshold must never be raised past it)."""
+    torch, ah = gpu
+    rng = np.random.default_rng(91 + nq)
+    B, n, R = 256, 3000, 64
+    lut = rng.choice(np.array([-128, 127], dtype=np.int8), size=(nq, B, 16))
+    lut[1] = 127
+    lut[2] = -128
+    codes = synth.random_codes(rng, n, B)
+    _scan_check(torch, ah, lut, codes, R)
+
+
+@pytest.mark.parametrize("nq", [1, 3])
+def test_scan_stream_partitioned(gpu, nq):
+    torch, ah = gpu
+    rng = np.random.default_rng(300 + nq)
+    B, n, L, nl, R = 48, 40000, 25, 5, 90
+    sizes = synth.random_leaf_sizes(rng, n, L, skew=1.0)
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    lut = synth.random_lut_i8(rng, nq, B)
+    codes = synth.random_codes(rng, n, B)
+    perm = rng.permutation(n).astype(np.int32)
+    leaves = synth.random_probe_lists(rng, nq, L, nl)
+    _scan_check(torch, ah, lut, codes, R, ids=perm, offs=offs, leaves=leaves)
+
+
 def test_scan_overflow_fallback(gpu):
     """All sums equal: the threshold cannot rise, candidate lists overflow and the
     exact fallback must return the R lowest ids."""
