@@ -164,6 +164,44 @@ def cpu_baseline(w, ix, X, Q, gt, gpu_ids, budget_s=20.0):
     }
 
 
+# ----------------------------------------------------------------------------- code-scan HBM probe
+# Single-pass streaming scans at low reuse: 1 and 4 queries over codes of the
+# 20M x 384-dim (192 blocks, 96 B rows) and 2M x 1536-dim (768 blocks, 384 B
+# rows) workloads' shapes, no partitioning.  Both code arrays exceed the 256 MB
+# last-level cache, so every run reads them from HBM.  Codes are uniform random
+# nibbles generated on the GPU (seeded); tables are uniform int8.
+PROBE_SHAPES = (("wiki20m", 20_000_000, 192, 300), ("openai2m", 2_000_000, 768, 400))
+
+
+def code_scan_probe(torch, ahlib, ev, runs=5):
+    out = {}
+    for name, n, B, R in PROBE_SHAPES:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(4242 + B)
+        codes = torch.randint(0, 256, (n, (B + 1) // 2), generator=g, device="cuda", dtype=torch.uint8)
+        for nq in (1, 4):
+            lut = torch.randint(-127, 128, (nq, B, 16), generator=g, device="cuda", dtype=torch.int8)
+            ws = torch.empty(ahlib.ah_scan_workspace_bytes(nq, B, n, 0, 0, R), dtype=torch.uint8, device="cuda")
+            e0, e1 = ev.create(), ev.create()
+            ts = []
+            for it in range(runs + 1):
+                ahlib.ah_scan_topk(lut, codes, R, workspace=ws, main_events=(e0, e1))
+                torch.cuda.synchronize()
+                if it:
+                    ts.append(ev.elapsed_ms(e0, e1))
+            ms = float(np.median(ts))
+            gbps = codes.numel() / (ms / 1e3) / 1e9
+            o_cnt = (nq * 4 + 255) & ~255  # candidate counters follow the thresholds in the workspace
+            appended = ws[o_cnt:o_cnt + nq * 4].view(torch.int32).cpu().numpy()
+            out[f"{name}_q{nq}"] = {"code_bytes": int(codes.numel()), "blocks": B, "queries": nq,
+                                    "scan_ms": ms, "GBps": gbps, "frac_of_8TBps": gbps / PEAK_HBM_GBPS,
+                                    "candidates_per_query": float(appended.mean())}
+            del ws
+        del codes
+    torch.cuda.empty_cache()
+    return out
+
+
 # ----------------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -173,6 +211,8 @@ def main():
     ap.add_argument("--workload", default="sift1m", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-probe", action="store_true", help="skip the code-scan HBM probe")
+    ap.add_argument("--probe-only", action="store_true", help="only run the code-scan HBM probe")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device 5 times (calibrates FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
@@ -189,6 +229,13 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_per_launch": src.numel() * 4, "launches": 5}))
+        return
+
+    if args.probe_only:
+        import torch
+        from mips_ah_partition_amd import ahlib
+        ahlib.lib()
+        print(json.dumps({"code_scan_hbm": code_scan_probe(torch, ahlib, HipEvents())}), flush=True)
         return
 
     w = synth.WORKLOADS[args.workload]
@@ -270,6 +317,8 @@ def main():
                      "peak": PEAK_INT8_TOPS, "unit": "TOP/s", "frac": achieved_tops / PEAK_INT8_TOPS,
                      "traffic": profiled_traffic(w.name)},
     }
+    if not args.no_probe:
+        out["code_scan_hbm"] = code_scan_probe(torch, ahlib, ev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, ix, X, Q, gt, gpu_ids, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -71,6 +71,9 @@ static ScanLayout scan_layout(int64_t nq, int32_t B, int64_t n, int32_t L, int32
     ScanLayout s{};
     int64_t cap = 16 * (int64_t)R;
     if (cap < 32768) cap = 32768;
+    // a few queries scanned by every workgroup at once log many rows before
+    // their thresholds meet: give them long lists (4M entries between them)
+    if (nq > 0 && nq <= 4 && cap < (int64_t)(1 << 22) / nq) cap = (int64_t)(1 << 22) / nq;
     if (cap > n) cap = n > 0 ? n : 1;
     s.cap = cap;
     size_t o = 0;
@@ -178,7 +181,7 @@ __global__ void leaf_count_kernel(const int32_t* __restrict__ leaves, int64_t pa
 // Single workgroup: query offsets per leaf and item offsets per leaf.
 __global__ __launch_bounds__(1024) void leaf_scan_kernel(const uint32_t* __restrict__ lcnt,
                                                          const int64_t* __restrict__ leaf_offsets, int32_t L,
-                                                         int32_t qg, int32_t* __restrict__ lqoff,
+                                                         int32_t qg, int32_t ipts, int32_t* __restrict__ lqoff,
                                                          int64_t* __restrict__ itemoff) {
     __shared__ int64_t part_q[1024], part_i[1024];
     const int tid = threadIdx.x;
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(1024) void leaf_scan_kernel(const uint32_t* __restr
         const int64_t nqL = lcnt[l];
         const int64_t rows = leaf_offsets[l + 1] - leaf_offsets[l];
         sq += nqL;
-        si += (nqL > 0 && rows > 0) ? ((nqL + qg - 1) / qg) * ((rows + kItemPts - 1) / kItemPts) : 0;
+        si += (nqL > 0 && rows > 0) ? ((nqL + qg - 1) / qg) * ((rows + ipts - 1) / ipts) : 0;
     }
     part_q[tid] = sq;
     part_i[tid] = si;
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(1024) void leaf_scan_kernel(const uint32_t* __restr
         const int64_t nqL = lcnt[l];
         const int64_t rows = leaf_offsets[l + 1] - leaf_offsets[l];
         cq += nqL;
-        ci += (nqL > 0 && rows > 0) ? ((nqL + kQG - 1) / kQG) * ((rows + kItemPts - 1) / kItemPts) : 0;
+        ci += (nqL > 0 && rows > 0) ? ((nqL + qg - 1) / qg) * ((rows + ipts - 1) / ipts) : 0;
     }
 }
 
@@ -291,6 +294,7 @@ struct MainArgs {
     int32_t nkstep;   // k-steps of 4 blocks (blocks rounded up to 8)
     int32_t nchunk;   // 64-block chunks
     int32_t qg;       // queries per item
+    int32_t item_pts; // rows per item (at most kItemPts)
     int32_t nqg;      // query groups (full scan)
     int64_t n_items;  // items (full scan); partitioned: itemoff[L]
     const int32_t* lqoff;
@@ -308,8 +312,8 @@ __device__ __forceinline__ void decode_item(const MainArgs& a, int64_t item, int
     const int64_t G = a.qg;
     if (!p.leaves) {
         const int64_t chunk = item / a.nqg, grp = item % a.nqg;
-        p0 = chunk * kItemPts;
-        p1 = p0 + kItemPts < p.n ? p0 + kItemPts : p.n;
+        p0 = chunk * a.item_pts;
+        p1 = p0 + a.item_pts < p.n ? p0 + a.item_pts : p.n;
         qbase = grp * G;
         qn = (int)(p.nq - qbase < G ? p.nq - qbase : G);
     } else {
@@ -324,8 +328,8 @@ __device__ __forceinline__ void decode_item(const MainArgs& a, int64_t item, int
         const int64_t loc = item - a.itemoff[l];
         const int64_t chunk = loc / ng, grp = loc % ng;
         const int64_t ra = p.leaf_offsets[l], rb = p.leaf_offsets[l + 1];
-        p0 = ra + chunk * kItemPts;
-        p1 = p0 + kItemPts < rb ? p0 + kItemPts : rb;
+        p0 = ra + chunk * a.item_pts;
+        p1 = p0 + a.item_pts < rb ? p0 + a.item_pts : rb;
         qbase = a.lqoff[l] + grp * G;
         qn = (int)(nqL - grp * G < G ? nqL - grp * G : G);
     }
@@ -346,7 +350,9 @@ __device__ __forceinline__ v4i onehot16(uint32_t x) {
 }
 
 // Appends a wave's logged hits to the queries' candidate lists and counts them
-// in the item's LDS histogram (lh: kLB bins per local query, starting at the
+// (kGlobalHist: also in the global histograms, hit by hit; fh: also in the
+// wave's flush histogram, merged into the global ones after the flush) in the
+// item's LDS histogram (lh: kLB bins per local query, starting at the
 // query's global bin jb_s at item start; the top bin also takes everything
 // above it).  Log entry: sum (high 32 bits) | local query (bits 16..21) |
 // row - p0 (low 16).  Each lane takes four entries per pass.  The pass first
@@ -354,9 +360,11 @@ __device__ __forceinline__ v4i onehot16(uint32_t x) {
 // reserves each query's list slots with one global atomic per query, so the
 // per-query counters see one atomic per pass instead of one per hit and no
 // two lanes of an atomic share an address.
+template <bool kGlobalHist>
 __device__ __forceinline__ void flush_log(const Problem& p, const ScanState& st, const uint64_t* log,
                                           int log_n, const int32_t* qid_s, uint32_t* qapp_s, int64_t p0,
-                                          uint32_t* wq, uint32_t* wm, uint32_t* lh, const int32_t* jb_s) {
+                                          uint32_t* wq, uint32_t* wm, uint32_t* lh, const int32_t* jb_s,
+                                          uint32_t* fh = nullptr) {
     const int lane = lane_id();
     for (int base = 0; base < log_n; base += 4 * kWave) {
         wq[lane] = 0;
@@ -382,8 +390,11 @@ __device__ __forceinline__ void flush_log(const Problem& p, const ScanState& st,
                 // dropped (never counted where it could overstate a bound)
                 const int gbin = hist_bin((int32_t)(uint32_t)(ent[u] >> 32), st.hlo, st.hsh);
                 const int bl = gbin - jb_s[ql[u]];
-                if (bl >= 0) atomicAdd(&lh[ql[u] * kLB + (bl < kLB ? bl : kLB - 1)], 1u);
-                atomicMax(&wm[ql[u]], (uint32_t)gbin);
+                if (bl >= 0) {
+                    atomicAdd(&lh[ql[u] * kLB + (bl < kLB ? bl : kLB - 1)], 1u);
+                    if (fh) atomicAdd(&fh[ql[u] * kLB + (bl < kLB ? bl : kLB - 1)], 1u);
+                }
+                if (kGlobalHist) atomicMax(&wm[ql[u]], (uint32_t)gbin);
             }
         }
         wave_fence();
@@ -392,7 +403,7 @@ __device__ __forceinline__ void flush_log(const Problem& p, const ScanState& st,
         uint32_t gb = 0;
         if (c) {
             gb = atomicAdd(&st.cnt[q], c);
-            atomicMax(&st.hmax[q], wm[lane]);
+            if (kGlobalHist) atomicMax(&st.hmax[q], wm[lane]);
             atomicAdd(&qapp_s[lane], c);
         }
         wq[lane] = gb;
@@ -412,7 +423,7 @@ __device__ __forceinline__ void flush_log(const Problem& p, const ScanState& st,
             const uint32_t slot = wq[ql[u]] + li[u];
             const int qq = qid_s[ql[u]];
             if ((int64_t)slot < st.cap) st.cand[(int64_t)qq * st.cap + slot] = int_key(sv, idv[u]);
-            atomicAdd(&st.hist[(int64_t)qq * kNB + hist_bin(sv, st.hlo, st.hsh)], 1u);
+            if (kGlobalHist) atomicAdd(&st.hist[(int64_t)qq * kNB + hist_bin(sv, st.hlo, st.hsh)], 1u);
         }
         wave_fence();
     }
@@ -433,6 +444,29 @@ __device__ __forceinline__ void local_refresh(const uint32_t* lh, int32_t* tau_s
         const uint64_t mk = __ballot(incl >= R);
         if (mk && lane == __ffsll((unsigned long long)mk) - 1)
             atomicMax(&tau_s[ql], (int32_t)(hlo + ((int64_t)(jb_s[ql] + b) << hsh)));
+    }
+}
+
+// Adds a wave's flush histogram (fh: kLB bins per local query from jb_s) to the
+// global histograms and clears it (a bin past the global range is merged into
+// the last one, which can only undercount higher bins); raises hmax to the
+// highest bin added.
+__device__ __forceinline__ void merge_flush(const ScanState& st, uint32_t* fh, const int32_t* jb_s,
+                                            const int32_t* qid_s, int qn) {
+    const int lane = lane_id();
+#pragma unroll 1
+    for (int ql = 0; ql < qn; ++ql) {
+        const int q = qid_s[ql];
+        const uint32_t c = fh[ql * kLB + lane];
+        fh[ql * kLB + lane] = 0;
+        int gb = jb_s[ql] + lane;
+        gb = gb >= kNB ? kNB - 1 : gb;
+        if (c) atomicAdd(&st.hist[(int64_t)q * kNB + gb], c);
+        const uint64_t nz = __ballot(c != 0);
+        if (lane == 0 && nz) {
+            const int top = jb_s[ql] + 63 - __clzll((long long)nz);
+            atomicMax(&st.hmax[q], (uint32_t)(top >= kNB ? kNB - 1 : top));
+        }
     }
 }
 
@@ -469,12 +503,14 @@ __device__ __forceinline__ void refresh_tau(const ScanState& st, int q, int R) {
 // refresh_tau for the (up to 8) queries ql = w, w+8, ... of one wave that got
 // appends in this item, with every load of all of them issued together (one
 // round trip for thresholds and histogram tops, one for the 64-bin windows).
+// Queries ql = first + stride * k (k < 8); with tau_s, each query's item-local
+// threshold is also raised to the global one and to the new bound.
 __device__ __forceinline__ void refresh_tau_wave(const ScanState& st, const int32_t* qid_s, const uint32_t* qapp_s,
-                                                 int qn, int w, int R) {
+                                                 int qn, int first, int stride, int R, int32_t* tau_s = nullptr) {
     const int lane = lane_id();
     int qk = -1;
     if (lane < 8) {
-        const int ql = w + kScanWaves * lane;
+        const int ql = first + stride * lane;
         if (ql < qn && qapp_s[ql] > 0) qk = qid_s[ql];
     }
     if (__ballot(qk >= 0) == 0) return;
@@ -484,6 +520,7 @@ __device__ __forceinline__ void refresh_tau_wave(const ScanState& st, const int3
         tc = ld_coherent(st.tau + qk);
         jm = (int)ld_coherent(st.hmax + qk);
     }
+    if (tau_s && qk >= 0) atomicMax(&tau_s[first + stride * lane], tc);
     int qs[8], top[8], jt[8], v[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -501,7 +538,11 @@ __device__ __forceinline__ void refresh_tau_wave(const ScanState& st, const int3
         const uint64_t mk = __ballot(incl >= R);
         if (mk) {
             const int l = __ffsll((unsigned long long)mk) - 1;
-            if (lane == 0) atomicMax(st.tau + qs[k], (int32_t)(st.hlo + ((int64_t)(top[k] - l) << st.hsh)));
+            const int32_t nt = (int32_t)(st.hlo + ((int64_t)(top[k] - l) << st.hsh));
+            if (lane == 0) {
+                atomicMax(st.tau + qs[k], nt);
+                if (tau_s) atomicMax(&tau_s[first + stride * k], nt);
+            }
         } else if (top[k] - kWave >= jt[k]) {
             refresh_tau(st, qs[k], R);  // the R-th best lies below the first window
         }
@@ -763,7 +804,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                     for (int m = 0; m < 4; ++m) {
                         if (__ballot(mm[m] >= tq[nt]) == 0) continue;
                         if (log_n > kLogCap - 4 * kWave) {
-                            flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave, lh, jb_s);
+                            flush_log<true>(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave, lh, jb_s);
                             log_n = 0;
                             local_refresh(lh, tau_s, jb_s, qn, w, p.R, st.hlo, st.hsh);
                         }
@@ -797,11 +838,11 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
             if (nu < nunits) load_codes(rowbase_of(nu), nc, px0, px1, pkeep);
             wave_fence();
         }
-        if (log_n > 0) flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave, lh, jb_s);
+        if (log_n > 0) flush_log<true>(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave, lh, jb_s);
         __syncthreads();
         local_refresh(lh, tau_s, jb_s, qn, w, p.R, st.hlo, st.hsh);
         publish_item(st, tau_s, qid_s, qn, w);
-        refresh_tau_wave(st, qid_s, qapp_s, qn, w, p.R);
+        refresh_tau_wave(st, qid_s, qapp_s, qn, w, kScanWaves, p.R);
         __syncthreads();
     }
 }
@@ -810,32 +851,30 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
 // For a handful of queries (at most kStreamMaxQ) the one-hot contraction would
 // leave most of every 16-query MFMA tile empty and the scan is bound by
 // streaming the codes from HBM.  Each thread then sums one row's table entries
-// itself, by LDS lookups, while its next 16 code bytes load:
-//  * G = 1: the table is the query's int8 entries, [block][center];
-//  * G = 4: entry (b, c) is a dword holding the four queries' entries + 128
-//    (bytes 0..3); the even and odd bytes are accumulated as two pairs of
-//    16-bit fields (at most 256 blocks between folds into int32, so no field
-//    overflows), and 128 B is subtracted at the end.  Absent queries hold 128.
-// Items, thresholds, hit logs and flushes are those of the main kernel, with
-// G queries per item.
+// itself, by LDS lookups, while its next 16 code bytes load.  Table layouts
+// (G queries per item):
+//  * pair tables (kPair), indexed by a whole code byte (two blocks): G = 1:
+//    int16 T[2p][lo] + T[2p+1][hi]; G = 2: a dword of both queries' pair sums
+//    + 256 as 16-bit fields, added as one 32-bit word (at most 128 pairs
+//    between folds into int32, so no field overflows);
+//  * nibble tables, for tables too large as pairs: G = 1: the int8 entries;
+//    G = 4: a dword of the four queries' entries + 128, the even and odd bytes
+//    accumulated as 16-bit fields (at most 256 blocks between folds).
+// An odd last block leaves the high nibble of its byte out of the pair sums.
+// Absent queries' entries are the bias (value 0).  Items, thresholds, hit logs
+// and flushes are those of the main kernel, with G queries per item; every
+// flush also merges into the global histograms and refreshes the global
+// thresholds, because every workgroup scans rows of the same few queries.
 constexpr int kStreamMaxQ = 4;
-constexpr size_t kStreamMaxTable = 96 * 1024;  // LDS bytes for the table
+constexpr size_t kStreamMaxTable = 120 * 1024;  // LDS bytes for the table
+constexpr int kStreamWaves = 12;               // one workgroup (and one table copy) per CU, 3 waves per SIMD
+constexpr int kStreamThreads = kStreamWaves * kWave;
 
-// 16 code bytes of a row from src; nbytes (1..16) of them are the row's own.
-// Aligned rows (stride a multiple of 16 bytes) read the whole 16 bytes, which
-// stay inside the row's stride; others read byte by byte and zero the rest.
-__device__ __forceinline__ uint4 load_code16(const uint8_t* src, int nbytes, bool fast) {
-    if (fast) return *reinterpret_cast<const uint4*>(src);
-    uint32_t wd[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        uint32_t v = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (4 * k + e < nbytes) v |= (uint32_t)src[4 * k + e] << (8 * e);
-        wd[k] = v;
-    }
-    return make_uint4(wd[0], wd[1], wd[2], wd[3]);
+// 16 code bytes of a row from src.  The streaming kernel runs only on aligned
+// rows (stride a multiple of 16 bytes), so the whole 16 bytes stay inside the
+// row's stride; entries past the row's blocks are never added.
+__device__ __forceinline__ uint4 load_code16(const uint8_t* src) {
+    return *reinterpret_cast<const uint4*>(src);
 }
 
 // Raises the item-local thresholds of all of an item's qn queries (one wave).
@@ -852,39 +891,73 @@ __device__ __forceinline__ void local_refresh_all(const uint32_t* lh, int32_t* t
     }
 }
 
-// Adds the table entries of the 32 blocks [32 j0, 32 j0 + nb) coded in v
-// (byte k holds blocks 32 j0 + 2k (low nibble) and + 2k + 1 (high)).
-template <int G>
-__device__ __forceinline__ void stream_accumulate(const unsigned char* tbl, int j0, uint4 v, int nb, int32_t& s1,
-                                                  uint32_t& ae, uint32_t& ao) {
-    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+template <int G, bool kPair>
+struct StreamAcc {
+    int32_t s[G == 1 ? 1 : 4] = {};
+    uint32_t f0 = 0, f1 = 0;  // packed 16-bit fields
+
+    // segment j of 16 code bytes: nb blocks (pair tables: nb bytes).  Lookups
+    // are issued sixteen at a time before any is added, so they overlap.
+    __device__ __forceinline__ void add(const unsigned char* tbl, int j, uint4 v, int nb) {
+        constexpr int N = kPair ? 16 : 32;  // entries per segment
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+        for (int h = 0; h < N; h += 16) {
+            uint32_t x[16];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int bl = 8 * k + e;  // block within the segment
-            if (bl >= nb) break;
-            const uint32_t c = (wd[k] >> (4 * e)) & 15u;
-            const int b = 32 * j0 + bl;
-            if (G == 1) {
-                s1 += (int32_t)reinterpret_cast<const int8_t*>(tbl)[b * 16 + (int)c];
-            } else {
-                const uint32_t x = reinterpret_cast<const uint32_t*>(tbl)[b * 16 + (int)c];
-                ae += x & 0x00FF00FFu;
-                ao += __builtin_amdgcn_perm(x, x, 0x0c030c01u);  // bytes 1 and 3 -> 16-bit fields
+            for (int i = 0; i < 16; ++i) {
+                const int u = h + i;
+                const uint32_t w32 = wd[u / (N / 4)];
+                const int e = u % (N / 4);
+                if (u >= nb) {
+                    x[i] = 0;
+                } else if (kPair) {
+                    const int c = (int)((w32 >> (8 * e)) & 255u);
+                    x[i] = G == 1 ? (uint32_t)(int32_t)reinterpret_cast<const int16_t*>(tbl)[(16 * j + u) * 256 + c]
+                                  : reinterpret_cast<const uint32_t*>(tbl)[(16 * j + u) * 256 + c];
+                } else {
+                    const int c = (int)((w32 >> (4 * e)) & 15u);
+                    x[i] = G == 1 ? (uint32_t)(int32_t)reinterpret_cast<const int8_t*>(tbl)[(32 * j + u) * 16 + c]
+                                  : reinterpret_cast<const uint32_t*>(tbl)[(32 * j + u) * 16 + c];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (G == 1) {
+                    s[0] += (int32_t)x[i];
+                } else if (kPair) {
+                    f0 += x[i];
+                } else {
+                    f0 += x[i] & 0x00FF00FFu;
+                    f1 += __builtin_amdgcn_perm(x[i], x[i], 0x0c030c01u);  // bytes 1 and 3 -> 16-bit fields
+                }
             }
         }
     }
-}
+    __device__ __forceinline__ void fold() {
+        if (G == 1) return;
+        s[0] += (int32_t)(f0 & 0xFFFFu);
+        s[G == 2 ? 1 : 2] += (int32_t)(f0 >> 16);
+        if (G == 4) {
+            s[1] += (int32_t)(f1 & 0xFFFFu);
+            s[3] += (int32_t)(f1 >> 16);
+        }
+        f0 = f1 = 0;
+    }
+};
 
-template <int G>
-__global__ __launch_bounds__(kScanThreads, 2) void scan_stream_kernel(MainArgs a) {
-    extern __shared__ __align__(16) unsigned char tbl[];  // B * 16 entries of G == 1 ? 1 : 4 bytes
-    __shared__ uint64_t log_s[kScanWaves * kLogCap];
+// kSegs > 0: rows of at most kSegs 16-byte segments stay whole in registers;
+// kSegs = 0: longer rows stream through a ring of four segments.
+template <int G, bool kPair, int kSegs>
+__global__ __launch_bounds__(kStreamThreads) void scan_stream_kernel(MainArgs a) {
+    constexpr int kCap = G * kWave + 128;  // log entries per wave: room for one batch of hits
+    extern __shared__ __align__(16) unsigned char tbl[];  // the table; nibble entries staged after it
+    __shared__ uint64_t log_s[kStreamWaves * kCap];
     __shared__ int32_t qid_s[kQG];  // flushes read kQG entries
     __shared__ uint32_t qapp_s[kQG];
-    __shared__ uint32_t fl_s[kScanWaves * 2 * kWave];
+    __shared__ uint32_t fl_s[kStreamWaves * 2 * kWave];
     __shared__ uint32_t lh[G * kLB];
+    __shared__ uint32_t fh_s[kStreamWaves * G * kLB];  // per-wave flush histograms
     __shared__ int32_t tau_s[kQG];
     __shared__ int32_t jb_s[kQG];
     __shared__ int64_t item_s, p0_s, p1_s, qbase_s;
@@ -894,13 +967,19 @@ __global__ __launch_bounds__(kScanThreads, 2) void scan_stream_kernel(MainArgs a
     const ScanState& st = a.st;
     const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
     const int64_t n_items = p.leaves ? a.itemoff[p.L] : a.n_items;
-    uint64_t* mylog = log_s + w * kLogCap;
+    uint64_t* mylog = log_s + w * kCap;
     uint32_t* mywq = fl_s + w * 2 * kWave;
-    const int cb = (p.B + 1) / 2;     // code bytes per row
+    uint32_t* myfh = fh_s + w * G * kLB;
+    for (int e = lane; e < G * kLB; e += kWave) myfh[e] = 0;
+    const int cb = (p.B + 1) / 2;     // code bytes per row (= pairs)
     const int nseg = (cb + 15) / 16;  // 16-byte segments per row (the last may be partial)
-    const bool fast = a.fast_codes != 0;
+    const int lastb = cb - 16 * (nseg - 1);
+    const size_t tbl_bytes = kPair ? (size_t)cb * 256 * (G == 1 ? 2 : 4) : (size_t)p.B * 16 * (G == 1 ? 1 : 4);
+    int8_t* nib_s = reinterpret_cast<int8_t*>(tbl + ((tbl_bytes + 15) & ~(size_t)15));  // pair tables: G x B x 16
 
     int64_t claimed = 0;
+    int64_t staged_qbase = -1;  // the query group whose table is in LDS
+    int staged_qn = 0;
     if (tid == 0) claimed = (int64_t)atomicAdd(&st.ctrl[0], 1u);
     for (;;) {
         if (tid == 0) {
@@ -922,6 +1001,7 @@ __global__ __launch_bounds__(kScanThreads, 2) void scan_stream_kernel(MainArgs a
         if (item >= n_items) break;
         const int64_t p0 = p0_s, p1 = p1_s;
         const int qn = qn_s;
+        const bool restage = qbase_s != staged_qbase || qn != staged_qn;
         if (tid < kQG) {
             int32_t qq = 0;
             if (tid < qn) qq = p.leaves ? a.qlist[qbase_s + tid] : (int32_t)(qbase_s + tid);
@@ -931,91 +1011,171 @@ __global__ __launch_bounds__(kScanThreads, 2) void scan_stream_kernel(MainArgs a
             tau_s[tid] = t;
             jb_s[tid] = (t == INT_MIN || t == INT_MAX) ? 0 : hist_bin(t, st.hlo, st.hsh);
         }
-        for (int e = tid; e < G * kLB; e += kScanThreads) lh[e] = 0;
+        for (int e = tid; e < G * kLB; e += kStreamThreads) lh[e] = 0;
         __syncthreads();
-        // table staging
-        if (G == 1) {
-            const int8_t* src = p.lut + (int64_t)qid_s[0] * p.B * 16;
-            if ((reinterpret_cast<uintptr_t>(p.lut) & 15) == 0) {
-                for (int e = tid; e < p.B; e += kScanThreads)
-                    reinterpret_cast<uint4*>(tbl)[e] = reinterpret_cast<const uint4*>(src)[e];
-            } else {
-                for (int e = tid; e < p.B * 16; e += kScanThreads) tbl[e] = (unsigned char)src[e];
-            }
-        } else {
-            for (int e = tid; e < p.B * 16; e += kScanThreads) {
-                uint32_t x = 0;
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const int32_t t = g < qn ? (int32_t)p.lut[(int64_t)qid_s[g] * p.B * 16 + e] : 0;
-                    x |= (uint32_t)(t + 128) << (8 * g);
+        if (restage) {  // table staging (items of one query group reuse it)
+            staged_qbase = qbase_s;
+            staged_qn = qn;
+            if (kPair) {
+                for (int e = tid; e < G * p.B * 16; e += kStreamThreads) {
+                    const int g = e / (p.B * 16), r = e - g * (p.B * 16);
+                    nib_s[e] = g < qn ? p.lut[(int64_t)qid_s[g] * p.B * 16 + r] : (int8_t)0;
                 }
-                reinterpret_cast<uint32_t*>(tbl)[e] = x;
+                __syncthreads();
+                for (int e = tid; e < cb * 256; e += kStreamThreads) {
+                    const int pr = e >> 8, c = e & 255;
+                    const bool hi = 2 * pr + 1 < p.B;
+                    if (G == 1) {
+                        const int v = nib_s[(2 * pr) * 16 + (c & 15)] + (hi ? nib_s[(2 * pr + 1) * 16 + (c >> 4)] : 0);
+                        reinterpret_cast<int16_t*>(tbl)[e] = (int16_t)v;
+                    } else {
+                        uint32_t x = 0;
+#pragma unroll
+                        for (int g = 0; g < 2; ++g) {
+                            const int8_t* t = nib_s + g * p.B * 16;
+                            const int v = t[(2 * pr) * 16 + (c & 15)] + (hi ? t[(2 * pr + 1) * 16 + (c >> 4)] : 0);
+                            x |= (uint32_t)(v + 256) << (16 * g);
+                        }
+                        reinterpret_cast<uint32_t*>(tbl)[e] = x;
+                    }
+                }
+            } else if (G == 1) {
+                const int8_t* src = p.lut + (int64_t)qid_s[0] * p.B * 16;
+                for (int e = tid; e < p.B * 16; e += kStreamThreads) tbl[e] = (unsigned char)src[e];
+            } else {
+                for (int e = tid; e < p.B * 16; e += kStreamThreads) {
+                    uint32_t x = 0;
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const int32_t t = g < qn ? (int32_t)p.lut[(int64_t)qid_s[g] * p.B * 16 + e] : 0;
+                        x |= (uint32_t)(t + 128) << (8 * g);
+                    }
+                    reinterpret_cast<uint32_t*>(tbl)[e] = x;
+                }
             }
+            __syncthreads();
         }
-        __syncthreads();
 
         int log_n = 0;
-        for (int64_t rb = p0 + w * kWave; rb < p1; rb += kScanThreads) {
-            const int64_t row = rb + lane;
+        // appends a wave's log, raises the item's thresholds from its
+        // histogram, merges the flush into the global histograms and refreshes
+        // the global thresholds (every workgroup scans rows of the same few
+        // queries, so they all profit at once)
+        auto flush_publish = [&](int n) {
+            flush_log<false>(p, st, mylog, n, qid_s, qapp_s, p0, mywq, mywq + kWave, lh, jb_s, myfh);
+            local_refresh_all(lh, tau_s, jb_s, qn, p.R, st.hlo, st.hsh);
+            merge_flush(st, myfh, jb_s, qid_s, qn);
+            if (lane < qn) atomicMax(st.tau + qid_s[lane], tau_s[lane]);
+            refresh_tau_wave(st, qid_s, qapp_s, qn, 0, 1, p.R, tau_s);
+        };
+        // thresholds, sums of the G queries for the lane's row, then the filter
+        auto finish_row = [&](int64_t row, const StreamAcc<G, kPair>& acc) {
             const bool valid = row < p1;
-            const uint8_t* src = p.codes + (valid ? row : p1 - 1) * p.stride;
             int32_t tq[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) tq[g] = g < qn ? tau_s[g] : INT_MAX;
-            int32_t s1 = 0;
-            int32_t sg[4] = {0, 0, 0, 0};
-            uint32_t ae = 0, ao = 0;
-            // segments j < nseg - 1 are full (32 blocks); the next one is
-            // loaded while the current one is summed
-            const int lastb = cb - 16 * (nseg - 1);  // code bytes in the last segment
-            uint4 cur = load_code16(src, nseg == 1 ? lastb : 16, fast);
-            for (int j = 0; j < nseg - 1; ++j) {
-                const int jn = j + 1;
-                const uint4 nxt = load_code16(src + 16 * jn, jn < nseg - 1 ? 16 : lastb, fast);
-                stream_accumulate<G>(tbl, j, cur, 32, s1, ae, ao);
-                if (G != 1 && (j & 7) == 7) {  // 256 blocks: fold the 16-bit fields
-                    sg[0] += (int32_t)(ae & 0xFFFFu); sg[2] += (int32_t)(ae >> 16);
-                    sg[1] += (int32_t)(ao & 0xFFFFu); sg[3] += (int32_t)(ao >> 16);
-                    ae = ao = 0;
-                }
-                cur = nxt;
-            }
-            stream_accumulate<G>(tbl, nseg - 1, cur, p.B - 32 * (nseg - 1), s1, ae, ao);  // 1..32 blocks
             int32_t sum[G];
-            if (G == 1) {
-                sum[0] = s1;
-            } else {
-                sg[0] += (int32_t)(ae & 0xFFFFu); sg[2] += (int32_t)(ae >> 16);
-                sg[1] += (int32_t)(ao & 0xFFFFu); sg[3] += (int32_t)(ao >> 16);
 #pragma unroll
-                for (int g = 0; g < G; ++g) sum[g] = sg[g] - 128 * p.B;
-            }
-            if (log_n > kLogCap - G * kWave) {
-                flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave, lh, jb_s);
-                log_n = 0;
-                local_refresh_all(lh, tau_s, jb_s, qn, p.R, st.hlo, st.hsh);
-            }
-            const uint32_t lr = (uint32_t)(row - p0);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const bool hit = valid && sum[g] >= tq[g];
-                const uint64_t mk = __ballot(hit);
-                if (mk) {
-                    if (hit)
-                        mylog[log_n + __popcll(mk & lanemask_lt())] =
-                            ((uint64_t)(uint32_t)sum[g] << 32) | ((uint64_t)g << 16) | (uint64_t)lr;
-                    log_n += __popcll(mk);
+            for (int g = 0; g < G; ++g)
+                sum[g] = G == 1 ? acc.s[0] : acc.s[g] - (kPair ? 256 * cb : 128 * p.B);
+                if (log_n > kCap - G * kWave) {
+                    flush_publish(log_n);
+                    log_n = 0;
                 }
+                const uint32_t lr = (uint32_t)(row - p0);
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const bool hit = valid && sum[g] >= tq[g];
+                    const uint64_t mk = __ballot(hit);
+                    if (mk) {
+                        if (hit)
+                            mylog[log_n + __popcll(mk & lanemask_lt())] =
+                                ((uint64_t)(uint32_t)sum[g] << 32) | ((uint64_t)g << 16) | (uint64_t)lr;
+                        log_n += __popcll(mk);
+                    }
+                }
+        };
+        const int fulln = kPair ? 16 : 32;                                 // entries of a full segment
+        const int lastn = kPair ? lastb : p.B - 32 * (nseg - 1);           // entries of the last one
+        const int64_t rb0 = p0 + w * kWave;
+        if (kSegs > 0) {
+            // whole rows in registers; the next batch's rows load while this
+            // batch's are summed.  Every load is unconditional (rows past the
+            // item and segments past the row read the last valid ones), so the
+            // compiler can wait for exactly the loads it needs.
+            auto load_row = [&](int64_t rb, uint4* r) {
+                const int64_t row = rb + lane;
+                const uint8_t* src = p.codes + (row < p1 ? row : p1 - 1) * p.stride;
+#pragma unroll
+                for (int j = 0; j < kSegs; ++j) {
+                    const int jj = j < nseg ? j : nseg - 1;
+                    r[j] = load_code16(src + 16 * jj);
+                }
+            };
+            auto batch = [&](int64_t rb, const uint4* r, uint4* nr) {
+                load_row(rb + kStreamThreads, nr);
+                StreamAcc<G, kPair> acc;
+#pragma unroll
+                for (int j = 0; j < kSegs; ++j) {
+                    if (j >= nseg) break;
+                    if (j < nseg - 1) acc.add(tbl, j, r[j], fulln);
+                    else acc.add(tbl, j, r[j], lastn);
+                }
+                acc.fold();
+                finish_row(rb + lane, acc);
+            };
+            uint4 ra[kSegs > 0 ? kSegs : 1], rbuf[kSegs > 0 ? kSegs : 1];
+            load_row(rb0, ra);
+            for (int64_t rb = rb0; rb < p1; rb += 2 * kStreamThreads) {
+                batch(rb, ra, rbuf);
+                if (rb + kStreamThreads >= p1) break;
+                batch(rb + kStreamThreads, rbuf, ra);
+            }
+        } else {
+            // long rows: a ring of four segments in flight within the row
+            for (int64_t rb = rb0; rb < p1; rb += kStreamThreads) {
+                const int64_t row = rb + lane;
+                const uint8_t* src = p.codes + (row < p1 ? row : p1 - 1) * p.stride;
+                uint4 ring[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (k < nseg) ring[k] = load_code16(src + 16 * k);
+                StreamAcc<G, kPair> acc;
+                for (int j0 = 0; j0 < nseg; j0 += 4) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int j = j0 + k;
+                        if (j >= nseg) break;
+                        const uint4 v = ring[k];
+                        if (j + 4 < nseg) ring[k] = load_code16(src + 16 * (j + 4));
+                        if (j < nseg - 1) acc.add(tbl, j, v, fulln);
+                        else acc.add(tbl, j, v, lastn);
+                        if (j % 8 == 7) acc.fold();  // 128 pairs, or 256 blocks
+                    }
+                }
+                acc.fold();
+                finish_row(row, acc);
             }
         }
-        if (log_n > 0) flush_log(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave, lh, jb_s);
+        if (log_n > 0) {
+            flush_log<false>(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave, lh, jb_s, myfh);
+            merge_flush(st, myfh, jb_s, qid_s, qn);
+        }
         __syncthreads();
         local_refresh(lh, tau_s, jb_s, qn, w, p.R, st.hlo, st.hsh);
         publish_item(st, tau_s, qid_s, qn, w);
-        refresh_tau_wave(st, qid_s, qapp_s, qn, w, p.R);
+        refresh_tau_wave(st, qid_s, qapp_s, qn, w, kScanWaves, p.R);
         __syncthreads();
     }
+}
+
+// LDS bytes of the streaming kernel's dynamic area (0: the variant does not fit).
+static size_t stream_lds(int G, bool pair, int32_t B) {
+    const size_t cb = (size_t)(B + 1) / 2;
+    const size_t t = pair ? cb * 256 * (G == 1 ? 2 : 4) : (size_t)B * 16 * (G == 1 ? 1 : 4);
+    const size_t extra = pair ? (size_t)G * B * 16 : 0;
+    const size_t total = ((t + 15) & ~(size_t)15) + extra;
+    return total <= kStreamMaxTable ? total : 0;
 }
 
 // ------------------------------------------------------------------ final selection
@@ -1123,6 +1283,21 @@ static void allow_lds(K kernel, size_t bytes) {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
+template <int G, bool kPair, int kSegs>
+static void launch_stream1(int grid, size_t lds, hipStream_t stream, const MainArgs& ma) {
+    allow_lds(scan_stream_kernel<G, kPair, kSegs>, lds);
+    hipLaunchKernelGGL((scan_stream_kernel<G, kPair, kSegs>), dim3(grid), dim3(kStreamThreads), lds, stream, ma);
+}
+
+// Row length classes: up to 2 or 6 segments of 16 code bytes whole in
+// registers, longer rows through the ring.
+template <int G, bool kPair>
+static void launch_stream(int nseg, int grid, size_t lds, hipStream_t stream, const MainArgs& ma) {
+    if (nseg <= 2) launch_stream1<G, kPair, 2>(grid, lds, stream, ma);
+    else if (nseg <= 6) launch_stream1<G, kPair, 6>(grid, lds, stream, ma);
+    else launch_stream1<G, kPair, 0>(grid, lds, stream, ma);
+}
+
 static int device_cus() {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -1165,14 +1340,34 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     const int32_t B8 = (sp.B + 7) & ~7;
     ma.nkstep = B8 / 4;
     ma.nchunk = (ma.nkstep + kKC - 1) / kKC;
-    // small batches stream the codes through VALU lookups (G = 1 or 4 queries
-    // per item); larger ones use the MFMA kernel with 64 queries per item
-    const int sg = sp.nq <= 1 ? 1 : 4;
-    const size_t stbl = (size_t)sp.B * 16 * (sg == 1 ? 1 : 4);
-    const bool streaming = sp.nq <= kStreamMaxQ && stbl <= kStreamMaxTable;
+    // small batches stream the codes through VALU lookups: one query, or two
+    // per item, by byte-pair tables; else one or four per item by nibble
+    // tables; larger batches use the MFMA kernel with 64 queries per item
+    int sg = 0;
+    bool spair = false;
+    size_t stbl = 0;
+    const bool aligned = (sp.stride % 16) == 0 && (reinterpret_cast<uintptr_t>(sp.codes) & 15) == 0;
+    if (sp.nq >= 1 && sp.nq <= kStreamMaxQ && aligned) {
+        const int gp = sp.nq == 1 ? 1 : 2, gn = sp.nq == 1 ? 1 : 4;
+        if ((stbl = stream_lds(gp, true, sp.B)) != 0) {
+            sg = gp;
+            spair = true;
+        } else if ((stbl = stream_lds(gn, false, sp.B)) != 0) {
+            sg = gn;
+        }
+    }
+    const bool streaming = sg != 0;
     ma.qg = streaming ? sg : kQG;
     ma.nqg = (int32_t)((sp.nq + ma.qg - 1) / ma.qg);
-    ma.n_items = (int64_t)ma.nqg * ((sp.n + kItemPts - 1) / kItemPts);
+    // the MFMA kernel's items are kItemPts rows; the streaming kernel's are cut
+    // so that every CU gets at least two of them
+    ma.item_pts = kItemPts;
+    if (streaming) {
+        const int64_t rows = part ? (sp.n * sp.nl + sp.L - 1) / (sp.L > 0 ? sp.L : 1) : sp.n;  // rows per query group, roughly
+        while (ma.item_pts > 1024 && (int64_t)ma.nqg * ((rows + ma.item_pts - 1) / ma.item_pts) < 2LL * device_cus())
+            ma.item_pts >>= 1;
+    }
+    ma.n_items = (int64_t)ma.nqg * ((sp.n + ma.item_pts - 1) / ma.item_pts);
     ma.fast_codes = (sp.stride % 16) == 0 && (reinterpret_cast<uintptr_t>(sp.codes) & 15) == 0;
     if (part) {
         uint32_t* lcnt = reinterpret_cast<uint32_t*>(base + lay.lcnt);
@@ -1185,8 +1380,8 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
         const int64_t pairs = sp.nq * sp.nl;
         const unsigned gb = (unsigned)((pairs + 255) / 256 < 4096 ? (pairs + 255) / 256 : 4096);
         hipLaunchKernelGGL(leaf_count_kernel, dim3(gb), dim3(256), 0, stream, sp.leaves, pairs, sp.L, lcnt);
-        hipLaunchKernelGGL(leaf_scan_kernel, dim3(1), dim3(1024), 0, stream, lcnt, sp.leaf_offsets, sp.L, ma.qg, lqoff,
-                           itemoff);
+        hipLaunchKernelGGL(leaf_scan_kernel, dim3(1), dim3(1024), 0, stream, lcnt, sp.leaf_offsets, sp.L, ma.qg,
+                           ma.item_pts, lqoff, itemoff);
         hipLaunchKernelGGL(leaf_scatter_kernel, dim3(gb), dim3(256), 0, stream, sp.leaves, sp.nq, sp.nl, sp.L, lqoff, lcur, qlist);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         ma.lqoff = lqoff;
@@ -1197,23 +1392,24 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     // thresholds tighten it within the first items
     int32_t W = 2 * sp.R;
     if (W < 512) W = 512;
+    if (streaming) W = 8192;  // a few queries: a tighter first bound is cheap and every workgroup starts from it
     if (W > 8192) W = 8192;
     const size_t lut_bytes = ((size_t)sp.B * 16 + 15) & ~(size_t)15;
     allow_lds(warmup_kernel, lut_bytes + (size_t)W * 8);
     hipLaunchKernelGGL(warmup_kernel, dim3((unsigned)sp.nq), dim3(kSelThreads), lut_bytes + (size_t)W * 8, stream, p, st, W);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t max_items = part ? (int64_t)sp.nq * sp.nl + sp.L : ma.n_items;
-    int grid = device_cus() * (streaming ? 2 : 1);
+    int grid = device_cus();
     if (max_items < grid) grid = (int)(max_items > 0 ? max_items : 1);
     if (main_start && (e = hipEventRecord(main_start, stream)) != hipSuccess) return e;
     if (!streaming) {
         hipLaunchKernelGGL(scan_main_kernel, dim3(grid), dim3(kScanThreads), 0, stream, ma);
-    } else if (sg == 1) {
-        allow_lds(scan_stream_kernel<1>, stbl);
-        hipLaunchKernelGGL(scan_stream_kernel<1>, dim3(grid), dim3(kScanThreads), stbl, stream, ma);
     } else {
-        allow_lds(scan_stream_kernel<4>, stbl);
-        hipLaunchKernelGGL(scan_stream_kernel<4>, dim3(grid), dim3(kScanThreads), stbl, stream, ma);
+        const int nseg = ((sp.B + 1) / 2 + 15) / 16;
+        if (spair && sg == 1) launch_stream<1, true>(nseg, grid, stbl, stream, ma);
+        else if (spair) launch_stream<2, true>(nseg, grid, stbl, stream, ma);
+        else if (sg == 1) launch_stream<1, false>(nseg, grid, stbl, stream, ma);
+        else launch_stream<4, false>(nseg, grid, stbl, stream, ma);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (main_stop && (e = hipEventRecord(main_stop, stream)) != hipSuccess) return e;

@@ -137,18 +137,21 @@ def test_scan_partitioned_parity(gpu):
     _scan_check(torch, ah, lut, codes, R, ids=perm, offs=offs, leaves=leaves)
 
 
-# Small batches (at most four queries) take the streaming kernel: one query, or
-# four queries packed per table entry.  Cases cover segment folds past 256
-# blocks, partial last segments, unaligned rows, R > n and a 64 KB table.
+# Small batches (at most four queries) on rows aligned to 16 bytes take the
+# streaming kernel: byte-pair tables for one or two queries per item, nibble
+# tables (one query, or four packed) when pair tables would not fit.  Cases
+# cover segment folds past 256 blocks, partial last segments, R > n, a 64 KB
+# table and every row-length class (2, 6, 8 segments, longer).
 @pytest.mark.parametrize("B,n,nq,R,stride_pad", [
     (32, 10000, 1, 100, 0),
     (64, 50000, 4, 200, 0),
-    (50, 3001, 2, 37, 0),       # 25 B rows: byte loads
+    (50, 3001, 2, 37, 7),       # 25 code bytes in 32 B rows
+    (50, 3001, 2, 37, 0),       # 25 B rows: unaligned, so the MFMA kernel
     (8, 700, 3, 1000, 0),       # R > n
     (200, 20000, 1, 300, 0),    # 100 B rows: partial last segment
     (300, 4000, 4, 50, 0),      # 300 blocks: packed fields folded mid-row
     (768, 5000, 4, 400, 0),     # 48 KB packed table
-    (33, 1234, 1, 10, 7),       # odd B, 24 B stride
+    (33, 1234, 1, 10, 15),      # odd B, 32 B stride
     (1, 999, 4, 5, 0),          # one block
     (4096, 600, 1, 20, 0),      # 64 KB single-query table
 ])
@@ -162,26 +165,32 @@ def test_scan_stream_parity(gpu, B, n, nq, R, stride_pad):
     _scan_check(torch, ah, lut, codes, R)
 
 
-@pytest.mark.parametrize("nq", [4, 70])
-def test_scan_extreme_tables(gpu, nq):
+@pytest.mark.parametrize("nq,B", [(1, 96), (2, 128), (4, 256), (70, 256)])
+def test_scan_extreme_tables(gpu, nq, B):
     """Entries of -128 and 127 only (streaming: packed fields at both ends of
-    their range), one query all 127 and one all -128 (every sum -128 B, the
-    lowest possible: a threshold must never be raised past it)."""
+    their range; one query: byte-pair table, two: packed pair table, four:
+    packed nibble table, 70: MFMA); where present, one query all 127 and one
+    all -128 (every sum -128 B, the lowest possible: a threshold must never be
+    raised past it)."""
     torch, ah = gpu
     rng = np.random.default_rng(91 + nq)
-    B, n, R = 256, 3000, 64
+    n, R = 3000, 64
     lut = rng.choice(np.array([-128, 127], dtype=np.int8), size=(nq, B, 16))
-    lut[1] = 127
-    lut[2] = -128
+    if nq > 1:
+        lut[-1] = -128
+    if nq > 2:
+        lut[1] = 127
     codes = synth.random_codes(rng, n, B)
     _scan_check(torch, ah, lut, codes, R)
 
 
-@pytest.mark.parametrize("nq", [1, 3])
-def test_scan_stream_partitioned(gpu, nq):
+@pytest.mark.parametrize("nq,B,L,nl", [(1, 48, 25, 5), (3, 48, 25, 5), (4, 48, 3, 2), (3, 400, 4, 3)])
+def test_scan_stream_partitioned(gpu, nq, B, L, nl):
+    """Few queries over leaves; with few leaves several queries share one, so a
+    leaf has more than one query group (two per item with pair tables)."""
     torch, ah = gpu
-    rng = np.random.default_rng(300 + nq)
-    B, n, L, nl, R = 48, 40000, 25, 5, 90
+    rng = np.random.default_rng(300 + nq + B + L)
+    n, R = 40000, 90
     sizes = synth.random_leaf_sizes(rng, n, L, skew=1.0)
     offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
     lut = synth.random_lut_i8(rng, nq, B)
