@@ -91,6 +91,26 @@ __device__ void bitonic_sort_desc(uint64_t* a, int P) {
     }
 }
 
+// Bitonic sort (descending) of P keys (P a power of two) in LDS by one wave,
+// with no workgroup barrier: a wave's LDS accesses complete in issue order, and
+// the wave-scope fence between stages keeps the compiler from reordering them.
+__device__ __forceinline__ void wave_bitonic_sort_desc(uint64_t* a, int P) {
+    const int lane = (int)__lane_id();
+    for (int size = 2; size <= P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = lane; i < (P >> 1); i += 64) {
+                const int lo = 2 * i - (i & (stride - 1));
+                const int hi = lo + stride;
+                const bool desc = (lo & size) == 0;
+                const uint64_t x = a[lo], y = a[hi];
+                if ((x < y) == desc) { a[lo] = y; a[hi] = x; }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
 __device__ __forceinline__ int next_pow2(int x) {
     int p = 1;
     while (p < x) p <<= 1;

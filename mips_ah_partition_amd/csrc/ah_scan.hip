@@ -60,7 +60,7 @@ constexpr int kSelThreads = 256;
 constexpr int kSelLds = 4096;                     // keys staged in LDS by the final select
 
 struct ScanLayout {
-    size_t tau, cnt, hmax, hist, cand, ctrl, ovf, fb, lcnt, lqoff, lcur, qlist, itemoff, total;
+    size_t tau, cnt, hmax, hist, cand, ctrl, ovf, dfr, fb, lcnt, lqoff, lcur, qlist, itemoff, total;
     int64_t cap;
 };
 
@@ -84,6 +84,7 @@ static ScanLayout scan_layout(int64_t nq, int32_t B, int64_t n, int32_t L, int32
     s.cand = o;    o = align_up(o + (size_t)nq * (size_t)cap * 8);
     s.ctrl = o;    o = align_up(o + 64);
     s.ovf = o;     o = align_up(o + (size_t)nq * 4);
+    s.dfr = o;     o = align_up(o + (size_t)nq * 4);
     s.fb = o;      o = align_up(o + (size_t)kFbSlots * (size_t)(n > 0 ? n : 1) * 8);
     const bool part = L > 0 && nl > 0;
     s.lcnt = o;    o = align_up(o + (part ? (size_t)L * 4 : 0));
@@ -107,6 +108,7 @@ struct ScanState {
     uint64_t* cand;
     uint32_t* ctrl;  // [0] work counter, [1] overflow count, [2] fallback cursor
     int32_t* ovf;
+    int32_t* dfr;  // queries whose final selection needs the workgroup path (ctrl[3] of them)
     uint64_t* fb;
     int64_t cap;
     int32_t hlo, hw, hsh;  // bin b covers sums [hlo + b*hw, hlo + (b+1)*hw), hw = 1 << hsh
@@ -1178,21 +1180,162 @@ static size_t stream_lds(int G, bool pair, int32_t B) {
     return total <= kStreamMaxTable ? total : 0;
 }
 
+// ------------------------------------------------------------------ one-wave warm-up and selection
+// Four queries per 256-thread workgroup, one wave each and no workgroup
+// barrier, for the common sizes: the warm-up when the query's table fits in
+// kWaveLut bytes; the final selection when at most kWaveKeys candidates reach
+// the query's threshold (others are deferred to the workgroup kernel).
+constexpr int kWaveKeys = 1024;
+constexpr int kWaveLut = 4096;
+
+// The warm-up threshold here is the lower edge of the histogram bin holding the
+// R-th best of the W sums (a valid bound, at most one bin below the exact R-th
+// best): one histogram instead of a sort.
+__global__ __launch_bounds__(kSelThreads) void warmup_wave_kernel(Problem p, ScanState st, int32_t W) {
+    __shared__ __align__(16) int8_t lut_all[4][kWaveLut];
+    __shared__ uint32_t hist_all[4][kNB];
+    const int w = threadIdx.x / kWave, lane = lane_id();
+    const int64_t q = (int64_t)blockIdx.x * 4 + w;
+    if (q == 0 && lane < 16) st.ctrl[lane] = 0;
+    if (q >= p.nq) return;
+    int8_t* lut_s = lut_all[w];
+    uint32_t* hw_s = hist_all[w];
+    for (int e = lane; e < p.B * 16; e += kWave) lut_s[e] = p.lut[q * p.B * 16 + e];
+    for (int j = lane; j < kNB; j += kWave) st.hist[q * kNB + j] = 0;
+    if (lane == 0) {
+        st.cnt[q] = 0;
+        st.hmax[q] = 0;
+    }
+    const bool al4 = (p.stride & 3) == 0 && (reinterpret_cast<uintptr_t>(p.codes) & 3) == 0;
+    // 16-byte aligned rows (then the stride holds every 16-byte segment of the codes)
+    const bool al16 = (p.stride & 15) == 0 && (reinterpret_cast<uintptr_t>(p.codes) & 15) == 0;
+    const int nseg = ((p.B + 1) / 2 + 15) / 16;
+    for (int j = lane; j < kNB; j += kWave) hw_s[j] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    int64_t got = 0;
+    const int nsrc = p.leaves ? p.nl : 1;
+    for (int j = 0; j < nsrc && got < W; ++j) {
+        int64_t a, b;
+        if (p.leaves) {
+            const int32_t l = p.leaves[q * p.nl + j];
+            const bool okl = l >= 0 && l < p.L;
+            a = okl ? p.leaf_offsets[l] : 0;
+            b = okl ? p.leaf_offsets[l + 1] : 0;
+        } else {
+            a = 0;
+            b = p.n;
+        }
+        const int64_t take = b - a < W - got ? b - a : W - got;
+        for (int64_t t = lane; t < take; t += kWave) {
+            const int64_t row = a + t;
+            const uint8_t* src = p.codes + row * p.stride;
+            int32_t sv = 0;
+            if (al16) {
+                // the whole row's code bytes (at most 8 x 16) in one round trip
+                uint4 seg[kWaveLut / 512];
+#pragma unroll
+                for (int j = 0; j < kWaveLut / 512; ++j)
+                    if (j < nseg) seg[j] = *reinterpret_cast<const uint4*>(src + 16 * j);
+#pragma unroll
+                for (int j = 0; j < kWaveLut / 512; ++j) {
+                    if (j >= nseg) break;
+                    const uint32_t wd[4] = {seg[j].x, seg[j].y, seg[j].z, seg[j].w};
+#pragma unroll
+                    for (int u = 0; u < 32; ++u) {
+                        const int blk = 32 * j + u;
+                        if (blk < p.B) sv += lut_s[blk * 16 + (int)((wd[u >> 3] >> (4 * (u & 7))) & 15u)];
+                    }
+                }
+            } else {
+                sv = row_sum(lut_s, p.B, src, al4);
+            }
+            atomicAdd(&hw_s[hist_bin(sv, st.hlo, st.hsh)], 1u);
+        }
+        got += take;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // the highest bin edge with at least R sums at or above it: lane l owns
+    // the 16 bins from the top 16 l down
+    if (got < p.R) {
+        if (lane == 0) st.tau[q] = INT_MIN;
+        return;
+    }
+    int c[16], tot = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        c[k] = (int)hw_s[kNB - 1 - 16 * lane - k];
+        tot += c[k];
+    }
+    const int incl = wave_inclusive_sum(tot);
+    const uint64_t mk = __ballot(incl >= p.R);
+    const int l = __ffsll((unsigned long long)mk) - 1;  // got >= R, so some lane reaches R
+    if (lane == l) {
+        int cum = incl - tot, bin = kNB - 1 - 16 * lane;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            cum += c[k];
+            if (cum >= p.R) {
+                bin = kNB - 1 - 16 * lane - k;
+                break;
+            }
+        }
+        st.tau[q] = (int32_t)(st.hlo + ((int64_t)bin << st.hsh));
+    }
+}
+
+__global__ __launch_bounds__(kSelThreads) void final_select_wave_kernel(Problem p, ScanState st) {
+    __shared__ uint64_t stage_all[4][kWaveKeys];
+    const int w = threadIdx.x / kWave, lane = lane_id();
+    const int64_t q = (int64_t)blockIdx.x * 4 + w;
+    if (q >= p.nq) return;
+    const uint32_t total = st.cnt[q];
+    if ((int64_t)total > st.cap) {
+        if (lane == 0) st.ovf[atomicAdd(&st.ctrl[1], 1u)] = (int32_t)q;
+        return;
+    }
+    const int32_t tau = st.tau[q];
+    const uint64_t* list = st.cand + q * st.cap;
+    uint64_t* stage = stage_all[w];
+    int n = 0;  // keys at or above tau, staged while they fit
+    for (uint32_t b0 = 0; b0 < total; b0 += kWave) {
+        const uint32_t i = b0 + lane;
+        const uint64_t k = i < total ? list[i] : 0;
+        const bool keep = k != 0 && key_int_score(k) >= tau;
+        const uint64_t mk = __ballot(keep);
+        const int pos = n + __popcll(mk & lanemask_lt());
+        if (keep && pos < kWaveKeys) stage[pos] = k;
+        n += __popcll(mk);
+    }
+    if (n > kWaveKeys) {
+        if (lane == 0) st.dfr[atomicAdd(&st.ctrl[3], 1u)] = (int32_t)q;
+        return;
+    }
+    const int P = next_pow2(n > 0 ? n : 1);
+    for (int j = n + lane; j < P; j += kWave) stage[j] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    wave_bitonic_sort_desc(stage, P);
+    const int m = n < p.R ? n : p.R;
+    for (int r = lane; r < p.R; r += kWave) {
+        const uint64_t k = r < m ? stage[r] : 0;
+        p.out_ids[q * p.R + r] = r < m ? key_id(k) : -1;
+        p.out_scores[q * p.R + r] = r < m ? key_int_score(k) : INT_MIN;
+    }
+}
+
 // ------------------------------------------------------------------ final selection
+// The workgroup selection, for the queries the one-wave kernel deferred
+// (workgroup i takes the i-th of them; the list has ctrl[3] entries).
 __global__ __launch_bounds__(kSelThreads) void final_select_kernel(Problem p, ScanState st) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ SelectShared sh;
     __shared__ uint32_t nst;
-    const int64_t q = blockIdx.x;
+    if (blockIdx.x >= st.ctrl[3]) return;
+    const int64_t q = st.dfr[blockIdx.x];
     const int tid = threadIdx.x;
     const uint32_t total = st.cnt[q];
-    if ((int64_t)total > st.cap) {
-        if (tid == 0) {
-            const uint32_t k = atomicAdd(&st.ctrl[1], 1u);
-            st.ovf[k] = (int32_t)q;
-        }
-        return;
-    }
     const int32_t tau = st.tau[q];
     const uint64_t* list = st.cand + q * st.cap;
     uint64_t* stage = reinterpret_cast<uint64_t*>(smem);
@@ -1321,6 +1464,7 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     st.cand = reinterpret_cast<uint64_t*>(base + lay.cand);
     st.ctrl = reinterpret_cast<uint32_t*>(base + lay.ctrl);
     st.ovf = reinterpret_cast<int32_t*>(base + lay.ovf);
+    st.dfr = reinterpret_cast<int32_t*>(base + lay.dfr);
     st.fb = reinterpret_cast<uint64_t*>(base + lay.fb);
     st.cap = lay.cap;
     st.hlo = -128 * sp.B;  // every sum lies in [-128 B, 127 B], so no sum falls below bin 0's edge
@@ -1391,12 +1535,17 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     // warm-up rows per query: enough for a first bound; the item-local
     // thresholds tighten it within the first items
     int32_t W = 2 * sp.R;
-    if (W < 512) W = 512;
+    if (W < 1024) W = 1024;
     if (streaming) W = 8192;  // a few queries: a tighter first bound is cheap and every workgroup starts from it
     if (W > 8192) W = 8192;
     const size_t lut_bytes = ((size_t)sp.B * 16 + 15) & ~(size_t)15;
-    allow_lds(warmup_kernel, lut_bytes + (size_t)W * 8);
-    hipLaunchKernelGGL(warmup_kernel, dim3((unsigned)sp.nq), dim3(kSelThreads), lut_bytes + (size_t)W * 8, stream, p, st, W);
+    if ((size_t)sp.B * 16 <= (size_t)kWaveLut) {
+        hipLaunchKernelGGL(warmup_wave_kernel, dim3((unsigned)((sp.nq + 3) / 4)), dim3(kSelThreads), 0, stream, p, st, W);
+    } else {
+        allow_lds(warmup_kernel, lut_bytes + (size_t)W * 8);
+        hipLaunchKernelGGL(warmup_kernel, dim3((unsigned)sp.nq), dim3(kSelThreads), lut_bytes + (size_t)W * 8, stream, p,
+                           st, W);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t max_items = part ? (int64_t)sp.nq * sp.nl + sp.L : ma.n_items;
     int grid = device_cus();
@@ -1415,6 +1564,8 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     if (main_stop && (e = hipEventRecord(main_stop, stream)) != hipSuccess) return e;
     int Rp = 1;
     while (Rp < sp.R) Rp <<= 1;
+    hipLaunchKernelGGL(final_select_wave_kernel, dim3((unsigned)((sp.nq + 3) / 4)), dim3(kSelThreads), 0, stream, p, st);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     allow_lds(final_select_kernel, (size_t)(kSelLds + Rp) * 8);
     hipLaunchKernelGGL(final_select_kernel, dim3((unsigned)sp.nq), dim3(kSelThreads), (size_t)(kSelLds + Rp) * 8, stream, p, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -90,6 +90,8 @@ def _scan_check(torch, ah, lut, codes, R, ids=None, offs=None, leaves=None):
     (200, 2000, 20, 300, 0),    # several 64-block chunks
     (768, 1500, 8, 400, 0),     # 768 blocks
     (33, 1234, 5, 10, 7),       # odd B, padded rows
+    (16, 20000, 10, 1500, 0),   # R > 1024: the workgroup final selection
+    (300, 3000, 6, 40, 0),      # 300 blocks: the workgroup warm-up
 ])
 def test_scan_full_parity(gpu, B, n, nq, R, stride_pad):
     torch, ah = gpu
