@@ -202,6 +202,60 @@ def code_scan_probe(torch, ahlib, ev, runs=5):
     return out
 
 
+# ----------------------------------------------------------------------------- other rows at their shapes
+# Centroid scoring (a1), table build (a2) and bf16 reorder (a5) at the shapes of
+# the partitioned workloads, on seeded random inputs generated on the GPU, each
+# against its roofline: a1 is a dense fp32 contraction (2 nq L d FLOP, MFMA fp32
+# peak), a2 writes the int8 tables (nq B 16 bytes, HBM), a5 gathers the
+# candidates' rows (nq R d 2 bytes for bf16, HBM).
+PEAK_FP32_MFMA_TFLOPS = 157.3
+
+
+def _time_ms(torch, fn, runs=5):
+    ts = []
+    for it in range(runs + 1):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        if it:
+            ts.append(a.elapsed_time(b))
+    return float(np.median(ts))
+
+
+def stage_probes(torch, ahlib):
+    out = {}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5151)
+    for name in ("glove1m", "openai2m", "wiki20m"):
+        w = synth.WORKLOADS[name]
+        Q = torch.randn((w.nq, w.d), generator=g, device="cuda")
+        C = torch.randn((w.num_leaves, w.d), generator=g, device="cuda")
+        ms = _time_ms(torch, lambda: ahlib.ah_partition_score(Q, C, w.leaves_to_search))
+        tf = 2.0 * w.nq * w.num_leaves * w.d / (ms / 1e3) / 1e12
+        out[f"a1_partition_{name}"] = {"nq": w.nq, "leaves": w.num_leaves, "d": w.d, "searched": w.leaves_to_search,
+                                       "ms": ms, "TFLOPs": tf, "frac_of_fp32_mfma": tf / PEAK_FP32_MFMA_TFLOPS}
+        cb = torch.randn((w.blocks, 16, w.dpb), generator=g, device="cuda")
+        ms = _time_ms(torch, lambda: ahlib.ah_build_lut(Q, cb))
+        byt = w.nq * w.blocks * 16 + w.nq * w.d * 4
+        out[f"a2_lut_{name}"] = {"nq": w.nq, "blocks": w.blocks, "ms": ms, "GBps": byt / (ms / 1e3) / 1e9,
+                                 "frac_of_8TBps": byt / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
+        del C
+    # bf16 reorder at the 2M x 1536 shape: 1,000 queries x 400 random candidates
+    w = synth.WORKLOADS["openai2m"]
+    base = torch.randn((w.n, w.d), generator=g, device="cuda").to(torch.bfloat16)
+    Q = torch.randn((w.nq, w.d), generator=g, device="cuda")
+    cand = torch.randint(0, w.n, (w.nq, w.reorder), generator=g, device="cuda", dtype=torch.int32)
+    ms = _time_ms(torch, lambda: ahlib.ah_reorder_exact(Q, base, cand, w.k))
+    byt = w.nq * w.reorder * w.d * 2
+    out["a5_reorder_bf16_openai2m"] = {"nq": w.nq, "R": w.reorder, "d": w.d, "ms": ms,
+                                       "GBps": byt / (ms / 1e3) / 1e9, "frac_of_8TBps": byt / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
+    del base
+    torch.cuda.empty_cache()
+    return out
+
+
 # ----------------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -213,6 +267,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-probe", action="store_true", help="skip the code-scan HBM probe")
     ap.add_argument("--probe-only", action="store_true", help="only run the code-scan HBM probe")
+    ap.add_argument("--stages-only", action="store_true", help="only run the other rows' probes (a1, a2, a5)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device 5 times (calibrates FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
@@ -231,6 +286,12 @@ def main():
         print(json.dumps({"copy_calibration_bytes_per_launch": src.numel() * 4, "launches": 5}))
         return
 
+    if args.stages_only:
+        import torch
+        from mips_ah_partition_amd import ahlib
+        ahlib.lib()
+        print(json.dumps({"stage_probes": stage_probes(torch, ahlib)}), flush=True)
+        return
     if args.probe_only:
         import torch
         from mips_ah_partition_amd import ahlib
@@ -319,6 +380,7 @@ def main():
     }
     if not args.no_probe:
         out["code_scan_hbm"] = code_scan_probe(torch, ahlib, ev)
+        out["stage_probes"] = stage_probes(torch, ahlib)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, ix, X, Q, gt, gpu_ids, args.cpu_budget)
     print(json.dumps(out), flush=True)

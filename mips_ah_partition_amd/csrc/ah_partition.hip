@@ -8,23 +8,42 @@
 //
 // Design: a dense fp32 contraction (M = queries, N = leaves, K = d) on the
 // gfx950 matrix cores with v_mfma_f32_16x16x4_f32 (fp32 in, fp32 accumulate;
-// bf16 inputs would not hold the 1e-4 relative bound).  Workgroup tile 64 x 64,
-// four waves of 32 x 32, K staged through LDS 32 at a time with rows padded to
-// 36 floats so the 16-byte operand reads are bank-conflict free.  Within each
-// group of four k-steps a lane feeds k = 4*(lane/16) + j, so one ds_read_b128
-// serves four MFMAs; A and B use the same k permutation, which leaves the
-// contraction unchanged.  Scores go to the workspace; a second kernel selects
-// each query's best nl with the exact workgroup top-K selection.
+// bf16 inputs would not hold the 1e-4 relative bound).  Workgroup tile
+// 128 x 128, four waves of 64 x 64 (16 MFMA tiles, so each operand fragment
+// read from LDS feeds four MFMAs of each of four tiles), K staged through LDS
+// 16 at a time with rows padded to 20 floats (conflict-free 16-byte reads)
+// and the next stage loaded from memory into registers while the current one
+// computes.  A lane feeds k = 4*(lane/16) + j to the j-th MFMA of a group, so
+// one ds_read_b128 serves four MFMAs; A and B use the same k permutation,
+// which leaves the contraction unchanged.  Scores go to the workspace; a
+// second kernel selects each query's best nl with the exact workgroup top-K
+// selection over the query's scores staged in LDS.
 #include "ah_device.hpp"
 #include "ah_kernels.hpp"
 
 namespace ah {
 
 constexpr int kGemmThreads = 256;
-constexpr int kGT = 64;       // tile rows / cols
-constexpr int kGK = 32;       // K per LDS stage
+constexpr int kGT = 128;      // tile rows / cols
+constexpr int kGK = 16;       // K per LDS stage
 constexpr int kGS = kGK + 4;  // padded row stride (floats)
 
+// Four consecutive k of row r of a [rows x d] matrix, zero outside it.  kVec:
+// d % 4 == 0 and a 16-byte aligned base, so one float4 load.
+template <bool kVec>
+__device__ __forceinline__ float4 fetch4(const float* __restrict__ m, int64_t rows, int32_t d, int64_t r, int k) {
+    if (kVec) {
+        if (r < rows && k < d) return *reinterpret_cast<const float4*>(m + r * d + k);
+        return make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float t[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = (r < rows && k + e < d) ? m[r * d + k + e] : 0.f;
+    return make_float4(t[0], t[1], t[2], t[3]);
+}
+
+// kVec: d % 4 == 0 and 16-byte aligned rows, so stages load as float4
+template <bool kVec>
 __global__ __launch_bounds__(kGemmThreads) void centroid_scores_kernel(
     const float* __restrict__ q, int64_t nq, int32_t d, const float* __restrict__ cent, int32_t L,
     float* __restrict__ S) {
@@ -34,37 +53,45 @@ __global__ __launch_bounds__(kGemmThreads) void centroid_scores_kernel(
     const int64_t ntl = (L + kGT - 1) / kGT;  // leaf tiles; consecutive blocks share a query tile
     const int64_t q0 = ((int64_t)blockIdx.x / ntl) * kGT;
     const int64_t l0 = ((int64_t)blockIdx.x % ntl) * kGT;
-    const int wm = (w >> 1) * 32, wn = (w & 1) * 32;  // wave's 32x32 sub-tile
-    v4f acc[2][2];
+    const int wm = (w >> 1) * 64, wn = (w & 1) * 64;  // wave's 64x64 sub-tile
+    v4f acc[4][4];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < 4; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    // staging: thread t holds rows t/4 and t/4 + 64 of each operand, k 4*(t%4)..+3
+    const int sr = tid >> 2, sk = 4 * (tid & 3);
+    float4 nq0, nq1, nc0, nc1;
+#define AH_FETCH(K0)                                                                         \
+    do {                                                                                      \
+        nq0 = fetch4<kVec>(q, nq, d, q0 + sr, (K0) + sk);                                     \
+        nq1 = fetch4<kVec>(q, nq, d, q0 + sr + 64, (K0) + sk);                                \
+        nc0 = fetch4<kVec>(cent, L, d, l0 + sr, (K0) + sk);                                   \
+        nc1 = fetch4<kVec>(cent, L, d, l0 + sr + 64, (K0) + sk);                              \
+    } while (0)
+    AH_FETCH(0);
     for (int k0 = 0; k0 < d; k0 += kGK) {
-        // stage 64 x 32 of Q and of C (zero beyond the edges)
-        for (int e = tid; e < kGT * kGK; e += kGemmThreads) {
-            const int r = e / kGK, kk = e % kGK;
-            const int64_t qr = q0 + r, lr = l0 + r;
-            const int kd = k0 + kk;
-            qa[r * kGS + kk] = (qr < nq && kd < d) ? q[qr * d + kd] : 0.0f;
-            cb[r * kGS + kk] = (lr < L && kd < d) ? cent[lr * d + kd] : 0.0f;
-        }
+        *reinterpret_cast<float4*>(&qa[sr * kGS + sk]) = nq0;
+        *reinterpret_cast<float4*>(&qa[(sr + 64) * kGS + sk]) = nq1;
+        *reinterpret_cast<float4*>(&cb[sr * kGS + sk]) = nc0;
+        *reinterpret_cast<float4*>(&cb[(sr + 64) * kGS + sk]) = nc1;
         __syncthreads();
+        if (k0 + kGK < d) AH_FETCH(k0 + kGK);  // in flight while this stage computes
+        const int kk = 4 * (lane >> 4);
 #pragma unroll
         for (int kb = 0; kb < kGK; kb += 16) {
-            const int kk = kb + 4 * (lane >> 4);
-            float4 av[2], bv[2];
+            float4 av[4], bv[4];
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
-                av[a] = *reinterpret_cast<const float4*>(&qa[(wm + 16 * a + (lane & 15)) * kGS + kk]);
+            for (int a = 0; a < 4; ++a)
+                av[a] = *reinterpret_cast<const float4*>(&qa[(wm + 16 * a + (lane & 15)) * kGS + kb + kk]);
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-                bv[b] = *reinterpret_cast<const float4*>(&cb[(wn + 16 * b + (lane & 15)) * kGS + kk]);
+            for (int b = 0; b < 4; ++b)
+                bv[b] = *reinterpret_cast<const float4*>(&cb[(wn + 16 * b + (lane & 15)) * kGS + kb + kk]);
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+            for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
+                for (int b = 0; b < 4; ++b) {
                     acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a].x, bv[b].x, acc[a][b], 0, 0, 0);
                     acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a].y, bv[b].y, acc[a][b], 0, 0, 0);
                     acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a].z, bv[b].z, acc[a][b], 0, 0, 0);
@@ -75,9 +102,9 @@ __global__ __launch_bounds__(kGemmThreads) void centroid_scores_kernel(
     }
     // D[row][col]: lane holds rows 4*(lane/16)+i of column lane%16
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int64_t qr = q0 + wm + 16 * a + 4 * (lane >> 4) + i;
@@ -85,6 +112,7 @@ __global__ __launch_bounds__(kGemmThreads) void centroid_scores_kernel(
                 if (qr < nq && lc < L) S[qr * L + lc] = acc[a][b][i];
             }
 }
+#undef AH_FETCH
 
 struct ScoreKeys {
     const float* s;
@@ -93,6 +121,8 @@ struct ScoreKeys {
 
 constexpr int kSelThreads = 256;
 
+constexpr int kLeafLds = 8192;  // scores staged in LDS as keys up to this many leaves
+
 __global__ __launch_bounds__(kSelThreads) void leaf_select_kernel(const float* __restrict__ S, int32_t L,
                                                                   int32_t nl, int32_t* __restrict__ leaves,
                                                                   float* __restrict__ scores) {
@@ -100,11 +130,319 @@ __global__ __launch_bounds__(kSelThreads) void leaf_select_kernel(const float* _
     __shared__ SelectShared sh;
     uint64_t* sel = reinterpret_cast<uint64_t*>(smem);
     const int64_t qi = blockIdx.x;
-    const int m = wg_select_topk<kSelThreads>(ScoreKeys{S + qi * L}, L, nl, sh, sel);
+    int m;
+    if (L <= kLeafLds) {  // the query's L scores read once, as keys, into LDS
+        const int Kp = next_pow2(nl);
+        uint64_t* keys = sel + Kp;
+        for (int i = threadIdx.x; i < L; i += kSelThreads) keys[i] = float_key(S[qi * L + i], i);
+        __syncthreads();
+        m = wg_select_topk<kSelThreads>(LdsKeys{keys}, L, nl, sh, sel);
+    } else {
+        m = wg_select_topk<kSelThreads>(ScoreKeys{S + qi * L}, L, nl, sh, sel);
+    }
     for (int r = threadIdx.x; r < nl; r += kSelThreads) {
         leaves[qi * nl + r] = r < m ? key_id(sel[r]) : -1;
         if (scores) scores[qi * nl + r] = r < m ? key_float_score(sel[r]) : -__builtin_huge_valf();
     }
+}
+
+// One wave per query (four per workgroup, no workgroup barrier) for L <=
+// kWaveLeaves and nl <= kLeafSort: the query's scores, as order-preserving
+// uint32, sit in registers (kPer per lane, all loads in flight at once); a
+// radix select narrows the candidates with 256 LDS buckets per pass: one pass
+// of equal-width buckets over the query's score range, then passes over the
+// chosen bucket's range of score orders, then, if one score value still holds
+// too many, over the leaf ids (lower id first), until every key at or above
+// the current bucket's lower edge fits in Pt = next_pow2(max(nl, 64)) keys;
+// those are sorted in registers and the first nl taken.  At the last id digit
+// the bucket is the nl-th key itself, so the candidates never exceed Pt.
+// Scores are assumed finite (NaN has no place in the order).
+constexpr int kWaveLeaves = 4096;
+constexpr int kLeafSort = 512;
+constexpr int kLeafQ = 4;
+
+// one select pass: the bucket (of 256, highest first) holding the need-th
+// largest counted candidate, and the count above it
+struct SelDigit {
+    int digit, before, cnt;
+};
+__device__ __forceinline__ SelDigit pick_digit(const uint32_t* hist, int need, int lane) {
+    uint32_t c[4];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        c[j] = hist[255 - 4 * lane - j];
+        sum += (int)c[j];
+    }
+    const int incl = wave_inclusive_sum(sum);
+    const uint64_t mk = __ballot(incl >= need);
+    const int l = __ffsll((unsigned long long)mk) - 1;
+    SelDigit r{0, 0, 0};
+    if (lane == l) {
+        int cum = incl - sum;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (cum < need && cum + (int)c[j] >= need) r = SelDigit{255 - 4 * lane - j, cum, (int)c[j]};
+            cum += (int)c[j];
+        }
+    }
+    r.digit = __shfl(r.digit, l, kWave);
+    r.before = __shfl(r.before, l, kWave);
+    r.cnt = __shfl(r.cnt, l, kWave);
+    return r;
+}
+
+// Sorts the 64*E keys of srt (descending) in registers, key k*64+lane held by
+// the lane in v[k], and writes the first nl as leaf ids (and scores).  Strides
+// below 64 swap across lanes, larger ones within a lane.
+template <int E>
+__device__ __forceinline__ void wave_sort_emit(const uint64_t* srt, int nl, int lane, int32_t* leaves, float* scores) {
+    uint64_t v[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) v[k] = srt[k * kWave + lane];
+#pragma unroll
+    for (int size = 2; size <= E * kWave; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride >= kWave) {
+                const int ks = stride / kWave;
+#pragma unroll
+                for (int k = 0; k < E; ++k) {
+                    if (k & ks) continue;
+                    const bool desc = ((k * kWave) & size) == 0;
+                    const uint64_t x = v[k], y = v[k | ks];
+                    const bool sw = (x < y) == desc;
+                    v[k] = sw ? y : x;
+                    v[k | ks] = sw ? x : y;
+                }
+            } else {
+                const bool lower = (lane & stride) == 0;
+#pragma unroll
+                for (int k = 0; k < E; ++k) {
+                    const bool desc = ((k * kWave + lane) & size) == 0;
+                    const uint32_t plo = (uint32_t)__shfl_xor((int)(uint32_t)v[k], stride, kWave);
+                    const uint32_t phi = (uint32_t)__shfl_xor((int)(uint32_t)(v[k] >> 32), stride, kWave);
+                    const uint64_t p = ((uint64_t)phi << 32) | plo;
+                    const bool take_max = lower == desc;
+                    v[k] = take_max ? (p > v[k] ? p : v[k]) : (p < v[k] ? p : v[k]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        const int r = k * kWave + lane;
+        if (r < nl) {
+            leaves[r] = key_id(v[k]);
+            if (scores) scores[r] = key_float_score(v[k]);
+        }
+    }
+}
+
+template <int kPer, int kWv>
+__global__ __launch_bounds__(kLeafQ * kWave, kPer <= 16 ? 5 : 3) void leaf_select_wave_kernel(const float* __restrict__ S, int64_t nq,
+                                                                          int32_t L, int32_t nl,
+                                                                          int32_t* __restrict__ leaves,
+                                                                          float* __restrict__ scores) {
+    constexpr int kQs = kLeafQ / kWv;  // queries per workgroup
+    static_assert(kWv == 1 || kQs == 1, "a query spread over waves fills its workgroup");
+    __shared__ uint32_t hist_all[kQs][256];
+    __shared__ uint64_t srt_all[kQs][kLeafSort];
+    __shared__ uint32_t red_all[kQs][kWv][2];
+    __shared__ int cnt_all[kQs];
+    const int w = threadIdx.x / kWave, lane = lane_id();
+    const int qs = w / kWv, wq = w % kWv;  // query slot, wave within the query
+    const int64_t qi = (int64_t)blockIdx.x * kQs + qs;
+    if (kWv == 1 && qi >= nq) return;  // a multi-wave query is never partial: kQs == 1 there
+    uint32_t* hist = hist_all[qs];
+    uint64_t* srt = srt_all[qs];
+    uint32_t(*red)[2] = red_all[qs];
+    const float* s = S + qi * L;
+    // element i = (j * kWv + wq) * 64 + lane
+    const int first = wq * kWave + lane;
+    const int nv = first < L ? (L - first + kWv * kWave - 1) / (kWv * kWave) : 0;  // o[0 .. nv) are real
+    uint32_t o[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) o[j] = j < nv ? float_order(s[j * kWv * kWave + first]) : 0u;
+    auto sync = [] {
+        if constexpr (kWv == 1) {
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+        } else {
+            __syncthreads();
+        }
+    };
+    // min and max over the query's keys (all its waves)
+    auto range_of = [&](uint32_t mn, uint32_t mx, uint32_t& rmin, uint32_t& rmax) {
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1) {
+            const uint32_t x = __shfl_xor(mn, off, kWave), y = __shfl_xor(mx, off, kWave);
+            mn = x < mn ? x : mn;
+            mx = y > mx ? y : mx;
+        }
+        if constexpr (kWv > 1) {
+            if (lane == 0) {
+                red[wq][0] = mn;
+                red[wq][1] = mx;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int v = 0; v < kWv; ++v) {
+                mn = red[v][0] < mn ? red[v][0] : mn;
+                mx = red[v][1] > mx ? red[v][1] : mx;
+            }
+            __syncthreads();
+        }
+        rmin = mn;
+        rmax = mx;
+    };
+    auto clear_hist = [&] {
+#pragma unroll
+        for (int j = wq * kWave + lane; j < 256; j += kWv * kWave) hist[j] = 0;
+        sync();
+    };
+    uint32_t omin, omax;
+    {
+        uint32_t mn = 0xFFFFFFFFu, mx = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            if (j < nv) {
+                mn = o[j] < mn ? o[j] : mn;
+                mx = o[j] > mx ? o[j] : mx;
+            }
+        }
+        range_of(mn, mx, omin, omax);
+    }
+    auto key = [&](int j) -> uint64_t {
+        return ((uint64_t)o[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(j * kWv * kWave + first));
+    };
+    int need = nl;   // still to pick at or below the current bucket
+    int above = 0;   // keys known to be selected (above the bucket)
+    int inb = L;     // keys in the current bucket
+    const int Pt = next_pow2(nl > kWave ? nl : kWave);  // candidates to reach: one sort of Pt keys
+    // First pass, on the score values: 256 equal-width buckets over [fmin, fmax]
+    // (the bucket is non-decreasing in the score, so a bucket's members are
+    // exactly the scores between its smallest and largest order).  The order
+    // space is far from linear in the score, so this pass splits a typical
+    // score distribution much better than the first order digit would.
+    {
+        const float fmin = order_float(omin), range = order_float(omax) - fmin;
+        if (above + inb > Pt && range > 0.f && range < __builtin_huge_valf()) {
+            const float scale = 256.f / range;
+            auto lbin = [&](int j) -> int {
+                const int b = (int)((order_float(o[j]) - fmin) * scale);
+                return b < 255 ? b : 255;
+            };
+            clear_hist();
+#pragma unroll
+            for (int j = 0; j < kPer; ++j)
+                if (j < nv) atomicAdd(&hist[lbin(j)], 1u);
+            sync();
+            const SelDigit r = pick_digit(hist, need, lane);  // every wave of the query, same result
+            sync();
+            need -= r.before;
+            above += r.before;
+            inb = r.cnt;
+            uint32_t mn = 0xFFFFFFFFu, mx = 0;
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                if (j < nv && lbin(j) == r.digit) {
+                    mn = o[j] < mn ? o[j] : mn;
+                    mx = o[j] > mx ? o[j] : mx;
+                }
+            }
+            range_of(mn, mx, omin, omax);
+        }
+    }
+    // score-order passes: 256 buckets of width 2^sh over [lo, hi)
+    uint32_t lo = omin;
+    uint64_t hi = (uint64_t)omax + 1;  // exclusive
+    int sh = 0;
+    while (sh < 24 && ((omax - omin) >> sh) > 255u) ++sh;
+    uint64_t edge = (uint64_t)lo << 32;  // the current bucket's lower edge as a key
+    bool tied = false;
+    while (above + inb > Pt) {
+        if (sh < 0) {  // one score value holds too many: resolve by id below
+            tied = true;
+            break;
+        }
+        clear_hist();
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (j < nv && o[j] >= lo && (uint64_t)o[j] < hi) atomicAdd(&hist[(o[j] - lo) >> sh], 1u);
+        sync();
+        const SelDigit r = pick_digit(hist, need, lane);
+        sync();
+        need -= r.before;
+        above += r.before;
+        inb = r.cnt;
+        lo += (uint32_t)r.digit << sh;
+        hi = hi < (uint64_t)lo + (1ull << sh) ? hi : (uint64_t)lo + (1ull << sh);
+        edge = (uint64_t)lo << 32;
+        sh = sh >= 8 ? sh - 8 : (sh > 0 ? 0 : -1);
+    }
+    if (tied) {
+        // every key left in the bucket has score order lo: 8-bit passes over ~id
+        uint64_t prefix = (uint64_t)lo << 32, mask = 0xFFFFFFFF00000000ull;
+        for (int shift = 24; shift >= 0 && above + inb > Pt; shift -= 8) {
+            clear_hist();
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const uint64_t k = key(j);
+                if (j < nv && (k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1u);
+            }
+            sync();
+            const SelDigit r = pick_digit(hist, need, lane);
+            sync();
+            need -= r.before;
+            above += r.before;
+            inb = r.cnt;
+            prefix |= (uint64_t)r.digit << shift;
+            mask |= (uint64_t)0xFF << shift;
+        }
+        edge = prefix;
+    }
+    // collect the keys at or above the bucket's lower edge, sort, take nl
+    if constexpr (kWv > 1) {
+        if (threadIdx.x == 0) cnt_all[qs] = 0;
+        __syncthreads();
+    }
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const uint64_t k = key(j);
+        const bool keep = j < nv && k >= edge;
+        const uint64_t mk = __ballot(keep);
+        if (mk == 0) continue;
+        int base = n;
+        if constexpr (kWv > 1) {
+            if (lane == 0) base = atomicAdd(&cnt_all[qs], __popcll(mk));
+            base = __shfl(base, 0, kWave);
+        }
+        const int pos = base + __popcll(mk & lanemask_lt());
+        if (keep && pos < Pt) srt[pos] = k;  // never more than Pt for finite scores
+        n += __popcll(mk);
+    }
+    sync();
+    if (wq != 0) return;
+    if constexpr (kWv > 1) n = cnt_all[qs];
+    for (int j = n + lane; j < Pt; j += kWave) srt[j] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    int32_t* lq = leaves + qi * nl;
+    float* sq = scores ? scores + qi * nl : nullptr;
+    if (Pt == kWave) wave_sort_emit<1>(srt, nl, lane, lq, sq);
+    else if (Pt == 2 * kWave) wave_sort_emit<2>(srt, nl, lane, lq, sq);
+    else if (Pt == 4 * kWave) wave_sort_emit<4>(srt, nl, lane, lq, sq);
+    else wave_sort_emit<8>(srt, nl, lane, lq, sq);
+}
+
+template <int kPer, int kWv>
+static void launch_leaf_wave(const float* S, int64_t nq, int32_t L, int32_t nl, int32_t* leaves, float* scores,
+                             hipStream_t stream) {
+    constexpr int kQs = kLeafQ / kWv;
+    hipLaunchKernelGGL((leaf_select_wave_kernel<kPer, kWv>), dim3((unsigned)((nq + kQs - 1) / kQs)),
+                       dim3(kLeafQ * kWave), 0, stream, S, nq, L, nl, leaves, scores);
 }
 
 size_t partition_workspace_bytes(int64_t nq, int32_t L) { return (size_t)nq * (size_t)L * 4 + 256; }
@@ -114,15 +452,27 @@ hipError_t launch_partition(const float* q, int64_t nq, int32_t d, const float* 
     if (nq == 0) return hipSuccess;
     float* S = reinterpret_cast<float*>(ws);
     dim3 grid((unsigned)(((L + kGT - 1) / kGT) * ((nq + kGT - 1) / kGT)));
-    hipLaunchKernelGGL(centroid_scores_kernel, grid, dim3(kGemmThreads), 0, stream, q, nq, d, cent, L, S);
+    const bool vec = (d % 4) == 0 && (reinterpret_cast<uintptr_t>(q) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(cent) & 15) == 0;
+    if (vec) hipLaunchKernelGGL(centroid_scores_kernel<true>, grid, dim3(kGemmThreads), 0, stream, q, nq, d, cent, L, S);
+    else hipLaunchKernelGGL(centroid_scores_kernel<false>, grid, dim3(kGemmThreads), 0, stream, q, nq, d, cent, L, S);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (L <= kWaveLeaves && nl <= kLeafSort) {
+        if (L <= 4 * kWave) launch_leaf_wave<4, 1>(S, nq, L, nl, leaves, scores, stream);
+        else if (L <= 8 * kWave) launch_leaf_wave<8, 1>(S, nq, L, nl, leaves, scores, stream);
+        else if (L <= 16 * kWave) launch_leaf_wave<16, 1>(S, nq, L, nl, leaves, scores, stream);
+        else if (L <= 32 * kWave) launch_leaf_wave<32, 1>(S, nq, L, nl, leaves, scores, stream);
+        else launch_leaf_wave<16, 4>(S, nq, L, nl, leaves, scores, stream);
+        return hipGetLastError();
+    }
     int Kp = 1;
     while (Kp < nl) Kp <<= 1;
-    if ((size_t)Kp * 8 > 48 * 1024)
+    const size_t lds = (size_t)Kp * 8 + (L <= kLeafLds ? (size_t)L * 8 : 0);
+    if (lds > 48 * 1024)
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(leaf_select_kernel),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, Kp * 8);
-    hipLaunchKernelGGL(leaf_select_kernel, dim3((unsigned)nq), dim3(kSelThreads), (size_t)Kp * 8, stream,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(leaf_select_kernel, dim3((unsigned)nq), dim3(kSelThreads), lds, stream,
                        S, L, nl, leaves, scores);
     return hipGetLastError();
 }

@@ -267,7 +267,11 @@ def test_reorder_parity(gpu, dtype, d, R, k):
 
 
 # ----------------------------------------------------------------------------- partition
-@pytest.mark.parametrize("nq,d,L,nl", [(100, 100, 1000, 50), (67, 128, 300, 7), (5, 1536, 130, 100), (3, 9, 5, 5)])
+# One wave per query selects the leaves up to 4096 leaves and 512 searched; the
+# workgroup selection beyond (5000 leaves; 600 searched).  d = 9 and 130 leaves
+# exercise the unaligned and ragged contraction tiles.
+@pytest.mark.parametrize("nq,d,L,nl", [(100, 100, 1000, 50), (67, 128, 300, 7), (5, 1536, 130, 100), (3, 9, 5, 5),
+                                       (20, 64, 5000, 30), (10, 32, 700, 600), (300, 384, 4000, 200)])
 def test_partition_parity(gpu, nq, d, L, nl):
     torch, ah = gpu
     rng = np.random.default_rng(nq + L)
@@ -281,3 +285,31 @@ def test_partition_parity(gpu, nq, d, L, nl):
                   lambda q, ids: Cd[ids] @ Qd[q], lambda q, ids: np.abs(Cd[ids]) @ np.abs(Qd[q]))
     agree = (_np(lv) == o_lv).mean()
     assert agree > 0.99
+
+
+def test_partition_tied_centroids(gpu):
+    """Every centroid repeated four times: equal scores, ties go to the lower leaf id."""
+    torch, ah = gpu
+    rng = np.random.default_rng(17)
+    Q = rng.integers(-3, 4, size=(40, 16)).astype(np.float32)
+    Cn = np.repeat(rng.integers(-3, 4, size=(250, 16)).astype(np.float32), 4, axis=0)
+    lv, sc = ah.ah_partition_score(_t(torch, Q), _t(torch, Cn), 37)
+    torch.cuda.synchronize()
+    o_lv, o_sc = oracle.partition(Q, Cn, 37)
+    assert np.array_equal(_np(lv), o_lv)  # small integers: exact scores, unique order
+    assert np.array_equal(_np(sc), o_sc.astype(np.float32))
+
+
+@pytest.mark.parametrize("L,nl,kinds", [(3000, 300, 1), (1000, 50, 2), (4000, 200, 3), (200, 64, 1)])
+def test_partition_few_score_values(gpu, L, nl, kinds):
+    """All leaves share one to three distinct scores: the selection is decided by leaf id alone."""
+    torch, ah = gpu
+    rng = np.random.default_rng(L + kinds)
+    Q = rng.integers(-3, 4, size=(9, 16)).astype(np.float32)
+    rows = rng.integers(-3, 4, size=(kinds, 16)).astype(np.float32)
+    Cn = rows[rng.integers(0, kinds, size=L)]
+    lv, sc = ah.ah_partition_score(_t(torch, Q), _t(torch, Cn), nl)
+    torch.cuda.synchronize()
+    o_lv, o_sc = oracle.partition(Q, Cn, nl)
+    assert np.array_equal(_np(lv), o_lv)
+    assert np.array_equal(_np(sc), o_sc.astype(np.float32))
