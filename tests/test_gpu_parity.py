@@ -40,7 +40,8 @@ def _np(t):
 
 
 # ----------------------------------------------------------------------------- LUT
-@pytest.mark.parametrize("dpb,B,nq", [(1, 5, 3), (2, 64, 37), (4, 32, 100), (2, 200, 17), (2, 768, 5), (3, 7, 66)])
+@pytest.mark.parametrize("dpb,B,nq", [(1, 5, 3), (2, 64, 37), (4, 32, 100), (2, 200, 17), (2, 768, 5), (3, 7, 66),
+                                      (1, 1, 2), (16, 300, 4), (2, 513, 9), (2, 4096, 3)])
 def test_build_lut_parity(gpu, dpb, B, nq):
     torch, ah = gpu
     rng = np.random.default_rng(1000 + B * 10 + dpb)
@@ -57,6 +58,33 @@ def test_build_lut_parity(gpu, dpb, B, nq):
     assert np.array_equal(_np(t8), o8)
     assert np.array_equal(_np(s), os_)
     assert np.array_equal(_np(beta), ob)
+
+
+def test_build_lut_unaligned_outputs(gpu):
+    """Output tables and inputs at odd offsets (element-wise stores and loads) equal the aligned results."""
+    torch, ah = gpu
+    rng = np.random.default_rng(33)
+    nq, B, dpb = 6, 70, 2
+    Q = _t(torch, rng.standard_normal((nq, B * dpb)).astype(np.float32))
+    cb = _t(torch, rng.standard_normal((B, 16, dpb)).astype(np.float32))
+    t8, s, beta, l32 = ah.ah_build_lut(Q, cb, want_f32=True)
+    raw8 = torch.zeros(nq * B * 16 + 1, dtype=torch.int8, device=Q.device)
+    raw32 = torch.zeros(nq * B * 16 + 1, dtype=torch.float32, device=Q.device)
+    u8 = raw8[1:].view(nq, B, 16)
+    u32 = raw32[1:].view(nq, B, 16)
+    ah.ah_build_lut(Q, cb, lut_i8_out=u8, lut_f32_out=u32, want_f32=True)
+    torch.cuda.synchronize()
+    assert torch.equal(u8, t8) and torch.equal(u32, l32)
+    # inputs at odd offsets too (element-wise loads)
+    rawq = torch.zeros(Q.numel() + 1, dtype=torch.float32, device=Q.device)
+    rawc = torch.zeros(cb.numel() + 1, dtype=torch.float32, device=Q.device)
+    uq = rawq[1:].view(Q.shape)
+    uc = rawc[1:].view(cb.shape)
+    uq.copy_(Q)
+    uc.copy_(cb)
+    v8, vs, vb, v32 = ah.ah_build_lut(uq, uc, want_f32=True)
+    torch.cuda.synchronize()
+    assert torch.equal(v8, t8) and torch.equal(v32, l32) and torch.equal(vs, s) and torch.equal(vb, beta)
 
 
 def test_build_lut_constant_table(gpu):
