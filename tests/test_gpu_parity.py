@@ -184,6 +184,12 @@ def test_scan_partitioned_parity(gpu):
     (33, 1234, 1, 10, 15),      # odd B, 32 B stride
     (1, 999, 4, 5, 0),          # one block
     (4096, 600, 1, 20, 0),      # 64 KB single-query table
+    (192, 20000, 1, 300, 0),    # 96 B rows: coalesced tiles of 32 rows in 3 load rounds
+    (192, 20001, 4, 300, 0),    # the same, two query pairs
+    (768, 6000, 1, 400, 0),     # 384 B rows: tiles of 8 rows, nibble table
+    (768, 6000, 3, 400, 0),     # the same, packed nibble table
+    (96, 7000, 2, 64, 0),       # 48 B rows: tiles of 64 rows in 3 rounds
+    (192, 3001, 3, 37, 32),     # 96 B of codes in 128 B rows: whole-row registers
 ])
 def test_scan_stream_parity(gpu, B, n, nq, R, stride_pad):
     torch, ah = gpu
@@ -214,10 +220,13 @@ def test_scan_extreme_tables(gpu, nq, B):
     _scan_check(torch, ah, lut, codes, R)
 
 
-@pytest.mark.parametrize("nq,B,L,nl", [(1, 48, 25, 5), (3, 48, 25, 5), (4, 48, 3, 2), (3, 400, 4, 3)])
+@pytest.mark.parametrize("nq,B,L,nl", [(1, 48, 25, 5), (3, 48, 25, 5), (4, 48, 3, 2), (3, 400, 4, 3),
+                                       (1, 192, 25, 5), (2, 192, 7, 3), (4, 64, 3, 2), (3, 768, 5, 2)])
 def test_scan_stream_partitioned(gpu, nq, B, L, nl):
     """Few queries over leaves; with few leaves several queries share one, so a
-    leaf has more than one query group (two per item with pair tables)."""
+    leaf has more than one query group (two per item with pair tables).  Rows of
+    24 and 200 code bytes are not 16-byte multiples (MFMA kernel); 32, 96 and
+    384 take the streaming kernel's coalesced tiles, starting at any row."""
     torch, ah = gpu
     rng = np.random.default_rng(300 + nq + B + L)
     n, R = 40000, 90
