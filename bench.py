@@ -174,30 +174,35 @@ PROBE_SHAPES = (("wiki20m", 20_000_000, 192, 300), ("openai2m", 2_000_000, 768, 
 
 
 def code_scan_probe(torch, ahlib, ev, runs=5):
+    """Single-pass scans of 1 and 4 queries over all codes, in the tiled layout
+    (ah_tile_codes; keys name_qN) and row-major (keys name_qN_rowmajor)."""
     out = {}
     for name, n, B, R in PROBE_SHAPES:
         g = torch.Generator(device="cuda")
         g.manual_seed(4242 + B)
         codes = torch.randint(0, 256, (n, (B + 1) // 2), generator=g, device="cuda", dtype=torch.uint8)
+        tiled = ahlib.ah_tile_codes(codes, B)
         for nq in (1, 4):
             lut = torch.randint(-127, 128, (nq, B, 16), generator=g, device="cuda", dtype=torch.int8)
             ws = torch.empty(ahlib.ah_scan_workspace_bytes(nq, B, n, 0, 0, R), dtype=torch.uint8, device="cuda")
             e0, e1 = ev.create(), ev.create()
-            ts = []
-            for it in range(runs + 1):
-                ahlib.ah_scan_topk(lut, codes, R, workspace=ws, main_events=(e0, e1))
-                torch.cuda.synchronize()
-                if it:
-                    ts.append(ev.elapsed_ms(e0, e1))
-            ms = float(np.median(ts))
-            gbps = codes.numel() / (ms / 1e3) / 1e9
-            o_cnt = (nq * 4 + 255) & ~255  # candidate counters follow the thresholds in the workspace
-            appended = ws[o_cnt:o_cnt + nq * 4].view(torch.int32).cpu().numpy()
-            out[f"{name}_q{nq}"] = {"code_bytes": int(codes.numel()), "blocks": B, "queries": nq,
-                                    "scan_ms": ms, "GBps": gbps, "frac_of_8TBps": gbps / PEAK_HBM_GBPS,
-                                    "candidates_per_query": float(appended.mean())}
+            for layout, src in (("", tiled), ("_rowmajor", codes)):
+                ts = []
+                for it in range(runs + 1):
+                    ahlib.ah_scan_topk(lut, src, R, workspace=ws, main_events=(e0, e1))
+                    torch.cuda.synchronize()
+                    if it:
+                        ts.append(ev.elapsed_ms(e0, e1))
+                ms = float(np.median(ts))
+                gbps = codes.numel() / (ms / 1e3) / 1e9
+                o_cnt = (nq * 4 + 255) & ~255  # candidate counters follow the thresholds in the workspace
+                appended = ws[o_cnt:o_cnt + nq * 4].view(torch.int32).cpu().numpy()
+                out[f"{name}_q{nq}{layout}"] = {"code_bytes": int(codes.numel()), "blocks": B, "queries": nq,
+                                                "layout": "tiled" if not layout else "row-major",
+                                                "scan_ms": ms, "GBps": gbps, "frac_of_8TBps": gbps / PEAK_HBM_GBPS,
+                                                "candidates_per_query": float(appended.mean())}
             del ws
-        del codes
+        del codes, tiled
     torch.cuda.empty_cache()
     return out
 

@@ -26,6 +26,9 @@
  *    set is unique.
  *  - Codes: row-major, `code_stride` bytes per row (>= ceil(B/2)); block b of a
  *    row is the nibble (row[b/2] >> 4*(b%2)) & 15 (low nibble = even block).
+ *    Or (code_stride == AH_CODES_TILED) the tiled layout of ah_tile_codes: the
+ *    same bytes, rearranged so that one 16-byte segment of 64 consecutive rows
+ *    is one contiguous 1 KB run.
  */
 #ifndef AH_H
 #define AH_H
@@ -53,6 +56,9 @@ enum { AH_F32 = 0, AH_BF16 = 1 };
 #define AH_MAX_DPB 16        /* dimensions_per_block */
 #define AH_MAX_R 4096        /* pre-reorder candidates (also max nl and k) */
 #define AH_MAX_DIM 16384     /* d */
+
+/* code_stride value selecting the tiled code layout (see ah_tile_codes). */
+#define AH_CODES_TILED 0
 
 const char* ah_status_string(int status);
 int ah_version(void);
@@ -106,7 +112,9 @@ int ah_build_lut(const float* q, int64_t nq, int32_t d, const float* codebooks, 
  * dominates the cost of a query).
  *
  *   lut_i8       int8 [nq][B][16]
- *   codes        uint8 [n][code_stride]  (leaf-sorted when partitioned)
+ *   codes        uint8 [n][code_stride]  (leaf-sorted when partitioned), or the
+ *                tiled layout of ah_tile_codes when code_stride == AH_CODES_TILED
+ *                (then 16-byte aligned, else AH_ERR_UNSUPPORTED)
  *   ids          int32 [n] original row id of each code row, or NULL (= row index)
  *   leaf_offsets int64 [L+1] rows of leaf l are [leaf_offsets[l], leaf_offsets[l+1]),
  *                or NULL when leaves == NULL
@@ -117,8 +125,8 @@ int ah_build_lut(const float* q, int64_t nq, int32_t d, const float* codebooks, 
  *   Slots beyond the number of scanned rows hold (-1, INT32_MIN).
  *   workspace    >= ah_scan_workspace_bytes(nq, B, n, L, nl, R) bytes
  * Sums are exact int32; the kept set is the unique top-R by (sum desc, id asc).
- * Errors: AH_ERR_NULL, AH_ERR_SHAPE (nq < 0, n < 0, B < 1, code_stride <
- * ceil(B/2), R < 1, leaves given with L < 1 or nl < 1 or nl > L or no
+ * Errors: AH_ERR_NULL, AH_ERR_SHAPE (nq < 0, n < 0, B < 1, code_stride neither
+ * AH_CODES_TILED nor >= ceil(B/2), R < 1, leaves given with L < 1 or nl < 1 or nl > L or no
  * leaf_offsets), AH_ERR_UNSUPPORTED (B > AH_MAX_BLOCKS, R > AH_MAX_R,
  * n >= 2^31), AH_ERR_WORKSPACE.
  */
@@ -127,6 +135,28 @@ int ah_scan_topk(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* cod
                  int32_t code_stride, int64_t n, const int32_t* ids, const int64_t* leaf_offsets,
                  int32_t L, const int32_t* leaves, int32_t nl, int32_t R, int32_t* cand_ids_out,
                  int32_t* cand_scores_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Code layout for the scan (same page and section as the scan: the codes are
+ * read once per query batch, so their layout decides how well the reads
+ * coalesce).  Not a step of the method: a rearrangement of the same bytes.
+ *
+ * ah_tile_codes writes the tiled layout of row-major codes:
+ *   codes      uint8 [n][code_stride] row-major (code_stride >= ceil(B/2))
+ *   tiled_out  >= ah_tiled_codes_bytes(n, B) bytes, 16-byte aligned
+ * With S = ceil(ceil(B/2) / 16) segments of 16 bytes per row (the last padded
+ * with zero bytes), byte k of row r goes to
+ *   (r / 64) * (64 * S * 16) + (k / 16) * 1024 + (r % 64) * 16 + k % 16;
+ * slots of the last tile past row n - 1 are zero.  Pass the result to
+ * ah_scan_topk with code_stride = AH_CODES_TILED; ids, leaf_offsets and leaves
+ * keep referring to row numbers.
+ * Errors: AH_ERR_SHAPE (n < 0, B < 1, code_stride < ceil(B/2), tiled_bytes too
+ * small), AH_ERR_UNSUPPORTED (B > AH_MAX_BLOCKS, n >= 2^31, tiled_out not 16-byte
+ * aligned), AH_ERR_NULL.  ah_tiled_codes_bytes returns 0 for n < 0 or B < 1.
+ */
+size_t ah_tiled_codes_bytes(int64_t n, int32_t B);
+int ah_tile_codes(const uint8_t* codes, int32_t code_stride, int64_t n, int32_t B, uint8_t* tiled_out,
+                  size_t tiled_bytes, void* stream);
 
 /* Same as ah_scan_topk.  When main_start_event / main_stop_event are non-NULL
  * hipEvent_t handles (created by the caller), they are recorded on `stream`

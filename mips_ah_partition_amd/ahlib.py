@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libah.so")
 
 AH_OK, AH_ERR_NULL, AH_ERR_SHAPE, AH_ERR_UNSUPPORTED, AH_ERR_WORKSPACE, AH_ERR_HIP = 0, -1, -2, -3, -4, -5
 AH_F32, AH_BF16 = 0, 1
+AH_CODES_TILED = 0
 
 # every symbol include/ah.h declares
 EXPORTS = (
@@ -26,6 +27,7 @@ EXPORTS = (
     "ah_partition_workspace_bytes", "ah_partition_score",
     "ah_build_lut",
     "ah_scan_workspace_bytes", "ah_scan_topk", "ah_scan_topk_timed",
+    "ah_tiled_codes_bytes", "ah_tile_codes",
     "ah_reorder_exact",
 )
 
@@ -61,6 +63,10 @@ def lib() -> C.CDLL:
         L.ah_scan_topk_timed.restype = C.c_int
         L.ah_scan_topk_timed.argtypes = [vp, i64, i32, vp, i32, i64, vp, vp, i32, vp, i32, i32, vp, vp, vp, sz, vp,
                                          vp, vp]
+        L.ah_tiled_codes_bytes.restype = sz
+        L.ah_tiled_codes_bytes.argtypes = [i64, i32]
+        L.ah_tile_codes.restype = C.c_int
+        L.ah_tile_codes.argtypes = [vp, i32, i64, i32, vp, sz, vp]
         L.ah_reorder_exact.restype = C.c_int
         L.ah_reorder_exact.argtypes = [vp, i64, i32, vp, i32, i64, vp, i32, i32, vp, vp, vp]
         _lib = L
@@ -160,17 +166,47 @@ def ah_scan_workspace_bytes(nq: int, B: int, n: int, L: int, nl: int, R: int) ->
     return int(lib().ah_scan_workspace_bytes(nq, B, n, L, nl, R))
 
 
+class TiledCodes:
+    """Codes in the tiled layout of ah_tile_codes: ``data`` (uint8, device) holds
+    ceil(n / 64) tiles; ``n`` rows of ``blocks`` 4-bit codes."""
+
+    def __init__(self, data, n, blocks):
+        self.data, self.n, self.blocks = data, int(n), int(blocks)
+
+
+def ah_tiled_codes_bytes(n: int, B: int) -> int:
+    return int(lib().ah_tiled_codes_bytes(n, B))
+
+
+def ah_tile_codes(codes, B=None, stream=None) -> TiledCodes:
+    """Row-major codes uint8 [n, stride] -> TiledCodes (B defaults to 2 * stride)."""
+    codes = _dev(codes, torch.uint8, "codes", 2)
+    n, stride = codes.shape
+    B = 2 * stride if B is None else int(B)
+    need = ah_tiled_codes_bytes(n, B)
+    out = torch.empty(max(need, 16), dtype=torch.uint8, device=codes.device)
+    _check(lib().ah_tile_codes(_ptr(codes), stride, n, B, _ptr(out), out.numel(), _stream(stream)), "ah_tile_codes")
+    return TiledCodes(out, n, B)
+
+
 def ah_scan_topk(lut_i8, codes, R, ids=None, leaf_offsets=None, leaves=None, cand_ids_out=None,
                  cand_scores_out=None, workspace=None, stream=None, main_events=None):
     """Top-R rows per query by exact int32 sum of table entries.
-    codes: uint8 [n, stride]; leaves: int32 [nq, nl] or None (scan all rows)."""
+    codes: uint8 [n, stride] row-major, or TiledCodes; leaves: int32 [nq, nl] or
+    None (scan all rows)."""
     lut_i8 = _dev(lut_i8, torch.int8, "lut_i8", 3)
-    codes = _dev(codes, torch.uint8, "codes", 2)
     _dev(ids, torch.int32, "ids")
     _dev(leaf_offsets, torch.int64, "leaf_offsets")
     _dev(leaves, torch.int32, "leaves")
     nq, B, _ = lut_i8.shape
-    n, stride = codes.shape
+    if isinstance(codes, TiledCodes):
+        if codes.blocks != B:
+            raise ValueError("tiled codes were made for another number of blocks")
+        n, stride = codes.n, AH_CODES_TILED
+        codes = _dev(codes.data, torch.uint8, "codes", 1)
+    else:
+        codes = _dev(codes, torch.uint8, "codes", 2)
+        n, stride = codes.shape
     L = 0 if leaf_offsets is None else leaf_offsets.numel() - 1
     nl = 0 if leaves is None else leaves.shape[1]
     dev = lut_i8.device

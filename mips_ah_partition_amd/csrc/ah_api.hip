@@ -66,16 +66,19 @@ int ah_scan_topk_timed(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_
                        int32_t L, const int32_t* leaves, int32_t nl, int32_t R, int32_t* cand_ids_out,
                        int32_t* cand_scores_out, void* workspace, size_t workspace_bytes, void* stream,
                        void* main_start_event, void* main_stop_event) {
-    if (nq < 0 || n < 0 || B < 1 || R < 1 || code_stride < (B + 1) / 2) return AH_ERR_SHAPE;
+    const bool tiled = code_stride == AH_CODES_TILED;
+    if (nq < 0 || n < 0 || B < 1 || R < 1 || (!tiled && code_stride < (B + 1) / 2)) return AH_ERR_SHAPE;
     if (leaves && (L < 1 || nl < 1 || nl > L || !leaf_offsets)) return AH_ERR_SHAPE;
     if (B > AH_MAX_BLOCKS || R > AH_MAX_R || n >= ((int64_t)1 << 31)) return AH_ERR_UNSUPPORTED;
     if (nq == 0) return AH_OK;
     if (!lut_i8 || !cand_ids_out || !cand_scores_out || (n > 0 && !codes)) return AH_ERR_NULL;
-    if (!a16(lut_i8)) return AH_ERR_UNSUPPORTED;
+    if (!a16(lut_i8) || (tiled && !a16(codes))) return AH_ERR_UNSUPPORTED;
     const int32_t Lw = leaves ? L : 0, nlw = leaves ? nl : 0;
     if (!workspace || workspace_bytes < ah::scan_workspace_bytes(nq, B, n, Lw, nlw, R)) return AH_ERR_WORKSPACE;
-    ah::ScanProblem sp{lut_i8, nq, B, codes, code_stride, n, ids, leaves ? leaf_offsets : nullptr, Lw,
-                       leaves, nlw, R, cand_ids_out, cand_scores_out};
+    const int32_t seg16 = ((B + 1) / 2 + 15) / 16;  // 16-byte segments per row
+    ah::ScanProblem sp{lut_i8, nq, B, codes, tiled ? 16 * seg16 : code_stride, n, ids,
+                       leaves ? leaf_offsets : nullptr, Lw, leaves, nlw, R, cand_ids_out, cand_scores_out,
+                       tiled ? (int64_t)1024 * seg16 : 0};
     return hip_status(ah::launch_scan(sp, workspace, workspace_bytes, static_cast<hipStream_t>(stream),
                                       static_cast<hipEvent_t>(main_start_event),
                                       static_cast<hipEvent_t>(main_stop_event)));
@@ -87,6 +90,22 @@ int ah_scan_topk(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* cod
                  int32_t* cand_scores_out, void* workspace, size_t workspace_bytes, void* stream) {
     return ah_scan_topk_timed(lut_i8, nq, B, codes, code_stride, n, ids, leaf_offsets, L, leaves, nl, R,
                               cand_ids_out, cand_scores_out, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+size_t ah_tiled_codes_bytes(int64_t n, int32_t B) {
+    if (n < 0 || B < 1) return 0;
+    return ah::tiled_codes_bytes(n, B);
+}
+
+int ah_tile_codes(const uint8_t* codes, int32_t code_stride, int64_t n, int32_t B, uint8_t* tiled_out,
+                  size_t tiled_bytes, void* stream) {
+    if (n < 0 || B < 1 || code_stride < (B + 1) / 2) return AH_ERR_SHAPE;
+    if (B > AH_MAX_BLOCKS || n >= ((int64_t)1 << 31)) return AH_ERR_UNSUPPORTED;
+    if (tiled_bytes < ah::tiled_codes_bytes(n, B)) return AH_ERR_SHAPE;
+    if (n == 0) return AH_OK;
+    if (!codes || !tiled_out) return AH_ERR_NULL;
+    if (!a16(tiled_out)) return AH_ERR_UNSUPPORTED;
+    return hip_status(ah::launch_tile_codes(codes, code_stride, n, B, tiled_out, static_cast<hipStream_t>(stream)));
 }
 
 int ah_reorder_exact(const float* q, int64_t nq, int32_t d, const void* base, int32_t base_dtype,

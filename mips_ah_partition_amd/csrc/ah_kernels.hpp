@@ -33,10 +33,15 @@ struct ScanProblem {
     int32_t R;
     int32_t* out_ids;
     int32_t* out_scores;
+    int64_t tile_bytes;  // tiled code layout: bytes per 64-row tile (stride = padded row bytes); 0 = row-major
 };
 size_t scan_workspace_bytes(int64_t nq, int32_t B, int64_t n, int32_t L, int32_t nl, int32_t R);
 hipError_t launch_scan(const ScanProblem& p, void* ws, size_t ws_bytes, hipStream_t stream,
                        hipEvent_t main_start = nullptr, hipEvent_t main_stop = nullptr);
+
+size_t tiled_codes_bytes(int64_t n, int32_t B);
+hipError_t launch_tile_codes(const uint8_t* codes, int32_t stride, int64_t n, int32_t B, uint8_t* tiled,
+                             hipStream_t stream);
 
 hipError_t launch_reorder(const float* q, int64_t nq, int32_t d, const void* base, int32_t dtype,
                           int64_t n, const int32_t* cand, int32_t R, int32_t k, int32_t* ids,

@@ -119,7 +119,7 @@ struct Problem {
     int64_t nq;
     int32_t B;
     const uint8_t* codes;
-    int32_t stride;
+    int32_t stride;       // bytes per row (tiled: the row's 16-byte segments, padded)
     int64_t n;
     const int32_t* ids;
     const int64_t* leaf_offsets;
@@ -129,7 +129,17 @@ struct Problem {
     int32_t R;
     int32_t* out_ids;
     int32_t* out_scores;
+    int64_t tile_bytes;   // tiled layout: bytes per 64-row tile (0: row-major)
 };
+
+// Row `row`'s first 16-byte segment and the distance between its segments:
+// row-major rows are contiguous; in the tiled layout segment j of the 64 rows
+// of a tile is one contiguous 1 KB run, so the same segment of consecutive rows
+// is consecutive in memory.
+__device__ __forceinline__ const uint8_t* code_row(const Problem& p, int64_t row) {
+    return p.tile_bytes ? p.codes + (row >> 6) * p.tile_bytes + (row & 63) * 16 : p.codes + row * p.stride;
+}
+__device__ __forceinline__ int32_t seg_step(const Problem& p) { return p.tile_bytes ? 1024 : 16; }
 
 __device__ __forceinline__ int hist_bin(int32_t s, int32_t hlo, int32_t hsh) {
     const int64_t d = (int64_t)s - hlo;
@@ -152,12 +162,13 @@ __device__ __forceinline__ void wave_fence() {
 __device__ __forceinline__ int nibble(const uint8_t* row, int b) { return (row[b >> 1] >> (4 * (b & 1))) & 15; }
 
 // Sum of one row's table entries; the table is int8 [B][16] in LDS.
-__device__ __forceinline__ int32_t row_sum(const int8_t* lut_s, int32_t B, const uint8_t* row, bool aligned4) {
+__device__ __forceinline__ int32_t row_sum(const int8_t* lut_s, int32_t B, const uint8_t* row, bool aligned4,
+                                           int32_t ss = 16) {
     int32_t s = 0;
-    if (aligned4) {
-        const uint32_t* r32 = reinterpret_cast<const uint32_t*>(row);
+    if (aligned4) {  // dword k of the row: segment k / 4 (ss bytes apart), word k % 4
         for (int b0 = 0; b0 < B; b0 += 8) {
-            const uint32_t wv = r32[b0 >> 3];
+            const int k = b0 >> 3;
+            const uint32_t wv = *reinterpret_cast<const uint32_t*>(row + (k >> 2) * ss + (k & 3) * 4);
             const int lim = B - b0 < 8 ? B - b0 : 8;
             for (int t = 0; t < lim; ++t) s += lut_s[(b0 + t) * 16 + ((wv >> (4 * t)) & 15)];
         }
@@ -276,7 +287,7 @@ __global__ __launch_bounds__(kSelThreads) void warmup_kernel(Problem p, ScanStat
         if (take > W - got) take = W - got;
         for (int64_t t = tid; t < take; t += kSelThreads) {
             const int64_t row = a + t;
-            const int32_t s = row_sum(lut_s, p.B, p.codes + row * p.stride, al4);
+            const int32_t s = row_sum(lut_s, p.B, code_row(p, row), al4, seg_step(p));
             keys[got + t] = int_key(s, p.ids ? p.ids[row] : (int32_t)row);
         }
         __syncthreads();
@@ -638,10 +649,11 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                 // row itself, or the item's last row), so the number of loads in
                 // flight is static
                 const int64_t r = live ? row : p1 - 1;
-                const uint8_t* base = p.codes + r * p.stride;
+                const uint8_t* base = code_row(p, r);
+                const int32_t ss = seg_step(p);
                 const int avail = p.stride - 32 * c;
-                x0 = *reinterpret_cast<const uint4*>(base + (avail >= 16 ? 32 * c : 0));
-                x1 = *reinterpret_cast<const uint4*>(base + (avail >= 32 ? 32 * c + 16 : 0));
+                x0 = *reinterpret_cast<const uint4*>(base + (avail >= 16 ? 2 * c * ss : 0));
+                x1 = *reinterpret_cast<const uint4*>(base + (avail >= 32 ? (2 * c + 1) * ss : 0));
                 keep = (live && avail >= 16 ? 1u : 0u) | (live && avail >= 32 ? 2u : 0u);
             } else {
                 keep = 3u;
@@ -1100,6 +1112,7 @@ __global__ __launch_bounds__(kStreamThreads) void scan_stream_kernel(MainArgs a)
         const int fulln = kPair ? 16 : 32;                                 // entries of a full segment
         const int lastn = kPair ? lastb : p.B - 32 * (nseg - 1);           // entries of the last one
         const int64_t rb0 = p0 + w * kWave;
+        const int32_t ss = seg_step(p);
         if (kSegs > 0) {
             // whole rows in registers; the next batch's rows load while this
             // batch's are summed.  Every load is unconditional (rows past the
@@ -1107,11 +1120,11 @@ __global__ __launch_bounds__(kStreamThreads) void scan_stream_kernel(MainArgs a)
             // compiler can wait for exactly the loads it needs.
             auto load_row = [&](int64_t rb, uint4* r) {
                 const int64_t row = rb + lane;
-                const uint8_t* src = p.codes + (row < p1 ? row : p1 - 1) * p.stride;
+                const uint8_t* src = code_row(p, row < p1 ? row : p1 - 1);
 #pragma unroll
                 for (int j = 0; j < kSegs; ++j) {
                     const int jj = j < nseg ? j : nseg - 1;
-                    r[j] = load_code16(src + 16 * jj);
+                    r[j] = load_code16(src + jj * ss);
                 }
             };
             auto batch = [&](int64_t rb, const uint4* r, uint4* nr) {
@@ -1137,11 +1150,11 @@ __global__ __launch_bounds__(kStreamThreads) void scan_stream_kernel(MainArgs a)
             // long rows: a ring of four segments in flight within the row
             for (int64_t rb = rb0; rb < p1; rb += kStreamThreads) {
                 const int64_t row = rb + lane;
-                const uint8_t* src = p.codes + (row < p1 ? row : p1 - 1) * p.stride;
+                const uint8_t* src = code_row(p, row < p1 ? row : p1 - 1);
                 uint4 ring[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
-                    if (k < nseg) ring[k] = load_code16(src + 16 * k);
+                    if (k < nseg) ring[k] = load_code16(src + k * ss);
                 StreamAcc<G, kPair> acc;
                 for (int j0 = 0; j0 < nseg; j0 += 4) {
 #pragma unroll
@@ -1149,7 +1162,7 @@ __global__ __launch_bounds__(kStreamThreads) void scan_stream_kernel(MainArgs a)
                         const int j = j0 + k;
                         if (j >= nseg) break;
                         const uint4 v = ring[k];
-                        if (j + 4 < nseg) ring[k] = load_code16(src + 16 * (j + 4));
+                        if (j + 4 < nseg) ring[k] = load_code16(src + (j + 4) * ss);
                         if (j < nseg - 1) acc.add(tbl, j, v, fulln);
                         else acc.add(tbl, j, v, lastn);
                         if (j % 8 == 7) acc.fold();  // 128 pairs, or 256 blocks
@@ -1229,14 +1242,15 @@ __global__ __launch_bounds__(kSelThreads) void warmup_wave_kernel(Problem p, Sca
         const int64_t take = b - a < W - got ? b - a : W - got;
         for (int64_t t = lane; t < take; t += kWave) {
             const int64_t row = a + t;
-            const uint8_t* src = p.codes + row * p.stride;
+            const uint8_t* src = code_row(p, row);
+            const int32_t ss = seg_step(p);
             int32_t sv = 0;
             if (al16) {
                 // the whole row's code bytes (at most 8 x 16) in one round trip
                 uint4 seg[kWaveLut / 512];
 #pragma unroll
                 for (int j = 0; j < kWaveLut / 512; ++j)
-                    if (j < nseg) seg[j] = *reinterpret_cast<const uint4*>(src + 16 * j);
+                    if (j < nseg) seg[j] = *reinterpret_cast<const uint4*>(src + j * ss);
 #pragma unroll
                 for (int j = 0; j < kWaveLut / 512; ++j) {
                     if (j >= nseg) break;
@@ -1248,7 +1262,7 @@ __global__ __launch_bounds__(kSelThreads) void warmup_wave_kernel(Problem p, Sca
                     }
                 }
             } else {
-                sv = row_sum(lut_s, p.B, src, al4);
+                sv = row_sum(lut_s, p.B, src, al4, ss);
             }
             atomicAdd(&hw_s[hist_bin(sv, st.hlo, st.hsh)], 1u);
         }
@@ -1404,7 +1418,7 @@ __global__ __launch_bounds__(kSelThreads) void fallback_kernel(Problem p, ScanSt
             if (b - a > p.n - m) b = a + (p.n - m);
             for (int64_t t = tid; t < b - a; t += kSelThreads) {
                 const int64_t row = a + t;
-                scratch[m + t] = int_key(row_sum(lut_s, p.B, p.codes + row * p.stride, al4),
+                scratch[m + t] = int_key(row_sum(lut_s, p.B, code_row(p, row), al4, seg_step(p)),
                                          p.ids ? p.ids[row] : (int32_t)row);
             }
             m += b - a;
@@ -1455,7 +1469,7 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     const ScanLayout lay = scan_layout(sp.nq, sp.B, sp.n, sp.L, sp.nl, sp.R);
     char* base = reinterpret_cast<char*>(ws);
     Problem p{sp.lut, sp.nq, sp.B, sp.codes, sp.stride, sp.n, sp.ids, sp.leaf_offsets, sp.L,
-              sp.leaves, sp.nl, sp.R, sp.out_ids, sp.out_scores};
+              sp.leaves, sp.nl, sp.R, sp.out_ids, sp.out_scores, sp.tile_bytes};
     ScanState st{};
     st.tau = reinterpret_cast<int32_t*>(base + lay.tau);
     st.cnt = reinterpret_cast<uint32_t*>(base + lay.cnt);
@@ -1571,6 +1585,46 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     if ((e = hipGetLastError()) != hipSuccess) return e;
     allow_lds(fallback_kernel, (size_t)Rp * 8 + lut_bytes);
     hipLaunchKernelGGL(fallback_kernel, dim3(kFbSlots), dim3(kSelThreads), (size_t)Rp * 8 + lut_bytes, stream, p, st);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ tiled code layout
+// One thread per destination 16-byte unit (tile t, segment j, row slot r, in
+// that order): the unit holds bytes [16 j, 16 j + 16) of row 64 t + r, zero
+// past the row's code bytes or past the last row.
+__global__ void tile_codes_kernel(const uint8_t* __restrict__ src, int32_t stride, int64_t n, int32_t cb, int32_t S,
+                                  uint4* __restrict__ dst, int64_t units) {
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < units;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = e / (64 * S);
+        const int rem = (int)(e - t * 64 * S);
+        const int j = rem >> 6, r = rem & 63;
+        const int64_t row = t * 64 + r;
+        uint32_t wd[4] = {0, 0, 0, 0};
+        if (row < n) {
+            const uint8_t* rp = src + row * stride;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int idx = 16 * j + k;
+                if (idx < cb) wd[k >> 2] |= (uint32_t)rp[idx] << (8 * (k & 3));
+            }
+        }
+        dst[e] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    }
+}
+
+size_t tiled_codes_bytes(int64_t n, int32_t B) {
+    const int64_t S = ((B + 1) / 2 + 15) / 16;
+    return (size_t)((n + 63) / 64) * 64 * (size_t)S * 16;
+}
+
+hipError_t launch_tile_codes(const uint8_t* codes, int32_t stride, int64_t n, int32_t B, uint8_t* tiled,
+                             hipStream_t stream) {
+    const int32_t cb = (B + 1) / 2, S = (cb + 15) / 16;
+    const int64_t units = ((n + 63) / 64) * 64 * S;
+    const int64_t blocks = (units + 255) / 256;
+    hipLaunchKernelGGL(tile_codes_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, stream,
+                       codes, stride, n, cb, S, reinterpret_cast<uint4*>(tiled), units);
     return hipGetLastError();
 }
 

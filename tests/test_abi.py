@@ -77,3 +77,28 @@ def test_host_side_validation(lib):
     # partition: nl > L, workspace too small
     assert lib.ah_partition_score(fake, 3, 8, fake, 4, 5, fake, None, fake, 1 << 30, None) == -2
     assert lib.ah_partition_score(fake, 3, 8, fake, 4, 2, fake, None, fake, 8, None) == -4
+
+
+def test_tiled_layout_validation(lib):
+    vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    lib.ah_tiled_codes_bytes.restype = sz
+    lib.ah_tiled_codes_bytes.argtypes = [i64, i32]
+    lib.ah_tile_codes.argtypes = [vp, i32, i64, i32, vp, sz, vp]
+    lib.ah_scan_topk.argtypes = [vp, i64, i32, vp, i32, i64, vp, vp, i32, vp, i32, i32, vp, vp, vp, sz, vp]
+    # ceil(n / 64) tiles of 64 rows x ceil(ceil(B/2) / 16) segments of 16 bytes
+    assert lib.ah_tiled_codes_bytes(1, 1) == 1024
+    assert lib.ah_tiled_codes_bytes(64, 64) == 2048
+    assert lib.ah_tiled_codes_bytes(65, 192) == 2 * 64 * 6 * 16
+    assert lib.ah_tiled_codes_bytes(0, 8) == 0
+    assert lib.ah_tiled_codes_bytes(-1, 8) == 0 and lib.ah_tiled_codes_bytes(5, 0) == 0
+    fake, odd = vp(4096), vp(4097)  # never dereferenced: every case below fails validation first
+    need = lib.ah_tiled_codes_bytes(100, 64)
+    assert lib.ah_tile_codes(fake, 31, 100, 64, fake, need, None) == -2      # stride below ceil(B/2)
+    assert lib.ah_tile_codes(fake, 32, 100, 64, fake, need - 1, None) == -2  # output too small
+    assert lib.ah_tile_codes(fake, 4096, 100, 8192, fake, 1 << 40, None) == -3  # B above the limit
+    assert lib.ah_tile_codes(None, 32, 100, 64, fake, need, None) == -1
+    assert lib.ah_tile_codes(fake, 32, 100, 64, odd, need, None) == -3       # output not 16-byte aligned
+    assert lib.ah_tile_codes(None, 32, 0, 64, None, 0, None) == 0            # n == 0: no-op
+    # scan on tiled codes (code_stride 0) needs 16-byte aligned codes
+    assert lib.ah_scan_topk(fake, 2, 8, odd, 0, 10, None, None, 0, None, 0, 5, fake, fake, fake, 1 << 30, None) == -3
+    assert lib.ah_scan_topk(fake, 2, 8, fake, -1, 10, None, None, 0, None, 0, 5, fake, fake, fake, 1 << 30, None) == -2

@@ -239,6 +239,74 @@ def test_scan_stream_partitioned(gpu, nq, B, L, nl):
     _scan_check(torch, ah, lut, codes, R, ids=perm, offs=offs, leaves=leaves)
 
 
+def _tiled_reference(codes, B):
+    """The tiled layout written out from its definition in ah.h (byte k of row r
+    at (r // 64) * 64 * S * 16 + (k // 16) * 1024 + (r % 64) * 16 + k % 16)."""
+    n = codes.shape[0]
+    cb = (B + 1) // 2
+    S = (cb + 15) // 16
+    out = np.zeros(((n + 63) // 64) * 64 * S * 16, dtype=np.uint8)
+    for r in range(n):
+        for k in range(cb):
+            out[(r // 64) * 64 * S * 16 + (k // 16) * 1024 + (r % 64) * 16 + k % 16] = codes[r, k]
+    return out
+
+
+@pytest.mark.parametrize("B,n,pad", [(64, 130, 0), (192, 64, 0), (50, 200, 7), (1, 5, 0), (600, 70, 3)])
+def test_tile_codes_layout(gpu, B, n, pad):
+    torch, ah = gpu
+    rng = np.random.default_rng(B + n)
+    codes = synth.random_codes(rng, n, B)
+    if pad:
+        codes = np.concatenate([codes, rng.integers(0, 256, size=(n, pad), dtype=np.uint8)], axis=1)
+    tc = ah.ah_tile_codes(_t(torch, codes), B)
+    torch.cuda.synchronize()
+    assert tc.data.numel() == ah.ah_tiled_codes_bytes(n, B)
+    assert np.array_equal(_np(tc.data), _tiled_reference(codes, B))
+
+
+# The tiled layout through every kernel that reads codes: streaming (1-4
+# queries), MFMA (more), warm-up (wave and workgroup), final selection and the
+# exact fallback, full and partitioned scans (leaves start at any row, so a
+# wave's rows may span two tiles).
+@pytest.mark.parametrize("nq,B,n,R,parts", [
+    (1, 192, 20000, 300, 0), (4, 192, 9000, 100, 0), (2, 64, 5001, 64, 0), (3, 768, 3000, 200, 0),
+    (70, 64, 5000, 200, 0), (20, 200, 2000, 300, 0), (9, 300, 3000, 40, 0),
+    (1, 192, 40000, 90, 25), (4, 64, 40000, 90, 3), (65, 96, 40000, 90, 30),
+])
+def test_scan_tiled_parity(gpu, nq, B, n, R, parts):
+    torch, ah = gpu
+    rng = np.random.default_rng(7 * nq + B + n + parts)
+    lut = synth.random_lut_i8(rng, nq, B)
+    codes = synth.random_codes(rng, n, B)
+    tc = ah.ah_tile_codes(_t(torch, codes), B)
+    ids = offs = leaves = None
+    kw = {}
+    if parts:
+        sizes = synth.random_leaf_sizes(rng, n, parts, skew=1.0)
+        offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+        ids = rng.permutation(n).astype(np.int32)
+        leaves = synth.random_probe_lists(rng, nq, parts, max(1, parts // 5))
+        kw = dict(ids=_t(torch, ids), leaf_offsets=_t(torch, offs), leaves=_t(torch, leaves))
+    g_ids, g_sc = ah.ah_scan_topk(_t(torch, lut), tc, R, **kw)
+    torch.cuda.synchronize()
+    o_ids, o_sc = oracle.scan_topk(lut, codes, R, ids=ids, leaf_offsets=offs, leaves=leaves)
+    assert np.array_equal(_np(g_ids), o_ids) and np.array_equal(_np(g_sc), o_sc)
+
+
+def test_scan_tiled_overflow_fallback(gpu):
+    """Equal sums on tiled codes: lists overflow, the exact fallback reads the tiles."""
+    torch, ah = gpu
+    B, n, nq, R = 64, 40000, 6, 50
+    lut = np.zeros((nq, B, 16), dtype=np.int8)
+    codes = synth.random_codes(np.random.default_rng(3), n, B)
+    tc = ah.ah_tile_codes(_t(torch, codes), B)
+    g_ids, g_sc = ah.ah_scan_topk(_t(torch, lut), tc, R)
+    torch.cuda.synchronize()
+    o_ids, o_sc = oracle.scan_topk(lut, codes, R)
+    assert np.array_equal(_np(g_ids), o_ids) and np.array_equal(_np(g_sc), o_sc)
+
+
 def test_scan_overflow_fallback(gpu):
     """All sums equal: the threshold cannot rise, candidate lists overflow and the
     exact fallback must return the R lowest ids."""
