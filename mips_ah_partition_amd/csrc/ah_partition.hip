@@ -46,13 +46,18 @@ __device__ __forceinline__ float4 fetch4(const float* __restrict__ m, int64_t ro
 template <bool kVec>
 __global__ __launch_bounds__(kGemmThreads) void centroid_scores_kernel(
     const float* __restrict__ q, int64_t nq, int32_t d, const float* __restrict__ cent, int32_t L,
-    float* __restrict__ S) {
+    float* __restrict__ S, int32_t kchunk) {
     __shared__ __align__(16) float qa[kGT * kGS];
     __shared__ __align__(16) float cb[kGT * kGS];
     const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
     const int64_t ntl = (L + kGT - 1) / kGT;  // leaf tiles; consecutive blocks share a query tile
-    const int64_t q0 = ((int64_t)blockIdx.x / ntl) * kGT;
-    const int64_t l0 = ((int64_t)blockIdx.x % ntl) * kGT;
+    const int64_t tiles = ((nq + kGT - 1) / kGT) * ntl;
+    const int64_t kz = (int64_t)blockIdx.x / tiles, t = (int64_t)blockIdx.x - kz * tiles;  // K split, tile
+    const int64_t q0 = (t / ntl) * kGT;
+    const int64_t l0 = (t % ntl) * kGT;
+    // this split's K range (kchunk is a multiple of kGK, so stages never cross it)
+    const int kb0 = (int)kz * kchunk, kb1 = kb0 + kchunk < d ? kb0 + kchunk : d;
+    S += kz * nq * (int64_t)L;
     const int wm = (w >> 1) * 64, wn = (w & 1) * 64;  // wave's 64x64 sub-tile
     v4f acc[4][4];
 #pragma unroll
@@ -70,14 +75,14 @@ __global__ __launch_bounds__(kGemmThreads) void centroid_scores_kernel(
         nc0 = fetch4<kVec>(cent, L, d, l0 + sr, (K0) + sk);                                   \
         nc1 = fetch4<kVec>(cent, L, d, l0 + sr + 64, (K0) + sk);                              \
     } while (0)
-    AH_FETCH(0);
-    for (int k0 = 0; k0 < d; k0 += kGK) {
+    AH_FETCH(kb0);
+    for (int k0 = kb0; k0 < kb1; k0 += kGK) {
         *reinterpret_cast<float4*>(&qa[sr * kGS + sk]) = nq0;
         *reinterpret_cast<float4*>(&qa[(sr + 64) * kGS + sk]) = nq1;
         *reinterpret_cast<float4*>(&cb[sr * kGS + sk]) = nc0;
         *reinterpret_cast<float4*>(&cb[(sr + 64) * kGS + sk]) = nc1;
         __syncthreads();
-        if (k0 + kGK < d) AH_FETCH(k0 + kGK);  // in flight while this stage computes
+        if (k0 + kGK < kb1) AH_FETCH(k0 + kGK);  // in flight while this stage computes
         const int kk = 4 * (lane >> 4);
 #pragma unroll
         for (int kb = 0; kb < kGK; kb += 16) {
@@ -243,7 +248,7 @@ template <int kPer, int kWv>
 __global__ __launch_bounds__(kLeafQ * kWave, kPer <= 16 ? 5 : 3) void leaf_select_wave_kernel(const float* __restrict__ S, int64_t nq,
                                                                           int32_t L, int32_t nl,
                                                                           int32_t* __restrict__ leaves,
-                                                                          float* __restrict__ scores) {
+                                                                          float* __restrict__ scores, int32_t nsplit) {
     constexpr int kQs = kLeafQ / kWv;  // queries per workgroup
     static_assert(kWv == 1 || kQs == 1, "a query spread over waves fills its workgroup");
     __shared__ uint32_t hist_all[kQs][256];
@@ -261,9 +266,19 @@ __global__ __launch_bounds__(kLeafQ * kWave, kPer <= 16 ? 5 : 3) void leaf_selec
     // element i = (j * kWv + wq) * 64 + lane
     const int first = wq * kWave + lane;
     const int nv = first < L ? (L - first + kWv * kWave - 1) / (kWv * kWave) : 0;  // o[0 .. nv) are real
+    // the score is the sum of the K splits' partial planes, in split order
+    float sv[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) sv[j] = j < nv ? s[j * kWv * kWave + first] : 0.f;
+    for (int z = 1; z < nsplit; ++z) {
+        const float* sz = s + z * nq * (int64_t)L;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (j < nv) sv[j] += sz[j * kWv * kWave + first];
+    }
     uint32_t o[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) o[j] = j < nv ? float_order(s[j * kWv * kWave + first]) : 0u;
+    for (int j = 0; j < kPer; ++j) o[j] = j < nv ? float_order(sv[j]) : 0u;
     auto sync = [] {
         if constexpr (kWv == 1) {
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -439,31 +454,50 @@ __global__ __launch_bounds__(kLeafQ * kWave, kPer <= 16 ? 5 : 3) void leaf_selec
 
 template <int kPer, int kWv>
 static void launch_leaf_wave(const float* S, int64_t nq, int32_t L, int32_t nl, int32_t* leaves, float* scores,
-                             hipStream_t stream) {
+                             int32_t nsplit, hipStream_t stream) {
     constexpr int kQs = kLeafQ / kWv;
     hipLaunchKernelGGL((leaf_select_wave_kernel<kPer, kWv>), dim3((unsigned)((nq + kQs - 1) / kQs)),
-                       dim3(kLeafQ * kWave), 0, stream, S, nq, L, nl, leaves, scores);
+                       dim3(kLeafQ * kWave), 0, stream, S, nq, L, nl, leaves, scores, nsplit);
 }
 
-size_t partition_workspace_bytes(int64_t nq, int32_t L) { return (size_t)nq * (size_t)L * 4 + 256; }
+// K splits of the contraction: when the tile grid has fewer than 256 tiles (one
+// per CU) and the one-wave selection (which adds the partial planes) applies,
+// up to four splits bring it to about 512 workgroups.
+static int max_splits(int64_t nq, int32_t L) {
+    const int64_t tiles = ((nq + kGT - 1) / kGT) * ((L + kGT - 1) / kGT);
+    if (L > kWaveLeaves || tiles >= 256) return 1;
+    const int64_t want = (512 + tiles - 1) / tiles;
+    return (int)(want < 4 ? want : 4);
+}
+
+size_t partition_workspace_bytes(int64_t nq, int32_t L) {
+    return (size_t)max_splits(nq, L) * (size_t)nq * (size_t)L * 4 + 256;
+}
 
 hipError_t launch_partition(const float* q, int64_t nq, int32_t d, const float* cent, int32_t L,
                             int32_t nl, int32_t* leaves, float* scores, void* ws, hipStream_t stream) {
     if (nq == 0) return hipSuccess;
     float* S = reinterpret_cast<float*>(ws);
-    dim3 grid((unsigned)(((L + kGT - 1) / kGT) * ((nq + kGT - 1) / kGT)));
+    const bool wave_sel = L <= kWaveLeaves && nl <= kLeafSort;
+    const int nstage = (d + kGK - 1) / kGK;
+    int nsplit = wave_sel ? max_splits(nq, L) : 1;
+    nsplit = nsplit < nstage ? nsplit : nstage;
+    const int kchunk = ((nstage + nsplit - 1) / nsplit) * kGK;
+    nsplit = (d + kchunk - 1) / kchunk;  // no empty split
+    const int64_t tiles = ((L + kGT - 1) / kGT) * ((nq + kGT - 1) / kGT);
+    dim3 grid((unsigned)(tiles * nsplit));
     const bool vec = (d % 4) == 0 && (reinterpret_cast<uintptr_t>(q) & 15) == 0 &&
                      (reinterpret_cast<uintptr_t>(cent) & 15) == 0;
-    if (vec) hipLaunchKernelGGL(centroid_scores_kernel<true>, grid, dim3(kGemmThreads), 0, stream, q, nq, d, cent, L, S);
-    else hipLaunchKernelGGL(centroid_scores_kernel<false>, grid, dim3(kGemmThreads), 0, stream, q, nq, d, cent, L, S);
+    if (vec) hipLaunchKernelGGL(centroid_scores_kernel<true>, grid, dim3(kGemmThreads), 0, stream, q, nq, d, cent, L, S, kchunk);
+    else hipLaunchKernelGGL(centroid_scores_kernel<false>, grid, dim3(kGemmThreads), 0, stream, q, nq, d, cent, L, S, kchunk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (L <= kWaveLeaves && nl <= kLeafSort) {
-        if (L <= 4 * kWave) launch_leaf_wave<4, 1>(S, nq, L, nl, leaves, scores, stream);
-        else if (L <= 8 * kWave) launch_leaf_wave<8, 1>(S, nq, L, nl, leaves, scores, stream);
-        else if (L <= 16 * kWave) launch_leaf_wave<16, 1>(S, nq, L, nl, leaves, scores, stream);
-        else if (L <= 32 * kWave) launch_leaf_wave<32, 1>(S, nq, L, nl, leaves, scores, stream);
-        else launch_leaf_wave<16, 4>(S, nq, L, nl, leaves, scores, stream);
+    if (wave_sel) {
+        if (L <= 4 * kWave) launch_leaf_wave<4, 1>(S, nq, L, nl, leaves, scores, nsplit, stream);
+        else if (L <= 8 * kWave) launch_leaf_wave<8, 1>(S, nq, L, nl, leaves, scores, nsplit, stream);
+        else if (L <= 16 * kWave) launch_leaf_wave<16, 1>(S, nq, L, nl, leaves, scores, nsplit, stream);
+        else if (L <= 32 * kWave) launch_leaf_wave<32, 1>(S, nq, L, nl, leaves, scores, nsplit, stream);
+        else launch_leaf_wave<16, 4>(S, nq, L, nl, leaves, scores, nsplit, stream);
         return hipGetLastError();
     }
     int Kp = 1;
