@@ -190,6 +190,9 @@ def test_scan_partitioned_parity(gpu):
     (768, 6000, 3, 400, 0),     # the same, packed nibble table
     (96, 7000, 2, 64, 0),       # 48 B rows: tiles of 64 rows in 3 rounds
     (192, 3001, 3, 37, 32),     # 96 B of codes in 128 B rows: whole-row registers
+    (500, 4000, 1, 100, 6),     # one query, nibble table, partial last segment
+    (1001, 3000, 1, 64, 11),    # odd B in 512 B rows
+    (1536, 2000, 1, 50, 0),     # 768 B rows
 ])
 def test_scan_stream_parity(gpu, B, n, nq, R, stride_pad):
     torch, ah = gpu
@@ -201,7 +204,7 @@ def test_scan_stream_parity(gpu, B, n, nq, R, stride_pad):
     _scan_check(torch, ah, lut, codes, R)
 
 
-@pytest.mark.parametrize("nq,B", [(1, 96), (2, 128), (4, 256), (70, 256)])
+@pytest.mark.parametrize("nq,B", [(1, 96), (2, 128), (4, 256), (70, 256), (1, 768)])
 def test_scan_extreme_tables(gpu, nq, B):
     """Entries of -128 and 127 only (streaming: packed fields at both ends of
     their range; one query: byte-pair table, two: packed pair table, four:
@@ -273,6 +276,7 @@ def test_tile_codes_layout(gpu, B, n, pad):
     (1, 192, 20000, 300, 0), (4, 192, 9000, 100, 0), (2, 64, 5001, 64, 0), (3, 768, 3000, 200, 0),
     (70, 64, 5000, 200, 0), (20, 200, 2000, 300, 0), (9, 300, 3000, 40, 0),
     (1, 192, 40000, 90, 25), (4, 64, 40000, 90, 3), (65, 96, 40000, 90, 30),
+    (1, 768, 20000, 200, 0), (1, 768, 30000, 90, 12),  # one query with a nibble table, full and partitioned
 ])
 def test_scan_tiled_parity(gpu, nq, B, n, R, parts):
     torch, ah = gpu
