@@ -61,6 +61,8 @@ def lib() -> C.CDLL:
                                        _i32p, _f64p]
         L.oracle_brute_force.argtypes = [_f32p, C.c_int64, C.c_int32, C.c_void_p, C.c_int32,
                                          C.c_int64, C.c_int32, _i32p, _f64p]
+        L.oracle_encode.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_int32, _f32p, C.c_int32, C.c_int32,
+                                    C.c_double, C.c_int32, _u8p, C.c_int32]
         _LIB = L
     return _LIB
 
@@ -176,6 +178,22 @@ def brute_force(Q, base, k):
     osc = np.empty((nq, k), dtype=np.float64)
     lib().oracle_brute_force(Q, nq, Q.shape[1], _ptr(b), dt, b.shape[0], k, oi, osc)
     return oi, osc
+
+
+def encode(rows, codebooks, eta, sweeps=2, stride=None):
+    """Anisotropic coupled encoding (block-coordinate descent from the per-block
+    nearest centers).  rows: float32 [n, d] or bfloat16 bits as uint16 [n, d];
+    codebooks float32 [B, 16, dpb].  Returns uint8 [n, stride] nibble codes."""
+    b, dt = _base_args(rows)
+    cb = _c(codebooks, np.float32)
+    B, _, dpb = cb.shape
+    n, d = b.shape
+    if d != B * dpb:
+        raise ValueError("rows do not have B * dpb columns")
+    stride = (B + 1) // 2 if stride is None else int(stride)
+    out = np.zeros((n, stride), dtype=np.uint8)
+    lib().oracle_encode(_ptr(b), dt, n, d, cb, B, dpb, float(eta), int(sweeps), out, stride)
+    return out
 
 
 def recall_at_k(found: np.ndarray, truth: np.ndarray) -> float:

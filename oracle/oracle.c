@@ -266,3 +266,89 @@ void oracle_brute_force(const float* qv, int64_t nq, int32_t d, const void* base
         free(best);
     }
 }
+
+/* Anisotropic encoding of rows with given per-block codebooks (the next step
+ * before the query path: the ScaNN page, sections "The loss in one paragraph"
+ * and "Training an anisotropic codebook yourself").  A row x with direction
+ * u = x/|x| is scored by the loss (eta-1)*(u.r)^2 + |r|^2 of its residual
+ * r = x - decode(code).  The page only says the coupled block choices are
+ * refined iteratively; the reading taken here is block-coordinate descent:
+ *   - start from the per-block nearest center (squared L2, lowest index on ties);
+ *   - a sweep visits b = 0..B-1 and gives block b the center minimising the
+ *     loss with every other block fixed (lowest index on ties);
+ *   - `sweeps` sweeps.
+ * The parallel residual u.r is the sum over blocks of p_b(c) =
+ * sum_t (x_t/|x|)(x_t - c_t); the sweep keeps the running total s and, for
+ * block b, the total without it, s - p_b(code_b).  All arithmetic in float64,
+ * in exactly this order (x_t/|x| formed as x_t * (1/|x|); p_b and |r_b|^2
+ * accumulated over t in order; the candidate's loss as
+ * ((eta-1)*par)*par + |r_b|^2 with par = (s - p_b(code_b)) + p_b(c)); the
+ * decision is an argmin of these float64 values.  Rows: float32 (dtype 0) or
+ * bfloat16 (dtype 1, widened exactly).  Codes nibble-packed, low nibble = even
+ * block, unused bits zero. */
+static double oracle_pb(const double* xv, double invn, const float* cen, int32_t dpb) {
+    double p = 0.0;
+    for (int32_t t = 0; t < dpb; ++t) p += (xv[t] * invn) * (xv[t] - (double)cen[t]);
+    return p;
+}
+
+void oracle_encode(const void* rows, int32_t dtype, int64_t n, int32_t d, const float* cb, int32_t B,
+                   int32_t dpb, double eta, int32_t sweeps, uint8_t* codes, int32_t stride) {
+    #pragma omp parallel
+    {
+        double* xv = (double*)malloc(sizeof(double) * (size_t)d);
+        uint8_t* code = (uint8_t*)malloc((size_t)B);
+        #pragma omp for schedule(static)
+        for (int64_t i = 0; i < n; ++i) {
+            double ss = 0.0;
+            for (int32_t j = 0; j < d; ++j) {
+                xv[j] = load_row_elem(rows, dtype, i * d + j);
+                ss += xv[j] * xv[j];
+            }
+            const double invn = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+            for (int32_t b = 0; b < B; ++b) {
+                double best = INFINITY;
+                int bc = 0;
+                for (int c = 0; c < 16; ++c) {
+                    const float* cen = cb + ((int64_t)b * 16 + c) * dpb;
+                    double nr = 0.0;
+                    for (int32_t t = 0; t < dpb; ++t) {
+                        const double r = xv[b * dpb + t] - (double)cen[t];
+                        nr += r * r;
+                    }
+                    if (nr < best) { best = nr; bc = c; }
+                }
+                code[b] = (uint8_t)bc;
+            }
+            for (int32_t sw = 0; sw < sweeps; ++sw) {
+                double s = 0.0;
+                for (int32_t b = 0; b < B; ++b)
+                    s += oracle_pb(xv + b * dpb, invn, cb + ((int64_t)b * 16 + code[b]) * dpb, dpb);
+                for (int32_t b = 0; b < B; ++b) {
+                    const double sm = s - oracle_pb(xv + b * dpb, invn, cb + ((int64_t)b * 16 + code[b]) * dpb, dpb);
+                    double best = INFINITY, bp = 0.0;
+                    int bc = 0;
+                    for (int c = 0; c < 16; ++c) {
+                        const float* cen = cb + ((int64_t)b * 16 + c) * dpb;
+                        const double p = oracle_pb(xv + b * dpb, invn, cen, dpb);
+                        double nr = 0.0;
+                        for (int32_t t = 0; t < dpb; ++t) {
+                            const double r = xv[b * dpb + t] - (double)cen[t];
+                            nr += r * r;
+                        }
+                        const double par = sm + p;
+                        const double L = ((eta - 1.0) * par) * par + nr;
+                        if (L < best) { best = L; bc = c; bp = p; }
+                    }
+                    code[b] = (uint8_t)bc;
+                    s = sm + bp;
+                }
+            }
+            uint8_t* row = codes + i * (int64_t)stride;
+            memset(row, 0, (size_t)stride);
+            for (int32_t b = 0; b < B; ++b) row[b >> 1] |= (uint8_t)(code[b] << (4 * (b & 1)));
+        }
+        free(xv);
+        free(code);
+    }
+}

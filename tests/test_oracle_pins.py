@@ -326,3 +326,86 @@ def test_recall_ignores_empty_slots_and_averages():
     t = np.array([[1, 2], [3, 4]])
     f = np.array([[2, -1], [4, 3]])
     assert oracle.recall_at_k(f, t) == pytest.approx(0.75)
+
+
+# ----------------------------------------------------------------------------- anisotropic encoding
+def _decode(codes, cb):
+    B, _, dpb = cb.shape
+    n = codes.shape[0]
+    out = np.zeros((n, B * dpb))
+    for b in range(B):
+        c = (codes[:, b >> 1] >> (4 * (b & 1))) & 15
+        out[:, b * dpb:(b + 1) * dpb] = cb[b, c].astype(np.float64)
+    return out
+
+
+def _aniso_loss(X, codes, cb, eta):
+    """(eta - 1)(u.r)^2 + |r|^2 per row, written from the definition in float64."""
+    Xd = X.astype(np.float64)
+    r = Xd - _decode(codes, cb)
+    nrm = np.linalg.norm(Xd, axis=1, keepdims=True)
+    u = np.divide(Xd, nrm, out=np.zeros_like(Xd), where=nrm > 0)
+    return (eta - 1.0) * np.sum(u * r, axis=1) ** 2 + np.sum(r * r, axis=1)
+
+
+@pytest.mark.parametrize("dpb,B", [(1, 5), (2, 7), (4, 3)])
+def test_encode_eta_one_is_per_block_nearest(dpb, B):
+    """eta = 1 drops the parallel term: each block takes its nearest center
+    (lowest index on ties; small integers make ties frequent)."""
+    rng = np.random.default_rng(dpb * 10 + B)
+    X = rng.integers(-2, 3, size=(300, B * dpb)).astype(np.float32)
+    cb = rng.integers(-2, 3, size=(B, 16, dpb)).astype(np.float32)
+    got = oracle.encode(X, cb, 1.0, sweeps=3)
+    for b in range(B):
+        dist = ((X[:, None, b * dpb:(b + 1) * dpb].astype(np.float64) - cb[b][None].astype(np.float64)) ** 2).sum(-1)
+        want = np.argmin(dist, axis=1)  # first minimum: the lowest index
+        assert np.array_equal((got[:, b >> 1] >> (4 * (b & 1))) & 15, want)
+
+
+def test_encode_zero_row_takes_nearest_centers():
+    rng = np.random.default_rng(3)
+    cb = rng.standard_normal((6, 16, 2)).astype(np.float32)
+    X = np.zeros((2, 12), dtype=np.float32)
+    got = oracle.encode(X, cb, 9.0, sweeps=2)
+    want = np.argmin((cb.astype(np.float64) ** 2).sum(-1), axis=1)
+    for b in range(6):
+        assert ((got[:, b >> 1] >> (4 * (b & 1))) & 15 == want[b]).all()
+
+
+def test_encode_sweeps_never_raise_the_loss():
+    """Each coordinate step takes the minimiser with the other blocks fixed, so
+    the row loss cannot rise from one sweep to the next."""
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((400, 24)).astype(np.float32)
+    cb = rng.standard_normal((12, 16, 2)).astype(np.float32)
+    prev = None
+    for sw in range(5):
+        loss = _aniso_loss(X, oracle.encode(X, cb, 4.0, sweeps=sw), cb, 4.0)
+        if prev is not None:
+            assert (loss <= prev * (1 + 1e-12) + 1e-12).all()
+        prev = loss
+    assert (prev < _aniso_loss(X, oracle.encode(X, cb, 4.0, sweeps=0), cb, 4.0) - 1e-9).any()
+
+
+def test_encode_converged_blocks_are_coordinate_optima():
+    """After many sweeps no single block can lower its row's loss (brute force
+    over the 16 centers of every block)."""
+    rng = np.random.default_rng(12)
+    n, B, dpb, eta = 60, 4, 2, 6.0
+    X = rng.standard_normal((n, B * dpb)).astype(np.float32)
+    cb = rng.standard_normal((B, 16, dpb)).astype(np.float32)
+    codes = oracle.encode(X, cb, eta, sweeps=40)
+    base = _aniso_loss(X, codes, cb, eta)
+    for b in range(B):
+        for c in range(16):
+            alt = codes.copy()
+            alt[:, b >> 1] = (alt[:, b >> 1] & (0xF0 if b % 2 == 0 else 0x0F)) | (c << (4 * (b & 1)))
+            assert (_aniso_loss(X, alt, cb, eta) >= base * (1 - 1e-12) - 1e-12).all()
+
+
+def test_encode_bf16_rows_widen_exactly():
+    rng = np.random.default_rng(13)
+    X = rng.standard_normal((100, 16)).astype(np.float32)
+    bits = synth.to_bf16_bits(X)
+    cb = rng.standard_normal((8, 16, 2)).astype(np.float32)
+    assert np.array_equal(oracle.encode(bits, cb, 4.0), oracle.encode(synth.bf16_bits_to_f32(bits), cb, 4.0))
