@@ -214,6 +214,7 @@ def code_scan_probe(torch, ahlib, ev, runs=5):
 # peak), a2 writes the int8 tables (nq B 16 bytes, HBM), a5 gathers the
 # candidates' rows (nq R d 2 bytes for bf16, HBM).
 PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_FP64_TFLOPS = 78.6  # vector float64
 
 
 def _time_ms(torch, fn, runs=5):
@@ -230,6 +231,7 @@ def _time_ms(torch, fn, runs=5):
 
 
 def stage_probes(torch, ahlib):
+    from mips_ah_partition_amd import costs
     out = {}
     g = torch.Generator(device="cuda")
     g.manual_seed(5151)
@@ -247,6 +249,19 @@ def stage_probes(torch, ahlib):
         out[f"a2_lut_{name}"] = {"nq": w.nq, "blocks": w.blocks, "ms": ms, "GBps": byt / (ms / 1e3) / 1e9,
                                  "frac_of_8TBps": byt / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
         del C
+    # encoding (the codes the scan reads) at the 20M x 384 shape, bf16 rows, two sweeps:
+    # a float64 vector-ALU kernel, counted by costs.encode_flops_per_row
+    w = synth.WORKLOADS["wiki20m"]
+    X = synth.gpu_normal_rows(torch, w.n, w.d, 6161, torch.bfloat16)
+    cb = 0.5 * torch.randn((w.blocks, 16, w.dpb), generator=g, device="cuda")
+    codes = torch.empty((w.n, (w.blocks + 1) // 2), dtype=torch.uint8, device="cuda")
+    ms = _time_ms(torch, lambda: ahlib.ah_encode(X, cb, w.eta, sweeps=2, codes_out=codes), runs=3)
+    fl = w.n * costs.encode_flops_per_row(w.d, w.dpb, 2)
+    out["encode_wiki20m"] = {"rows": w.n, "d": w.d, "dtype": "bf16", "sweeps": 2, "ms": ms, "rows_per_s": w.n / (ms / 1e3),
+                             "fp64_TFLOPs": fl / (ms / 1e3) / 1e12,
+                             "frac_of_fp64_vector": fl / (ms / 1e3) / 1e12 / PEAK_FP64_TFLOPS}
+    del X, codes
+    torch.cuda.empty_cache()
     # bf16 reorder at the 2M x 1536 shape: 1,000 queries x 400 random candidates
     w = synth.WORKLOADS["openai2m"]
     base = torch.randn((w.n, w.d), generator=g, device="cuda").to(torch.bfloat16)

@@ -137,6 +137,29 @@ int ah_scan_topk(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* cod
                  int32_t* cand_scores_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Encoding: the codes the scan reads (ScaNN page, sections "The loss in one
+ * paragraph" and "Training an anisotropic codebook yourself": a row's loss is
+ * (eta-1)*(u.r)^2 + |r|^2 for its residual r = x - decode(code) and direction
+ * u = x/|x|; the coupled block choices are refined iteratively).  Reading
+ * taken: block-coordinate descent from the per-block nearest centers (squared
+ * L2), `sweeps` sweeps over b = 0..B-1, each block taking the center that
+ * minimises the row's loss with the other blocks fixed; ties to the lowest
+ * center index.  Float64 arithmetic in a fixed order, so the codes are
+ * reproducible bit for bit.
+ *
+ *   rows       [n][d] float32 (rows_dtype AH_F32) or bfloat16 (AH_BF16)
+ *   codebooks  float32 [B][16][dpb], d == B * dpb
+ *   eta        >= 0 (1 = plain nearest-center encoding); sweeps 0..64
+ *   codes_out  uint8 [n][code_stride] (code_stride >= ceil(B/2)), nibbles as
+ *              described above; bytes past ceil(B/2) are written as zero
+ * Errors: AH_ERR_SHAPE (n < 0, B < 1, dpb < 1, d != B*dpb, code_stride <
+ * ceil(B/2), sweeps outside 0..64, eta < 0 or not finite), AH_ERR_UNSUPPORTED
+ * (dtype, dpb > AH_MAX_DPB, B > AH_MAX_BLOCKS), AH_ERR_NULL.
+ */
+int ah_encode(const void* rows, int32_t rows_dtype, int64_t n, int32_t d, const float* codebooks, int32_t B,
+              int32_t dpb, double eta, int32_t sweeps, uint8_t* codes_out, int32_t code_stride, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Code layout for the scan (same page and section as the scan: the codes are
  * read once per query batch, so their layout decides how well the reads
  * coalesce).  Not a step of the method: a rearrangement of the same bytes.

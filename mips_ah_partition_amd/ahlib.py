@@ -27,7 +27,7 @@ EXPORTS = (
     "ah_partition_workspace_bytes", "ah_partition_score",
     "ah_build_lut",
     "ah_scan_workspace_bytes", "ah_scan_topk", "ah_scan_topk_timed",
-    "ah_tiled_codes_bytes", "ah_tile_codes",
+    "ah_encode", "ah_tiled_codes_bytes", "ah_tile_codes",
     "ah_reorder_exact",
 )
 
@@ -63,6 +63,8 @@ def lib() -> C.CDLL:
         L.ah_scan_topk_timed.restype = C.c_int
         L.ah_scan_topk_timed.argtypes = [vp, i64, i32, vp, i32, i64, vp, vp, i32, vp, i32, i32, vp, vp, vp, sz, vp,
                                          vp, vp]
+        L.ah_encode.restype = C.c_int
+        L.ah_encode.argtypes = [vp, i32, i64, i32, vp, i32, i32, C.c_double, i32, vp, i32, vp]
         L.ah_tiled_codes_bytes.restype = sz
         L.ah_tiled_codes_bytes.argtypes = [i64, i32]
         L.ah_tile_codes.restype = C.c_int
@@ -164,6 +166,28 @@ def ah_build_lut(q, codebooks, lut_i8_out=None, scale_out=None, bias_out=None, l
 # ----------------------------------------------------------------------------- steps 3+4
 def ah_scan_workspace_bytes(nq: int, B: int, n: int, L: int, nl: int, R: int) -> int:
     return int(lib().ah_scan_workspace_bytes(nq, B, n, L, nl, R))
+
+
+def ah_encode(rows, codebooks, eta, sweeps=2, codes_out=None, stride=None, stream=None):
+    """Anisotropic coupled codes of rows (float32 or bfloat16 [n, d]) for
+    codebooks float32 [B, 16, dpb]; returns uint8 [n, stride]."""
+    if rows.dtype == torch.float32:
+        dt = AH_F32
+    elif rows.dtype == torch.bfloat16:
+        dt = AH_BF16
+    else:
+        raise TypeError("rows must be float32 or bfloat16")
+    _dev(rows, rows.dtype, "rows", 2)
+    codebooks = _dev(codebooks, torch.float32, "codebooks", 3)
+    n, d = rows.shape
+    B, _, dpb = codebooks.shape
+    stride = (B + 1) // 2 if stride is None else int(stride)
+    if codes_out is None:
+        codes_out = torch.empty((n, stride), dtype=torch.uint8, device=rows.device)
+    _dev(codes_out, torch.uint8, "codes_out", 2)
+    _check(lib().ah_encode(_ptr(rows), dt, n, d, _ptr(codebooks), B, dpb, float(eta), int(sweeps), _ptr(codes_out),
+                           codes_out.shape[1], _stream(stream)), "ah_encode")
+    return codes_out
 
 
 class TiledCodes:

@@ -54,3 +54,15 @@ def scan_bytes(nq: int, B: int, scanned_rows_total: float, unique_rows: int) -> 
 def reorder_bytes(nq: int, R: int, d: int, elem_bytes: int) -> int:
     """Rows gathered by the exact reorder: R rows of d elements per query."""
     return nq * R * d * elem_bytes
+
+
+def encode_flops_per_row(d: int, dpb: int, sweeps: int) -> int:
+    """Float64 operations the coupled encoding needs per row: the squared norm
+    (2 d); the nearest-center start (16 candidates x dpb x (subtract, square,
+    add) per block); and per sweep and block the running parallel sum and the
+    current center's term (each dpb x 6: r, (x * 1/|x|) r, r r and two adds)
+    plus 16 candidates x (6 dpb + 4: par, ((eta - 1) par) par, + |r|^2)."""
+    B = d // dpb
+    init = B * 16 * 3 * dpb
+    sweep = B * (6 * dpb + 6 * dpb + 16 * (6 * dpb + 4))
+    return 2 * d + init + sweeps * sweep

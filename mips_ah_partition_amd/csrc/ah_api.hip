@@ -92,6 +92,19 @@ int ah_scan_topk(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* cod
                               cand_ids_out, cand_scores_out, workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
+int ah_encode(const void* rows, int32_t rows_dtype, int64_t n, int32_t d, const float* codebooks, int32_t B,
+              int32_t dpb, double eta, int32_t sweeps, uint8_t* codes_out, int32_t code_stride, void* stream) {
+    if (n < 0 || B < 1 || dpb < 1 || (int64_t)B * dpb != d || code_stride < (B + 1) / 2 || sweeps < 0 ||
+        sweeps > 64 || !(eta >= 0.0) || !(eta < 1e300))
+        return AH_ERR_SHAPE;
+    if ((rows_dtype != AH_F32 && rows_dtype != AH_BF16) || dpb > AH_MAX_DPB || B > AH_MAX_BLOCKS)
+        return AH_ERR_UNSUPPORTED;
+    if (n == 0) return AH_OK;
+    if (!rows || !codebooks || !codes_out) return AH_ERR_NULL;
+    return hip_status(ah::launch_encode(rows, rows_dtype, n, d, codebooks, B, dpb, eta, sweeps, codes_out,
+                                        code_stride, static_cast<hipStream_t>(stream)));
+}
+
 size_t ah_tiled_codes_bytes(int64_t n, int32_t B) {
     if (n < 0 || B < 1) return 0;
     return ah::tiled_codes_bytes(n, B);

@@ -39,6 +39,10 @@ size_t scan_workspace_bytes(int64_t nq, int32_t B, int64_t n, int32_t L, int32_t
 hipError_t launch_scan(const ScanProblem& p, void* ws, size_t ws_bytes, hipStream_t stream,
                        hipEvent_t main_start = nullptr, hipEvent_t main_stop = nullptr);
 
+hipError_t launch_encode(const void* rows, int32_t dtype, int64_t n, int32_t d, const float* cb, int32_t B,
+                         int32_t dpb, double eta, int32_t sweeps, uint8_t* codes, int32_t stride,
+                         hipStream_t stream);
+
 size_t tiled_codes_bytes(int64_t n, int32_t B);
 hipError_t launch_tile_codes(const uint8_t* codes, int32_t stride, int64_t n, int32_t B, uint8_t* tiled,
                              hipStream_t stream);

@@ -168,3 +168,15 @@ def random_probe_lists(rng: np.random.Generator, nq: int, num_leaves: int, nl: i
     for i in range(nq):
         out[i] = rng.choice(num_leaves, size=nl, replace=False)
     return out
+
+
+def gpu_normal_rows(torch, n: int, d: int, seed: int, dtype, chunk_rows: int = 1 << 20):
+    """n x d standard-normal rows generated on the GPU (seeded, in chunks of
+    chunk_rows), stored as dtype."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    out = torch.empty((n, d), dtype=dtype, device="cuda")
+    for a in range(0, n, chunk_rows):
+        b = min(n, a + chunk_rows)
+        out[a:b] = torch.randn((b - a, d), generator=g, device="cuda").to(dtype)
+    return out

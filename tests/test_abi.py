@@ -102,3 +102,18 @@ def test_tiled_layout_validation(lib):
     # scan on tiled codes (code_stride 0) needs 16-byte aligned codes
     assert lib.ah_scan_topk(fake, 2, 8, odd, 0, 10, None, None, 0, None, 0, 5, fake, fake, fake, 1 << 30, None) == -3
     assert lib.ah_scan_topk(fake, 2, 8, fake, -1, 10, None, None, 0, None, 0, 5, fake, fake, fake, 1 << 30, None) == -2
+
+
+def test_encode_validation(lib):
+    vp, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
+    lib.ah_encode.argtypes = [vp, i32, i64, i32, vp, i32, i32, C.c_double, i32, vp, i32, vp]
+    fake = vp(4096)  # never dereferenced: every case below fails validation first
+    assert lib.ah_encode(fake, 0, 10, 9, fake, 4, 2, 4.0, 2, fake, 2, None) == -2   # d != B * dpb
+    assert lib.ah_encode(fake, 0, 10, 8, fake, 4, 2, 4.0, 2, fake, 1, None) == -2   # stride below ceil(B/2)
+    assert lib.ah_encode(fake, 0, 10, 8, fake, 4, 2, 4.0, 65, fake, 2, None) == -2  # too many sweeps
+    assert lib.ah_encode(fake, 0, 10, 8, fake, 4, 2, -1.0, 2, fake, 2, None) == -2  # eta < 0
+    assert lib.ah_encode(fake, 0, 10, 8, fake, 4, 2, float("nan"), 2, fake, 2, None) == -2
+    assert lib.ah_encode(fake, 5, 10, 8, fake, 4, 2, 4.0, 2, fake, 2, None) == -3   # dtype
+    assert lib.ah_encode(fake, 0, 10, 68, fake, 2, 34, 4.0, 2, fake, 1, None) == -3  # dpb above the limit
+    assert lib.ah_encode(None, 0, 10, 8, fake, 4, 2, 4.0, 2, fake, 2, None) == -1
+    assert lib.ah_encode(None, 0, 0, 8, None, 4, 2, 4.0, 2, None, 2, None) == 0     # n == 0: no-op

@@ -192,3 +192,26 @@ def test_openai2m_partitioned_shape(gpu):
 
 def test_wiki20m_partitioned_shape(gpu):
     _partitioned_case(gpu, "wiki20m", True)
+
+
+def test_encode_fullsize_sampled(gpu):
+    """Coupled encoding of the 20M x 384 bf16 shape in one launch (as the
+    benchmark times it); sampled rows re-encoded by the oracle must match bit
+    for bit."""
+    torch, ah = gpu
+    w = synth.WORKLOADS["wiki20m"]
+    _log("encode: generating 20M x 384 bf16 rows on the GPU")
+    X = synth.gpu_normal_rows(torch, w.n, w.d, 6161, torch.bfloat16)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    cb = 0.5 * torch.randn((w.blocks, 16, w.dpb), generator=g, device="cuda")
+    codes = ah.ah_encode(X, cb, w.eta, sweeps=2)
+    torch.cuda.synchronize()
+    _log("encode: done; checking sampled rows")
+    idx = torch.tensor(sorted(set([0, 1, 63, 64, w.n // 2, w.n - 2, w.n - 1] +
+                                  list(range(1_000_003, w.n, 2_000_017)))), device="cuda")
+    rows = X[idx].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    want = oracle.encode(rows, cb.cpu().numpy(), w.eta, sweeps=2)
+    assert np.array_equal(codes[idx].cpu().numpy(), want)
+    del X, codes
+    torch.cuda.empty_cache()

@@ -425,3 +425,40 @@ def test_partition_few_score_values(gpu, L, nl, kinds):
     o_lv, o_sc = oracle.partition(Q, Cn, nl)
     assert np.array_equal(_np(lv), o_lv)
     assert np.array_equal(_np(sc), o_sc.astype(np.float32))
+
+
+# ----------------------------------------------------------------------------- encoding (codes for the scan)
+# Bit-exact against the oracle: both take the argmins in float64 in the same
+# order.  dpb 1, 2 and 4 have their own kernels, 3 and 16 the generic one;
+# small-integer rows make exact ties (lowest center wins) frequent, and a few
+# rows are all zero (u = 0: the loss is |r|^2).
+@pytest.mark.parametrize("dtype,n,B,dpb,eta,sweeps,pad", [
+    ("f32", 3001, 64, 2, 4.0, 2, 0),
+    ("bf16", 2000, 192, 2, 4.0, 2, 0),
+    ("f32", 500, 7, 3, 6.0, 3, 5),
+    ("f32", 1000, 32, 4, 1.0, 1, 0),
+    ("bf16", 777, 50, 1, 4.0, 0, 0),
+    ("f32", 300, 5, 16, 9.0, 4, 0),
+    ("int", 1000, 16, 2, 4.0, 2, 3),
+])
+def test_encode_parity(gpu, dtype, n, B, dpb, eta, sweeps, pad):
+    torch, ah = gpu
+    rng = np.random.default_rng(n + B + dpb)
+    d = B * dpb
+    if dtype == "int":
+        X = rng.integers(-2, 3, size=(n, d)).astype(np.float32)
+        cb = rng.integers(-2, 3, size=(B, 16, dpb)).astype(np.float32)
+    else:
+        X = rng.standard_normal((n, d)).astype(np.float32)
+        cb = (0.5 * rng.standard_normal((B, 16, dpb))).astype(np.float32)
+    X[::97] = 0.0
+    stride = (B + 1) // 2 + pad
+    if dtype == "bf16":
+        bits = synth.to_bf16_bits(X)
+        rows_np, rows_t = bits, _t(torch, bits.view(np.int16)).view(torch.bfloat16)
+    else:
+        rows_np, rows_t = X, _t(torch, X)
+    got = ah.ah_encode(rows_t, _t(torch, cb), eta, sweeps=sweeps, stride=stride)
+    torch.cuda.synchronize()
+    want = oracle.encode(rows_np, cb, eta, sweeps=sweeps, stride=stride)
+    assert np.array_equal(_np(got), want)
