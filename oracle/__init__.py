@@ -61,6 +61,7 @@ def lib() -> C.CDLL:
                                        _i32p, _f64p]
         L.oracle_brute_force.argtypes = [_f32p, C.c_int64, C.c_int32, C.c_void_p, C.c_int32,
                                          C.c_int64, C.c_int32, _i32p, _f64p]
+        L.oracle_nearest.argtypes = [_f32p, C.c_int64, C.c_int32, _f32p, C.c_int32, _i32p, _f64p]
         L.oracle_encode.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_int32, _f32p, C.c_int32, C.c_int32,
                                     C.c_double, C.c_int32, _u8p, C.c_int32]
         _LIB = L
@@ -178,6 +179,18 @@ def brute_force(Q, base, k):
     osc = np.empty((nq, k), dtype=np.float64)
     lib().oracle_brute_force(Q, nq, Q.shape[1], _ptr(b), dt, b.shape[0], k, oi, osc)
     return oi, osc
+
+
+def nearest(X, centroids):
+    """Nearest centroid per row (float64 squared distance, lowest id on ties):
+    (ids int32 [n], squared distances float64 [n])."""
+    X = _c(X, np.float32)
+    Cn = _c(centroids, np.float32)
+    n, d = X.shape
+    ids = np.empty(n, dtype=np.int32)
+    dist = np.empty(n, dtype=np.float64)
+    lib().oracle_nearest(X, n, d, Cn, Cn.shape[0], ids, dist)
+    return ids, dist
 
 
 def encode(rows, codebooks, eta, sweeps=2, stride=None):

@@ -352,3 +352,25 @@ void oracle_encode(const void* rows, int32_t dtype, int64_t n, int32_t d, const 
         free(code);
     }
 }
+
+/* Nearest centroid of each row (the assignment step of the partitioning; the
+ * ScaNN page, "Three stages of a search": rows are grouped under centroids):
+ * argmin_l |x - c_l|^2 in float64, summed over t in order, lowest l on ties. */
+void oracle_nearest(const float* x, int64_t n, int32_t d, const float* cent, int32_t L, int32_t* out,
+                    double* dist2) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        double best = INFINITY;
+        int32_t bl = 0;
+        for (int32_t l = 0; l < L; ++l) {
+            double s = 0.0;
+            for (int32_t t = 0; t < d; ++t) {
+                const double r = (double)x[i * d + t] - (double)cent[(int64_t)l * d + t];
+                s += r * r;
+            }
+            if (s < best) { best = s; bl = l; }
+        }
+        out[i] = bl;
+        if (dist2) dist2[i] = best;
+    }
+}

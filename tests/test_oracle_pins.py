@@ -409,3 +409,26 @@ def test_encode_bf16_rows_widen_exactly():
     bits = synth.to_bf16_bits(X)
     cb = rng.standard_normal((8, 16, 2)).astype(np.float32)
     assert np.array_equal(oracle.encode(bits, cb, 4.0), oracle.encode(synth.bf16_bits_to_f32(bits), cb, 4.0))
+
+
+# ----------------------------------------------------------------------------- nearest centroid
+def test_nearest_matches_exact_integer_argmax_form():
+    """On small integers every quantity is exact: argmin |x - c|^2 equals the
+    first argmax of x.c - |c|^2/2 computed in int64 (2 x.c - |c|^2)."""
+    rng = np.random.default_rng(21)
+    X = rng.integers(-3, 4, size=(500, 12)).astype(np.float32)
+    Cn = rng.integers(-3, 4, size=(40, 12)).astype(np.float32)
+    Cn[7] = Cn[3]  # a duplicate: the lower id must win
+    ids, dist = oracle.nearest(X, Cn)
+    Xi, Ci = X.astype(np.int64), Cn.astype(np.int64)
+    score = 2 * Xi @ Ci.T - (Ci * Ci).sum(1)[None, :]
+    assert np.array_equal(ids, np.argmax(score, axis=1))
+    assert np.array_equal(dist, ((Xi[:, None, :] - Ci[None]) ** 2).sum(-1).min(1).astype(np.float64))
+    assert not (ids == 7).any()
+
+
+def test_nearest_zero_row_takes_smallest_norm():
+    rng = np.random.default_rng(22)
+    Cn = rng.standard_normal((30, 8)).astype(np.float32)
+    ids, _ = oracle.nearest(np.zeros((3, 8), dtype=np.float32), Cn)
+    assert (ids == np.argmin((Cn.astype(np.float64) ** 2).sum(1))).all()
