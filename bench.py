@@ -249,6 +249,20 @@ def stage_probes(torch, ahlib):
         out[f"a2_lut_{name}"] = {"nq": w.nq, "blocks": w.blocks, "ms": ms, "GBps": byt / (ms / 1e3) / 1e9,
                                  "frac_of_8TBps": byt / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
         del C
+    # partition assignment (nearest of 4,000 centroids) for 4M rows of the 20M x 384 shape:
+    # the fp32 MFMA contraction (2 n L d FLOP) plus the one-wave selection per row
+    w = synth.WORKLOADS["wiki20m"]
+    na = 4_000_000
+    X = synth.gpu_normal_rows(torch, na, w.d, 6262, torch.float32)
+    C = torch.randn((w.num_leaves, w.d), generator=g, device="cuda")
+    lv = torch.empty(na, dtype=torch.int32, device="cuda")
+    wsa = torch.empty(ahlib.ah_assign_workspace_bytes(na, w.num_leaves), dtype=torch.uint8, device="cuda")
+    ms = _time_ms(torch, lambda: ahlib.ah_assign_leaves(X, C, leaf_out=lv, workspace=wsa), runs=3)
+    tf = 2.0 * na * w.num_leaves * w.d / (ms / 1e3) / 1e12
+    out["assign_wiki20m_4M_rows"] = {"rows": na, "leaves": w.num_leaves, "d": w.d, "ms": ms, "TFLOPs": tf,
+                                     "frac_of_fp32_mfma": tf / PEAK_FP32_MFMA_TFLOPS}
+    del X, wsa, lv
+    torch.cuda.empty_cache()
     # encoding (the codes the scan reads) at the 20M x 384 shape, bf16 rows, two sweeps:
     # a float64 vector-ALU kernel, counted by costs.encode_flops_per_row
     w = synth.WORKLOADS["wiki20m"]

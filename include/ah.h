@@ -57,6 +57,8 @@ enum { AH_F32 = 0, AH_BF16 = 1 };
 #define AH_MAX_R 4096        /* pre-reorder candidates (also max nl and k) */
 #define AH_MAX_DIM 16384     /* d */
 
+#define AH_MAX_ASSIGN_LEAVES 4096 /* L for ah_assign_leaves */
+
 /* code_stride value selecting the tiled code layout (see ah_tile_codes). */
 #define AH_CODES_TILED 0
 
@@ -135,6 +137,25 @@ int ah_scan_topk(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* cod
                  int32_t code_stride, int64_t n, const int32_t* ids, const int64_t* leaf_offsets,
                  int32_t L, const int32_t* leaves, int32_t nl, int32_t R, int32_t* cand_ids_out,
                  int32_t* cand_scores_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Partition assignment (the k-means assignment step behind the partition the
+ * first stage searches; ScaNN page, section "Three stages of a search"): each
+ * row goes to the centroid nearest to it.
+ *
+ *   x          float32 [n][d] rows
+ *   centroids  float32 [L][d], L <= AH_MAX_ASSIGN_LEAVES
+ *   leaf_out   int32 [n]  argmin_l |x - c_l|^2, computed as argmax_l
+ *              (x . c_l - |c_l|^2 / 2) in fp32 (MFMA contraction, fp32
+ *              accumulation), lowest leaf id on ties
+ *   score_out  float32 [n] that maximum, or NULL
+ *   workspace  >= ah_assign_workspace_bytes(n, L) bytes
+ * Errors: AH_ERR_NULL, AH_ERR_SHAPE (n < 0, d < 1, L < 1),
+ * AH_ERR_UNSUPPORTED (L > AH_MAX_ASSIGN_LEAVES, d > AH_MAX_DIM), AH_ERR_WORKSPACE.
+ */
+size_t ah_assign_workspace_bytes(int64_t n, int32_t L);
+int ah_assign_leaves(const float* x, int64_t n, int32_t d, const float* centroids, int32_t L, int32_t* leaf_out,
+                     float* score_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Encoding: the codes the scan reads (ScaNN page, sections "The loss in one

@@ -27,6 +27,7 @@ EXPORTS = (
     "ah_partition_workspace_bytes", "ah_partition_score",
     "ah_build_lut",
     "ah_scan_workspace_bytes", "ah_scan_topk", "ah_scan_topk_timed",
+    "ah_assign_workspace_bytes", "ah_assign_leaves",
     "ah_encode", "ah_tiled_codes_bytes", "ah_tile_codes",
     "ah_reorder_exact",
 )
@@ -63,6 +64,10 @@ def lib() -> C.CDLL:
         L.ah_scan_topk_timed.restype = C.c_int
         L.ah_scan_topk_timed.argtypes = [vp, i64, i32, vp, i32, i64, vp, vp, i32, vp, i32, i32, vp, vp, vp, sz, vp,
                                          vp, vp]
+        L.ah_assign_workspace_bytes.restype = sz
+        L.ah_assign_workspace_bytes.argtypes = [i64, i32]
+        L.ah_assign_leaves.restype = C.c_int
+        L.ah_assign_leaves.argtypes = [vp, i64, i32, vp, i32, vp, vp, vp, sz, vp]
         L.ah_encode.restype = C.c_int
         L.ah_encode.argtypes = [vp, i32, i64, i32, vp, i32, i32, C.c_double, i32, vp, i32, vp]
         L.ah_tiled_codes_bytes.restype = sz
@@ -166,6 +171,32 @@ def ah_build_lut(q, codebooks, lut_i8_out=None, scale_out=None, bias_out=None, l
 # ----------------------------------------------------------------------------- steps 3+4
 def ah_scan_workspace_bytes(nq: int, B: int, n: int, L: int, nl: int, R: int) -> int:
     return int(lib().ah_scan_workspace_bytes(nq, B, n, L, nl, R))
+
+
+def ah_assign_workspace_bytes(n: int, L: int) -> int:
+    return int(lib().ah_assign_workspace_bytes(n, L))
+
+
+def ah_assign_leaves(x, centroids, leaf_out=None, score_out=None, workspace=None, want_scores=False, stream=None):
+    """Nearest centroid of every row (lowest id on ties); returns (leaves int32 [n], scores or None)."""
+    x = _dev(x, torch.float32, "x", 2)
+    centroids = _dev(centroids, torch.float32, "centroids", 2)
+    n, d = x.shape
+    L = centroids.shape[0]
+    if centroids.shape[1] != d:
+        raise ValueError("centroids dimension differs from rows")
+    if leaf_out is None:
+        leaf_out = torch.empty(n, dtype=torch.int32, device=x.device)
+    if score_out is None and want_scores:
+        score_out = torch.empty(n, dtype=torch.float32, device=x.device)
+    _dev(leaf_out, torch.int32, "leaf_out")
+    _dev(score_out, torch.float32, "score_out")
+    need = ah_assign_workspace_bytes(n, L)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().ah_assign_leaves(_ptr(x), n, d, _ptr(centroids), L, _ptr(leaf_out), _ptr(score_out), _ptr(workspace),
+                                  workspace.numel(), _stream(stream)), "ah_assign_leaves")
+    return leaf_out, score_out
 
 
 def ah_encode(rows, codebooks, eta, sweeps=2, codes_out=None, stride=None, stream=None):

@@ -92,6 +92,22 @@ int ah_scan_topk(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* cod
                               cand_ids_out, cand_scores_out, workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
+size_t ah_assign_workspace_bytes(int64_t n, int32_t L) {
+    if (n < 0 || L < 1) return 0;
+    return ah::assign_workspace_bytes(n, L);
+}
+
+int ah_assign_leaves(const float* x, int64_t n, int32_t d, const float* centroids, int32_t L, int32_t* leaf_out,
+                     float* score_out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (n < 0 || d < 1 || L < 1) return AH_ERR_SHAPE;
+    if (L > AH_MAX_ASSIGN_LEAVES || d > AH_MAX_DIM) return AH_ERR_UNSUPPORTED;
+    if (n == 0) return AH_OK;
+    if (!x || !centroids || !leaf_out) return AH_ERR_NULL;
+    if (!workspace || workspace_bytes < ah::assign_workspace_bytes(n, L)) return AH_ERR_WORKSPACE;
+    return hip_status(ah::launch_assign(x, n, d, centroids, L, leaf_out, score_out, workspace,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 int ah_encode(const void* rows, int32_t rows_dtype, int64_t n, int32_t d, const float* codebooks, int32_t B,
               int32_t dpb, double eta, int32_t sweeps, uint8_t* codes_out, int32_t code_stride, void* stream) {
     if (n < 0 || B < 1 || dpb < 1 || (int64_t)B * dpb != d || code_stride < (B + 1) / 2 || sweeps < 0 ||

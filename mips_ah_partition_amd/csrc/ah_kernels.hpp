@@ -39,6 +39,10 @@ size_t scan_workspace_bytes(int64_t nq, int32_t B, int64_t n, int32_t L, int32_t
 hipError_t launch_scan(const ScanProblem& p, void* ws, size_t ws_bytes, hipStream_t stream,
                        hipEvent_t main_start = nullptr, hipEvent_t main_stop = nullptr);
 
+size_t assign_workspace_bytes(int64_t n, int32_t L);
+hipError_t launch_assign(const float* x, int64_t n, int32_t d, const float* cent, int32_t L, int32_t* leaves,
+                         float* scores, void* ws, hipStream_t stream);
+
 hipError_t launch_encode(const void* rows, int32_t dtype, int64_t n, int32_t d, const float* cb, int32_t B,
                          int32_t dpb, double eta, int32_t sweeps, uint8_t* codes, int32_t stride,
                          hipStream_t stream);

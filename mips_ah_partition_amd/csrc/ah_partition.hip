@@ -248,7 +248,8 @@ template <int kPer, int kWv>
 __global__ __launch_bounds__(kLeafQ * kWave, kPer <= 16 ? 5 : 3) void leaf_select_wave_kernel(const float* __restrict__ S, int64_t nq,
                                                                           int32_t L, int32_t nl,
                                                                           int32_t* __restrict__ leaves,
-                                                                          float* __restrict__ scores, int32_t nsplit) {
+                                                                          float* __restrict__ scores, int32_t nsplit,
+                                                                          const float* __restrict__ bias) {
     constexpr int kQs = kLeafQ / kWv;  // queries per workgroup
     static_assert(kWv == 1 || kQs == 1, "a query spread over waves fills its workgroup");
     __shared__ uint32_t hist_all[kQs][256];
@@ -275,6 +276,11 @@ __global__ __launch_bounds__(kLeafQ * kWave, kPer <= 16 ? 5 : 3) void leaf_selec
 #pragma unroll
         for (int j = 0; j < kPer; ++j)
             if (j < nv) sv[j] += sz[j * kWv * kWave + first];
+    }
+    if (bias) {  // per-leaf additive term (nearest-centroid assignment)
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (j < nv) sv[j] += bias[j * kWv * kWave + first];
     }
     uint32_t o[kPer];
 #pragma unroll
@@ -454,10 +460,10 @@ __global__ __launch_bounds__(kLeafQ * kWave, kPer <= 16 ? 5 : 3) void leaf_selec
 
 template <int kPer, int kWv>
 static void launch_leaf_wave(const float* S, int64_t nq, int32_t L, int32_t nl, int32_t* leaves, float* scores,
-                             int32_t nsplit, hipStream_t stream) {
+                             int32_t nsplit, hipStream_t stream, const float* bias = nullptr) {
     constexpr int kQs = kLeafQ / kWv;
     hipLaunchKernelGGL((leaf_select_wave_kernel<kPer, kWv>), dim3((unsigned)((nq + kQs - 1) / kQs)),
-                       dim3(kLeafQ * kWave), 0, stream, S, nq, L, nl, leaves, scores, nsplit);
+                       dim3(kLeafQ * kWave), 0, stream, S, nq, L, nl, leaves, scores, nsplit, bias);
 }
 
 // K splits of the contraction: when the tile grid has fewer than 256 tiles (one
@@ -509,6 +515,60 @@ hipError_t launch_partition(const float* q, int64_t nq, int32_t d, const float* 
     hipLaunchKernelGGL(leaf_select_kernel, dim3((unsigned)nq), dim3(kSelThreads), lds, stream,
                        S, L, nl, leaves, scores);
     return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ nearest-centroid assignment
+// The k-means assignment step of the partitioning (the ScaNN page's
+// "Three stages of a search": rows are grouped under the centroid they are
+// closest to): argmin_l |x - c_l|^2 = argmax_l (x . c_l - |c_l|^2 / 2), lowest
+// leaf id on ties.  The same fp32 MFMA contraction as the centroid scoring, in
+// row chunks whose score block fits the workspace, then the one-wave selection
+// of the single best leaf with -|c_l|^2 / 2 added to every score.
+__global__ void half_norm_kernel(const float* __restrict__ cent, int32_t L, int32_t d, float* __restrict__ bias) {
+    const int64_t l = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (l >= L) return;
+    float s = 0.f;
+    for (int t = 0; t < d; ++t) s = __fmaf_rn(cent[l * d + t], cent[l * d + t], s);
+    bias[l] = -0.5f * s;
+}
+
+constexpr int64_t kAssignChunk = 65536;  // rows per contraction and selection
+
+static int64_t assign_chunk(int64_t n) { return n < kAssignChunk ? (n > 0 ? n : 1) : kAssignChunk; }
+
+size_t assign_workspace_bytes(int64_t n, int32_t L) {
+    return (((size_t)L * 4 + 255) & ~(size_t)255) + (size_t)assign_chunk(n) * (size_t)L * 4 + 256;
+}
+
+hipError_t launch_assign(const float* x, int64_t n, int32_t d, const float* cent, int32_t L, int32_t* leaves,
+                         float* scores, void* ws, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    float* bias = reinterpret_cast<float*>(ws);
+    float* S = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (((size_t)L * 4 + 255) & ~(size_t)255));
+    hipLaunchKernelGGL(half_norm_kernel, dim3((unsigned)((L + 255) / 256)), dim3(256), 0, stream, cent, L, d, bias);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t chunk = assign_chunk(n);
+    for (int64_t r0 = 0; r0 < n; r0 += chunk) {
+        const int64_t m = n - r0 < chunk ? n - r0 : chunk;
+        const float* q = x + r0 * d;
+        const int64_t tiles = ((L + kGT - 1) / kGT) * ((m + kGT - 1) / kGT);
+        const int kchunk = ((d + kGK - 1) / kGK) * kGK;
+        const bool vec = (d % 4) == 0 && (reinterpret_cast<uintptr_t>(q) & 15) == 0 &&
+                         (reinterpret_cast<uintptr_t>(cent) & 15) == 0;
+        if (vec) hipLaunchKernelGGL(centroid_scores_kernel<true>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream, q, m, d, cent, L, S, kchunk);
+        else hipLaunchKernelGGL(centroid_scores_kernel<false>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream, q, m, d, cent, L, S, kchunk);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        int32_t* lo = leaves + r0;
+        float* so = scores ? scores + r0 : nullptr;
+        if (L <= 4 * kWave) launch_leaf_wave<4, 1>(S, m, L, 1, lo, so, 1, stream, bias);
+        else if (L <= 8 * kWave) launch_leaf_wave<8, 1>(S, m, L, 1, lo, so, 1, stream, bias);
+        else if (L <= 16 * kWave) launch_leaf_wave<16, 1>(S, m, L, 1, lo, so, 1, stream, bias);
+        else if (L <= 32 * kWave) launch_leaf_wave<32, 1>(S, m, L, 1, lo, so, 1, stream, bias);
+        else launch_leaf_wave<16, 4>(S, m, L, 1, lo, so, 1, stream, bias);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace ah

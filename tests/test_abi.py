@@ -117,3 +117,18 @@ def test_encode_validation(lib):
     assert lib.ah_encode(fake, 0, 10, 68, fake, 2, 34, 4.0, 2, fake, 1, None) == -3  # dpb above the limit
     assert lib.ah_encode(None, 0, 10, 8, fake, 4, 2, 4.0, 2, fake, 2, None) == -1
     assert lib.ah_encode(None, 0, 0, 8, None, 4, 2, 4.0, 2, None, 2, None) == 0     # n == 0: no-op
+
+
+def test_assign_validation(lib):
+    vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    lib.ah_assign_workspace_bytes.restype = sz
+    lib.ah_assign_workspace_bytes.argtypes = [i64, i32]
+    lib.ah_assign_leaves.argtypes = [vp, i64, i32, vp, i32, vp, vp, vp, sz, vp]
+    fake = vp(4096)  # never dereferenced: every case below fails validation first
+    need = lib.ah_assign_workspace_bytes(1000, 64)
+    assert need > 1000 * 64 * 4 and lib.ah_assign_workspace_bytes(5, 0) == 0
+    assert lib.ah_assign_leaves(fake, 1000, 0, fake, 64, fake, None, fake, need, None) == -2
+    assert lib.ah_assign_leaves(fake, 1000, 8, fake, 5000, fake, None, fake, 1 << 40, None) == -3
+    assert lib.ah_assign_leaves(None, 1000, 8, fake, 64, fake, None, fake, need, None) == -1
+    assert lib.ah_assign_leaves(fake, 1000, 8, fake, 64, fake, None, fake, need - 1, None) == -4
+    assert lib.ah_assign_leaves(None, 0, 8, None, 64, None, None, None, 0, None) == 0

@@ -215,3 +215,30 @@ def test_encode_fullsize_sampled(gpu):
     assert np.array_equal(codes[idx].cpu().numpy(), want)
     del X, codes
     torch.cuda.empty_cache()
+
+
+def test_assign_fullsize_sampled(gpu):
+    """Nearest of 4,000 centroids for all 20M x 384 rows in one call (row chunks
+    inside); sampled rows checked against the float64 oracle with the fp32 rule."""
+    torch, ah = gpu
+    w = synth.WORKLOADS["wiki20m"]
+    _log("assign: generating 20M x 384 fp32 rows on the GPU")
+    X = synth.gpu_normal_rows(torch, w.n, w.d, 6363, torch.float32)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(78)
+    C = torch.randn((w.num_leaves, w.d), generator=g, device="cuda")
+    ids, _ = ah.ah_assign_leaves(X, C)
+    torch.cuda.synchronize()
+    _log("assign: done; checking sampled rows")
+    idx = torch.tensor(sorted(set([0, 1, 65535, 65536, w.n // 2, w.n - 1] +
+                                  list(range(1_000_003, w.n, 1_000_033)))), device="cuda")
+    Xs = X[idx].cpu().numpy()
+    Cn = C.cpu().numpy()
+    gi = ids[idx].cpu().numpy()
+    o_ids, o_dist = oracle.nearest(Xs, Cn)
+    Xd, Cd = Xs.astype(np.float64), Cn.astype(np.float64)
+    g_dist = ((Xd - Cd[gi]) ** 2).sum(1)
+    scale = (Xd * Xd).sum(1) + (Cd[gi] * Cd[gi]).sum(1) + 2 * np.abs(Xd * Cd[gi]).sum(1)
+    assert (g_dist <= o_dist + TOL * scale).all()
+    del X
+    torch.cuda.empty_cache()

@@ -462,3 +462,37 @@ def test_encode_parity(gpu, dtype, n, B, dpb, eta, sweeps, pad):
     torch.cuda.synchronize()
     want = oracle.encode(rows_np, cb, eta, sweeps=sweeps, stride=stride)
     assert np.array_equal(_np(got), want)
+
+
+# ----------------------------------------------------------------------------- partition assignment
+# fp32 contraction against the float64 oracle: a GPU choice is accepted when its
+# float64 distance is within the tolerance of the oracle's minimum (R10's rule);
+# on small integers everything is exact and the ids must be equal.
+@pytest.mark.parametrize("n,d,L,kind", [(5000, 100, 1000, "f"), (3000, 384, 4000, "f"), (70001, 16, 300, "f"),
+                                       (2000, 12, 40, "int"), (100, 1536, 2000, "f"), (10, 3, 5, "f")])
+def test_assign_leaves_parity(gpu, n, d, L, kind):
+    torch, ah = gpu
+    rng = np.random.default_rng(n + d + L)
+    if kind == "int":
+        X = rng.integers(-3, 4, size=(n, d)).astype(np.float32)
+        Cn = rng.integers(-3, 4, size=(L, d)).astype(np.float32)
+        Cn[L // 2] = Cn[1]
+    else:
+        X = rng.standard_normal((n, d)).astype(np.float32)
+        Cn = rng.standard_normal((L, d)).astype(np.float32)
+    X[::997] = 0.0
+    ids, sc = ah.ah_assign_leaves(_t(torch, X), _t(torch, Cn), want_scores=True)
+    torch.cuda.synchronize()
+    ids, sc = _np(ids), _np(sc)
+    o_ids, o_dist = oracle.nearest(X, Cn)
+    if kind == "int":
+        assert np.array_equal(ids, o_ids)
+        return
+    Xd, Cd = X.astype(np.float64), Cn.astype(np.float64)
+    g_dist = ((Xd - Cd[ids]) ** 2).sum(1)
+    scale = (Xd * Xd).sum(1) + (Cd[ids] * Cd[ids]).sum(1) + 2 * np.abs(Xd * Cd[ids]).sum(1)
+    assert (g_dist <= o_dist + TOL * scale).all()
+    assert (ids == o_ids).mean() > 0.99
+    # the reported score is x.c - |c|^2/2 of the chosen leaf
+    ref = (Xd * Cd[ids]).sum(1) - 0.5 * (Cd[ids] * Cd[ids]).sum(1)
+    assert (np.abs(sc - ref) <= TOL * (np.abs(Xd * Cd[ids]).sum(1) + 0.5 * (Cd[ids] * Cd[ids]).sum(1))).all()
