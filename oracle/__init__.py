@@ -61,6 +61,9 @@ def lib() -> C.CDLL:
                                        _i32p, _f64p]
         L.oracle_brute_force.argtypes = [_f32p, C.c_int64, C.c_int32, C.c_void_p, C.c_int32,
                                          C.c_int64, C.c_int32, _i32p, _f64p]
+        L.oracle_sq8_quantize.argtypes = [_f32p, C.c_int64, C.c_int32, C.c_double, _i8p, _f32p]
+        L.oracle_sq8_topk.argtypes = [_i8p, _f32p, C.c_int64, _i8p, _f32p, C.c_int64, C.c_int32, C.c_int32,
+                                      _i32p, _f32p]
         L.oracle_nearest.argtypes = [_f32p, C.c_int64, C.c_int32, _f32p, C.c_int32, _i32p, _f64p]
         L.oracle_encode.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_int32, _f32p, C.c_int32, C.c_int32,
                                     C.c_double, C.c_int32, _u8p, C.c_int32]
@@ -179,6 +182,28 @@ def brute_force(Q, base, k):
     osc = np.empty((nq, k), dtype=np.float64)
     lib().oracle_brute_force(Q, nq, Q.shape[1], _ptr(b), dt, b.shape[0], k, oi, osc)
     return oi, osc
+
+
+def sq8_quantize(X, pct=99.9):
+    """Per-vector int8 codes and float32 steps (robust percentile scale)."""
+    X = _c(X, np.float32)
+    n, d = X.shape
+    codes = np.empty((n, d), dtype=np.int8)
+    scale = np.empty(n, dtype=np.float32)
+    lib().oracle_sq8_quantize(X, n, d, float(pct), codes, scale)
+    return codes, scale
+
+
+def sq8_topk(q8, qs, d8, ds, R):
+    """Top-R documents per query by (float)(q8 . d8) * s_q * s_d, ties to the lower id."""
+    q8, d8 = _c(q8, np.int8), _c(d8, np.int8)
+    qs, ds = _c(qs, np.float32), _c(ds, np.float32)
+    nq, d = q8.shape
+    n = d8.shape[0]
+    ids = np.empty((nq, R), dtype=np.int32)
+    sc = np.empty((nq, R), dtype=np.float32)
+    lib().oracle_sq8_topk(q8, qs, nq, d8, ds, n, d, int(R), ids, sc)
+    return ids, sc
 
 
 def nearest(X, centroids):

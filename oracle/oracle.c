@@ -374,3 +374,76 @@ void oracle_nearest(const float* x, int64_t n, int32_t d, const float* cent, int
         if (dist2) dist2[i] = best;
     }
 }
+
+/* ----------------------------------------------------------------------------
+ * Int8 scalar-quantised flat search (the page "Incoherence-Aware Asymmetric
+ * Quantization for Retrieval", sections "A Specialized int8 Retrieval Engine"
+ * and the robust int8 scale): every vector gets its own step
+ * s = max(P, 1e-8) / 127 with P the pct-th percentile of its absolute values,
+ * codes clip(round(x / s), -127, 127) (round half to even), and a query/document
+ * pair scores (float)(q8 . d8) * s_q * s_d with the integer dot exact.
+ * Readings: P by linear interpolation between order statistics (position
+ * pct/100 * (d-1); fraction t; a + (b-a)*t when t < 0.5, else b - (b-a)*(1-t),
+ * with b-a in float32 and the rest in float64, as numpy's linear percentile); s in float32 (the float32 P, then / 127);
+ * x / s in float32; the score's multiplications left to right in float32;
+ * ranking by (score desc, document id asc). */
+static int cmp_f32(const void* a, const void* b) {
+    const float x = *(const float*)a, y = *(const float*)b;
+    return (x > y) - (x < y);
+}
+
+void oracle_sq8_quantize(const float* x, int64_t n, int32_t d, double pct, int8_t* codes, float* scale) {
+    #pragma omp parallel
+    {
+        float* a = (float*)malloc(sizeof(float) * (size_t)(d > 0 ? d : 1));
+        #pragma omp for schedule(static)
+        for (int64_t i = 0; i < n; ++i) {
+            for (int32_t t = 0; t < d; ++t) a[t] = fabsf(x[i * d + t]);
+            qsort(a, (size_t)d, sizeof(float), cmp_f32);
+            const float pos = (float)(d - 1) * (float)(pct / 100.0);
+            int64_t lo = (int64_t)floorf(pos);
+            if (lo > d - 1) lo = d - 1;
+            const int64_t hi = lo + 1 < d ? lo + 1 : d - 1;
+            const float t = pos - (float)lo;
+            const float diff = a[hi] - a[lo];
+            const float P = t < 0.5f ? a[lo] + diff * t : a[hi] - diff * (1.0f - t);
+            const float s = (P > 1e-8f ? P : 1e-8f) / 127.0f;
+            scale[i] = s;
+            for (int32_t k = 0; k < d; ++k) {
+                float v = rintf(x[i * d + k] / s);
+                if (v > 127.0f) v = 127.0f;
+                if (v < -127.0f) v = -127.0f;
+                codes[i * d + k] = (int8_t)v;
+            }
+        }
+        free(a);
+    }
+}
+
+typedef struct { float score; int32_t id; } FSC;
+static int cmp_fsc(const void* a, const void* b) {
+    const FSC* x = (const FSC*)a; const FSC* y = (const FSC*)b;
+    if (x->score != y->score) return x->score > y->score ? -1 : 1;
+    return (x->id > y->id) - (x->id < y->id);
+}
+
+void oracle_sq8_topk(const int8_t* q8, const float* qs, int64_t nq, const int8_t* d8, const float* ds, int64_t n,
+                     int32_t d, int32_t R, int32_t* out_ids, float* out_scores) {
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t q = 0; q < nq; ++q) {
+        FSC* all = (FSC*)malloc(sizeof(FSC) * (size_t)(n > 0 ? n : 1));
+        for (int64_t j = 0; j < n; ++j) {
+            int64_t dot = 0;
+            for (int32_t t = 0; t < d; ++t) dot += (int64_t)q8[q * d + t] * (int64_t)d8[j * d + t];
+            const float f = (float)(int32_t)dot;
+            all[j].score = (f * qs[q]) * ds[j];
+            all[j].id = (int32_t)j;
+        }
+        qsort(all, (size_t)n, sizeof(FSC), cmp_fsc);
+        for (int32_t r = 0; r < R; ++r) {
+            out_ids[q * R + r] = r < n ? all[r].id : -1;
+            out_scores[q * R + r] = r < n ? all[r].score : -INFINITY;
+        }
+        free(all);
+    }
+}

@@ -432,3 +432,45 @@ def test_nearest_zero_row_takes_smallest_norm():
     Cn = rng.standard_normal((30, 8)).astype(np.float32)
     ids, _ = oracle.nearest(np.zeros((3, 8), dtype=np.float32), Cn)
     assert (ids == np.argmin((Cn.astype(np.float64) ** 2).sum(1))).all()
+
+
+# ----------------------------------------------------------------------------- int8 flat search (next row 3)
+@pytest.mark.parametrize("d,pct", [(512, 99.9), (7, 99.9), (1, 99.9), (100, 50.0), (64, 100.0), (33, 0.0)])
+def test_sq8_scale_is_numpy_linear_percentile(d, pct):
+    rng = np.random.default_rng(d)
+    X = rng.standard_normal((50, d)).astype(np.float32)
+    X[3] = 0.0  # all zero: the 1e-8 floor
+    _, s = oracle.sq8_quantize(X, pct)
+    P = np.percentile(np.abs(X), pct, axis=1)
+    want = np.maximum(P.astype(np.float32), np.float32(1e-8)) / np.float32(127.0)
+    assert np.array_equal(s, want.astype(np.float32))
+
+
+def test_sq8_codes_round_half_even_and_clip():
+    """A row whose 99.9th percentile of |x| is exactly 127 has step 1: codes are
+    x rounded half to even and clipped (127.5 -> 128 -> 127, 2.5 -> 2, 3.5 -> 4)."""
+    d = 5001  # position 4995: the five largest values sit above the percentile
+    x = np.full(d, 127.0, dtype=np.float32)
+    x[:4] = [2.5, 3.5, -2.5, -0.5]
+    x[-5:] = [127.5, -300.0, 200.0, -150.0, 128.0]
+    codes, s = oracle.sq8_quantize(x[None], 99.9)
+    assert s[0] == np.float32(1.0)
+    assert list(codes[0, :4]) == [2, 4, -2, 0]
+    assert list(codes[0, -5:]) == [127, -127, 127, -127, 127]
+
+
+def test_sq8_topk_is_brute_force_over_exact_dots():
+    rng = np.random.default_rng(5)
+    D = rng.standard_normal((300, 40)).astype(np.float32)
+    D[17] = D[5]  # a duplicate document: equal scores, the lower id first
+    Q = rng.standard_normal((9, 40)).astype(np.float32)
+    d8, ds = oracle.sq8_quantize(D)
+    q8, qs = oracle.sq8_quantize(Q)
+    ids, sc = oracle.sq8_topk(q8, qs, d8, ds, 25)
+    dots = q8.astype(np.int64) @ d8.astype(np.int64).T  # exact
+    full = (dots.astype(np.float32) * qs[:, None]).astype(np.float32) * ds[None, :]
+    for q in range(9):
+        order = np.lexsort((np.arange(300), -full[q]))[:25]
+        assert np.array_equal(ids[q], order)
+        assert np.array_equal(sc[q], full[q][order])
+    assert all(list(ids[q]).index(5) < list(ids[q]).index(17) for q in range(9) if 5 in ids[q] and 17 in ids[q])
