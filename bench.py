@@ -249,6 +249,28 @@ def stage_probes(torch, ahlib):
         out[f"a2_lut_{name}"] = {"nq": w.nq, "blocks": w.blocks, "ms": ms, "GBps": byt / (ms / 1e3) / 1e9,
                                  "frac_of_8TBps": byt / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
         del C
+    # int8 flat search (second workload): 1M documents x 512 dims, 10,000 queries, R = 100,
+    # then the exact fp32 rescore to k = 10; the contraction is int8 MFMA (2 nq n d ops)
+    nd, dd, nqs, Rs = 1_000_000, 512, 10_000, 100
+    Dv = synth.gpu_normal_rows(torch, nd, dd, 6464, torch.float32)
+    Qv = synth.gpu_normal_rows(torch, nqs, dd, 6465, torch.float32)
+    d8, dsc = ahlib.ah_sq8_quantize(Dv)
+    q8, qsc = ahlib.ah_sq8_quantize(Qv)
+    wss = torch.empty(ahlib.ah_sq8_workspace_bytes(nqs, nd), dtype=torch.uint8, device="cuda")
+    ids = torch.empty((nqs, Rs), dtype=torch.int32, device="cuda")
+    scs = torch.empty((nqs, Rs), dtype=torch.float32, device="cuda")
+    ms_q = _time_ms(torch, lambda: ahlib.ah_sq8_quantize(Qv, codes_out=q8, scale_out=qsc), runs=3)
+    ms_s = _time_ms(torch, lambda: ahlib.ah_sq8_scan_topk(q8, qsc, d8, dsc, Rs, ids_out=ids, scores_out=scs,
+                                                          workspace=wss), runs=3)
+    ms_r = _time_ms(torch, lambda: ahlib.ah_reorder_exact(Qv, Dv, ids, 10), runs=3)
+    ops = 2.0 * nqs * nd * dd
+    out["sq8_flat_1m_x_512"] = {"docs": nd, "d": dd, "queries": nqs, "R": Rs, "k": 10,
+                                "quantize_queries_ms": ms_q, "scan_topk_ms": ms_s, "rescore_ms": ms_r,
+                                "queries_per_s": nqs / ((ms_q + ms_s + ms_r) / 1e3),
+                                "scan_int8_TOPs": ops / (ms_s / 1e3) / 1e12,
+                                "scan_frac_of_int8_peak": ops / (ms_s / 1e3) / 1e12 / 5000.0}
+    del Dv, Qv, d8, wss
+    torch.cuda.empty_cache()
     # partition assignment (nearest of 4,000 centroids) for 4M rows of the 20M x 384 shape:
     # the fp32 MFMA contraction (2 n L d FLOP) plus the one-wave selection per row
     w = synth.WORKLOADS["wiki20m"]

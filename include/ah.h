@@ -139,6 +139,39 @@ int ah_scan_topk(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* cod
                  int32_t* cand_scores_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Int8 scalar-quantised flat search (a second workload; page "Incoherence-Aware
+ * Asymmetric Quantization for Retrieval": a robust per-vector int8 scale, and
+ * "A Specialized int8 Retrieval Engine": exact integer dots scaled by both
+ * steps, best k).  The exact rescore of the kept candidates is
+ * ah_reorder_exact.
+ *
+ * ah_sq8_quantize: per row, P = the pct-th percentile of |x| (linear
+ * interpolation between order statistics, every step in float32 as numpy
+ * computes it for a float32 vector), step s = max(P, 1e-8) / 127 (float32),
+ * codes clip(round_half_even(x / s), -127, 127).
+ *   x          float32 [n][d];  pct in [0, 100] (the page uses 99.9)
+ *   codes_out  int8 [n][d];  scale_out float32 [n]
+ * Errors: AH_ERR_SHAPE (n < 0, d < 1, pct outside [0, 100]),
+ * AH_ERR_UNSUPPORTED (d > AH_MAX_DIM), AH_ERR_NULL.
+ *
+ * ah_sq8_scan_topk: for every query the R best documents by
+ * score = ((float)(q8 . d8) * q_scale) * d_scale (float32 products left to
+ * right, the integer dot exact), ties to the lower document id.
+ *   q8 int8 [nq][d], q_scale float32 [nq], d8 int8 [n][d], d_scale float32 [n]
+ *   ids_out int32 [nq][R], scores_out float32 [nq][R] (or NULL)
+ *   workspace >= ah_sq8_workspace_bytes(nq, n) bytes
+ * Errors: AH_ERR_SHAPE (nq < 0, n < 1, d < 1, R < 1, R > n), AH_ERR_UNSUPPORTED
+ * (d % 16 != 0, q8 or d8 not 16-byte aligned, d > AH_MAX_DIM, R > AH_MAX_R,
+ * n >= 2^31), AH_ERR_NULL, AH_ERR_WORKSPACE.
+ */
+int ah_sq8_quantize(const float* x, int64_t n, int32_t d, double pct, int8_t* codes_out, float* scale_out,
+                    void* stream);
+size_t ah_sq8_workspace_bytes(int64_t nq, int64_t n);
+int ah_sq8_scan_topk(const int8_t* q8, const float* q_scale, int64_t nq, const int8_t* d8, const float* d_scale,
+                     int64_t n, int32_t d, int32_t R, int32_t* ids_out, float* scores_out, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Partition assignment (the k-means assignment step behind the partition the
  * first stage searches; ScaNN page, section "Three stages of a search"): each
  * row goes to the centroid nearest to it.

@@ -27,6 +27,7 @@ EXPORTS = (
     "ah_partition_workspace_bytes", "ah_partition_score",
     "ah_build_lut",
     "ah_scan_workspace_bytes", "ah_scan_topk", "ah_scan_topk_timed",
+    "ah_sq8_quantize", "ah_sq8_workspace_bytes", "ah_sq8_scan_topk",
     "ah_assign_workspace_bytes", "ah_assign_leaves",
     "ah_encode", "ah_tiled_codes_bytes", "ah_tile_codes",
     "ah_reorder_exact",
@@ -64,6 +65,12 @@ def lib() -> C.CDLL:
         L.ah_scan_topk_timed.restype = C.c_int
         L.ah_scan_topk_timed.argtypes = [vp, i64, i32, vp, i32, i64, vp, vp, i32, vp, i32, i32, vp, vp, vp, sz, vp,
                                          vp, vp]
+        L.ah_sq8_quantize.restype = C.c_int
+        L.ah_sq8_quantize.argtypes = [vp, i64, i32, C.c_double, vp, vp, vp]
+        L.ah_sq8_workspace_bytes.restype = sz
+        L.ah_sq8_workspace_bytes.argtypes = [i64, i64]
+        L.ah_sq8_scan_topk.restype = C.c_int
+        L.ah_sq8_scan_topk.argtypes = [vp, vp, i64, vp, vp, i64, i32, i32, vp, vp, vp, sz, vp]
         L.ah_assign_workspace_bytes.restype = sz
         L.ah_assign_workspace_bytes.argtypes = [i64, i32]
         L.ah_assign_leaves.restype = C.c_int
@@ -171,6 +178,46 @@ def ah_build_lut(q, codebooks, lut_i8_out=None, scale_out=None, bias_out=None, l
 # ----------------------------------------------------------------------------- steps 3+4
 def ah_scan_workspace_bytes(nq: int, B: int, n: int, L: int, nl: int, R: int) -> int:
     return int(lib().ah_scan_workspace_bytes(nq, B, n, L, nl, R))
+
+
+def ah_sq8_quantize(x, pct=99.9, codes_out=None, scale_out=None, stream=None):
+    """Per-row int8 codes and float32 steps (robust percentile scale)."""
+    x = _dev(x, torch.float32, "x", 2)
+    n, d = x.shape
+    if codes_out is None:
+        codes_out = torch.empty((n, d), dtype=torch.int8, device=x.device)
+    if scale_out is None:
+        scale_out = torch.empty(n, dtype=torch.float32, device=x.device)
+    _dev(codes_out, torch.int8, "codes_out", 2)
+    _dev(scale_out, torch.float32, "scale_out", 1)
+    _check(lib().ah_sq8_quantize(_ptr(x), n, d, float(pct), _ptr(codes_out), _ptr(scale_out), _stream(stream)),
+           "ah_sq8_quantize")
+    return codes_out, scale_out
+
+
+def ah_sq8_workspace_bytes(nq: int, n: int) -> int:
+    return int(lib().ah_sq8_workspace_bytes(nq, n))
+
+
+def ah_sq8_scan_topk(q8, q_scale, d8, d_scale, R, ids_out=None, scores_out=None, workspace=None, stream=None):
+    """Top-R documents per query by ((float)(q8 . d8) * q_scale) * d_scale, ties to the lower id."""
+    q8 = _dev(q8, torch.int8, "q8", 2)
+    d8 = _dev(d8, torch.int8, "d8", 2)
+    q_scale = _dev(q_scale, torch.float32, "q_scale", 1)
+    d_scale = _dev(d_scale, torch.float32, "d_scale", 1)
+    nq, d = q8.shape
+    n = d8.shape[0]
+    if ids_out is None:
+        ids_out = torch.empty((nq, R), dtype=torch.int32, device=q8.device)
+    if scores_out is None:
+        scores_out = torch.empty((nq, R), dtype=torch.float32, device=q8.device)
+    need = ah_sq8_workspace_bytes(nq, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q8.device)
+    _check(lib().ah_sq8_scan_topk(_ptr(q8), _ptr(q_scale), nq, _ptr(d8), _ptr(d_scale), n, d, int(R), _ptr(ids_out),
+                                  _ptr(scores_out), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "ah_sq8_scan_topk")
+    return ids_out, scores_out
 
 
 def ah_assign_workspace_bytes(n: int, L: int) -> int:

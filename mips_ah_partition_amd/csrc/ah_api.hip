@@ -92,6 +92,33 @@ int ah_scan_topk(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* cod
                               cand_ids_out, cand_scores_out, workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
+int ah_sq8_quantize(const float* x, int64_t n, int32_t d, double pct, int8_t* codes_out, float* scale_out,
+                    void* stream) {
+    if (n < 0 || d < 1 || !(pct >= 0.0 && pct <= 100.0)) return AH_ERR_SHAPE;
+    if (d > AH_MAX_DIM) return AH_ERR_UNSUPPORTED;
+    if (n == 0) return AH_OK;
+    if (!x || !codes_out || !scale_out) return AH_ERR_NULL;
+    return hip_status(ah::launch_sq8_quantize(x, n, d, pct, codes_out, scale_out, static_cast<hipStream_t>(stream)));
+}
+
+size_t ah_sq8_workspace_bytes(int64_t nq, int64_t n) {
+    if (nq < 0 || n < 1) return 0;
+    return ah::sq8_workspace_bytes(nq, n);
+}
+
+int ah_sq8_scan_topk(const int8_t* q8, const float* q_scale, int64_t nq, const int8_t* d8, const float* d_scale,
+                     int64_t n, int32_t d, int32_t R, int32_t* ids_out, float* scores_out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    if (nq < 0 || n < 1 || d < 1 || R < 1 || R > n) return AH_ERR_SHAPE;
+    if (d % 16 != 0 || d > AH_MAX_DIM || R > AH_MAX_R || n >= ((int64_t)1 << 31)) return AH_ERR_UNSUPPORTED;
+    if (nq == 0) return AH_OK;
+    if (!q8 || !q_scale || !d8 || !d_scale || !ids_out) return AH_ERR_NULL;
+    if (!a16(q8) || !a16(d8)) return AH_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < ah::sq8_workspace_bytes(nq, n)) return AH_ERR_WORKSPACE;
+    return hip_status(ah::launch_sq8_topk(q8, q_scale, nq, d8, d_scale, n, d, R, ids_out, scores_out, workspace,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 size_t ah_assign_workspace_bytes(int64_t n, int32_t L) {
     if (n < 0 || L < 1) return 0;
     return ah::assign_workspace_bytes(n, L);

@@ -39,6 +39,16 @@ size_t scan_workspace_bytes(int64_t nq, int32_t B, int64_t n, int32_t L, int32_t
 hipError_t launch_scan(const ScanProblem& p, void* ws, size_t ws_bytes, hipStream_t stream,
                        hipEvent_t main_start = nullptr, hipEvent_t main_stop = nullptr);
 
+hipError_t launch_rows_topk(const float* S, int64_t rows, int32_t L, int32_t k, int32_t* ids, float* scores,
+                            hipStream_t stream);
+
+hipError_t launch_sq8_quantize(const float* x, int64_t n, int32_t d, double pct, int8_t* codes, float* scale,
+                               hipStream_t stream);
+size_t sq8_workspace_bytes(int64_t nq, int64_t n);
+hipError_t launch_sq8_topk(const int8_t* q8, const float* qs, int64_t nq, const int8_t* d8, const float* ds,
+                           int64_t n, int32_t d, int32_t R, int32_t* ids, float* scores, void* ws,
+                           hipStream_t stream);
+
 size_t assign_workspace_bytes(int64_t n, int32_t L);
 hipError_t launch_assign(const float* x, int64_t n, int32_t d, const float* cent, int32_t L, int32_t* leaves,
                          float* scores, void* ws, hipStream_t stream);

@@ -571,4 +571,28 @@ hipError_t launch_assign(const float* x, int64_t n, int32_t d, const float* cent
     return hipSuccess;
 }
 
+// The best k columns of each row of a score block [rows][L] by (score desc,
+// column asc): the one-wave selection for L <= kWaveLeaves and k <= kLeafSort,
+// else the workgroup selection.
+hipError_t launch_rows_topk(const float* S, int64_t rows, int32_t L, int32_t k, int32_t* ids, float* scores,
+                            hipStream_t stream) {
+    if (rows == 0) return hipSuccess;
+    if (L <= kWaveLeaves && k <= kLeafSort) {
+        if (L <= 4 * kWave) launch_leaf_wave<4, 1>(S, rows, L, k, ids, scores, 1, stream);
+        else if (L <= 8 * kWave) launch_leaf_wave<8, 1>(S, rows, L, k, ids, scores, 1, stream);
+        else if (L <= 16 * kWave) launch_leaf_wave<16, 1>(S, rows, L, k, ids, scores, 1, stream);
+        else if (L <= 32 * kWave) launch_leaf_wave<32, 1>(S, rows, L, k, ids, scores, 1, stream);
+        else launch_leaf_wave<16, 4>(S, rows, L, k, ids, scores, 1, stream);
+        return hipGetLastError();
+    }
+    int Kp = 1;
+    while (Kp < k) Kp <<= 1;
+    const size_t lds = (size_t)Kp * 8 + (L <= kLeafLds ? (size_t)L * 8 : 0);
+    if (lds > 48 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(leaf_select_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(leaf_select_kernel, dim3((unsigned)rows), dim3(kSelThreads), lds, stream, S, L, k, ids, scores);
+    return hipGetLastError();
+}
+
 }  // namespace ah

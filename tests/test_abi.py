@@ -132,3 +132,24 @@ def test_assign_validation(lib):
     assert lib.ah_assign_leaves(None, 1000, 8, fake, 64, fake, None, fake, need, None) == -1
     assert lib.ah_assign_leaves(fake, 1000, 8, fake, 64, fake, None, fake, need - 1, None) == -4
     assert lib.ah_assign_leaves(None, 0, 8, None, 64, None, None, None, 0, None) == 0
+
+
+def test_sq8_validation(lib):
+    vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    lib.ah_sq8_quantize.argtypes = [vp, i64, i32, C.c_double, vp, vp, vp]
+    lib.ah_sq8_workspace_bytes.restype = sz
+    lib.ah_sq8_workspace_bytes.argtypes = [i64, i64]
+    lib.ah_sq8_scan_topk.argtypes = [vp, vp, i64, vp, vp, i64, i32, i32, vp, vp, vp, sz, vp]
+    fake, odd = vp(4096), vp(4097)  # never dereferenced: every case below fails validation first
+    assert lib.ah_sq8_quantize(fake, 10, 0, 99.9, fake, fake, None) == -2
+    assert lib.ah_sq8_quantize(fake, 10, 8, 100.5, fake, fake, None) == -2
+    assert lib.ah_sq8_quantize(fake, 10, 20000, 99.9, fake, fake, None) == -3
+    assert lib.ah_sq8_quantize(None, 10, 8, 99.9, fake, fake, None) == -1
+    assert lib.ah_sq8_quantize(None, 0, 8, 99.9, None, None, None) == 0
+    need = lib.ah_sq8_workspace_bytes(100, 1000)
+    assert need >= 100 * 1000 * 4
+    assert lib.ah_sq8_scan_topk(fake, fake, 100, fake, fake, 1000, 64, 1001, fake, None, fake, need, None) == -2  # R > n
+    assert lib.ah_sq8_scan_topk(fake, fake, 100, fake, fake, 1000, 40, 10, fake, None, fake, need, None) == -3   # d % 16
+    assert lib.ah_sq8_scan_topk(odd, fake, 100, fake, fake, 1000, 64, 10, fake, None, fake, need, None) == -3    # alignment
+    assert lib.ah_sq8_scan_topk(fake, fake, 100, fake, fake, 1000, 64, 10, fake, None, fake, need - 1, None) == -4
+    assert lib.ah_sq8_scan_topk(fake, None, 100, fake, fake, 1000, 64, 10, fake, None, fake, need, None) == -1

@@ -496,3 +496,41 @@ def test_assign_leaves_parity(gpu, n, d, L, kind):
     # the reported score is x.c - |c|^2/2 of the chosen leaf
     ref = (Xd * Cd[ids]).sum(1) - 0.5 * (Cd[ids] * Cd[ids]).sum(1)
     assert (np.abs(sc - ref) <= TOL * (np.abs(Xd * Cd[ids]).sum(1) + 0.5 * (Cd[ids] * Cd[ids]).sum(1))).all()
+
+
+# ----------------------------------------------------------------------------- int8 flat search (next row 3)
+@pytest.mark.parametrize("n,d,pct,kind", [(300, 512, 99.9, "f"), (200, 7, 99.9, "f"), (100, 1, 99.9, "f"),
+                                          (257, 100, 50.0, "f"), (64, 4096, 100.0, "f"), (90, 33, 0.0, "f"),
+                                          (500, 64, 99.9, "int")])
+def test_sq8_quantize_parity(gpu, n, d, pct, kind):
+    torch, ah = gpu
+    rng = np.random.default_rng(n + d)
+    X = (rng.integers(-4, 5, size=(n, d)) if kind == "int" else rng.standard_normal((n, d))).astype(np.float32)
+    X[::37] = 0.0
+    codes, scale = ah.ah_sq8_quantize(_t(torch, X), pct)
+    torch.cuda.synchronize()
+    o_codes, o_scale = oracle.sq8_quantize(X, pct)
+    assert np.array_equal(_np(scale), o_scale)
+    assert np.array_equal(_np(codes), o_codes)
+
+
+# Stage-chained: the oracle ranks the GPU's own codes and steps.  The page's
+# notebook shape (20,000 x 512, 200 queries, 20-center mixture), ragged tiles,
+# R = n, R above the one-wave selection's limit, duplicate documents.
+@pytest.mark.parametrize("nq,n,d,R", [(200, 20000, 512, 10), (70, 3001, 64, 100), (5, 500, 16, 500),
+                                      (130, 10000, 128, 600), (1, 4097, 32, 64)])
+def test_sq8_topk_parity(gpu, nq, n, d, R):
+    torch, ah = gpu
+    rng = np.random.default_rng(nq + n + d)
+    centers = rng.standard_normal((20, d)).astype(np.float32)
+    D = centers[rng.integers(0, 20, n)] + 0.5 * rng.standard_normal((n, d)).astype(np.float32)
+    D /= np.linalg.norm(D, axis=1, keepdims=True)
+    D[n // 2] = D[3]
+    Q = centers[rng.integers(0, 20, nq)] + 0.5 * rng.standard_normal((nq, d)).astype(np.float32)
+    d8, ds = ah.ah_sq8_quantize(_t(torch, D.astype(np.float32)))
+    q8, qs = ah.ah_sq8_quantize(_t(torch, Q.astype(np.float32)))
+    ids, sc = ah.ah_sq8_scan_topk(q8, qs, d8, ds, R)
+    torch.cuda.synchronize()
+    o_ids, o_sc = oracle.sq8_topk(_np(q8), _np(qs), _np(d8), _np(ds), R)
+    assert np.array_equal(_np(ids), o_ids)
+    assert np.array_equal(_np(sc), o_sc)
