@@ -256,7 +256,7 @@ def stage_probes(torch, ahlib):
     Qv = synth.gpu_normal_rows(torch, nqs, dd, 6465, torch.float32)
     d8, dsc = ahlib.ah_sq8_quantize(Dv)
     q8, qsc = ahlib.ah_sq8_quantize(Qv)
-    wss = torch.empty(ahlib.ah_sq8_workspace_bytes(nqs, nd), dtype=torch.uint8, device="cuda")
+    wss = torch.empty(ahlib.ah_sq8_workspace_bytes(nqs, nd, dd, Rs), dtype=torch.uint8, device="cuda")
     ids = torch.empty((nqs, Rs), dtype=torch.int32, device="cuda")
     scs = torch.empty((nqs, Rs), dtype=torch.float32, device="cuda")
     ms_q = _time_ms(torch, lambda: ahlib.ah_sq8_quantize(Qv, codes_out=q8, scale_out=qsc), runs=3)

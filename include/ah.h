@@ -159,14 +159,14 @@ int ah_scan_topk(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* cod
  * right, the integer dot exact), ties to the lower document id.
  *   q8 int8 [nq][d], q_scale float32 [nq], d8 int8 [n][d], d_scale float32 [n]
  *   ids_out int32 [nq][R], scores_out float32 [nq][R] (or NULL)
- *   workspace >= ah_sq8_workspace_bytes(nq, n) bytes
+ *   workspace >= ah_sq8_workspace_bytes(nq, n, d, R) bytes (0 for invalid sizes)
  * Errors: AH_ERR_SHAPE (nq < 0, n < 1, d < 1, R < 1, R > n), AH_ERR_UNSUPPORTED
  * (d % 16 != 0, q8 or d8 not 16-byte aligned, d > AH_MAX_DIM, R > AH_MAX_R,
  * n >= 2^31), AH_ERR_NULL, AH_ERR_WORKSPACE.
  */
 int ah_sq8_quantize(const float* x, int64_t n, int32_t d, double pct, int8_t* codes_out, float* scale_out,
                     void* stream);
-size_t ah_sq8_workspace_bytes(int64_t nq, int64_t n);
+size_t ah_sq8_workspace_bytes(int64_t nq, int64_t n, int32_t d, int32_t R);
 int ah_sq8_scan_topk(const int8_t* q8, const float* q_scale, int64_t nq, const int8_t* d8, const float* d_scale,
                      int64_t n, int32_t d, int32_t R, int32_t* ids_out, float* scores_out, void* workspace,
                      size_t workspace_bytes, void* stream);

@@ -68,7 +68,7 @@ def lib() -> C.CDLL:
         L.ah_sq8_quantize.restype = C.c_int
         L.ah_sq8_quantize.argtypes = [vp, i64, i32, C.c_double, vp, vp, vp]
         L.ah_sq8_workspace_bytes.restype = sz
-        L.ah_sq8_workspace_bytes.argtypes = [i64, i64]
+        L.ah_sq8_workspace_bytes.argtypes = [i64, i64, i32, i32]
         L.ah_sq8_scan_topk.restype = C.c_int
         L.ah_sq8_scan_topk.argtypes = [vp, vp, i64, vp, vp, i64, i32, i32, vp, vp, vp, sz, vp]
         L.ah_assign_workspace_bytes.restype = sz
@@ -195,8 +195,8 @@ def ah_sq8_quantize(x, pct=99.9, codes_out=None, scale_out=None, stream=None):
     return codes_out, scale_out
 
 
-def ah_sq8_workspace_bytes(nq: int, n: int) -> int:
-    return int(lib().ah_sq8_workspace_bytes(nq, n))
+def ah_sq8_workspace_bytes(nq: int, n: int, d: int, R: int) -> int:
+    return int(lib().ah_sq8_workspace_bytes(nq, n, int(d), int(R)))
 
 
 def ah_sq8_scan_topk(q8, q_scale, d8, d_scale, R, ids_out=None, scores_out=None, workspace=None, stream=None):
@@ -211,7 +211,7 @@ def ah_sq8_scan_topk(q8, q_scale, d8, d_scale, R, ids_out=None, scores_out=None,
         ids_out = torch.empty((nq, R), dtype=torch.int32, device=q8.device)
     if scores_out is None:
         scores_out = torch.empty((nq, R), dtype=torch.float32, device=q8.device)
-    need = ah_sq8_workspace_bytes(nq, n)
+    need = ah_sq8_workspace_bytes(nq, n, d, R)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q8.device)
     _check(lib().ah_sq8_scan_topk(_ptr(q8), _ptr(q_scale), nq, _ptr(d8), _ptr(d_scale), n, d, int(R), _ptr(ids_out),

@@ -101,9 +101,9 @@ int ah_sq8_quantize(const float* x, int64_t n, int32_t d, double pct, int8_t* co
     return hip_status(ah::launch_sq8_quantize(x, n, d, pct, codes_out, scale_out, static_cast<hipStream_t>(stream)));
 }
 
-size_t ah_sq8_workspace_bytes(int64_t nq, int64_t n) {
-    if (nq < 0 || n < 1) return 0;
-    return ah::sq8_workspace_bytes(nq, n);
+size_t ah_sq8_workspace_bytes(int64_t nq, int64_t n, int32_t d, int32_t R) {
+    if (nq < 0 || n < 1 || d < 1 || R < 1) return 0;
+    return ah::sq8_workspace_bytes(nq, n, d, R);
 }
 
 int ah_sq8_scan_topk(const int8_t* q8, const float* q_scale, int64_t nq, const int8_t* d8, const float* d_scale,
@@ -114,7 +114,7 @@ int ah_sq8_scan_topk(const int8_t* q8, const float* q_scale, int64_t nq, const i
     if (nq == 0) return AH_OK;
     if (!q8 || !q_scale || !d8 || !d_scale || !ids_out) return AH_ERR_NULL;
     if (!a16(q8) || !a16(d8)) return AH_ERR_UNSUPPORTED;
-    if (!workspace || workspace_bytes < ah::sq8_workspace_bytes(nq, n)) return AH_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < ah::sq8_workspace_bytes(nq, n, d, R)) return AH_ERR_WORKSPACE;
     return hip_status(ah::launch_sq8_topk(q8, q_scale, nq, d8, d_scale, n, d, R, ids_out, scores_out, workspace,
                                           static_cast<hipStream_t>(stream)));
 }

@@ -41,10 +41,15 @@ hipError_t launch_scan(const ScanProblem& p, void* ws, size_t ws_bytes, hipStrea
 
 hipError_t launch_rows_topk(const float* S, int64_t rows, int32_t L, int32_t k, int32_t* ids, float* scores,
                             hipStream_t stream);
+// Best k of each row of a candidate list: row r holds rowcnt[r] scores S[r * cap
+// + j] with ids idmap[r * cap + j]; rows with rowcnt[r] > cap are skipped.
+// cap <= 4096, k <= 512.
+hipError_t launch_list_topk(const float* S, const int32_t* idmap, const uint32_t* rowcnt, int64_t rows, int32_t cap,
+                            int32_t k, int32_t* ids, float* scores, hipStream_t stream);
 
 hipError_t launch_sq8_quantize(const float* x, int64_t n, int32_t d, double pct, int8_t* codes, float* scale,
                                hipStream_t stream);
-size_t sq8_workspace_bytes(int64_t nq, int64_t n);
+size_t sq8_workspace_bytes(int64_t nq, int64_t n, int32_t d, int32_t R);
 hipError_t launch_sq8_topk(const int8_t* q8, const float* qs, int64_t nq, const int8_t* d8, const float* ds,
                            int64_t n, int32_t d, int32_t R, int32_t* ids, float* scores, void* ws,
                            hipStream_t stream);

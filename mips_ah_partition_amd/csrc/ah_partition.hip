@@ -244,12 +244,17 @@ __device__ __forceinline__ void wave_sort_emit(const uint64_t* srt, int nl, int 
     }
 }
 
-template <int kPer, int kWv>
-__global__ __launch_bounds__(kLeafQ * kWave, kPer <= 16 ? 5 : 3) void leaf_select_wave_kernel(const float* __restrict__ S, int64_t nq,
+// kMap: the row is a candidate list, its element j carrying the id idmap[row * L
+// + j] (unique within the row) and only the first rowcnt[row] elements being
+// real; a row with more than L of them is skipped (left to the caller).
+template <int kPer, int kWv, bool kMap = false>
+__global__ __launch_bounds__(kLeafQ * kWave, kMap ? 2 : (kPer <= 16 ? 5 : 3)) void leaf_select_wave_kernel(const float* __restrict__ S, int64_t nq,
                                                                           int32_t L, int32_t nl,
                                                                           int32_t* __restrict__ leaves,
                                                                           float* __restrict__ scores, int32_t nsplit,
-                                                                          const float* __restrict__ bias) {
+                                                                          const float* __restrict__ bias,
+                                                                          const int32_t* __restrict__ idmap = nullptr,
+                                                                          const uint32_t* __restrict__ rowcnt = nullptr) {
     constexpr int kQs = kLeafQ / kWv;  // queries per workgroup
     static_assert(kWv == 1 || kQs == 1, "a query spread over waves fills its workgroup");
     __shared__ uint32_t hist_all[kQs][256];
@@ -264,9 +269,15 @@ __global__ __launch_bounds__(kLeafQ * kWave, kPer <= 16 ? 5 : 3) void leaf_selec
     uint64_t* srt = srt_all[qs];
     uint32_t(*red)[2] = red_all[qs];
     const float* s = S + qi * L;
+    int32_t Lr = L;  // real elements in the row
+    if constexpr (kMap) {
+        const uint32_t c = rowcnt[qi];
+        if (c > (uint32_t)L) return;  // every wave of the query leaves (kQs == 1 when kWv > 1)
+        Lr = (int32_t)c;
+    }
     // element i = (j * kWv + wq) * 64 + lane
     const int first = wq * kWave + lane;
-    const int nv = first < L ? (L - first + kWv * kWave - 1) / (kWv * kWave) : 0;  // o[0 .. nv) are real
+    const int nv = first < Lr ? (Lr - first + kWv * kWave - 1) / (kWv * kWave) : 0;  // o[0 .. nv) are real
     // the score is the sum of the K splits' partial planes, in split order
     float sv[kPer];
 #pragma unroll
@@ -285,6 +296,12 @@ __global__ __launch_bounds__(kLeafQ * kWave, kPer <= 16 ? 5 : 3) void leaf_selec
     uint32_t o[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) o[j] = j < nv ? float_order(sv[j]) : 0u;
+    uint32_t idv[kMap ? kPer : 1];
+    if constexpr (kMap) {
+        const int32_t* im = idmap + qi * L;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) idv[j] = j < nv ? (uint32_t)im[j * kWv * kWave + first] : 0u;
+    }
     auto sync = [] {
         if constexpr (kWv == 1) {
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -335,11 +352,14 @@ __global__ __launch_bounds__(kLeafQ * kWave, kPer <= 16 ? 5 : 3) void leaf_selec
         range_of(mn, mx, omin, omax);
     }
     auto key = [&](int j) -> uint64_t {
-        return ((uint64_t)o[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(j * kWv * kWave + first));
+        uint32_t id;
+        if constexpr (kMap) id = idv[j];
+        else id = (uint32_t)(j * kWv * kWave + first);
+        return ((uint64_t)o[j] << 32) | (uint64_t)(0xFFFFFFFFu - id);
     };
     int need = nl;   // still to pick at or below the current bucket
     int above = 0;   // keys known to be selected (above the bucket)
-    int inb = L;     // keys in the current bucket
+    int inb = Lr;    // keys in the current bucket
     const int Pt = next_pow2(nl > kWave ? nl : kWave);  // candidates to reach: one sort of Pt keys
     // First pass, on the score values: 256 equal-width buckets over [fmin, fmax]
     // (the bucket is non-decreasing in the score, so a bucket's members are
@@ -463,7 +483,8 @@ static void launch_leaf_wave(const float* S, int64_t nq, int32_t L, int32_t nl, 
                              int32_t nsplit, hipStream_t stream, const float* bias = nullptr) {
     constexpr int kQs = kLeafQ / kWv;
     hipLaunchKernelGGL((leaf_select_wave_kernel<kPer, kWv>), dim3((unsigned)((nq + kQs - 1) / kQs)),
-                       dim3(kLeafQ * kWave), 0, stream, S, nq, L, nl, leaves, scores, nsplit, bias);
+                       dim3(kLeafQ * kWave), 0, stream, S, nq, L, nl, leaves, scores, nsplit, bias, nullptr,
+                       nullptr);
 }
 
 // K splits of the contraction: when the tile grid has fewer than 256 tiles (one
@@ -574,6 +595,22 @@ hipError_t launch_assign(const float* x, int64_t n, int32_t d, const float* cent
 // The best k columns of each row of a score block [rows][L] by (score desc,
 // column asc): the one-wave selection for L <= kWaveLeaves and k <= kLeafSort,
 // else the workgroup selection.
+hipError_t launch_list_topk(const float* S, const int32_t* idmap, const uint32_t* rowcnt, int64_t rows, int32_t cap,
+                            int32_t k, int32_t* ids, float* scores, hipStream_t stream) {
+    if (rows == 0) return hipSuccess;
+    if (cap > kWaveLeaves || k > kLeafSort) return hipErrorInvalidValue;
+#define AH_LIST(P, W)                                                                                          \
+    hipLaunchKernelGGL((leaf_select_wave_kernel<P, W, true>), dim3((unsigned)((rows + kLeafQ / W - 1) / (kLeafQ / W))), \
+                       dim3(kLeafQ * kWave), 0, stream, S, rows, cap, k, ids, scores, 1, nullptr, idmap, rowcnt)
+    if (cap <= 4 * kWave) AH_LIST(4, 1);
+    else if (cap <= 8 * kWave) AH_LIST(8, 1);
+    else if (cap <= 16 * kWave) AH_LIST(16, 1);
+    else if (cap <= 32 * kWave) AH_LIST(32, 1);
+    else AH_LIST(16, 4);
+#undef AH_LIST
+    return hipGetLastError();
+}
+
 hipError_t launch_rows_topk(const float* S, int64_t rows, int32_t L, int32_t k, int32_t* ids, float* scores,
                             hipStream_t stream) {
     if (rows == 0) return hipSuccess;

@@ -29,6 +29,8 @@
 #include "ah_device.hpp"
 #include "ah_kernels.hpp"
 
+#include <limits.h>
+
 namespace ah {
 
 // ------------------------------------------------------------------ quantisation
@@ -140,17 +142,55 @@ hipError_t launch_sq8_quantize(const float* x, int64_t n, int32_t d, double pct,
 constexpr int kSqThreads = 256;
 constexpr int kSqDocs = 256;    // documents per workgroup (64 per wave)
 constexpr int kSqQueries = 64;  // queries per workgroup
+constexpr int kSqGroup = 64;    // documents per group (one wave's rows) for the threshold
+constexpr int kSqCap = 4096;    // candidates kept per query
+constexpr int kSqFb = 8;        // fallback workgroups
+constexpr int kSqMaxSel = 512;  // largest R the candidate path selects
 
+enum SqMode { kSqWriteS = 0, kSqGroupMax = 1, kSqEmit = 2 };
+
+struct SqOut {
+    float* S;              // kSqWriteS: [nq][n]
+    float* gmax;           // kSqGroupMax: [nq][G0], group j = documents of 64-row tile j * gstep
+    int32_t G0;
+    int64_t gstep;
+    const float* tau;      // kSqEmit: the query's bound at tau[q * tau_stride + tau_stride - 1]
+    int32_t tau_stride;
+    uint32_t* cnt;         // kSqEmit: [nq] candidates appended
+    float* cs;             // kSqEmit: [nq][cap] scores
+    int32_t* ci;           //          [nq][cap] document ids
+    int32_t cap;
+};
+
+// The rescaled score of one (query, document) pair: the same expression in
+// every mode, so the threshold and the candidates agree bit for bit.
+__device__ __forceinline__ float sq8_score(int32_t dot, float sq, float sd) {
+#pragma clang fp contract(off)
+    return ((float)dot * sq) * sd;
+}
+
+// Generic form (any d that is a multiple of 16): each wave computes 64
+// documents x 64 queries with operands loaded straight from global memory.
+template <int kMode>
 __global__ __launch_bounds__(kSqThreads) void sq8_scores_kernel(const int8_t* __restrict__ q8,
                                                                 const float* __restrict__ qs, int64_t nq,
                                                                 const int8_t* __restrict__ d8,
                                                                 const float* __restrict__ ds, int64_t n, int32_t d,
-                                                                float* __restrict__ S) {
-#pragma clang fp contract(off)
+                                                                int64_t ndt, SqOut o) {
     const int w = threadIdx.x / kWave, lane = lane_id();
-    const int64_t ndt = (n + kSqDocs - 1) / kSqDocs;  // consecutive workgroups share a query tile
+    // consecutive workgroups share a query tile; ndt doc tiles per query tile
     const int64_t q0 = ((int64_t)blockIdx.x / ndt) * kSqQueries;
-    const int64_t doc0 = ((int64_t)blockIdx.x % ndt) * kSqDocs + 64 * w;
+    const int64_t dt = (int64_t)blockIdx.x % ndt;
+    int64_t doc0;
+    int32_t grp = 0;
+    if constexpr (kMode == kSqGroupMax) {
+        grp = (int32_t)(dt * 4 + w);
+        if (grp >= o.G0) return;  // whole waves; no barrier in this kernel
+        doc0 = (int64_t)grp * o.gstep * kSqGroup;
+    } else {
+        doc0 = dt * kSqDocs + 64 * w;
+        if (doc0 >= n) return;
+    }
     const int r16 = lane & 15, g = lane >> 4;
     v4i acc[4][4];
 #pragma unroll
@@ -181,46 +221,509 @@ __global__ __launch_bounds__(kSqThreads) void sq8_scores_kernel(const int8_t* __
 #pragma unroll
             for (int t = 0; t < 4; ++t) acc[m][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[m], b[t], acc[m][t], 0, 0, 0);
     }
-    // D[doc][query]: lane holds documents 4 g + i of query column r16
+    // D[doc][query]: lane holds documents 16 m + 4 g + i of query column 16 t + r16
+    float sdv[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t doc = doc0 + 16 * m + 4 * g + i;
+            sdv[m][i] = ds[doc < n ? doc : n - 1];
+        }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int64_t qq = q0 + 16 * t + r16;
-        if (qq >= nq) continue;
-        const float sq = qs[qq];
+        const bool qok = qq < nq;
+        const float sq = qs[qok ? qq : nq - 1];
+        if constexpr (kMode == kSqWriteS) {
+            if (!qok) continue;
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t doc = doc0 + 16 * m + 4 * g + i;
-                if (doc < n) S[qq * n + doc] = ((float)acc[m][t][i] * sq) * ds[doc];
-            }
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t doc = doc0 + 16 * m + 4 * g + i;
+                    if (doc < n) o.S[qq * n + doc] = sq8_score(acc[m][t][i], sq, sdv[m][i]);
+                }
+        } else if constexpr (kMode == kSqGroupMax) {
+            float mx = -__builtin_huge_valf();
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t doc = doc0 + 16 * m + 4 * g + i;
+                    const float v = sq8_score(acc[m][t][i], sq, sdv[m][i]);
+                    if (doc < n && v > mx) mx = v;
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));  // the four lanes of a query column
+            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+            if (g == 0 && qok) o.gmax[qq * o.G0 + grp] = mx;
+        } else {
+            if (!qok) continue;
+            const float tq = o.tau[qq * o.tau_stride + o.tau_stride - 1];
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t doc = doc0 + 16 * m + 4 * g + i;
+                    const float v = sq8_score(acc[m][t][i], sq, sdv[m][i]);
+                    if (doc < n && v >= tq) {
+                        const uint32_t pos = atomicAdd(&o.cnt[qq], 1u);
+                        if (pos < (uint32_t)o.cap) {
+                            o.cs[qq * o.cap + pos] = v;
+                            o.ci[qq * o.cap + pos] = (int32_t)doc;
+                        }
+                    }
+                }
+        }
     }
 }
 
-static int64_t sq8_chunk(int64_t nq, int64_t n) {
-    int64_t c = ((int64_t)1 << 28) / (n > 0 ? n : 1);  // score block up to 1 GiB
-    c = c < kSqQueries ? kSqQueries : (c / kSqQueries) * kSqQueries;
-    return c < nq ? c : (nq > 0 ? nq : 1);
+// Document-stationary form for d <= 64 KS: each wave keeps its 48 documents'
+// codes for the whole K in registers (KS k-steps x 3 row groups x 16 bytes per
+// lane, loaded once), and the workgroup (8 waves, two per SIMD, so one wave's
+// epilogue overlaps the other's matrix work) streams blocks of 64 queries
+// through LDS, double-buffered, rows padded by 16 bytes so the 16 lanes of a
+// row group read 16 different bank groups.  Per block a wave issues 12 KS
+// MFMAs and reads the block's 64 x 64 KS bytes from LDS once (96 int8 ops per
+// LDS byte).  Workgroup x covers 384 documents (or, for the group maxima,
+// eight sampled groups of 48) and query blocks [qb0, qb1) of its split.
+constexpr int kDsQB = 64;                  // queries per block
+constexpr int kDsM = 3;                    // 16-row groups per wave
+constexpr int kDsW = 8;                    // waves per workgroup
+constexpr int kDsRows = 16 * kDsM;         // documents per wave (= rows per threshold group)
+constexpr int kDsThreads = kDsW * kWave;   // 512
+constexpr int kDsDocs = kDsRows * kDsW;    // documents per workgroup
+constexpr int kDsLog = 256;                // candidate log entries per wave
+
+__device__ __forceinline__ void wave_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
 }
 
-size_t sq8_workspace_bytes(int64_t nq, int64_t n) { return (size_t)sq8_chunk(nq, n) * (size_t)n * 4 + 256; }
+// A block's staging: rows x (4 KS) 16-byte chunks, thread tid taking chunks
+// tid + 512 j (chunks past d re-read the row's last chunk: those k meet zero
+// document codes), and the block's 64 query steps and bounds (threads 0..127).
+template <int KS>
+struct DsStage {
+    static constexpr int kPer = (64 * 4 * KS + kDsThreads - 1) / kDsThreads;
+    v4i v[kPer];
+    float meta;
+};
+template <int KS, int kMode>
+__device__ __forceinline__ void ds_stage_load(const int8_t* __restrict__ q8, const float* __restrict__ qs,
+                                              const SqOut& o, int64_t nq, int32_t d, int64_t qb, int tid,
+                                              DsStage<KS>& st) {
+#pragma unroll
+    for (int j = 0; j < DsStage<KS>::kPer; ++j) {
+        int c = tid + kDsThreads * j;
+        c = c < 64 * 4 * KS ? c : 64 * 4 * KS - 1;  // KS = 1: the second half re-reads the last chunk
+        const int row = c / (4 * KS), col = c % (4 * KS);
+        int64_t q = qb * kDsQB + row;
+        q = q < nq ? q : nq - 1;
+        const int off = col * 16 < d ? col * 16 : d - 16;
+        st.v[j] = *reinterpret_cast<const v4i*>(q8 + q * d + off);
+    }
+    int64_t q = qb * kDsQB + (tid & 63);
+    q = q < nq ? q : nq - 1;
+    // one unconditional load per thread (threads 64..127 take the bound when there is one)
+    const float* src = qs + q;
+    if (kMode == kSqEmit && tid >= 64 && tid < 128) src = o.tau + q * o.tau_stride + o.tau_stride - 1;
+    st.meta = *src;
+}
+template <int KS>
+__device__ __forceinline__ void ds_stage_store(int8_t* buf, float* meta, int tid, const DsStage<KS>& st) {
+    constexpr int kRow = KS * 64 + 16;
+#pragma unroll
+    for (int j = 0; j < DsStage<KS>::kPer; ++j) {
+        const int c = tid + kDsThreads * j;
+        const int row = c / (4 * KS), col = c % (4 * KS);
+        if (c < 64 * 4 * KS) *reinterpret_cast<v4i*>(buf + row * kRow + col * 16) = st.v[j];
+    }
+    if (tid < 128) meta[tid] = st.meta;
+}
+
+template <int KS, int kMode>
+__global__ __launch_bounds__(kDsThreads, 1) void sq8_dstat_kernel(const int8_t* __restrict__ q8,
+                                                                   const float* __restrict__ qs, int64_t nq,
+                                                                   const int8_t* __restrict__ d8,
+                                                                   const float* __restrict__ ds, int64_t n, int32_t d,
+                                                                   int64_t ndt, int64_t qb_per, SqOut o) {
+    constexpr int kRow = KS * 64 + 16;
+    constexpr int kLogN = kMode == kSqEmit ? kDsLog : 1;
+    __shared__ __align__(16) int8_t qbuf[2][kDsQB * kRow];
+    __shared__ float qmeta[2][128];  // [0, 64): query steps, [64, 128): bounds
+    // candidates found by each wave, appended to the global lists in batches
+    __shared__ int32_t logq[kDsW][kLogN], logd[kDsW][kLogN];
+    __shared__ float logs[kDsW][kLogN];
+    __shared__ uint32_t logn[kDsW];
+    const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+    const int r16 = lane & 15, g = lane >> 4;
+    const int64_t dt = (int64_t)blockIdx.x % ndt;
+    const int64_t nqb = (nq + kDsQB - 1) / kDsQB;
+    const int64_t qb0 = ((int64_t)blockIdx.x / ndt) * qb_per;
+    const int64_t qb1 = qb0 + qb_per < nqb ? qb0 + qb_per : nqb;
+    if (qb0 >= qb1) return;  // the whole workgroup
+    // this wave's 48 documents; a wave with none still stages and meets the barriers
+    int64_t doc0;
+    int32_t grp = 0;
+    bool active;
+    if constexpr (kMode == kSqGroupMax) {
+        grp = (int32_t)(dt * kDsW + w);
+        active = grp < o.G0;
+        doc0 = active ? (int64_t)grp * o.gstep * kDsRows : 0;
+    } else {
+        doc0 = dt * kDsDocs + kDsRows * w;
+        active = doc0 < n;
+        doc0 = active ? doc0 : 0;
+    }
+    DsStage<KS> st;
+    ds_stage_load<KS, kMode>(q8, qs, o, nq, d, qb0, tid, st);
+    v4i a[KS][kDsM];
+#pragma unroll
+    for (int m = 0; m < kDsM; ++m) {
+        int64_t r = doc0 + 16 * m + r16;
+        r = r < n ? r : n - 1;  // rows past the end read the last row; their results are dropped
+        const int8_t* row = d8 + r * d;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int kk = ks * 64 + 16 * g;
+            a[ks][m] = kk < d ? *reinterpret_cast<const v4i*>(row + kk) : v4i{0, 0, 0, 0};
+        }
+    }
+    float sdv[kDsM][4];
+    float sdmax = 0.f;  // the wave's largest document step (for the candidate pre-filter)
+#pragma unroll
+    for (int m = 0; m < kDsM; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t doc = doc0 + 16 * m + 4 * g + i;
+            sdv[m][i] = ds[doc < n ? doc : n - 1];
+            sdmax = fmaxf(sdmax, sdv[m][i]);
+        }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) sdmax = fmaxf(sdmax, __shfl_xor(sdmax, off, kWave));
+    // rows of this wave that are real: local index 16 m + 4 g + i < nloc
+    const int32_t nloc = n - doc0 < kDsRows ? (int32_t)(n - doc0) : kDsRows;
+    ds_stage_store<KS>(qbuf[0], qmeta[0], tid, st);
+    if (lane == 0) logn[w] = 0;
+    // nothing is left in flight at the loop's entry, so the only memory waits
+    // inside the loop are for the next block's staging
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // the wave's log: appends to the query's global list, one atomic per lane
+    auto flush = [&](uint32_t cnt) {
+        wave_fence();
+        for (uint32_t e = lane; e < cnt; e += kWave) {
+            const int32_t qq = logq[w][e];
+            const uint32_t pos = atomicAdd(&o.cnt[qq], 1u);
+            if (pos < (uint32_t)o.cap) {
+                o.cs[(int64_t)qq * o.cap + pos] = logs[w][e];
+                o.ci[(int64_t)qq * o.cap + pos] = logd[w][e];
+            }
+        }
+        wave_fence();
+        if (lane == 0) logn[w] = 0;
+        wave_fence();
+    };
+    for (int64_t qb = qb0; qb < qb1; ++qb) {
+        const int buf = (int)((qb - qb0) & 1);
+        const bool more = qb + 1 < qb1;
+        if (more) ds_stage_load<KS, kMode>(q8, qs, o, nq, d, qb + 1, tid, st);  // in flight during the block
+        v4i acc[kDsM][4];
+#pragma unroll
+        for (int m = 0; m < kDsM; ++m)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[m][t] = v4i{0, 0, 0, 0};
+        const int8_t* qb_lds = qbuf[buf] + r16 * kRow + 16 * g;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            v4i b[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) b[t] = *reinterpret_cast<const v4i*>(qb_lds + 16 * t * kRow + ks * 64);
+#pragma unroll
+            for (int m = 0; m < kDsM; ++m)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    acc[m][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[ks][m], b[t], acc[m][t], 0, 0, 0);
+        }
+        // the next block goes to the other buffer now (its loads have had the
+        // whole block to arrive; the previous block's stores are long done)
+        if (more) ds_stage_store<KS>(qbuf[buf ^ 1], qmeta[buf ^ 1], tid, st);
+        // lane holds documents 16 m + 4 g + i of query column 16 t + r16
+        if (active) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int32_t qloc = (int32_t)(nq - qb * kDsQB) - 16 * t;  // query column real if r16 < qloc
+                const bool qok = r16 < qloc;
+                const int64_t qq = qb * kDsQB + 16 * t + r16;
+                const float sq = qmeta[buf][16 * t + r16];
+                if constexpr (kMode == kSqWriteS) {
+                    if (!qok) continue;
+#pragma unroll
+                    for (int m = 0; m < kDsM; ++m)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (16 * m + 4 * g + i < nloc)
+                                o.S[qq * n + doc0 + 16 * m + 4 * g + i] = sq8_score(acc[m][t][i], sq, sdv[m][i]);
+                } else if constexpr (kMode == kSqGroupMax) {
+                    // the group's best score, exactly (rows past the end are skipped)
+                    float mx = -__builtin_huge_valf();
+                    if (nloc == kDsRows) {
+#pragma unroll
+                        for (int m = 0; m < kDsM; ++m)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sq8_score(acc[m][t][i], sq, sdv[m][i]));
+                    } else {
+#pragma unroll
+                        for (int m = 0; m < kDsM; ++m)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const float v = sq8_score(acc[m][t][i], sq, sdv[m][i]);
+                                mx = 16 * m + 4 * g + i < nloc && v > mx ? v : mx;
+                            }
+                    }
+                    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+                    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+                    if (g == 0 && qok) o.gmax[qq * o.G0 + grp] = mx;
+                } else {
+                    if (!qok) continue;
+                    const float tq = qmeta[buf][64 + 16 * t + r16];
+                    // pre-filter: the exact score is within (1 + 2^-24)^3 of acc sq sd and
+                    // fl(fl(acc sd) sq) within (1 - 2^-24)^3 of it, so no score of the lane's
+                    // column reaches tq > 0 unless max_e fl(acc_e sd_e) * sq >= tq (1 - 2^-20)
+                    if (tq > 0.f) {
+                        float ym = -__builtin_huge_valf();
+#pragma unroll
+                        for (int m = 0; m < kDsM; ++m)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) ym = fmaxf(ym, (float)acc[m][t][i] * sdv[m][i]);
+                        if (ym * sq < tq * 0.99999905f) continue;
+                    }
+#pragma unroll
+                    for (int m = 0; m < kDsM; ++m)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int32_t li = 16 * m + 4 * g + i;
+                            const float v = sq8_score(acc[m][t][i], sq, sdv[m][i]);
+                            if (li < nloc && v >= tq) {
+                                const int64_t doc = doc0 + li;
+                                const uint32_t p = atomicAdd(&logn[w], 1u);
+                                if (p < (uint32_t)kDsLog) {
+                                    logq[w][p] = (int32_t)qq;
+                                    logd[w][p] = (int32_t)doc;
+                                    logs[w][p] = v;
+                                } else {  // the log is full (many ties at the bound): append directly
+                                    const uint32_t pos = atomicAdd(&o.cnt[qq], 1u);
+                                    if (pos < (uint32_t)o.cap) {
+                                        o.cs[qq * o.cap + pos] = v;
+                                        o.ci[qq * o.cap + pos] = (int32_t)doc;
+                                    }
+                                }
+                            }
+                        }
+                }
+            }
+        }
+        if constexpr (kMode == kSqEmit) {
+            wave_fence();
+            uint32_t c = logn[w];
+            c = c < (uint32_t)kDsLog ? c : (uint32_t)kDsLog;
+            if (c > (uint32_t)(kDsLog / 2) || (!more && c > 0)) flush(c);
+        }
+        __syncthreads();
+    }
+}
+
+__global__ void sq8_zero_kernel(uint32_t* p, int64_t count) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) p[i] = 0;
+}
+
+// A query whose candidates overflowed the list (many documents tied at its
+// bound) is redone exactly: every document's score into a private slot, then
+// the workgroup selection.  Workgroup b takes queries b, b + kSqFb, ...
+struct SlotKeys {
+    const float* s;
+    __device__ uint64_t operator()(int64_t i) const { return float_key(s[i], (int32_t)i); }
+};
+
+__global__ __launch_bounds__(kSqThreads) void sq8_fallback_kernel(const int8_t* __restrict__ q8,
+                                                                  const float* __restrict__ qs, int64_t nq,
+                                                                  const int8_t* __restrict__ d8,
+                                                                  const float* __restrict__ ds, int64_t n, int32_t d,
+                                                                  int32_t R, const uint32_t* __restrict__ cnt,
+                                                                  int32_t cap, float* __restrict__ slots,
+                                                                  int32_t* __restrict__ ids, float* __restrict__ scores) {
+    __shared__ SelectShared sh;
+    __shared__ uint64_t sel[kSqMaxSel];
+    float* slot = slots + (int64_t)blockIdx.x * n;
+    const int tid = threadIdx.x;
+    for (int64_t q = blockIdx.x; q < nq; q += gridDim.x) {
+        if (cnt[q] <= (uint32_t)cap) continue;  // the same value for every thread
+        const int8_t* qr = q8 + q * d;
+        const float sq = qs[q];
+        for (int64_t i = tid; i < n; i += kSqThreads) {
+            const int8_t* dr = d8 + i * d;
+            int32_t dot = 0;
+            for (int k = 0; k < d; k += 16) {
+                const v4i a = *reinterpret_cast<const v4i*>(qr + k);
+                const v4i b = *reinterpret_cast<const v4i*>(dr + k);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dot = __builtin_amdgcn_sdot4(a[j], b[j], dot, false);
+            }
+            slot[i] = sq8_score(dot, sq, ds[i]);
+        }
+        __syncthreads();
+        const int m = wg_select_topk<kSqThreads>(SlotKeys{slot}, n, R, sh, sel);
+        for (int r = tid; r < R; r += kSqThreads) {
+            ids[q * R + r] = r < m ? key_id(sel[r]) : -1;
+            if (scores) scores[q * R + r] = r < m ? key_float_score(sel[r]) : -__builtin_huge_valf();
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------ host side
+// Two ways to the top R:
+//  * direct (small n, R above kSqMaxSel, or fewer 64-row groups than R): the
+//    score block of a chunk of queries, then the row selection;
+//  * candidate path: (1) scores of G0 sampled 64-row groups (every gstep-th),
+//    keeping each group's maximum; the R-th largest maximum is a lower bound on
+//    the query's R-th best score, as R distinct documents reach it; (2) all
+//    scores again, appending those at or above the bound to the query's list;
+//    (3) the one-wave selection of the list; (4) the exact fallback for lists
+//    that overflowed.  The sample is sized so that about 512 documents per
+//    query pass the bound for scores in random order.
+struct SqPlan {
+    bool direct;
+    int64_t chunk;  // queries per pass
+    int32_t G0;
+    int64_t gstep;
+    size_t off_gmax, off_tid, off_tsc, off_cnt, off_cs, off_ci, off_slots, total;
+};
+
+static size_t sq_align(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// rows per threshold group: one wave's documents in the scoring kernel used for d
+static int32_t sq8_group_rows(int32_t d) { return d <= 8 * 64 ? kDsRows : kSqGroup; }
+
+static SqPlan sq8_plan(int64_t nq, int64_t n, int32_t d, int32_t R) {
+    SqPlan p{};
+    const int32_t gsz = sq8_group_rows(d);
+    const int64_t ngroups = (n + gsz - 1) / gsz;
+    p.direct = n <= 4096 || R > kSqMaxSel || ngroups < R;
+    const int64_t q1 = nq > 0 ? nq : 1;
+    if (p.direct) {
+        int64_t c = ((int64_t)1 << 28) / n;  // score block up to 1 GiB
+        c = c < kSqQueries ? kSqQueries : (c / kSqQueries) * kSqQueries;
+        p.chunk = c < q1 ? c : q1;
+        p.total = (size_t)p.chunk * (size_t)n * 4 + 256;
+        return p;
+    }
+    int64_t g0 = (ngroups * R + 511) / 512;
+    g0 = g0 < R ? R : g0;
+    g0 = g0 > ngroups ? ngroups : g0;
+    p.G0 = (int32_t)g0;
+    p.gstep = ngroups / g0;
+    const size_t per_q = (size_t)g0 * 4 + (size_t)R * 8 + 4 + (size_t)kSqCap * 8;
+    int64_t c = (int64_t)(((size_t)1 << 29) / per_q);  // lists and maxima up to 512 MiB per pass
+    c = c < kSqQueries ? kSqQueries : (c / kSqQueries) * kSqQueries;
+    p.chunk = c < q1 ? c : q1;
+    size_t o = 0;
+    p.off_gmax = o;  o = sq_align(o + (size_t)p.chunk * g0 * 4);
+    p.off_tid = o;   o = sq_align(o + (size_t)p.chunk * R * 4);
+    p.off_tsc = o;   o = sq_align(o + (size_t)p.chunk * R * 4);
+    p.off_cnt = o;   o = sq_align(o + (size_t)p.chunk * 4);
+    p.off_cs = o;    o = sq_align(o + (size_t)p.chunk * kSqCap * 4);
+    p.off_ci = o;    o = sq_align(o + (size_t)p.chunk * kSqCap * 4);
+    p.off_slots = o; o = sq_align(o + (size_t)kSqFb * (size_t)n * 4);
+    p.total = o;
+    return p;
+}
+
+size_t sq8_workspace_bytes(int64_t nq, int64_t n, int32_t d, int32_t R) { return sq8_plan(nq, n, d, R).total; }
+
+// One scoring pass over `units` work units along the documents (256-document
+// tiles, or for the group maxima four sampled groups per unit).
+template <int kMode, int KS>
+static void launch_dstat(const int8_t* q8, const float* qs, int64_t m, const int8_t* d8, const float* ds, int64_t n,
+                         int32_t d, const SqOut& o, hipStream_t stream) {
+    const int64_t units = kMode == kSqGroupMax ? (o.G0 + kDsW - 1) / kDsW : (n + kDsDocs - 1) / kDsDocs;
+    const int64_t nqb = (m + kDsQB - 1) / kDsQB;
+    int64_t split = (1024 + units - 1) / units;  // about 1024 workgroups
+    const int64_t most = nqb / 4 > 1 ? nqb / 4 : 1;  // at least four query blocks per workgroup
+    split = split < most ? split : most;
+    const int64_t per = (nqb + split - 1) / split;
+    split = (nqb + per - 1) / per;
+    hipLaunchKernelGGL((sq8_dstat_kernel<KS, kMode>), dim3((unsigned)(units * split)), dim3(kDsThreads), 0, stream,
+                       q8, qs, m, d8, ds, n, d, units, per, o);
+}
+
+template <int kMode>
+static hipError_t launch_scores(const int8_t* q8, const float* qs, int64_t m, const int8_t* d8, const float* ds,
+                                int64_t n, int32_t d, const SqOut& o, hipStream_t stream) {
+    switch ((d + 63) / 64) {
+        case 1: launch_dstat<kMode, 1>(q8, qs, m, d8, ds, n, d, o, stream); break;
+        case 2: launch_dstat<kMode, 2>(q8, qs, m, d8, ds, n, d, o, stream); break;
+        case 3: launch_dstat<kMode, 3>(q8, qs, m, d8, ds, n, d, o, stream); break;
+        case 4: launch_dstat<kMode, 4>(q8, qs, m, d8, ds, n, d, o, stream); break;
+        case 5: launch_dstat<kMode, 5>(q8, qs, m, d8, ds, n, d, o, stream); break;
+        case 6: launch_dstat<kMode, 6>(q8, qs, m, d8, ds, n, d, o, stream); break;
+        case 7: launch_dstat<kMode, 7>(q8, qs, m, d8, ds, n, d, o, stream); break;
+        case 8: launch_dstat<kMode, 8>(q8, qs, m, d8, ds, n, d, o, stream); break;
+        default: {
+            const int64_t units = kMode == kSqGroupMax ? (o.G0 + 3) / 4 : (n + kSqDocs - 1) / kSqDocs;
+            const int64_t qt = (m + kSqQueries - 1) / kSqQueries;
+            hipLaunchKernelGGL(sq8_scores_kernel<kMode>, dim3((unsigned)(qt * units)), dim3(kSqThreads), 0, stream,
+                               q8, qs, m, d8, ds, n, d, units, o);
+        }
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_sq8_topk(const int8_t* q8, const float* qs, int64_t nq, const int8_t* d8, const float* ds,
                            int64_t n, int32_t d, int32_t R, int32_t* ids, float* scores, void* ws,
                            hipStream_t stream) {
     if (nq == 0) return hipSuccess;
-    float* S = reinterpret_cast<float*>(ws);
-    const int64_t chunk = sq8_chunk(nq, n);
-    for (int64_t a = 0; a < nq; a += chunk) {
-        const int64_t m = nq - a < chunk ? nq - a : chunk;
-        const int64_t grid = ((m + kSqQueries - 1) / kSqQueries) * ((n + kSqDocs - 1) / kSqDocs);
-        hipLaunchKernelGGL(sq8_scores_kernel, dim3((unsigned)grid), dim3(kSqThreads), 0, stream, q8 + a * d, qs + a, m,
-                           d8, ds, n, d, S);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        if ((e = launch_rows_topk(S, m, (int32_t)n, R, ids + a * R, scores ? scores + a * R : nullptr, stream)) !=
-            hipSuccess)
-            return e;
+    const SqPlan p = sq8_plan(nq, n, d, R);
+    char* base = reinterpret_cast<char*>(ws);
+    for (int64_t a = 0; a < nq; a += p.chunk) {
+        const int64_t m = nq - a < p.chunk ? nq - a : p.chunk;
+        const int8_t* qa = q8 + a * d;
+        const float* qsa = qs + a;
+        int32_t* ida = ids + a * R;
+        float* sca = scores ? scores + a * R : nullptr;
+        SqOut o{};
+        hipError_t e;
+        if (p.direct) {
+            o.S = reinterpret_cast<float*>(base);
+            if ((e = launch_scores<kSqWriteS>(qa, qsa, m, d8, ds, n, d, o, stream)) != hipSuccess) return e;
+            if ((e = launch_rows_topk(o.S, m, (int32_t)n, R, ida, sca, stream)) != hipSuccess) return e;
+            continue;
+        }
+        o.gmax = reinterpret_cast<float*>(base + p.off_gmax);
+        o.G0 = p.G0;
+        o.gstep = p.gstep;
+        int32_t* tid = reinterpret_cast<int32_t*>(base + p.off_tid);
+        float* tsc = reinterpret_cast<float*>(base + p.off_tsc);
+        o.tau = tsc;
+        o.tau_stride = R;
+        o.cnt = reinterpret_cast<uint32_t*>(base + p.off_cnt);
+        o.cs = reinterpret_cast<float*>(base + p.off_cs);
+        o.ci = reinterpret_cast<int32_t*>(base + p.off_ci);
+        o.cap = kSqCap;
+        float* slots = reinterpret_cast<float*>(base + p.off_slots);
+        // (1) sampled group maxima and the bound
+        if ((e = launch_scores<kSqGroupMax>(qa, qsa, m, d8, ds, n, d, o, stream)) != hipSuccess) return e;
+        if ((e = launch_rows_topk(o.gmax, m, p.G0, R, tid, tsc, stream)) != hipSuccess) return e;
+        // (2) candidates at or above the bound
+        hipLaunchKernelGGL(sq8_zero_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, stream, o.cnt, m);
+        if ((e = launch_scores<kSqEmit>(qa, qsa, m, d8, ds, n, d, o, stream)) != hipSuccess) return e;
+        // (3) selection of each list, (4) exact redo of overflowed lists
+        if ((e = launch_list_topk(o.cs, o.ci, o.cnt, m, kSqCap, R, ida, sca, stream)) != hipSuccess) return e;
+        hipLaunchKernelGGL(sq8_fallback_kernel, dim3(kSqFb), dim3(kSqThreads), 0, stream, qa, qsa, m, d8, ds, n, d, R,
+                           o.cnt, kSqCap, slots, ida, sca);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
 }

@@ -138,7 +138,7 @@ def test_sq8_validation(lib):
     vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
     lib.ah_sq8_quantize.argtypes = [vp, i64, i32, C.c_double, vp, vp, vp]
     lib.ah_sq8_workspace_bytes.restype = sz
-    lib.ah_sq8_workspace_bytes.argtypes = [i64, i64]
+    lib.ah_sq8_workspace_bytes.argtypes = [i64, i64, i32, i32]
     lib.ah_sq8_scan_topk.argtypes = [vp, vp, i64, vp, vp, i64, i32, i32, vp, vp, vp, sz, vp]
     fake, odd = vp(4096), vp(4097)  # never dereferenced: every case below fails validation first
     assert lib.ah_sq8_quantize(fake, 10, 0, 99.9, fake, fake, None) == -2
@@ -146,8 +146,9 @@ def test_sq8_validation(lib):
     assert lib.ah_sq8_quantize(fake, 10, 20000, 99.9, fake, fake, None) == -3
     assert lib.ah_sq8_quantize(None, 10, 8, 99.9, fake, fake, None) == -1
     assert lib.ah_sq8_quantize(None, 0, 8, 99.9, None, None, None) == 0
-    need = lib.ah_sq8_workspace_bytes(100, 1000)
-    assert need >= 100 * 1000 * 4
+    need = lib.ah_sq8_workspace_bytes(100, 1000, 64, 10)
+    assert need >= 100 * 1000 * 4  # small n: the score block of all queries
+    assert lib.ah_sq8_workspace_bytes(100, 1000, 64, 0) == 0
     assert lib.ah_sq8_scan_topk(fake, fake, 100, fake, fake, 1000, 64, 1001, fake, None, fake, need, None) == -2  # R > n
     assert lib.ah_sq8_scan_topk(fake, fake, 100, fake, fake, 1000, 40, 10, fake, None, fake, need, None) == -3   # d % 16
     assert lib.ah_sq8_scan_topk(odd, fake, 100, fake, fake, 1000, 64, 10, fake, None, fake, need, None) == -3    # alignment

@@ -242,3 +242,28 @@ def test_assign_fullsize_sampled(gpu):
     assert (g_dist <= o_dist + TOL * scale).all()
     del X
     torch.cuda.empty_cache()
+
+
+def test_sq8_flat_fullsize_sampled(gpu):
+    """Int8 flat search at 1M x 512 with 10,000 queries and R = 100, in the
+    launch configuration the benchmark times (one call, candidate path);
+    sampled queries ranked by the oracle over the same codes and steps must
+    match exactly."""
+    torch, ah = gpu
+    nd, dd, nqs, R = 1_000_000, 512, 10_000, 100
+    _log("sq8: generating and quantising 1M x 512 documents, 10k queries")
+    Dv = synth.gpu_normal_rows(torch, nd, dd, 6464, torch.float32)
+    Qv = synth.gpu_normal_rows(torch, nqs, dd, 6465, torch.float32)
+    d8, ds = ah.ah_sq8_quantize(Dv)
+    q8, qs = ah.ah_sq8_quantize(Qv)
+    del Dv, Qv
+    ids, sc = ah.ah_sq8_scan_topk(q8, qs, d8, ds, R)
+    torch.cuda.synchronize()
+    _log("sq8: done; checking sampled queries")
+    idx = _sample(nqs) + [4097, 7777]
+    o_ids, o_sc = oracle.sq8_topk(q8[idx].cpu().numpy(), qs[idx].cpu().numpy(), d8.cpu().numpy(),
+                                  ds.cpu().numpy(), R)
+    assert np.array_equal(ids[idx].cpu().numpy(), o_ids)
+    assert np.array_equal(sc[idx].cpu().numpy(), o_sc)
+    del d8, q8
+    torch.cuda.empty_cache()

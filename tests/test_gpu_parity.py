@@ -516,17 +516,26 @@ def test_sq8_quantize_parity(gpu, n, d, pct, kind):
 
 # Stage-chained: the oracle ranks the GPU's own codes and steps.  The page's
 # notebook shape (20,000 x 512, 200 queries, 20-center mixture), ragged tiles,
-# R = n, R above the one-wave selection's limit, duplicate documents.
-@pytest.mark.parametrize("nq,n,d,R", [(200, 20000, 512, 10), (70, 3001, 64, 100), (5, 500, 16, 500),
-                                      (130, 10000, 128, 600), (1, 4097, 32, 64)])
-def test_sq8_topk_parity(gpu, nq, n, d, R):
+# R = n, R above the one-wave selection's limit, and both ways to the top R:
+# the direct score block (n <= 4096, R > 512) and the candidate path (a bound
+# from sampled 64-row group maxima, every gstep-th group when the sample is a
+# fraction, then the candidate lists).  `dup` copies of one document at random
+# positions make ties at the top (3,000 copies: a long tied run inside the
+# lists; every document equal: the lists overflow and the exact redo answers).
+@pytest.mark.parametrize("nq,n,d,R,dup", [(200, 20000, 512, 10, 2), (70, 3001, 64, 100, 2), (5, 500, 16, 500, 2),
+                                          (130, 10000, 128, 600, 2), (1, 4097, 32, 64, 2),
+                                          (300, 50000, 256, 512, 2), (100, 100000, 128, 100, 2),
+                                          (150, 40000, 128, 100, 3000), (20, 30000, 64, 50, 30000)])
+def test_sq8_topk_parity(gpu, nq, n, d, R, dup):
     torch, ah = gpu
     rng = np.random.default_rng(nq + n + d)
     centers = rng.standard_normal((20, d)).astype(np.float32)
     D = centers[rng.integers(0, 20, n)] + 0.5 * rng.standard_normal((n, d)).astype(np.float32)
     D /= np.linalg.norm(D, axis=1, keepdims=True)
-    D[n // 2] = D[3]
+    D[rng.choice(n, size=min(dup, n), replace=False)] = D[3]
     Q = centers[rng.integers(0, 20, nq)] + 0.5 * rng.standard_normal((nq, d)).astype(np.float32)
+    if dup >= 3000:
+        Q[::2] = D[3]  # half the queries score the copies highest
     d8, ds = ah.ah_sq8_quantize(_t(torch, D.astype(np.float32)))
     q8, qs = ah.ah_sq8_quantize(_t(torch, Q.astype(np.float32)))
     ids, sc = ah.ah_sq8_scan_topk(q8, qs, d8, ds, R)
