@@ -15,6 +15,10 @@ the passage it follows:
   (``partition``), per-block table of q.center (``lut_f64``), approximate score
   = sum of the row's table entries (``scan_sums``/``scan_topk``), exact reorder
   of the best candidates (``reorder``);
+* page "RSLM: Training-Free Vector Quantization for Approximate Nearest
+  Neighbor Search", relative mode (a row coded as its residual from a coarse
+  approximation, here its leaf centroid): the biased ``scan_topk`` and
+  ``residual_leaf_bias``;
 * same page, section "Measuring recall honestly", and the compression lesson's
   "Measuring what compression costs: recall@k": ``recall_at_k`` and the exact
   ground truth ``brute_force``.
@@ -52,7 +56,7 @@ def lib() -> C.CDLL:
         L.oracle_scan_sums.argtypes = [_i8p, C.c_int64, C.c_int32, _u8p, C.c_int64, C.c_int32, _i32p]
         L.oracle_scan_topk.argtypes = [_i8p, C.c_int64, C.c_int32, _u8p, C.c_int64, C.c_int32,
                                        C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32,
-                                       C.c_int32, _i32p, _i32p]
+                                       C.c_int32, _i32p, _i32p, C.c_void_p, C.c_int32]
         L.oracle_lut_f64.argtypes = [_f32p, C.c_int64, C.c_int32, _f32p, C.c_int32, C.c_int32, _f64p]
         L.oracle_quantize_lut.argtypes = [_f32p, C.c_int64, C.c_int32, _i8p, _f32p, _f32p]
         L.oracle_reorder.argtypes = [_f32p, C.c_int64, C.c_int32, C.c_void_p, C.c_int32, C.c_int64,
@@ -98,10 +102,12 @@ def scan_sums(lut_i8: np.ndarray, codes: np.ndarray) -> np.ndarray:
     return out
 
 
-def scan_topk(lut_i8, codes, R, ids=None, leaf_offsets=None, leaves=None):
+def scan_topk(lut_i8, codes, R, ids=None, leaf_offsets=None, leaves=None, leaf_bias=None, bias_bound=0):
     """Top-R (sum desc, id asc) per query over all rows, or over the rows of the
     leaves listed in ``leaves`` [nq, nl] (row ranges from ``leaf_offsets``).
-    Returns (ids int32 [nq, R], sums int32 [nq, R]); empty slots (-1, INT32_MIN)."""
+    Residual variant: with ``leaf_bias`` int32 [nq, nl], a row of the query's
+    j-th leaf scores sum + clip(leaf_bias[q, j], -bias_bound, bias_bound).
+    Returns (ids int32 [nq, R], scores int32 [nq, R]); empty slots (-1, INT32_MIN)."""
     lut_i8 = _c(lut_i8, np.int8)
     codes = _c(codes, np.uint8)
     nq, B, _ = lut_i8.shape
@@ -112,11 +118,30 @@ def scan_topk(lut_i8, codes, R, ids=None, leaf_offsets=None, leaves=None):
     lv = None if leaves is None else _c(leaves, np.int32)
     nl = 0 if lv is None else lv.shape[1]
     L = 0 if lo is None else lo.shape[0] - 1
+    lb = None if leaf_bias is None else _c(leaf_bias, np.int32)
     oi = np.empty((nq, R), dtype=np.int32)
     os_ = np.empty((nq, R), dtype=np.int32)
     lib().oracle_scan_topk(lut_i8, nq, B, codes, n, stride, _ptr(ids), _ptr(lo), L, _ptr(lv), nl,
-                           R, oi, os_)
+                           R, oi, os_, _ptr(lb), int(bias_bound))
     return oi, os_
+
+
+def residual_leaf_bias(part_scores, step, bound):
+    """Residual variant's per-leaf term in table units (the RSLM summary page's
+    relative mode: score = q.c_leaf + q.residual; the table approximates
+    q.residual as bias + step * sum, so q.c_leaf enters as q.c_leaf / step):
+    int32 [nq, nl] = clip(rint((s[q, j] - s[q, 0]) / step[q]), -bound, bound)
+    from the query's leaf scores ``part_scores`` float32 [nq, nl] (first = the
+    leaf everything is measured from), all in float32, rint half to even;
+    a query with step 0 gets 0 everywhere."""
+    s = _c(part_scores, np.float32)
+    st = _c(step, np.float32)
+    diff = s - s[:, :1]
+    out = np.zeros(s.shape, dtype=np.int32)
+    pos = st > 0
+    v = np.rint(diff[pos] / st[pos][:, None])
+    out[pos] = np.clip(v, -bound, bound).astype(np.int32)
+    return out
 
 
 def lut_f64(Q: np.ndarray, codebooks: np.ndarray) -> np.ndarray:
@@ -244,10 +269,14 @@ def recall_at_k(found: np.ndarray, truth: np.ndarray) -> float:
     return total / float(np.asarray(truth).size) if np.asarray(truth).size else 1.0
 
 
-def search(Q, codebooks, codes, base, R, k, centroids=None, leaf_offsets=None, ids=None, nl=0):
+def search(Q, codebooks, codes, base, R, k, centroids=None, leaf_offsets=None, ids=None, nl=0,
+           residual_bound=None):
     """The whole path on the CPU, each step fed the previous step's output:
     leaves (if partitioned) -> float64 table rounded to float32 -> int8 table ->
-    top-R by integer sum -> exact reorder to the best k.
+    top-R by integer sum -> exact reorder to the best k.  With
+    ``residual_bound`` (partitioned, codes of residuals from the leaf
+    centroids), the leaf scores rounded to float32 become per-leaf terms in
+    table units (``residual_leaf_bias``) added to the sums.
     Returns dict with every intermediate."""
     out = {}
     leaves = None
@@ -258,7 +287,12 @@ def search(Q, codebooks, codes, base, R, k, centroids=None, leaf_offsets=None, i
     l32 = lf.astype(np.float32)
     t8, s, beta = quantize_lut(l32)
     out.update(lut_f64=lf, lut_f32=l32, lut_i8=t8, scale=s, bias=beta)
-    ci, cs = scan_topk(t8, codes, R, ids=ids, leaf_offsets=leaf_offsets, leaves=leaves)
+    lb = None
+    if residual_bound is not None and leaves is not None:
+        lb = residual_leaf_bias(out["leaf_scores"].astype(np.float32), s, residual_bound)
+        out["leaf_bias"] = lb
+    ci, cs = scan_topk(t8, codes, R, ids=ids, leaf_offsets=leaf_offsets, leaves=leaves, leaf_bias=lb,
+                       bias_bound=0 if lb is None else residual_bound)
     out["cand_ids"], out["cand_sums"] = ci, cs
     fi, fs = reorder(Q, base, ci, k)
     out["ids"], out["scores"] = fi, fs

@@ -68,11 +68,21 @@ void oracle_scan_sums(const int8_t* lut, int64_t nq, int32_t B, const uint8_t* c
 
 /* Steps 3+4: for each query, score every row of the leaves it searches (all rows
  * when leaves == NULL), sort all (sum, id) pairs by (sum desc, id asc) and keep
- * the first R.  Missing slots are (-1, INT32_MIN). */
+ * the first R.  Missing slots are (-1, INT32_MIN).
+ *
+ * Residual (leaf-relative) variant, when bias != NULL (the RSLM summary page:
+ * in its relative mode a row is coded as the residual from a coarse
+ * approximation; with the leaf centroid as that approximation, q.x = q.c_leaf +
+ * q.residual, and the table scores the residual): a row of the query's j-th
+ * leaf scores sum + bias[q*nl + j], the bias clamped to [-bound, bound]. */
+static inline int32_t clamp_bias(int32_t v, int32_t bound) {
+    return v < -bound ? -bound : (v > bound ? bound : v);
+}
+
 void oracle_scan_topk(const int8_t* lut, int64_t nq, int32_t B, const uint8_t* codes, int64_t n,
                       int32_t stride, const int32_t* ids, const int64_t* leaf_offsets, int32_t L,
                       const int32_t* leaves, int32_t nl, int32_t R, int32_t* out_ids,
-                      int32_t* out_scores) {
+                      int32_t* out_scores, const int32_t* bias, int32_t bound) {
     (void)L;
     #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t q = 0; q < nq; ++q) {
@@ -91,8 +101,9 @@ void oracle_scan_topk(const int8_t* lut, int64_t nq, int32_t B, const uint8_t* c
         if (leaves) {
             for (int32_t j = 0; j < nl; ++j) {
                 int32_t l = leaves[q * nl + j];
+                int32_t add = bias ? clamp_bias(bias[q * nl + j], bound) : 0;
                 for (int64_t i = leaf_offsets[l]; i < leaf_offsets[l + 1]; ++i) {
-                    all[m].score = adc_sum(lq, B, codes + i * (int64_t)stride);
+                    all[m].score = adc_sum(lq, B, codes + i * (int64_t)stride) + add;
                     all[m].id = ids ? ids[i] : (int32_t)i;
                     ++m;
                 }

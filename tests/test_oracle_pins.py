@@ -474,3 +474,90 @@ def test_sq8_topk_is_brute_force_over_exact_dots():
         assert np.array_equal(ids[q], order)
         assert np.array_equal(sc[q], full[q][order])
     assert all(list(ids[q]).index(5) < list(ids[q]).index(17) for q in range(9) if 5 in ids[q] and 17 in ids[q])
+
+
+# ---------------------------------------------------------------- residual (leaf-relative) variant
+
+def test_residual_leaf_bias_hand_cases():
+    # step 0.25: differences 0, -0.5, -2, -0.125 leaf scores -> 0, -2, -8, -0.5 steps;
+    # rint takes -0.5 to 0 and -1.5 to -2 (half to even); the bound clips
+    s = np.array([[3.0, 2.5, 1.0, 2.875], [1.0, 0.625, 1.5, 1.0]], dtype=np.float32)
+    step = np.array([0.25, 0.25], dtype=np.float32)
+    assert oracle.residual_leaf_bias(s, step, 100).tolist() == [[0, -2, -8, 0], [0, -2, 2, 0]]
+    assert oracle.residual_leaf_bias(s, step, 5).tolist() == [[0, -2, -5, 0], [0, -2, 2, 0]]
+    # a constant table (step 0) carries no leaf term
+    assert (oracle.residual_leaf_bias(s, np.zeros(2, np.float32), 100) == 0).all()
+
+
+def test_residual_scores_decompose_exactly():
+    # The variant's premise: with rows x = c_leaf + decode(codes), q.x equals the
+    # leaf's centroid score plus the sum of the float64 table at the codes.
+    rng = np.random.default_rng(31)
+    B, dpb, L, n, nq = 6, 2, 5, 60, 3
+    d = B * dpb
+    cb = rng.standard_normal((B, 16, dpb)).astype(np.float32)
+    cent = rng.standard_normal((L, d)).astype(np.float32)
+    leaf = rng.integers(0, L, n)
+    codes = synth.random_codes(rng, n, B)
+    nib = _decode_nibbles(codes, B)
+    dec = np.stack([cb[b, nib[:, b]] for b in range(B)], axis=1).reshape(n, d).astype(np.float64)
+    X = cent[leaf].astype(np.float64) + dec
+    Q = rng.standard_normal((nq, d)).astype(np.float32)
+    lut = oracle.lut_f64(Q, cb)
+    adc = np.stack([lut[q][np.arange(B)[None, :], nib].sum(1) for q in range(nq)])
+    cs = Q.astype(np.float64) @ cent.astype(np.float64).T
+    want = Q.astype(np.float64) @ X.T
+    assert np.allclose(cs[:, leaf] + adc, want, rtol=0, atol=1e-9)
+
+
+def test_scan_topk_zero_bias_is_the_plain_scan():
+    rng = np.random.default_rng(32)
+    B, n, nq, L, nl, R = 7, 500, 6, 12, 5, 30
+    lut = synth.random_lut_i8(rng, nq, B)
+    codes = synth.random_codes(rng, n, B)
+    offs = np.concatenate([[0], np.cumsum(synth.random_leaf_sizes(rng, n, L))]).astype(np.int64)
+    leaves = synth.random_probe_lists(rng, nq, L, nl)
+    a = oracle.scan_topk(lut, codes, R, leaf_offsets=offs, leaves=leaves)
+    b = oracle.scan_topk(lut, codes, R, leaf_offsets=offs, leaves=leaves,
+                         leaf_bias=np.zeros((nq, nl), np.int32), bias_bound=50)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("seed,bound", [(0, 1000), (1, 7), (2, 0), (3, 40)])
+def test_scan_topk_biased_brute_force(seed, bound):
+    # independent formulation: one-hot sums plus each searched leaf's clipped
+    # bias, ranked by numpy lexsort over (score desc, id asc)
+    rng = np.random.default_rng(200 + seed)
+    B, n, nq, L, nl = int(rng.integers(1, 12)), int(rng.integers(50, 600)), 4, 9, 4
+    lut = synth.random_lut_i8(rng, nq, B, -6, 6)
+    codes = synth.random_codes(rng, n, B)
+    offs = np.concatenate([[0], np.cumsum(synth.random_leaf_sizes(rng, n, L, skew=1.0))]).astype(np.int64)
+    leaves = synth.random_probe_lists(rng, nq, L, nl)
+    bias = rng.integers(-60, 61, size=(nq, nl)).astype(np.int32)
+    perm = rng.permutation(n).astype(np.int32)
+    R = int(rng.integers(1, n))
+    ids, sc = oracle.scan_topk(lut, codes, R, ids=perm, leaf_offsets=offs, leaves=leaves, leaf_bias=bias,
+                               bias_bound=bound)
+    sums = _onehot_sums(lut, codes, B)
+    for q in range(nq):
+        rows = [np.arange(offs[l], offs[l + 1]) for l in leaves[q]]
+        tot = np.concatenate([sums[q, r] + int(np.clip(bias[q, j], -bound, bound)) for j, r in enumerate(rows)])
+        allr = np.concatenate(rows).astype(np.int64)
+        wi, ws = _lexsort_topr(tot.astype(np.int32), perm[allr], R)
+        assert np.array_equal(ids[q], wi) and np.array_equal(sc[q], ws)
+
+
+def test_scan_topk_bias_moves_a_row_across_leaves():
+    # two one-row leaves, one block: sums 5 (leaf 0) and 3 (leaf 1); a +3 bias on
+    # leaf 1 puts its row first, a +2 bias ties and the lower id wins
+    lut = np.zeros((1, 1, 16), np.int8)
+    lut[0, 0, 1], lut[0, 0, 2] = 5, 3
+    codes = np.array([[1], [2]], np.uint8)
+    offs = np.array([0, 1, 2], np.int64)
+    leaves = np.array([[0, 1]], np.int32)
+    ids, sc = oracle.scan_topk(lut, codes, 2, leaf_offsets=offs, leaves=leaves,
+                               leaf_bias=np.array([[0, 3]], np.int32), bias_bound=10)
+    assert ids.tolist() == [[1, 0]] and sc.tolist() == [[6, 5]]
+    ids, sc = oracle.scan_topk(lut, codes, 2, leaf_offsets=offs, leaves=leaves,
+                               leaf_bias=np.array([[0, 2]], np.int32), bias_bound=10)
+    assert ids.tolist() == [[0, 1]] and sc.tolist() == [[5, 5]]
