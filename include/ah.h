@@ -58,6 +58,7 @@ enum { AH_F32 = 0, AH_BF16 = 1 };
 #define AH_MAX_DIM 16384     /* d */
 
 #define AH_MAX_ASSIGN_LEAVES 4096 /* L for ah_assign_leaves */
+#define AH_MAX_LEAF_BIAS (1 << 24) /* bias_bound of the residual scan */
 
 /* code_stride value selecting the tiled code layout (see ah_tile_codes). */
 #define AH_CODES_TILED 0
@@ -246,6 +247,44 @@ int ah_scan_topk_timed(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_
                        int32_t R, int32_t* cand_ids_out, int32_t* cand_scores_out, void* workspace,
                        size_t workspace_bytes, void* stream, void* main_start_event,
                        void* main_stop_event);
+
+/* ---------------------------------------------------------------------------
+ * Residual (leaf-relative) variant of steps 3+4 (page "RSLM: Training-Free
+ * Vector Quantization for Approximate Nearest Neighbor Search", relative mode:
+ * a row is coded as its residual from a coarse approximation; here the coarse
+ * approximation is the row's leaf centroid, so q.x = q.c_leaf + q.residual and
+ * the table, built from the residual codebooks, scores the residual).
+ *
+ * ah_residual_leaf_bias: the leaf term in table units for each probed leaf:
+ *   bias_out[q][j] = clip(rint((leaf_scores[q][j] - leaf_scores[q][0]) / step[q]),
+ *                         -bias_bound, bias_bound)
+ * in float32 (round half to even), 0 for a query whose step is 0 (a constant
+ * table).  leaf_scores float32 [nq][nl] is ah_partition_score's scores_out (the
+ * first leaf is the best one), step float32 [nq] is ah_build_lut's scale_out.
+ *   bias_out int32 [nq][nl]
+ * Errors: AH_ERR_SHAPE (nq < 0, nl < 1, bias_bound < 0), AH_ERR_UNSUPPORTED
+ * (bias_bound > AH_MAX_LEAF_BIAS), AH_ERR_NULL.
+ *
+ * ah_scan_topk_residual: ah_scan_topk over the listed leaves, a row of the
+ * query's j-th leaf scoring its sum plus clip(leaf_bias[q][j], -bias_bound,
+ * bias_bound); the kept set is the unique top-R by (score desc, id asc) and
+ * cand_scores_out holds those int32 scores.  Arguments as ah_scan_topk, plus
+ *   leaf_bias   int32 [nq][nl] (device), aligned with leaves
+ *   bias_bound  in [0, AH_MAX_LEAF_BIAS]; a larger bound coarsens the scan's
+ *               internal score histograms (255 B + 2 bias_bound values over
+ *               1,024 bins), so the threshold rises in coarser steps
+ *   workspace   >= ah_scan_workspace_bytes(nq, B, n, L, nl, R) bytes
+ * Errors: as ah_scan_topk; AH_ERR_SHAPE also when leaves is NULL or
+ * bias_bound < 0, AH_ERR_NULL when leaf_bias is NULL, AH_ERR_UNSUPPORTED when
+ * bias_bound > AH_MAX_LEAF_BIAS.
+ */
+int ah_residual_leaf_bias(const float* leaf_scores, const float* step, int64_t nq, int32_t nl, int32_t bias_bound,
+                          int32_t* bias_out, void* stream);
+int ah_scan_topk_residual(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* codes, int32_t code_stride,
+                          int64_t n, const int32_t* ids, const int64_t* leaf_offsets, int32_t L,
+                          const int32_t* leaves, int32_t nl, const int32_t* leaf_bias, int32_t bias_bound, int32_t R,
+                          int32_t* cand_ids_out, int32_t* cand_scores_out, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* ---------------------------------------------------------------------------
  * Step 5: exact reorder (ScaNN page, "Three stages of a search": the best few

@@ -50,6 +50,16 @@ int ahx_train_pq(const float* X, int64_t m, int32_t d, int32_t B, int32_t dpb, d
 int ahx_encode(const float* X, int64_t n, int32_t d, int32_t B, int32_t dpb, double eta,
                const float* codebooks, int32_t sweeps, uint8_t* codes, int32_t stride);
 
+/* The same with the anisotropic direction taken from separate rows: u =
+ * V_i / |V_i| while X_i is the vector quantised (the residual variant: X holds
+ * residuals from the leaf centroids, V the original rows, since the score
+ * error of q.x is q.(r - r~) and its parallel part lies along x).  V may be
+ * NULL (then V = X, as in the functions above). */
+int ahx_train_pq_dir(const float* X, const float* V, int64_t m, int32_t d, int32_t B, int32_t dpb, double eta,
+                     int32_t iters, const int64_t* init_rows, float* codebooks, double* loss_out);
+int ahx_encode_dir(const float* X, const float* V, int64_t n, int32_t d, int32_t B, int32_t dpb, double eta,
+                   const float* codebooks, int32_t sweeps, uint8_t* codes, int32_t stride);
+
 /* Total loss of an encoding (float64). */
 double ahx_loss(const float* X, int64_t n, int32_t d, int32_t B, int32_t dpb, double eta,
                 const float* codebooks, const uint8_t* codes, int32_t stride);

@@ -27,6 +27,7 @@ EXPORTS = (
     "ah_partition_workspace_bytes", "ah_partition_score",
     "ah_build_lut",
     "ah_scan_workspace_bytes", "ah_scan_topk", "ah_scan_topk_timed",
+    "ah_residual_leaf_bias", "ah_scan_topk_residual",
     "ah_sq8_quantize", "ah_sq8_workspace_bytes", "ah_sq8_scan_topk",
     "ah_assign_workspace_bytes", "ah_assign_leaves",
     "ah_encode", "ah_tiled_codes_bytes", "ah_tile_codes",
@@ -65,6 +66,11 @@ def lib() -> C.CDLL:
         L.ah_scan_topk_timed.restype = C.c_int
         L.ah_scan_topk_timed.argtypes = [vp, i64, i32, vp, i32, i64, vp, vp, i32, vp, i32, i32, vp, vp, vp, sz, vp,
                                          vp, vp]
+        L.ah_scan_topk_residual.restype = C.c_int
+        L.ah_scan_topk_residual.argtypes = [vp, i64, i32, vp, i32, i64, vp, vp, i32, vp, i32, vp, i32, i32, vp, vp,
+                                            vp, sz, vp]
+        L.ah_residual_leaf_bias.restype = C.c_int
+        L.ah_residual_leaf_bias.argtypes = [vp, vp, i64, i32, i32, vp, vp]
         L.ah_sq8_quantize.restype = C.c_int
         L.ah_sq8_quantize.argtypes = [vp, i64, i32, C.c_double, vp, vp, vp]
         L.ah_sq8_workspace_bytes.restype = sz
@@ -292,10 +298,12 @@ def ah_tile_codes(codes, B=None, stream=None) -> TiledCodes:
 
 
 def ah_scan_topk(lut_i8, codes, R, ids=None, leaf_offsets=None, leaves=None, cand_ids_out=None,
-                 cand_scores_out=None, workspace=None, stream=None, main_events=None):
+                 cand_scores_out=None, workspace=None, stream=None, main_events=None, leaf_bias=None,
+                 bias_bound=0):
     """Top-R rows per query by exact int32 sum of table entries.
     codes: uint8 [n, stride] row-major, or TiledCodes; leaves: int32 [nq, nl] or
-    None (scan all rows)."""
+    None (scan all rows).  With leaf_bias (int32 [nq, nl], residual variant) the
+    call is ah_scan_topk_residual: the j-th leaf's rows add its clipped bias."""
     lut_i8 = _dev(lut_i8, torch.int8, "lut_i8", 3)
     _dev(ids, torch.int32, "ids")
     _dev(leaf_offsets, torch.int64, "leaf_offsets")
@@ -322,6 +330,15 @@ def ah_scan_topk(lut_i8, codes, R, ids=None, leaf_offsets=None, leaves=None, can
     need = ah_scan_workspace_bytes(nq, B, n, Lw, nlw, R)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if leaf_bias is not None:
+        _dev(leaf_bias, torch.int32, "leaf_bias", 2)
+        if main_events is not None:
+            raise ValueError("main_events are not supported with leaf_bias")
+        _check(lib().ah_scan_topk_residual(_ptr(lut_i8), nq, B, _ptr(codes), stride, n, _ptr(ids), _ptr(leaf_offsets),
+                                           L, _ptr(leaves), nl, _ptr(leaf_bias), int(bias_bound), R,
+                                           _ptr(cand_ids_out), _ptr(cand_scores_out), _ptr(workspace),
+                                           workspace.numel(), _stream(stream)), "ah_scan_topk_residual")
+        return cand_ids_out, cand_scores_out
     args = (_ptr(lut_i8), nq, B, _ptr(codes), stride, n, _ptr(ids), _ptr(leaf_offsets), L, _ptr(leaves), nl, R,
             _ptr(cand_ids_out), _ptr(cand_scores_out), _ptr(workspace), workspace.numel(), _stream(stream))
     if main_events is None:
@@ -330,6 +347,20 @@ def ah_scan_topk(lut_i8, codes, R, ids=None, leaf_offsets=None, leaves=None, can
         _check(lib().ah_scan_topk_timed(*args, C.c_void_p(main_events[0]), C.c_void_p(main_events[1])),
                "ah_scan_topk_timed")
     return cand_ids_out, cand_scores_out
+
+
+def ah_residual_leaf_bias(leaf_scores, step, bias_bound, bias_out=None, stream=None):
+    """Residual variant's leaf term in table units: int32 [nq, nl] =
+    clip(rint((s[q, j] - s[q, 0]) / step[q]), -bias_bound, bias_bound), 0 when step is 0."""
+    leaf_scores = _dev(leaf_scores, torch.float32, "leaf_scores", 2)
+    step = _dev(step, torch.float32, "step", 1)
+    nq, nl = leaf_scores.shape
+    if bias_out is None:
+        bias_out = torch.empty((nq, nl), dtype=torch.int32, device=leaf_scores.device)
+    _dev(bias_out, torch.int32, "bias_out", 2)
+    _check(lib().ah_residual_leaf_bias(_ptr(leaf_scores), _ptr(step), nq, nl, int(bias_bound), _ptr(bias_out),
+                                       _stream(stream)), "ah_residual_leaf_bias")
+    return bias_out
 
 
 # ----------------------------------------------------------------------------- step 5

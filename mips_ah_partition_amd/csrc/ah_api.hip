@@ -61,15 +61,17 @@ size_t ah_scan_workspace_bytes(int64_t nq, int32_t B, int64_t n, int32_t L, int3
     return ah::scan_workspace_bytes(nq, B, n, L, nl, R);
 }
 
-int ah_scan_topk_timed(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* codes,
-                       int32_t code_stride, int64_t n, const int32_t* ids, const int64_t* leaf_offsets,
-                       int32_t L, const int32_t* leaves, int32_t nl, int32_t R, int32_t* cand_ids_out,
-                       int32_t* cand_scores_out, void* workspace, size_t workspace_bytes, void* stream,
-                       void* main_start_event, void* main_stop_event) {
+static int scan_impl(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* codes, int32_t code_stride,
+                     int64_t n, const int32_t* ids, const int64_t* leaf_offsets, int32_t L, const int32_t* leaves,
+                     int32_t nl, const int32_t* leaf_bias, int32_t bias_bound, int32_t R, int32_t* cand_ids_out,
+                     int32_t* cand_scores_out, void* workspace, size_t workspace_bytes, void* stream,
+                     void* main_start_event, void* main_stop_event) {
     const bool tiled = code_stride == AH_CODES_TILED;
     if (nq < 0 || n < 0 || B < 1 || R < 1 || (!tiled && code_stride < (B + 1) / 2)) return AH_ERR_SHAPE;
     if (leaves && (L < 1 || nl < 1 || nl > L || !leaf_offsets)) return AH_ERR_SHAPE;
+    if (leaf_bias && (!leaves || bias_bound < 0)) return AH_ERR_SHAPE;
     if (B > AH_MAX_BLOCKS || R > AH_MAX_R || n >= ((int64_t)1 << 31)) return AH_ERR_UNSUPPORTED;
+    if (leaf_bias && bias_bound > AH_MAX_LEAF_BIAS) return AH_ERR_UNSUPPORTED;
     if (nq == 0) return AH_OK;
     if (!lut_i8 || !cand_ids_out || !cand_scores_out || (n > 0 && !codes)) return AH_ERR_NULL;
     if (!a16(lut_i8) || (tiled && !a16(codes))) return AH_ERR_UNSUPPORTED;
@@ -78,18 +80,52 @@ int ah_scan_topk_timed(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_
     const int32_t seg16 = ((B + 1) / 2 + 15) / 16;  // 16-byte segments per row
     ah::ScanProblem sp{lut_i8, nq, B, codes, tiled ? 16 * seg16 : code_stride, n, ids,
                        leaves ? leaf_offsets : nullptr, Lw, leaves, nlw, R, cand_ids_out, cand_scores_out,
-                       tiled ? (int64_t)1024 * seg16 : 0};
+                       tiled ? (int64_t)1024 * seg16 : 0, leaf_bias, leaf_bias ? bias_bound : 0};
     return hip_status(ah::launch_scan(sp, workspace, workspace_bytes, static_cast<hipStream_t>(stream),
                                       static_cast<hipEvent_t>(main_start_event),
                                       static_cast<hipEvent_t>(main_stop_event)));
+}
+
+int ah_scan_topk_timed(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* codes,
+                       int32_t code_stride, int64_t n, const int32_t* ids, const int64_t* leaf_offsets,
+                       int32_t L, const int32_t* leaves, int32_t nl, int32_t R, int32_t* cand_ids_out,
+                       int32_t* cand_scores_out, void* workspace, size_t workspace_bytes, void* stream,
+                       void* main_start_event, void* main_stop_event) {
+    return scan_impl(lut_i8, nq, B, codes, code_stride, n, ids, leaf_offsets, L, leaves, nl, nullptr, 0, R,
+                     cand_ids_out, cand_scores_out, workspace, workspace_bytes, stream, main_start_event,
+                     main_stop_event);
 }
 
 int ah_scan_topk(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* codes,
                  int32_t code_stride, int64_t n, const int32_t* ids, const int64_t* leaf_offsets,
                  int32_t L, const int32_t* leaves, int32_t nl, int32_t R, int32_t* cand_ids_out,
                  int32_t* cand_scores_out, void* workspace, size_t workspace_bytes, void* stream) {
-    return ah_scan_topk_timed(lut_i8, nq, B, codes, code_stride, n, ids, leaf_offsets, L, leaves, nl, R,
-                              cand_ids_out, cand_scores_out, workspace, workspace_bytes, stream, nullptr, nullptr);
+    return scan_impl(lut_i8, nq, B, codes, code_stride, n, ids, leaf_offsets, L, leaves, nl, nullptr, 0, R,
+                     cand_ids_out, cand_scores_out, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+int ah_scan_topk_residual(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* codes, int32_t code_stride,
+                          int64_t n, const int32_t* ids, const int64_t* leaf_offsets, int32_t L,
+                          const int32_t* leaves, int32_t nl, const int32_t* leaf_bias, int32_t bias_bound, int32_t R,
+                          int32_t* cand_ids_out, int32_t* cand_scores_out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    if (!leaves || !leaf_bias) {
+        if (nq < 0) return AH_ERR_SHAPE;
+        if (nq == 0) return AH_OK;
+        return !leaves ? AH_ERR_SHAPE : AH_ERR_NULL;
+    }
+    return scan_impl(lut_i8, nq, B, codes, code_stride, n, ids, leaf_offsets, L, leaves, nl, leaf_bias, bias_bound,
+                     R, cand_ids_out, cand_scores_out, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+int ah_residual_leaf_bias(const float* leaf_scores, const float* step, int64_t nq, int32_t nl, int32_t bias_bound,
+                          int32_t* bias_out, void* stream) {
+    if (nq < 0 || nl < 1 || bias_bound < 0) return AH_ERR_SHAPE;
+    if (bias_bound > AH_MAX_LEAF_BIAS) return AH_ERR_UNSUPPORTED;
+    if (nq == 0) return AH_OK;
+    if (!leaf_scores || !step || !bias_out) return AH_ERR_NULL;
+    return hip_status(ah::launch_residual_bias(leaf_scores, step, nq, nl, bias_bound, bias_out,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 int ah_sq8_quantize(const float* x, int64_t n, int32_t d, double pct, int8_t* codes_out, float* scale_out,

@@ -34,6 +34,8 @@ struct ScanProblem {
     int32_t* out_ids;
     int32_t* out_scores;
     int64_t tile_bytes;  // tiled code layout: bytes per 64-row tile (stride = padded row bytes); 0 = row-major
+    const int32_t* leaf_bias = nullptr;  // residual variant: [nq][nl] added to the sums of the j-th leaf's rows
+    int32_t bias_bound = 0;              // every bias is clipped to [-bias_bound, bias_bound]
 };
 size_t scan_workspace_bytes(int64_t nq, int32_t B, int64_t n, int32_t L, int32_t nl, int32_t R);
 hipError_t launch_scan(const ScanProblem& p, void* ws, size_t ws_bytes, hipStream_t stream,
@@ -44,6 +46,9 @@ hipError_t launch_rows_topk(const float* S, int64_t rows, int32_t L, int32_t k, 
 // Best k of each row of a candidate list: row r holds rowcnt[r] scores S[r * cap
 // + j] with ids idmap[r * cap + j]; rows with rowcnt[r] > cap are skipped.
 // cap <= 4096, k <= 512.
+// Residual variant's per-leaf term: clip(rint((s[q][j] - s[q][0]) / step[q]), -bound, bound), 0 when step is 0.
+hipError_t launch_residual_bias(const float* scores, const float* step, int64_t nq, int32_t nl, int32_t bound,
+                                int32_t* bias, hipStream_t stream);
 hipError_t launch_list_topk(const float* S, const int32_t* idmap, const uint32_t* rowcnt, int64_t rows, int32_t cap,
                             int32_t k, int32_t* ids, float* scores, hipStream_t stream);
 

@@ -595,6 +595,37 @@ hipError_t launch_assign(const float* x, int64_t n, int32_t d, const float* cent
 // The best k columns of each row of a score block [rows][L] by (score desc,
 // column asc): the one-wave selection for L <= kWaveLeaves and k <= kLeafSort,
 // else the workgroup selection.
+// ------------------------------------------------------------------ residual leaf terms
+// The residual (leaf-relative) variant scores a row as q.c_leaf + q.residual; the
+// int8 table approximates q.residual as bias + step * sum, so, in table units,
+// the leaf contributes q.c_leaf / step, taken relative to the query's first
+// leaf (a per-query constant does not change the ranking) and rounded half to
+// even.  One thread per (query, probed leaf); all float32, as defined.
+__global__ void residual_bias_kernel(const float* __restrict__ scores, const float* __restrict__ step, int64_t nq,
+                                     int32_t nl, int32_t bound, int32_t* __restrict__ bias) {
+#pragma clang fp contract(off)
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= nq * nl) return;
+    const int64_t q = e / nl;
+    const float st = step[q];
+    int32_t v = 0;
+    if (st > 0.f) {
+        float r = rintf((scores[e] - scores[q * nl]) / st);
+        r = fminf(fmaxf(r, -(float)bound), (float)bound);
+        v = (int32_t)r;
+    }
+    bias[e] = v;
+}
+
+hipError_t launch_residual_bias(const float* scores, const float* step, int64_t nq, int32_t nl, int32_t bound,
+                                int32_t* bias, hipStream_t stream) {
+    const int64_t total = nq * nl;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(residual_bias_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, scores, step,
+                       nq, nl, bound, bias);
+    return hipGetLastError();
+}
+
 hipError_t launch_list_topk(const float* S, const int32_t* idmap, const uint32_t* rowcnt, int64_t rows, int32_t cap,
                             int32_t k, int32_t* ids, float* scores, hipStream_t stream) {
     if (rows == 0) return hipSuccess;

@@ -60,7 +60,7 @@ constexpr int kSelThreads = 256;
 constexpr int kSelLds = 4096;                     // keys staged in LDS by the final select
 
 struct ScanLayout {
-    size_t tau, cnt, hmax, hist, cand, ctrl, ovf, dfr, fb, lcnt, lqoff, lcur, qlist, itemoff, total;
+    size_t tau, cnt, hmax, hist, cand, ctrl, ovf, dfr, fb, lcnt, lqoff, lcur, qlist, qbias, itemoff, total;
     int64_t cap;
 };
 
@@ -91,6 +91,7 @@ static ScanLayout scan_layout(int64_t nq, int32_t B, int64_t n, int32_t L, int32
     s.lqoff = o;   o = align_up(o + (part ? (size_t)(L + 1) * 4 : 0));
     s.lcur = o;    o = align_up(o + (part ? (size_t)L * 4 : 0));
     s.qlist = o;   o = align_up(o + (part ? (size_t)nq * nl * 4 : 0));
+    s.qbias = o;   o = align_up(o + (part ? (size_t)nq * nl * 4 : 0));
     s.itemoff = o; o = align_up(o + (part ? (size_t)(L + 1) * 8 : 0));
     s.total = o;
     return s;
@@ -130,7 +131,22 @@ struct Problem {
     int32_t* out_ids;
     int32_t* out_scores;
     int64_t tile_bytes;   // tiled layout: bytes per 64-row tile (0: row-major)
+    const int32_t* leaf_bias;  // residual variant: [nq][nl], or null
+    int32_t bias_bound;
 };
+
+// The residual variant's term for the query's j-th leaf (0 without one).
+__device__ __forceinline__ int32_t leaf_bias_at(const Problem& p, int64_t q, int j) {
+    if (!p.leaf_bias) return 0;
+    const int32_t v = p.leaf_bias[q * p.nl + j];
+    return v < -p.bias_bound ? -p.bias_bound : (v > p.bias_bound ? p.bias_bound : v);
+}
+// The threshold for a sum whose score is sum + off.  INT_MAX (disabled) and
+// INT_MIN (open) stay as they are; every other threshold is a score in the
+// histogram range, |tq| <= 255 B + bound, so tq - off cannot wrap.
+__device__ __forceinline__ int32_t sat_sub(int32_t tq, int32_t off) {
+    return (tq == INT_MAX || tq == INT_MIN) ? tq : tq - off;
+}
 
 // Row `row`'s first 16-byte segment and the distance between its segments:
 // row-major rows are contiguous; in the tiled layout segment j of the 64 rows
@@ -234,15 +250,21 @@ __global__ __launch_bounds__(1024) void leaf_scan_kernel(const uint32_t* __restr
     }
 }
 
+// Also carries each (query, leaf) pair's clipped residual term next to the
+// query in the leaf's list (qbias; 0 without the variant).
 __global__ void leaf_scatter_kernel(const int32_t* __restrict__ leaves, int64_t nq, int32_t nl, int32_t L,
                                     const int32_t* __restrict__ lqoff, uint32_t* __restrict__ lcur,
-                                    int32_t* __restrict__ qlist) {
+                                    int32_t* __restrict__ qlist, const int32_t* __restrict__ bias, int32_t bound,
+                                    int32_t* __restrict__ qbias) {
     const int64_t pairs = nq * nl;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < pairs; i += (int64_t)gridDim.x * blockDim.x) {
         const int32_t l = leaves[i];
         if (l < 0 || l >= L) continue;
         const uint32_t pos = atomicAdd(&lcur[l], 1u);
         qlist[lqoff[l] + pos] = (int32_t)(i / nl);
+        int32_t v = bias ? bias[i] : 0;
+        v = v < -bound ? -bound : (v > bound ? bound : v);
+        qbias[lqoff[l] + pos] = v;
     }
 }
 
@@ -285,9 +307,10 @@ __global__ __launch_bounds__(kSelThreads) void warmup_kernel(Problem p, ScanStat
         }
         int64_t take = b - a;
         if (take > W - got) take = W - got;
+        const int32_t off = p.leaves ? leaf_bias_at(p, q, j) : 0;
         for (int64_t t = tid; t < take; t += kSelThreads) {
             const int64_t row = a + t;
-            const int32_t s = row_sum(lut_s, p.B, code_row(p, row), al4, seg_step(p));
+            const int32_t s = row_sum(lut_s, p.B, code_row(p, row), al4, seg_step(p)) + off;
             keys[got + t] = int_key(s, p.ids ? p.ids[row] : (int32_t)row);
         }
         __syncthreads();
@@ -312,6 +335,7 @@ struct MainArgs {
     int64_t n_items;  // items (full scan); partitioned: itemoff[L]
     const int32_t* lqoff;
     const int32_t* qlist;
+    const int32_t* qbias;  // residual terms beside qlist, or null
     const int64_t* itemoff;
     int fast_codes;   // rows 16-byte aligned (stride % 16 == 0)
 };
@@ -562,6 +586,8 @@ __device__ __forceinline__ void refresh_tau_wave(const ScanState& st, const int3
     }
 }
 
+// kBias: the residual variant (a.qbias set); the plain scan compiles without it.
+template <bool kBias>
 __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) {
     __shared__ __align__(16) int8_t lut_s[kKC * 4 * kWave * 16];  // [kstep][ntile][lane][16]
     __shared__ __align__(16) uint32_t code_s[2][kTilePts * kCodeStride];
@@ -572,6 +598,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
     __shared__ uint32_t lh[kQG * kLB];  // this item's appended sums per query, bins from jb_s
     __shared__ int32_t tau_s[kQG];     // item-local thresholds (raised from lh)
     __shared__ int32_t jb_s[kQG];      // global bin of the threshold at item start
+    __shared__ int32_t off_s[kQG];     // residual variant: the item's leaf term per query (0 otherwise)
     __shared__ uint32_t fl_s[kScanWaves * 2 * kWave];  // per-wave flush scratch
     __shared__ int64_t item_s, p0_s, p1_s, qbase_s;
     __shared__ uint32_t slab_s;  // next 64-row slab of the item (one 64-block chunk)
@@ -618,6 +645,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
             if (tid < qn) qq = p.leaves ? a.qlist[qbase_s + tid] : (int32_t)(qbase_s + tid);
             qid_s[tid] = qq;
             qapp_s[tid] = 0;
+            if (kBias) off_s[tid] = tid < qn ? a.qbias[qbase_s + tid] : 0;
             const int32_t t = tid < qn ? ld_coherent(st.tau + qq) : INT_MAX;
             tau_s[tid] = t;
             jb_s[tid] = (t == INT_MIN || t == INT_MAX) ? 0 : hist_bin(t, st.hlo, st.hsh);
@@ -800,10 +828,17 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                 const int32_t lrow0 = (int32_t)(rowbase_of(cu) - p0) + 4 * g;  // item-local row of (m, i) = (0, 0)
                 const int32_t nloc = (int32_t)(p1 - p0);
                 const bool full = rowbase_of(cu) + 64 <= p1;
+                // a row's score is its sum plus the query's leaf term (residual
+                // variant), so the sums are tested against tau minus that term
+                int32_t ofs[4] = {0, 0, 0, 0};
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) {
                     tq[nt] = max(tq[nt], tau_s[16 * nt + r16]);
                     if (16 * nt + r16 >= qn) tq[nt] = INT_MAX;
+                    if (kBias) {
+                        ofs[nt] = off_s[16 * nt + r16];
+                        tq[nt] = sat_sub(tq[nt], ofs[nt]);
+                    }
                 }
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) {
@@ -830,7 +865,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                             if (mk) {
                                 if (hit)
                                     mylog[log_n + __popcll(mk & lanemask_lt())] =
-                                        ((uint64_t)(uint32_t)acc[m][nt][i] << 32) | qbits | (uint64_t)(uint32_t)lr;
+                                        ((uint64_t)(uint32_t)(kBias ? acc[m][nt][i] + ofs[nt] : acc[m][nt][i])
+                                         << 32) |
+                                        qbits | (uint64_t)(uint32_t)lr;
                                 log_n += __popcll(mk);
                             }
                         }
@@ -974,6 +1011,7 @@ __global__ __launch_bounds__(kStreamThreads) void scan_stream_kernel(MainArgs a)
     __shared__ uint32_t fh_s[kStreamWaves * G * kLB];  // per-wave flush histograms
     __shared__ int32_t tau_s[kQG];
     __shared__ int32_t jb_s[kQG];
+    __shared__ int32_t off_s[kQG];  // residual variant: the item's leaf term per query (0 otherwise)
     __shared__ int64_t item_s, p0_s, p1_s, qbase_s;
     __shared__ int32_t qn_s;
 
@@ -1021,6 +1059,7 @@ __global__ __launch_bounds__(kStreamThreads) void scan_stream_kernel(MainArgs a)
             if (tid < qn) qq = p.leaves ? a.qlist[qbase_s + tid] : (int32_t)(qbase_s + tid);
             qid_s[tid] = qq;
             qapp_s[tid] = 0;
+            off_s[tid] = (a.qbias && tid < qn) ? a.qbias[qbase_s + tid] : 0;
             const int32_t t = tid < qn ? ld_coherent(st.tau + qq) : INT_MAX;
             tau_s[tid] = t;
             jb_s[tid] = (t == INT_MIN || t == INT_MAX) ? 0 : hist_bin(t, st.hlo, st.hsh);
@@ -1085,9 +1124,14 @@ __global__ __launch_bounds__(kStreamThreads) void scan_stream_kernel(MainArgs a)
         // thresholds, sums of the G queries for the lane's row, then the filter
         auto finish_row = [&](int64_t row, const StreamAcc<G, kPair>& acc) {
             const bool valid = row < p1;
+            // residual variant: a row scores its sum plus the item's leaf term,
+            // so the sum is tested against the threshold minus that term
             int32_t tq[G];
 #pragma unroll
-            for (int g = 0; g < G; ++g) tq[g] = g < qn ? tau_s[g] : INT_MAX;
+            for (int g = 0; g < G; ++g) {
+                tq[g] = g < qn ? tau_s[g] : INT_MAX;
+                if (a.qbias) tq[g] = sat_sub(tq[g], off_s[g]);
+            }
             int32_t sum[G];
 #pragma unroll
             for (int g = 0; g < G; ++g)
@@ -1104,7 +1148,8 @@ __global__ __launch_bounds__(kStreamThreads) void scan_stream_kernel(MainArgs a)
                     if (mk) {
                         if (hit)
                             mylog[log_n + __popcll(mk & lanemask_lt())] =
-                                ((uint64_t)(uint32_t)sum[g] << 32) | ((uint64_t)g << 16) | (uint64_t)lr;
+                                ((uint64_t)(uint32_t)(sum[g] + (a.qbias ? off_s[g] : 0)) << 32) |
+                                ((uint64_t)g << 16) | (uint64_t)lr;
                         log_n += __popcll(mk);
                     }
                 }
@@ -1240,11 +1285,12 @@ __global__ __launch_bounds__(kSelThreads) void warmup_wave_kernel(Problem p, Sca
             b = p.n;
         }
         const int64_t take = b - a < W - got ? b - a : W - got;
+        const int32_t off = p.leaves ? leaf_bias_at(p, q, j) : 0;
         for (int64_t t = lane; t < take; t += kWave) {
             const int64_t row = a + t;
             const uint8_t* src = code_row(p, row);
             const int32_t ss = seg_step(p);
-            int32_t sv = 0;
+            int32_t sv = off;
             if (al16) {
                 // the whole row's code bytes (at most 8 x 16) in one round trip
                 uint4 seg[kWaveLut / 512];
@@ -1262,7 +1308,7 @@ __global__ __launch_bounds__(kSelThreads) void warmup_wave_kernel(Problem p, Sca
                     }
                 }
             } else {
-                sv = row_sum(lut_s, p.B, src, al4, ss);
+                sv += row_sum(lut_s, p.B, src, al4, ss);
             }
             atomicAdd(&hw_s[hist_bin(sv, st.hlo, st.hsh)], 1u);
         }
@@ -1416,9 +1462,10 @@ __global__ __launch_bounds__(kSelThreads) void fallback_kernel(Problem p, ScanSt
                 b = p.n;
             }
             if (b - a > p.n - m) b = a + (p.n - m);
+            const int32_t off = p.leaves ? leaf_bias_at(p, q, j) : 0;
             for (int64_t t = tid; t < b - a; t += kSelThreads) {
                 const int64_t row = a + t;
-                scratch[m + t] = int_key(row_sum(lut_s, p.B, code_row(p, row), al4, seg_step(p)),
+                scratch[m + t] = int_key(row_sum(lut_s, p.B, code_row(p, row), al4, seg_step(p)) + off,
                                          p.ids ? p.ids[row] : (int32_t)row);
             }
             m += b - a;
@@ -1468,8 +1515,10 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     if (sp.nq == 0) return hipSuccess;
     const ScanLayout lay = scan_layout(sp.nq, sp.B, sp.n, sp.L, sp.nl, sp.R);
     char* base = reinterpret_cast<char*>(ws);
+    const bool biased = sp.leaf_bias != nullptr && sp.leaves != nullptr;
     Problem p{sp.lut, sp.nq, sp.B, sp.codes, sp.stride, sp.n, sp.ids, sp.leaf_offsets, sp.L,
-              sp.leaves, sp.nl, sp.R, sp.out_ids, sp.out_scores, sp.tile_bytes};
+              sp.leaves, sp.nl, sp.R, sp.out_ids, sp.out_scores, sp.tile_bytes,
+              biased ? sp.leaf_bias : nullptr, biased ? sp.bias_bound : 0};
     ScanState st{};
     st.tau = reinterpret_cast<int32_t*>(base + lay.tau);
     st.cnt = reinterpret_cast<uint32_t*>(base + lay.cnt);
@@ -1481,9 +1530,12 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     st.dfr = reinterpret_cast<int32_t*>(base + lay.dfr);
     st.fb = reinterpret_cast<uint64_t*>(base + lay.fb);
     st.cap = lay.cap;
-    st.hlo = -128 * sp.B;  // every sum lies in [-128 B, 127 B], so no sum falls below bin 0's edge
+    // every sum lies in [-128 B, 127 B] (residual variant: widened by the bias
+    // bound on both sides), so no score falls below bin 0's edge
+    const int32_t bb = biased ? sp.bias_bound : 0;
+    st.hlo = -128 * sp.B - bb;
     {
-        const int64_t need = (255LL * sp.B + 1 + kNB - 1) / kNB;
+        const int64_t need = (255LL * sp.B + 2LL * bb + 1 + kNB - 1) / kNB;
         int32_t sh = 0;
         while ((1LL << sh) < need) ++sh;
         st.hsh = sh;
@@ -1532,6 +1584,7 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
         uint32_t* lcur = reinterpret_cast<uint32_t*>(base + lay.lcur);
         int32_t* lqoff = reinterpret_cast<int32_t*>(base + lay.lqoff);
         int32_t* qlist = reinterpret_cast<int32_t*>(base + lay.qlist);
+        int32_t* qbias = reinterpret_cast<int32_t*>(base + lay.qbias);
         int64_t* itemoff = reinterpret_cast<int64_t*>(base + lay.itemoff);
         hipLaunchKernelGGL(zero_u32_kernel, dim3(64), dim3(256), 0, stream, lcnt, (int64_t)sp.L);
         hipLaunchKernelGGL(zero_u32_kernel, dim3(64), dim3(256), 0, stream, lcur, (int64_t)sp.L);
@@ -1540,10 +1593,12 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
         hipLaunchKernelGGL(leaf_count_kernel, dim3(gb), dim3(256), 0, stream, sp.leaves, pairs, sp.L, lcnt);
         hipLaunchKernelGGL(leaf_scan_kernel, dim3(1), dim3(1024), 0, stream, lcnt, sp.leaf_offsets, sp.L, ma.qg,
                            ma.item_pts, lqoff, itemoff);
-        hipLaunchKernelGGL(leaf_scatter_kernel, dim3(gb), dim3(256), 0, stream, sp.leaves, sp.nq, sp.nl, sp.L, lqoff, lcur, qlist);
+        hipLaunchKernelGGL(leaf_scatter_kernel, dim3(gb), dim3(256), 0, stream, sp.leaves, sp.nq, sp.nl, sp.L, lqoff, lcur,
+                           qlist, p.leaf_bias, p.bias_bound, qbias);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         ma.lqoff = lqoff;
         ma.qlist = qlist;
+        ma.qbias = biased ? qbias : nullptr;
         ma.itemoff = itemoff;
     }
     // warm-up rows per query: enough for a first bound; the item-local
@@ -1566,7 +1621,8 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     if (max_items < grid) grid = (int)(max_items > 0 ? max_items : 1);
     if (main_start && (e = hipEventRecord(main_start, stream)) != hipSuccess) return e;
     if (!streaming) {
-        hipLaunchKernelGGL(scan_main_kernel, dim3(grid), dim3(kScanThreads), 0, stream, ma);
+        if (ma.qbias) hipLaunchKernelGGL(scan_main_kernel<true>, dim3(grid), dim3(kScanThreads), 0, stream, ma);
+        else hipLaunchKernelGGL(scan_main_kernel<false>, dim3(grid), dim3(kScanThreads), 0, stream, ma);
     } else {
         const int nseg = ((sp.B + 1) / 2 + 15) / 16;
         if (spair && sg == 1) launch_stream<1, true>(nseg, grid, stbl, stream, ma);

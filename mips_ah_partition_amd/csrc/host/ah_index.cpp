@@ -48,15 +48,17 @@ void nearest_codes(const float* x, const float* cb, int B, int dpb, uint8_t* cod
     }
 }
 
-// Parallel residual u_b . r_b of every block and their sum.
-double block_projections(const float* x, double invn, const float* cb, int B, int dpb, const uint8_t* code,
-                         double* proj) {
+// Parallel residual u_b . r_b of every block and their sum; u = v * invn is the
+// row's unit direction (v = x itself, or the original row when x is a residual).
+double block_projections(const float* x, const float* v, double invn, const float* cb, int B, int dpb,
+                         const uint8_t* code, double* proj) {
     double s = 0.0;
     for (int b = 0; b < B; ++b) {
         const float* xb = x + (int64_t)b * dpb;
+        const float* vb = v + (int64_t)b * dpb;
         const float* cc = cb + ((int64_t)b * kC + code[b]) * dpb;
         double pr = 0.0;
-        for (int t = 0; t < dpb; ++t) pr += (double)xb[t] * invn * ((double)xb[t] - cc[t]);
+        for (int t = 0; t < dpb; ++t) pr += (double)vb[t] * invn * ((double)xb[t] - cc[t]);
         proj[b] = pr;
         s += pr;
     }
@@ -65,12 +67,13 @@ double block_projections(const float* x, double invn, const float* cb, int B, in
 
 // One coordinate-descent sweep over the blocks in order: each block takes the
 // center minimising the row's loss with the other blocks fixed.
-void cd_sweep(const float* x, double invn, const float* cb, int B, int dpb, double eta, uint8_t* code,
-              double* proj) {
+void cd_sweep(const float* x, const float* v, double invn, const float* cb, int B, int dpb, double eta,
+              uint8_t* code, double* proj) {
     double s = 0.0;
     for (int b = 0; b < B; ++b) s += proj[b];
     for (int b = 0; b < B; ++b) {
         const float* xb = x + (int64_t)b * dpb;
+        const float* vb = v + (int64_t)b * dpb;
         const double sm = s - proj[b];
         double best = std::numeric_limits<double>::infinity(), bpr = 0.0;
         int bc = code[b];
@@ -79,7 +82,7 @@ void cd_sweep(const float* x, double invn, const float* cb, int B, int dpb, doub
             double pr = 0.0, nr = 0.0;
             for (int t = 0; t < dpb; ++t) {
                 const double r = (double)xb[t] - cc[t];
-                pr += (double)xb[t] * invn * r;
+                pr += (double)vb[t] * invn * r;
                 nr += r * r;
             }
             const double par = sm + pr;
@@ -92,16 +95,17 @@ void cd_sweep(const float* x, double invn, const float* cb, int B, int dpb, doub
     }
 }
 
-double row_loss(const float* x, const float* cb, int B, int dpb, double eta, const uint8_t* code) {
+double row_loss(const float* x, const float* v, const float* cb, int B, int dpb, double eta, const uint8_t* code) {
     const int d = B * dpb;
-    const double invn = inv_norm(x, d);
+    const double invn = inv_norm(v, d);
     double par = 0.0, nr = 0.0;
     for (int b = 0; b < B; ++b) {
         const float* xb = x + (int64_t)b * dpb;
+        const float* vb = v + (int64_t)b * dpb;
         const float* cc = cb + ((int64_t)b * kC + code[b]) * dpb;
         for (int t = 0; t < dpb; ++t) {
             const double r = (double)xb[t] - cc[t];
-            par += (double)xb[t] * invn * r;
+            par += (double)vb[t] * invn * r;
             nr += r * r;
         }
     }
@@ -133,14 +137,14 @@ bool solve(int n, double* A, double* rhs) {
     return true;
 }
 
-double total_loss(const float* X, int64_t m, int d, int B, int dpb, double eta, const float* cb,
+double total_loss(const float* X, const float* V, int64_t m, int d, int B, int dpb, double eta, const float* cb,
                   const uint8_t* codes, int64_t cstride) {
     std::vector<double> part(kChunks, 0.0);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t ch = 0; ch < kChunks; ++ch) {
         const int64_t a = m * ch / kChunks, z = m * (ch + 1) / kChunks;
         double s = 0.0;
-        for (int64_t i = a; i < z; ++i) s += row_loss(X + i * d, cb, B, dpb, eta, codes + i * cstride);
+        for (int64_t i = a; i < z; ++i) s += row_loss(X + i * d, V + i * d, cb, B, dpb, eta, codes + i * cstride);
         part[ch] = s;
     }
     double s = 0.0;
@@ -154,9 +158,15 @@ extern "C" {
 
 int ahx_train_pq(const float* X, int64_t m, int32_t d, int32_t B, int32_t dpb, double eta, int32_t iters,
                  const int64_t* init_rows, float* codebooks, double* loss_out) {
+    return ahx_train_pq_dir(X, nullptr, m, d, B, dpb, eta, iters, init_rows, codebooks, loss_out);
+}
+
+int ahx_train_pq_dir(const float* X, const float* V, int64_t m, int32_t d, int32_t B, int32_t dpb, double eta,
+                     int32_t iters, const int64_t* init_rows, float* codebooks, double* loss_out) {
     if (!X || !init_rows || !codebooks || m < 1 || B < 1 || dpb < 1 || dpb > 16 || (int64_t)B * dpb != d ||
         iters < 0)
         return -1;
+    if (!V) V = X;
     for (int c = 0; c < kC; ++c)
         if (init_rows[c] < 0 || init_rows[c] >= m) return -1;
     for (int b = 0; b < B; ++b)
@@ -168,11 +178,11 @@ int ahx_train_pq(const float* X, int64_t m, int32_t d, int32_t B, int32_t dpb, d
     std::vector<double> proj((size_t)m * B), invn((size_t)m);
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < m; ++i) {
-        invn[i] = inv_norm(X + i * d, d);
+        invn[i] = inv_norm(V + i * d, d);
         nearest_codes(X + i * d, codebooks, B, dpb, &codes[i * B]);
-        block_projections(X + i * d, invn[i], codebooks, B, dpb, &codes[i * B], &proj[i * B]);
+        block_projections(X + i * d, V + i * d, invn[i], codebooks, B, dpb, &codes[i * B], &proj[i * B]);
     }
-    if (loss_out) loss_out[0] = total_loss(X, m, d, B, dpb, eta, codebooks, codes.data(), B);
+    if (loss_out) loss_out[0] = total_loss(X, V, m, d, B, dpb, eta, codebooks, codes.data(), B);
 
     const int nA = dpb * dpb, nAcc = nA + dpb + 1;
     std::vector<double> acc((size_t)kChunks * kC * nAcc);
@@ -181,7 +191,7 @@ int ahx_train_pq(const float* X, int64_t m, int32_t d, int32_t B, int32_t dpb, d
         // assignment: one coordinate-descent sweep per row
 #pragma omp parallel for schedule(static)
         for (int64_t i = 0; i < m; ++i)
-            cd_sweep(X + i * d, invn[i], codebooks, B, dpb, eta, &codes[i * B], &proj[i * B]);
+            cd_sweep(X + i * d, V + i * d, invn[i], codebooks, B, dpb, eta, &codes[i * B], &proj[i * B]);
 #pragma omp parallel for schedule(static)
         for (int64_t i = 0; i < m; ++i) {
             double t = 0.0;
@@ -197,6 +207,7 @@ int ahx_train_pq(const float* X, int64_t m, int32_t d, int32_t B, int32_t dpb, d
                 double* A0 = &acc[(size_t)ch * kC * nAcc];
                 for (int64_t i = a; i < z; ++i) {
                     const float* xb = X + i * d + (int64_t)b * dpb;
+                    const float* vb = V + i * d + (int64_t)b * dpb;
                     const int c = codes[i * B + b];
                     double* Ac = A0 + c * nAcc;
                     double* rc = Ac + nA;
@@ -204,7 +215,7 @@ int ahx_train_pq(const float* X, int64_t m, int32_t d, int32_t B, int32_t dpb, d
                     double ux = 0.0;
                     double u[16];
                     for (int t = 0; t < dpb; ++t) {
-                        u[t] = (double)xb[t] * invn[i];
+                        u[t] = (double)vb[t] * invn[i];
                         ux += u[t] * xb[t];
                     }
                     const double w = (eta - 1.0) * (sm + ux);
@@ -231,23 +242,30 @@ int ahx_train_pq(const float* X, int64_t m, int32_t d, int32_t B, int32_t dpb, d
 #pragma omp parallel for schedule(static)
             for (int64_t i = 0; i < m; ++i) {
                 const float* xb = X + i * d + (int64_t)b * dpb;
+                const float* vb = V + i * d + (int64_t)b * dpb;
                 const float* cc = codebooks + ((int64_t)b * kC + codes[i * B + b]) * dpb;
                 double pr = 0.0;
-                for (int t = 0; t < dpb; ++t) pr += (double)xb[t] * invn[i] * ((double)xb[t] - cc[t]);
+                for (int t = 0; t < dpb; ++t) pr += (double)vb[t] * invn[i] * ((double)xb[t] - cc[t]);
                 s[i] += pr - proj[i * B + b];
                 proj[i * B + b] = pr;
             }
         }
-        if (loss_out) loss_out[it + 1] = total_loss(X, m, d, B, dpb, eta, codebooks, codes.data(), B);
+        if (loss_out) loss_out[it + 1] = total_loss(X, V, m, d, B, dpb, eta, codebooks, codes.data(), B);
     }
     return 0;
 }
 
 int ahx_encode(const float* X, int64_t n, int32_t d, int32_t B, int32_t dpb, double eta, const float* codebooks,
                int32_t sweeps, uint8_t* codes, int32_t stride) {
+    return ahx_encode_dir(X, nullptr, n, d, B, dpb, eta, codebooks, sweeps, codes, stride);
+}
+
+int ahx_encode_dir(const float* X, const float* V, int64_t n, int32_t d, int32_t B, int32_t dpb, double eta,
+                   const float* codebooks, int32_t sweeps, uint8_t* codes, int32_t stride) {
     if ((n > 0 && (!X || !codes)) || !codebooks || B < 1 || dpb < 1 || dpb > 16 || (int64_t)B * dpb != d ||
         stride < (B + 1) / 2 || sweeps < 0)
         return -1;
+    if (!V) V = X;
 #pragma omp parallel
     {
         std::vector<uint8_t> code(B);
@@ -255,10 +273,11 @@ int ahx_encode(const float* X, int64_t n, int32_t d, int32_t B, int32_t dpb, dou
 #pragma omp for schedule(static)
         for (int64_t i = 0; i < n; ++i) {
             const float* x = X + i * d;
-            const double invn = inv_norm(x, d);
+            const float* v = V + i * d;
+            const double invn = inv_norm(v, d);
             nearest_codes(x, codebooks, B, dpb, code.data());
-            block_projections(x, invn, codebooks, B, dpb, code.data(), proj.data());
-            for (int sw = 0; sw < sweeps; ++sw) cd_sweep(x, invn, codebooks, B, dpb, eta, code.data(), proj.data());
+            block_projections(x, v, invn, codebooks, B, dpb, code.data(), proj.data());
+            for (int sw = 0; sw < sweeps; ++sw) cd_sweep(x, v, invn, codebooks, B, dpb, eta, code.data(), proj.data());
             uint8_t* row = codes + i * (int64_t)stride;
             std::memset(row, 0, (size_t)stride);
             for (int b = 0; b < B; ++b) row[b >> 1] |= (uint8_t)(code[b] << (4 * (b & 1)));
@@ -278,7 +297,7 @@ double ahx_loss(const float* X, int64_t n, int32_t d, int32_t B, int32_t dpb, do
         for (int64_t i = a; i < z; ++i) {
             const uint8_t* row = codes + i * (int64_t)stride;
             for (int b = 0; b < B; ++b) code[b] = (row[b >> 1] >> (4 * (b & 1))) & 15;
-            s += row_loss(X + i * d, codebooks, B, dpb, eta, code.data());
+            s += row_loss(X + i * d, X + i * d, codebooks, B, dpb, eta, code.data());
         }
         part[ch] = s;
     }

@@ -44,6 +44,12 @@ def _host():
         L.ahx_encode.restype = C.c_int
         L.ahx_encode.argtypes = [f32, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_double, f32, C.c_int32,
                                  u8, C.c_int32]
+        L.ahx_train_pq_dir.restype = C.c_int
+        L.ahx_train_pq_dir.argtypes = [f32, C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_double,
+                                       C.c_int32, i64, f32, C.c_void_p]
+        L.ahx_encode_dir.restype = C.c_int
+        L.ahx_encode_dir.argtypes = [f32, C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_double, f32,
+                                     C.c_int32, u8, C.c_int32]
         L.ahx_loss.restype = C.c_double
         L.ahx_loss.argtypes = [f32, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_double, f32, u8, C.c_int32]
         _hl = L
@@ -66,10 +72,22 @@ def relative_threshold_for_eta(d: int, eta: float) -> float:
 
 
 # ------------------------------------------------------------------------- PQ
+def _dirs(dirs, X):
+    if dirs is None:
+        return None, None
+    V = np.ascontiguousarray(dirs, dtype=np.float32)
+    if V.shape != X.shape:
+        raise ValueError("direction rows must match the rows")
+    return V, V.ctypes.data_as(C.c_void_p)
+
+
 def train_codebooks(X: np.ndarray, dpb: int, eta: float, iters: int = ITERS, seed=0, init_rows=None,
-                    return_loss: bool = False):
-    """Anisotropic PQ codebooks float32 [B, 16, dpb] trained on rows X."""
+                    return_loss: bool = False, dirs: np.ndarray | None = None):
+    """Anisotropic PQ codebooks float32 [B, 16, dpb] trained on rows X (dirs:
+    rows whose directions weight the loss instead of X's own, e.g. the original
+    rows when X holds residuals)."""
     X = np.ascontiguousarray(X, dtype=np.float32)
+    V, vp = _dirs(dirs, X)
     m, d = X.shape
     B = d // dpb
     if init_rows is None:
@@ -77,20 +95,24 @@ def train_codebooks(X: np.ndarray, dpb: int, eta: float, iters: int = ITERS, see
     init_rows = np.ascontiguousarray(init_rows, dtype=np.int64)
     cb = np.empty((B, 16, dpb), dtype=np.float32)
     loss = np.empty(iters + 1, dtype=np.float64)
-    rc = _host().ahx_train_pq(X, m, d, B, dpb, float(eta), iters, init_rows, cb, loss.ctypes.data_as(C.c_void_p))
+    rc = _host().ahx_train_pq_dir(X, vp, m, d, B, dpb, float(eta), iters, init_rows, cb,
+                                  loss.ctypes.data_as(C.c_void_p))
     if rc != 0:
         raise ValueError("ahx_train_pq: bad arguments")
     return (cb, loss) if return_loss else cb
 
 
-def encode(X: np.ndarray, codebooks: np.ndarray, eta: float, sweeps: int = 2, stride: int | None = None) -> np.ndarray:
-    """Row-major nibble codes uint8 [n, stride] (low nibble = even block)."""
+def encode(X: np.ndarray, codebooks: np.ndarray, eta: float, sweeps: int = 2, stride: int | None = None,
+           dirs: np.ndarray | None = None) -> np.ndarray:
+    """Row-major nibble codes uint8 [n, stride] (low nibble = even block); dirs
+    as in train_codebooks."""
     X = np.ascontiguousarray(X, dtype=np.float32)
+    V, vp = _dirs(dirs, X)
     cb = np.ascontiguousarray(codebooks, dtype=np.float32)
     B, _, dpb = cb.shape
     stride = (B + 1) // 2 if stride is None else stride
     out = np.empty((X.shape[0], stride), dtype=np.uint8)
-    rc = _host().ahx_encode(X, X.shape[0], X.shape[1], B, dpb, float(eta), cb, sweeps, out, stride)
+    rc = _host().ahx_encode_dir(X, vp, X.shape[0], X.shape[1], B, dpb, float(eta), cb, sweeps, out, stride)
     if rc != 0:
         raise ValueError("ahx_encode: bad arguments")
     return out
@@ -153,29 +175,42 @@ class HostIndex:
     centroids: np.ndarray | None     # float32 [L, d]
     leaf_offsets: np.ndarray | None  # int64 [L+1]
     eta: float
+    residual: bool = False           # codes hold x - centroid(leaf) (the RSLM summary page's relative mode)
 
 
 def build(X: np.ndarray, dpb: int, eta: float, num_leaves: int = 0, seed: int = 0, sample_rows: int = SAMPLE_ROWS,
-          iters: int = ITERS, sweeps: int = 2) -> HostIndex:
-    """Train and encode an index over rows X (float32 [n, d])."""
+          iters: int = ITERS, sweeps: int = 2, residual: bool = False) -> HostIndex:
+    """Train and encode an index over rows X (float32 [n, d]).  residual (with
+    num_leaves > 0): the codebooks are trained on, and the codes encode, each
+    row's residual from its leaf centroid, x - c_leaf (float32), with the
+    anisotropic weight along the original row x (the score error q.(r - r~)
+    has its parallel part along x)."""
     n = X.shape[0]
     rng = np.random.default_rng(seed)
     sample = np.sort(rng.choice(n, min(n, sample_rows), replace=False)) if n > sample_rows else np.arange(n)
     Xs = X[sample]
-    centroids = leaf_offsets = ids = None
+    centroids = leaf_offsets = ids = assign = None
     if num_leaves > 0:
         centroids, _ = kmeans(Xs, num_leaves, iters, seed=rng)
         assign = nearest_centroid(X, centroids)
         ids, leaf_offsets = leaf_sort(assign, num_leaves)
-    cb = train_codebooks(Xs, dpb, eta, iters, seed=rng)
-    codes = encode(X, cb, eta, sweeps)
+    residual = residual and centroids is not None
+    if residual:
+        cb = train_codebooks(Xs - centroids[assign[sample]], dpb, eta, iters, seed=rng, dirs=Xs)
+        codes = np.empty((n, (cb.shape[0] + 1) // 2), dtype=np.uint8)
+        for a in range(0, n, 1 << 18):  # residual rows a chunk at a time
+            b = min(n, a + (1 << 18))
+            codes[a:b] = encode(X[a:b] - centroids[assign[a:b]], cb, eta, sweeps, dirs=X[a:b])
+    else:
+        cb = train_codebooks(Xs, dpb, eta, iters, seed=rng)
+        codes = encode(X, cb, eta, sweeps)
     if ids is not None:
         codes = np.ascontiguousarray(codes[ids])
-    return HostIndex(cb, codes, ids, centroids, leaf_offsets, eta)
+    return HostIndex(cb, codes, ids, centroids, leaf_offsets, eta, residual)
 
 
 def save(path: str, ix: HostIndex) -> None:
-    arrs = {"codebooks": ix.codebooks, "codes": ix.codes, "eta": np.array(ix.eta)}
+    arrs = {"codebooks": ix.codebooks, "codes": ix.codes, "eta": np.array(ix.eta), "residual": np.array(ix.residual)}
     for k in ("ids", "centroids", "leaf_offsets"):
         v = getattr(ix, k)
         if v is not None:
@@ -188,4 +223,5 @@ def save(path: str, ix: HostIndex) -> None:
 def load(path: str) -> HostIndex:
     z = np.load(path, allow_pickle=False)
     g = lambda k: z[k] if k in z.files else None  # noqa: E731
-    return HostIndex(z["codebooks"], z["codes"], g("ids"), g("centroids"), g("leaf_offsets"), float(z["eta"]))
+    res = bool(z["residual"]) if "residual" in z.files else False
+    return HostIndex(z["codebooks"], z["codes"], g("ids"), g("centroids"), g("leaf_offsets"), float(z["eta"]), res)

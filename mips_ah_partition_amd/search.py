@@ -32,6 +32,12 @@ class AHIndex:
             self.base = torch.from_numpy(np.ascontiguousarray(base).view(np.int16)).to(dev).view(torch.bfloat16)
         else:
             self.base = torch.from_numpy(np.ascontiguousarray(base, dtype=np.float32)).to(dev)
+        # residual (leaf-relative) codes: the leaves' scores enter the scan as
+        # per-leaf terms in table units (ah_residual_leaf_bias), clipped to
+        # +-2 * 255 * B (rows whose leaf lies further below the best one cannot
+        # outrank any row of the best leaf)
+        self.residual = bool(getattr(host, "residual", False)) and self.centroids is not None
+        self.bias_bound = min(2 * 255 * int(host.codebooks.shape[0]), 1 << 24)
         self.num_leaves_to_search = num_leaves_to_search
         self.reorder = reorder
         self.final_num_neighbors = final_num_neighbors
@@ -64,7 +70,7 @@ class AHIndex:
             ws = self._workspace("part", ahlib.ah_partition_workspace_bytes(nq, L))
             if "partition" in t:
                 t["partition"][0]()
-            leaves, _ = ahlib.ah_partition_score(Q, self.centroids, nl, workspace=ws, stream=stream)
+            leaves, leaf_scores = ahlib.ah_partition_score(Q, self.centroids, nl, workspace=ws, stream=stream)
             if "partition" in t:
                 t["partition"][1]()
         if "lut" in t:
@@ -77,10 +83,16 @@ class AHIndex:
         ws = self._workspace("scan", ahlib.ah_scan_workspace_bytes(nq, B, self.codes.shape[0], Lw, nlw, R))
         if "scan" in t:
             t["scan"][0]()
-        cand, _ = ahlib.ah_scan_topk(lut, self.codes, R, ids=self.ids,
-                                     leaf_offsets=self.leaf_offsets if leaves is not None else None,
-                                     leaves=leaves, workspace=ws, stream=stream,
-                                     main_events=t.get("scan_main"))
+        if self.residual and leaves is not None:
+            lb = ahlib.ah_residual_leaf_bias(leaf_scores, scale, self.bias_bound, stream=stream)
+            cand, _ = ahlib.ah_scan_topk(lut, self.codes, R, ids=self.ids, leaf_offsets=self.leaf_offsets,
+                                         leaves=leaves, workspace=ws, stream=stream, leaf_bias=lb,
+                                         bias_bound=self.bias_bound)
+        else:
+            cand, _ = ahlib.ah_scan_topk(lut, self.codes, R, ids=self.ids,
+                                         leaf_offsets=self.leaf_offsets if leaves is not None else None,
+                                         leaves=leaves, workspace=ws, stream=stream,
+                                         main_events=t.get("scan_main"))
         if "scan" in t:
             t["scan"][1]()
         if "reorder" in t:

@@ -154,3 +154,33 @@ def test_sq8_validation(lib):
     assert lib.ah_sq8_scan_topk(odd, fake, 100, fake, fake, 1000, 64, 10, fake, None, fake, need, None) == -3    # alignment
     assert lib.ah_sq8_scan_topk(fake, fake, 100, fake, fake, 1000, 64, 10, fake, None, fake, need - 1, None) == -4
     assert lib.ah_sq8_scan_topk(fake, None, 100, fake, fake, 1000, 64, 10, fake, None, fake, need, None) == -1
+
+
+def test_residual_validation(lib):
+    vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    lib.ah_scan_topk_residual.argtypes = [vp, i64, i32, vp, i32, i64, vp, vp, i32, vp, i32, vp, i32, i32, vp, vp, vp,
+                                          sz, vp]
+    lib.ah_residual_leaf_bias.argtypes = [vp, vp, i64, i32, i32, vp, vp]
+    fake, odd = vp(4096), vp(4097)  # never dereferenced: every case below fails validation first
+    big = 1 << 40
+    # leaf terms: nl < 1, negative or too large bound, missing pointers, empty batch
+    assert lib.ah_residual_leaf_bias(fake, fake, 4, 0, 10, fake, None) == -2
+    assert lib.ah_residual_leaf_bias(fake, fake, 4, 3, -1, fake, None) == -2
+    assert lib.ah_residual_leaf_bias(fake, fake, 4, 3, (1 << 24) + 1, fake, None) == -3
+    assert lib.ah_residual_leaf_bias(None, fake, 4, 3, 10, fake, None) == -1
+    assert lib.ah_residual_leaf_bias(None, None, 0, 3, 10, None, None) == 0
+    # biased scan: no leaves, no bias, negative or too large bound, unaligned table, small workspace
+    assert lib.ah_scan_topk_residual(fake, 2, 8, fake, 4, 100, None, None, 0, None, 0, fake, 10, 5, fake, fake, fake,
+                                     big, None) == -2
+    assert lib.ah_scan_topk_residual(fake, 2, 8, fake, 4, 100, None, fake, 4, fake, 2, None, 10, 5, fake, fake, fake,
+                                     big, None) == -1
+    assert lib.ah_scan_topk_residual(fake, 2, 8, fake, 4, 100, None, fake, 4, fake, 2, fake, -1, 5, fake, fake, fake,
+                                     big, None) == -2
+    assert lib.ah_scan_topk_residual(fake, 2, 8, fake, 4, 100, None, fake, 4, fake, 2, fake, (1 << 24) + 1, 5, fake,
+                                     fake, fake, big, None) == -3
+    assert lib.ah_scan_topk_residual(odd, 2, 8, fake, 4, 100, None, fake, 4, fake, 2, fake, 10, 5, fake, fake, fake,
+                                     big, None) == -3
+    assert lib.ah_scan_topk_residual(fake, 2, 8, fake, 4, 100, None, fake, 4, fake, 2, fake, 10, 5, fake, fake, fake,
+                                     16, None) == -4
+    assert lib.ah_scan_topk_residual(None, 0, 8, None, 4, 100, None, None, 4, None, 2, None, 10, 5, None, None, None,
+                                     0, None) == 0

@@ -122,3 +122,43 @@ def test_kmeans_and_leaf_sort():
     for l in range(5):
         seg = ids[offs[l]:offs[l + 1]]
         assert (a[seg] == l).all() and (np.diff(seg) > 0).all()
+
+
+def test_direction_rows_default_to_the_rows():
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((1500, 12)).astype(np.float32)
+    init = rng.choice(1500, 16, replace=False)
+    a = ix.train_codebooks(X, 2, 4.0, iters=3, init_rows=init)
+    b = ix.train_codebooks(X, 2, 4.0, iters=3, init_rows=init, dirs=X)
+    assert np.array_equal(a, b)
+    assert np.array_equal(ix.encode(X, a, 4.0), ix.encode(X, a, 4.0, dirs=X))
+
+
+def test_residual_vq_update_is_stationary_along_the_original_rows():
+    """Residual variant, one block: the trained center is a stationary point of
+    (eta-1)(u.(r - c))^2 + |r - c|^2 with u the original row's direction and r
+    the residual (the loss is not stationary with u taken along r)."""
+    rng = np.random.default_rng(6)
+    d, eta = 6, 4.0
+    X = rng.standard_normal((600, d)).astype(np.float32) + 2.0
+    Rr = (X - X.mean(0)).astype(np.float32)  # residuals from one centroid
+    init = rng.choice(600, 16, replace=False)
+    cb = ix.train_codebooks(Rr, d, eta, iters=1, init_rows=init, dirs=X)
+    C0 = Rr[init].astype(np.float64)
+    U = (X / np.linalg.norm(X, axis=1, keepdims=True)).astype(np.float64)
+    D = Rr[:, None, :] - C0[None]
+    L = (eta - 1) * np.einsum("nkd,nd->nk", D, U) ** 2 + (D ** 2).sum(-1)
+    a = L.argmin(1)
+    for j in range(16):
+        m = a == j
+        if not m.any():
+            continue
+        c = cb[0, j].astype(np.float64)
+        Rm, Um = Rr[m].astype(np.float64), U[m]
+        e = Rm - c
+        grad = -2 * ((eta - 1) * (e * Um).sum(1, keepdims=True) * Um + e).sum(0)
+        assert np.abs(grad).max() < 1e-3 * max(1.0, np.abs(Rm).sum())
+        Ur = Rm / np.linalg.norm(Rm, axis=1, keepdims=True)
+        grad_r = -2 * ((eta - 1) * (e * Ur).sum(1, keepdims=True) * Ur + e).sum(0)
+        if m.sum() > 3:
+            assert np.abs(grad_r).max() > 1e-3 * max(1.0, np.abs(Rm).sum())
