@@ -89,11 +89,18 @@ def load_index(w, X):
 
 
 def ground_truth(w, X, Q, torch, k=10, shortlist=64):
-    """Exact top-k by float64 score, (score desc, id asc): an fp32 GPU shortlist
-    of the best `shortlist` rows re-ranked in float64 on the host."""
+    """Exact top-k by float64 score, (score desc, id asc), cached per workload."""
     path = os.path.join(CACHE, f"{w.name}_gt_v{INDEX_VERSION}.npy")
     if os.path.exists(path):
         return np.load(path)
+    gt = exact_topk(X, Q, torch, k, shortlist)
+    np.save(path, gt)
+    return gt
+
+
+def exact_topk(X, Q, torch, k=10, shortlist=64):
+    """Exact top-k by float64 score, (score desc, id asc): an fp32 GPU shortlist
+    of the best `shortlist` rows re-ranked in float64 on the host."""
     Xt = torch.from_numpy(X).cuda()
     gt = np.empty((Q.shape[0], k), dtype=np.int32)
     step = max(1, (1 << 31) // (4 * X.shape[0]))
@@ -106,7 +113,6 @@ def ground_truth(w, X, Q, torch, k=10, shortlist=64):
             s = Xd[c] @ Q[a + i].astype(np.float64)
             gt[a + i] = c[np.lexsort((c, -s))[:k]]
     del Xt
-    np.save(path, gt)
     return gt
 
 
@@ -249,6 +255,27 @@ def stage_probes(torch, ahlib):
         out[f"a2_lut_{name}"] = {"nq": w.nq, "blocks": w.blocks, "ms": ms, "GBps": byt / (ms / 1e3) / 1e9,
                                  "frac_of_8TBps": byt / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
         del C
+    # residual (leaf-relative) codes against raw codes at equal bytes: 100,000 rows of the
+    # 1M x 100 mixture workload, 600 leaves (30 searched), 50 blocks x 2 dims, R = 50, k = 10,
+    # 1,000 queries; indexes trained on the host, the search on the GPU
+    from mips_ah_partition_amd import index as hix
+    from mips_ah_partition_amd.search import AHIndex
+    w = synth.WORKLOADS["glove1m"]
+    Xr = synth.database(w, 100_000)
+    Qr = synth.queries(w, 1000)
+    gt_r = exact_topk(Xr, Qr, torch, 10)
+    Qrd = torch.from_numpy(Qr).cuda()
+    res = {"rows": Xr.shape[0], "d": w.d, "leaves": 600, "searched": 30, "R": 50, "k": 10, "queries": Qr.shape[0]}
+    for tag, residual in (("raw", False), ("residual", True)):
+        host = hix.build(Xr, w.dpb, w.eta, num_leaves=600, residual=residual, iters=8)
+        ai = AHIndex(host, Xr, num_leaves_to_search=30, reorder=50, final_num_neighbors=10)
+        ids_r, _ = ai.search_batched(Qrd)
+        ms = _time_ms(torch, lambda: ai.search_batched(Qrd))
+        res[f"{tag}_recall_at_10"] = recall(ids_r.cpu().numpy(), gt_r)
+        res[f"{tag}_ms"] = ms
+        res[f"{tag}_queries_per_s"] = Qr.shape[0] / (ms / 1e3)
+    out["residual_vs_raw_glove_100k"] = res
+    del Xr, Qrd
     # int8 flat search (second workload): 1M documents x 512 dims, 10,000 queries, R = 100,
     # then the exact fp32 rescore to k = 10; the contraction is int8 MFMA (2 nq n d ops)
     nd, dd, nqs, Rs = 1_000_000, 512, 10_000, 100
