@@ -18,7 +18,9 @@ the passage it follows:
 * page "RSLM: Training-Free Vector Quantization for Approximate Nearest
   Neighbor Search", relative mode (a row coded as its residual from a coarse
   approximation, here its leaf centroid): the biased ``scan_topk`` and
-  ``residual_leaf_bias``;
+  ``residual_leaf_bias``; the same page's training-free rotation quantiser
+  (block Hadamard rotation, Lloyd-Max levels, norm-restoring scale) in
+  ``oracle.rslm``, whose scores are those of ``sq8_topk`` on the expanded levels;
 * same page, section "Measuring recall honestly", and the compression lesson's
   "Measuring what compression costs: recall@k": ``recall_at_k`` and the exact
   ground truth ``brute_force``.

@@ -561,3 +561,93 @@ def test_scan_topk_bias_moves_a_row_across_leaves():
     ids, sc = oracle.scan_topk(lut, codes, 2, leaf_offsets=offs, leaves=leaves,
                                leaf_bias=np.array([[0, 2]], np.int32), bias_bound=10)
     assert ids.tolist() == [[0, 1]] and sc.tolist() == [[5, 5]]
+
+
+# ---------------------------------------------------------------- training-free rotation quantiser
+from oracle import rslm  # noqa: E402
+
+
+def test_rslm_block_layout():
+    assert rslm.blocks(384) == [(0, 128), (128, 256), (256, 384)]
+    assert rslm.blocks(100) == [(0, 64), (36, 100)]
+    assert rslm.blocks(200) == [(0, 128), (72, 200)]
+    assert rslm.blocks(5) == [(0, 4), (1, 5)]
+    assert rslm.blocks(1) == [(0, 1)]
+
+
+def test_rslm_rotate_hand_cases():
+    s = 1 / np.sqrt(2)
+    got = rslm.rotate(np.array([[1.0, 0.0]]), [1, 1], [0, 1])
+    assert np.allclose(got, [[s, s]], atol=1e-15)
+    # signs (1, -1), permutation (1, 0): (3, 4) -> (3, -4) -> (-4, 3) -> ((-4+3)/sqrt2, (-4-3)/sqrt2)
+    got = rslm.rotate(np.array([[3.0, 4.0]]), [1, -1], [1, 0])
+    assert np.allclose(got, [[-s, -7 * s]], atol=1e-14)
+
+
+def _sylvester(b):
+    H = np.array([[1.0]])
+    while H.shape[0] < b:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+@pytest.mark.parametrize("d", [4, 64, 128])
+def test_rslm_single_block_is_sylvester_hadamard(d):
+    got = rslm.rotate(np.eye(d), np.ones(d), np.arange(d))
+    assert np.allclose(got, _sylvester(d) / np.sqrt(d), atol=1e-13)
+
+
+@pytest.mark.parametrize("d", [5, 100, 200, 384])
+def test_rslm_rotation_is_orthogonal(d):
+    rng = np.random.default_rng(d)
+    signs = rng.choice([-1.0, 1.0], d)
+    perm = rng.permutation(d)
+    R = rslm.rotate(np.eye(d), signs, perm)  # rows are the images of the unit vectors
+    assert np.allclose(R @ R.T, np.eye(d), atol=1e-12)
+    X = rng.standard_normal((20, d))
+    assert np.allclose(np.linalg.norm(rslm.rotate(X, signs, perm), axis=1), np.linalg.norm(X, axis=1), rtol=1e-12)
+
+
+def test_rslm_lloyd_max_levels():
+    from scipy import integrate
+    L = rslm.lloyd_max_gaussian(16)
+    assert np.allclose(L, -L[::-1], atol=1e-12)
+    # optimality: each level is the conditional mean of its cell (checked by quadrature)
+    m = 0.5 * (L[:-1] + L[1:])
+    edges = np.concatenate([[-np.inf], m, [np.inf]])
+    pdf = lambda z: np.exp(-0.5 * z * z) / np.sqrt(2 * np.pi)  # noqa: E731
+    for c in range(16):
+        a, b = edges[c], edges[c + 1]
+        num = integrate.quad(lambda z: z * pdf(z), a, b, epsabs=1e-13)[0]
+        den = integrate.quad(pdf, a, b, epsabs=1e-13)[0]
+        assert abs(num / den - L[c]) < 1e-8
+    # Max's (1960) table for 16 levels
+    want = [0.1284, 0.3881, 0.6568, 0.9424, 1.2562, 1.6180, 2.0690, 2.7326]
+    assert np.allclose(L[8:], want, atol=5e-4)
+
+
+def test_rslm_encode_hand_case():
+    L = rslm.lloyd_max_gaussian(16).astype(np.float32)
+    # y = (1, -1, 2, 0): |y|^2 = 6, u = y * 2/sqrt(6) = (0.816, -0.816, 1.633, 0): nearest
+    # levels 0.9424 (index 11), -0.9424 (4), 1.6180 (13), and 0 lies on the midpoint of
+    # +-0.1284, which goes to the lower level (7)
+    codes, step = rslm.encode(np.array([[1.0, -1.0, 2.0, 0.0]], np.float32), L)
+    assert codes.tolist() == [[11 | (4 << 4), 13 | (7 << 4)]]
+    lv = L[[11, 4, 13, 7]].astype(np.float64)
+    _, lam = rslm.int8_levels(L)
+    assert step[0] == np.float32(np.sqrt(6.0) / np.sqrt((lv * lv).sum()) / lam)
+    assert rslm.expand(codes, 4, rslm.int8_levels(L)[0]).tolist() == [
+        [int(v) for v in np.rint(L[[11, 4, 13, 7]].astype(np.float64) * lam)]]
+
+
+def test_rslm_reconstruction_keeps_the_norm():
+    rng = np.random.default_rng(12)
+    L = rslm.lloyd_max_gaussian(16).astype(np.float32)
+    Y = rng.standard_normal((50, 96)).astype(np.float32) * rng.random((50, 1)).astype(np.float32) * 5
+    codes, step = rslm.encode(Y, L)
+    lv8, lam = rslm.int8_levels(L)
+    nib = np.empty((50, 96), np.int64)
+    nib[:, 0::2], nib[:, 1::2] = codes & 15, codes >> 4
+    rec = (step.astype(np.float64) * lam)[:, None] * L[nib].astype(np.float64)
+    assert np.allclose(np.linalg.norm(rec, axis=1), np.linalg.norm(Y.astype(np.float64), axis=1), rtol=1e-6)
+    assert lv8[-1] == 127 and lv8[0] == -127 and (lv8 == -lv8[::-1]).all()
