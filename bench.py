@@ -290,6 +290,32 @@ def stage_probes(torch, ahlib):
     ms_s = _time_ms(torch, lambda: ahlib.ah_sq8_scan_topk(q8, qsc, d8, dsc, Rs, ids_out=ids, scores_out=scs,
                                                           workspace=wss), runs=3)
     ms_r = _time_ms(torch, lambda: ahlib.ah_reorder_exact(Qv, Dv, ids, 10), runs=3)
+    gt_v = exact_topk(Dv.cpu().numpy(), Qv.cpu().numpy(), torch, 10)
+    f_ids, _ = ahlib.ah_reorder_exact(Qv, Dv, ids, 10)
+    sq8_recall = recall(f_ids.cpu().numpy(), gt_v)
+    sq8_recall_cand = recall(ids[:, :10].cpu().numpy(), gt_v)
+    # the training-free rotation quantiser on the same corpus: 4-bit codes (256 MB instead of
+    # the int8 rows' 512 MB), the same int8 matrix-core scan reading them, the same rescore
+    from mips_ah_partition_amd.rslm import RSLMIndex
+    signs, perm = synth.rotation_draws(dd, 1)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    rix = RSLMIndex(Dv, signs, perm)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_build = t0.elapsed_time(t1)
+    r_ids, _ = rix.search(Qv, Rs, base=Dv, k=10)
+    r_cand, _ = rix.search(Qv, Rs)
+    ms_rs = _time_ms(torch, lambda: rix.search(Qv, Rs, base=Dv, k=10), runs=3)
+    out["rslm4_flat_1m_x_512"] = {"docs": nd, "d": dd, "queries": nqs, "R": Rs, "k": 10, "code_bytes_per_doc": dd // 2,
+                                  "encode_ms": ms_build, "search_ms": ms_rs,
+                                  "queries_per_s": nqs / (ms_rs / 1e3),
+                                  "recall_at_10": recall(r_ids.cpu().numpy(), gt_v),
+                                  "recall_at_10_before_rescore": recall(r_cand[:, :10].cpu().numpy(), gt_v),
+                                  "int8_recall_at_10_same_corpus": sq8_recall,
+                                  "int8_recall_at_10_before_rescore": sq8_recall_cand}
+    del rix
     ops = 2.0 * nqs * nd * dd
     out["sq8_flat_1m_x_512"] = {"docs": nd, "d": dd, "queries": nqs, "R": Rs, "k": 10,
                                 "quantize_queries_ms": ms_q, "scan_topk_ms": ms_s, "rescore_ms": ms_r,

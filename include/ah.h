@@ -173,6 +173,50 @@ int ah_sq8_scan_topk(const int8_t* q8, const float* q_scale, int64_t nq, const i
                      size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Training-free rotation quantiser (page "RSLM: Training-Free Vector
+ * Quantization for Approximate Nearest Neighbor Search", method points: a
+ * block-wise cascaded fast Walsh-Hadamard rotation of block size 128 with sign
+ * flips and a permutation, the tail dimensions handled by an overlapping block;
+ * a fixed Lloyd-Max codebook of at most 16 centroids for the rotated
+ * coordinates; a global scale restoring the L2 norm of the final
+ * reconstruction), 4 bits per dimension, scored on the int8 matrix cores.
+ *
+ * ah_rslm_rotate: y = rotation of x, per row: v = x * signs, v'[j] = v[perm[j]],
+ * then the orthonormal Sylvester Hadamard H_b / sqrt(b) on the blocks [k b,
+ * (k+1) b), k < d / b, and, when b does not divide d, on the tail block
+ * [d - b, d) last (b = min(128, largest power of two <= d)).  float32 butterflies.
+ *   x, y_out float32 [n][d];  signs float32 [d] (+-1);  perm int32 [d] (a permutation)
+ * Errors: AH_ERR_SHAPE (n < 0, d < 1), AH_ERR_UNSUPPORTED (d > AH_MAX_DIM), AH_ERR_NULL.
+ *
+ * ah_rslm_encode: 4-bit codes of rotated rows against 16 ascending levels
+ * (host memory; the Lloyd-Max levels of N(0,1)): f = float32(sqrt(d) / |y|)
+ * (0 for a zero row), u = y * f (float32), code = number of midpoints
+ * float32((L[c] + L[c+1]) / 2) strictly below u (the nearest level, ties to the
+ * lower); step = (|y| / |L[code]|) / Lam with Lam = 127 / L[15] (squares summed
+ * in float64), so that step * Lam * L[code] has the row's norm.
+ *   y float32 [n][d];  codes_out uint8 [n][ceil(d/2)] (low nibble = even
+ *   dimension);  step_out float32 [n]
+ * Errors: AH_ERR_SHAPE (n < 0, d < 1, levels not strictly increasing or
+ * L[15] <= 0), AH_ERR_UNSUPPORTED (d > AH_MAX_DIM), AH_ERR_NULL.
+ *
+ * ah_rslm_scan_topk: the int8 flat search (ah_sq8_scan_topk) with each
+ * document's int8 values levels_i8[code] (host memory, 16 bytes; usually
+ * rint(L[c] * Lam)) read from its 4-bit codes, and step as the document step:
+ * score = ((float)(q8 . levels_i8[codes]) * q_scale) * step, top-R by (score
+ * desc, id asc).  q8 and q_scale are the rotated queries' int8 codes and steps
+ * from ah_sq8_quantize.
+ *   codes uint8 [n][d/2], 8-byte aligned;  workspace >= ah_sq8_workspace_bytes(nq, n, d, R)
+ * Errors: as ah_sq8_scan_topk (codes not 8-byte aligned: AH_ERR_UNSUPPORTED).
+ */
+int ah_rslm_rotate(const float* x, int64_t n, int32_t d, const float* signs, const int32_t* perm, float* y_out,
+                   void* stream);
+int ah_rslm_encode(const float* y, int64_t n, int32_t d, const float* levels, uint8_t* codes_out, float* step_out,
+                   void* stream);
+int ah_rslm_scan_topk(const int8_t* q8, const float* q_scale, int64_t nq, const uint8_t* codes, const float* step,
+                      int64_t n, int32_t d, const int8_t* levels_i8, int32_t R, int32_t* ids_out, float* scores_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Partition assignment (the k-means assignment step behind the partition the
  * first stage searches; ScaNN page, section "Three stages of a search"): each
  * row goes to the centroid nearest to it.

@@ -12,6 +12,7 @@ from __future__ import annotations
 import ctypes as C
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,6 +30,7 @@ EXPORTS = (
     "ah_scan_workspace_bytes", "ah_scan_topk", "ah_scan_topk_timed",
     "ah_residual_leaf_bias", "ah_scan_topk_residual",
     "ah_sq8_quantize", "ah_sq8_workspace_bytes", "ah_sq8_scan_topk",
+    "ah_rslm_rotate", "ah_rslm_encode", "ah_rslm_scan_topk",
     "ah_assign_workspace_bytes", "ah_assign_leaves",
     "ah_encode", "ah_tiled_codes_bytes", "ah_tile_codes",
     "ah_reorder_exact",
@@ -71,6 +73,12 @@ def lib() -> C.CDLL:
                                             vp, sz, vp]
         L.ah_residual_leaf_bias.restype = C.c_int
         L.ah_residual_leaf_bias.argtypes = [vp, vp, i64, i32, i32, vp, vp]
+        L.ah_rslm_rotate.restype = C.c_int
+        L.ah_rslm_rotate.argtypes = [vp, i64, i32, vp, vp, vp, vp]
+        L.ah_rslm_encode.restype = C.c_int
+        L.ah_rslm_encode.argtypes = [vp, i64, i32, vp, vp, vp, vp]
+        L.ah_rslm_scan_topk.restype = C.c_int
+        L.ah_rslm_scan_topk.argtypes = [vp, vp, i64, vp, vp, i64, i32, vp, i32, vp, vp, vp, sz, vp]
         L.ah_sq8_quantize.restype = C.c_int
         L.ah_sq8_quantize.argtypes = [vp, i64, i32, C.c_double, vp, vp, vp]
         L.ah_sq8_workspace_bytes.restype = sz
@@ -223,6 +231,66 @@ def ah_sq8_scan_topk(q8, q_scale, d8, d_scale, R, ids_out=None, scores_out=None,
     _check(lib().ah_sq8_scan_topk(_ptr(q8), _ptr(q_scale), nq, _ptr(d8), _ptr(d_scale), n, d, int(R), _ptr(ids_out),
                                   _ptr(scores_out), _ptr(workspace), workspace.numel(), _stream(stream)),
            "ah_sq8_scan_topk")
+    return ids_out, scores_out
+
+
+def ah_rslm_rotate(x, signs, perm, y_out=None, stream=None):
+    """Block Hadamard rotation of rows (sign flips, permutation, blocks of up to 128)."""
+    x = _dev(x, torch.float32, "x", 2)
+    n, d = x.shape
+    signs = _dev(signs, torch.float32, "signs", 1)
+    perm = _dev(perm, torch.int32, "perm", 1)
+    if signs.numel() != d or perm.numel() != d:
+        raise ValueError("signs and perm need d entries")
+    if y_out is None:
+        y_out = torch.empty_like(x)
+    _dev(y_out, torch.float32, "y_out", 2)
+    _check(lib().ah_rslm_rotate(_ptr(x), n, d, _ptr(signs), _ptr(perm), _ptr(y_out), _stream(stream)),
+           "ah_rslm_rotate")
+    return y_out
+
+
+def ah_rslm_encode(y, levels, codes_out=None, step_out=None, stream=None):
+    """4-bit nearest-level codes of rotated rows and the norm-restoring row steps;
+    levels: 16 ascending floats (host)."""
+    y = _dev(y, torch.float32, "y", 2)
+    n, d = y.shape
+    lv = np.ascontiguousarray(levels, dtype=np.float32)
+    if lv.shape != (16,):
+        raise ValueError("16 levels")
+    if codes_out is None:
+        codes_out = torch.empty((n, (d + 1) // 2), dtype=torch.uint8, device=y.device)
+    if step_out is None:
+        step_out = torch.empty(n, dtype=torch.float32, device=y.device)
+    _dev(codes_out, torch.uint8, "codes_out", 2)
+    _dev(step_out, torch.float32, "step_out", 1)
+    _check(lib().ah_rslm_encode(_ptr(y), n, d, lv.ctypes.data_as(C.c_void_p), _ptr(codes_out), _ptr(step_out),
+                                _stream(stream)), "ah_rslm_encode")
+    return codes_out, step_out
+
+
+def ah_rslm_scan_topk(q8, q_scale, codes, step, d, levels_i8, R, ids_out=None, scores_out=None, workspace=None,
+                      stream=None):
+    """Top-R documents per query over 4-bit codes standing for the int8 values levels_i8 (16, host)."""
+    q8 = _dev(q8, torch.int8, "q8", 2)
+    q_scale = _dev(q_scale, torch.float32, "q_scale", 1)
+    codes = _dev(codes, torch.uint8, "codes", 2)
+    step = _dev(step, torch.float32, "step", 1)
+    nq = q8.shape[0]
+    n = codes.shape[0]
+    lv = np.ascontiguousarray(levels_i8, dtype=np.int8)
+    if lv.shape != (16,) or q8.shape[1] != d or codes.shape[1] != (d + 1) // 2:
+        raise ValueError("shapes")
+    if ids_out is None:
+        ids_out = torch.empty((nq, R), dtype=torch.int32, device=q8.device)
+    if scores_out is None:
+        scores_out = torch.empty((nq, R), dtype=torch.float32, device=q8.device)
+    need = ah_sq8_workspace_bytes(nq, n, d, R)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q8.device)
+    _check(lib().ah_rslm_scan_topk(_ptr(q8), _ptr(q_scale), nq, _ptr(codes), _ptr(step), n, d,
+                                   lv.ctypes.data_as(C.c_void_p), int(R), _ptr(ids_out), _ptr(scores_out),
+                                   _ptr(workspace), workspace.numel(), _stream(stream)), "ah_rslm_scan_topk")
     return ids_out, scores_out
 
 

@@ -155,6 +155,45 @@ int ah_sq8_scan_topk(const int8_t* q8, const float* q_scale, int64_t nq, const i
                                           static_cast<hipStream_t>(stream)));
 }
 
+int ah_rslm_rotate(const float* x, int64_t n, int32_t d, const float* signs, const int32_t* perm, float* y_out,
+                   void* stream) {
+    if (n < 0 || d < 1) return AH_ERR_SHAPE;
+    if (d > AH_MAX_DIM) return AH_ERR_UNSUPPORTED;
+    if (n == 0) return AH_OK;
+    if (!x || !signs || !perm || !y_out) return AH_ERR_NULL;
+    return hip_status(ah::launch_rslm_rotate(x, n, d, signs, perm, y_out, static_cast<hipStream_t>(stream)));
+}
+
+int ah_rslm_encode(const float* y, int64_t n, int32_t d, const float* levels, uint8_t* codes_out, float* step_out,
+                   void* stream) {
+    if (n < 0 || d < 1) return AH_ERR_SHAPE;
+    if (d > AH_MAX_DIM) return AH_ERR_UNSUPPORTED;
+    if (!levels) return AH_ERR_NULL;
+    for (int c = 0; c < 15; ++c)
+        if (!(levels[c] < levels[c + 1])) return AH_ERR_SHAPE;
+    if (!(levels[15] > 0.0f)) return AH_ERR_SHAPE;
+    if (n == 0) return AH_OK;
+    if (!y || !codes_out || !step_out) return AH_ERR_NULL;
+    float mids[15];
+    for (int c = 0; c < 15; ++c) mids[c] = (float)(((double)levels[c] + (double)levels[c + 1]) / 2.0);
+    const double lam = 127.0 / (double)levels[15];
+    return hip_status(ah::launch_rslm_encode(y, n, d, levels, mids, lam, codes_out, step_out,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int ah_rslm_scan_topk(const int8_t* q8, const float* q_scale, int64_t nq, const uint8_t* codes, const float* step,
+                      int64_t n, int32_t d, const int8_t* levels_i8, int32_t R, int32_t* ids_out, float* scores_out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (nq < 0 || n < 1 || d < 1 || R < 1 || R > n) return AH_ERR_SHAPE;
+    if (d % 16 != 0 || d > AH_MAX_DIM || R > AH_MAX_R || n >= ((int64_t)1 << 31)) return AH_ERR_UNSUPPORTED;
+    if (nq == 0) return AH_OK;
+    if (!q8 || !q_scale || !codes || !step || !levels_i8 || !ids_out) return AH_ERR_NULL;
+    if (!a16(q8) || (reinterpret_cast<uintptr_t>(codes) & 7)) return AH_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < ah::sq8_workspace_bytes(nq, n, d, R)) return AH_ERR_WORKSPACE;
+    return hip_status(ah::launch_sq8_topk(q8, q_scale, nq, nullptr, step, n, d, R, ids_out, scores_out, workspace,
+                                          static_cast<hipStream_t>(stream), codes, levels_i8));
+}
+
 size_t ah_assign_workspace_bytes(int64_t n, int32_t L) {
     if (n < 0 || L < 1) return 0;
     return ah::assign_workspace_bytes(n, L);

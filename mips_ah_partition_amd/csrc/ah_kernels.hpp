@@ -55,9 +55,18 @@ hipError_t launch_list_topk(const float* S, const int32_t* idmap, const uint32_t
 hipError_t launch_sq8_quantize(const float* x, int64_t n, int32_t d, double pct, int8_t* codes, float* scale,
                                hipStream_t stream);
 size_t sq8_workspace_bytes(int64_t nq, int64_t n, int32_t d, int32_t R);
+// d4 non-null: the documents are 4-bit codes [n][d/2] standing for the int8
+// values levels[16] (host memory), instead of int8 rows d8.
 hipError_t launch_sq8_topk(const int8_t* q8, const float* qs, int64_t nq, const int8_t* d8, const float* ds,
                            int64_t n, int32_t d, int32_t R, int32_t* ids, float* scores, void* ws,
-                           hipStream_t stream);
+                           hipStream_t stream, const uint8_t* d4 = nullptr, const int8_t* levels = nullptr);
+
+// Training-free rotation quantiser: block Hadamard rotation of rows, and the
+// nearest-level 4-bit encoding with the norm-restoring row step.
+hipError_t launch_rslm_rotate(const float* x, int64_t n, int32_t d, const float* signs, const int32_t* perm,
+                              float* y, hipStream_t stream);
+hipError_t launch_rslm_encode(const float* y, int64_t n, int32_t d, const float* levels, const float* mids,
+                              double lam, uint8_t* codes, float* step, hipStream_t stream);
 
 size_t assign_workspace_bytes(int64_t n, int32_t L);
 hipError_t launch_assign(const float* x, int64_t n, int32_t d, const float* cent, int32_t L, int32_t* leaves,

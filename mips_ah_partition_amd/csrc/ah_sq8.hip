@@ -162,6 +162,50 @@ struct SqOut {
     int32_t cap;
 };
 
+// The documents' codes: int8 rows [n][d], or (d4 non-null) 4-bit codes [n][d/2]
+// (low nibble = even dimension) whose nibbles stand for the int8 values lv
+// (16 bytes, nibble c -> byte c), expanded as they are loaded.
+struct DocSrc {
+    const int8_t* d8;
+    const uint8_t* d4;
+    uint32_t lv[4];
+};
+
+__device__ __forceinline__ uint32_t nib_value(const DocSrc& s, uint32_t c) {
+    const uint32_t w = c < 8 ? (c < 4 ? s.lv[0] : s.lv[1]) : (c < 12 ? s.lv[2] : s.lv[3]);
+    return (w >> (8 * (c & 3))) & 255u;
+}
+
+// The 16 values k = kk .. kk+15 of document row r (kk a multiple of 16, below d).
+// kForm: 0 = either (decided by d4), 1 = int8 rows, 2 = 4-bit codes.
+template <int kForm = 0>
+__device__ __forceinline__ v4i doc_chunk(const DocSrc& s, int64_t r, int32_t d, int kk) {
+    if (kForm == 1 || (kForm == 0 && !s.d4)) return *reinterpret_cast<const v4i*>(s.d8 + r * d + kk);
+    const uint2 c = *reinterpret_cast<const uint2*>(s.d4 + r * (d >> 1) + (kk >> 1));
+    v4i out;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t h = ((w < 2 ? c.x : c.y) >> (16 * (w & 1))) & 0xFFFFu;  // dimensions kk+4w .. kk+4w+3
+        out[w] = (int)(nib_value(s, h & 15u) | (nib_value(s, (h >> 4) & 15u) << 8) |
+                       (nib_value(s, (h >> 8) & 15u) << 16) | (nib_value(s, h >> 12) << 24));
+    }
+    return out;
+}
+
+// The document-stationary kernel's argument: only what its form needs.
+template <bool kNib>
+struct DocArg {
+    const int8_t* d8;
+    __device__ v4i chunk(int64_t r, int32_t d, int kk) const {
+        return *reinterpret_cast<const v4i*>(d8 + r * d + kk);
+    }
+};
+template <>
+struct DocArg<true> {
+    DocSrc s;
+    __device__ v4i chunk(int64_t r, int32_t d, int kk) const { return doc_chunk<2>(s, r, d, kk); }
+};
+
 // The rescaled score of one (query, document) pair: the same expression in
 // every mode, so the threshold and the candidates agree bit for bit.
 __device__ __forceinline__ float sq8_score(int32_t dot, float sq, float sd) {
@@ -174,7 +218,7 @@ __device__ __forceinline__ float sq8_score(int32_t dot, float sq, float sd) {
 template <int kMode>
 __global__ __launch_bounds__(kSqThreads) void sq8_scores_kernel(const int8_t* __restrict__ q8,
                                                                 const float* __restrict__ qs, int64_t nq,
-                                                                const int8_t* __restrict__ d8,
+                                                                DocSrc dsrc,
                                                                 const float* __restrict__ ds, int64_t n, int32_t d,
                                                                 int64_t ndt, SqOut o) {
     const int w = threadIdx.x / kWave, lane = lane_id();
@@ -198,12 +242,12 @@ __global__ __launch_bounds__(kSqThreads) void sq8_scores_kernel(const int8_t* __
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[m][t] = v4i{0, 0, 0, 0};
     // row pointers (rows past the end read the last row; their results are dropped)
-    const int8_t* arow[4];
+    int64_t arow[4];
     const int8_t* brow[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int64_t r = doc0 + 16 * m + r16;
-        arow[m] = d8 + (r < n ? r : n - 1) * d;
+        arow[m] = r < n ? r : n - 1;
         const int64_t c = q0 + 16 * m + r16;
         brow[m] = q8 + (c < nq ? c : nq - 1) * d;
     }
@@ -213,7 +257,7 @@ __global__ __launch_bounds__(kSqThreads) void sq8_scores_kernel(const int8_t* __
         v4i a[4], b[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            a[m] = in ? *reinterpret_cast<const v4i*>(arow[m] + kk) : v4i{0, 0, 0, 0};
+            a[m] = in ? doc_chunk(dsrc, arow[m], d, kk) : v4i{0, 0, 0, 0};
             b[m] = in ? *reinterpret_cast<const v4i*>(brow[m] + kk) : v4i{0, 0, 0, 0};
         }
 #pragma unroll
@@ -342,10 +386,10 @@ __device__ __forceinline__ void ds_stage_store(int8_t* buf, float* meta, int tid
     if (tid < 128) meta[tid] = st.meta;
 }
 
-template <int KS, int kMode>
+template <int KS, int kMode, bool kNib>
 __global__ __launch_bounds__(kDsThreads, 1) void sq8_dstat_kernel(const int8_t* __restrict__ q8,
                                                                    const float* __restrict__ qs, int64_t nq,
-                                                                   const int8_t* __restrict__ d8,
+                                                                   DocArg<kNib> dsrc,
                                                                    const float* __restrict__ ds, int64_t n, int32_t d,
                                                                    int64_t ndt, int64_t qb_per, SqOut o) {
     constexpr int kRow = KS * 64 + 16;
@@ -383,11 +427,10 @@ __global__ __launch_bounds__(kDsThreads, 1) void sq8_dstat_kernel(const int8_t* 
     for (int m = 0; m < kDsM; ++m) {
         int64_t r = doc0 + 16 * m + r16;
         r = r < n ? r : n - 1;  // rows past the end read the last row; their results are dropped
-        const int8_t* row = d8 + r * d;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int kk = ks * 64 + 16 * g;
-            a[ks][m] = kk < d ? *reinterpret_cast<const v4i*>(row + kk) : v4i{0, 0, 0, 0};
+            a[ks][m] = kk < d ? dsrc.chunk(r, d, kk) : v4i{0, 0, 0, 0};
         }
     }
     float sdv[kDsM][4];
@@ -549,7 +592,7 @@ struct SlotKeys {
 
 __global__ __launch_bounds__(kSqThreads) void sq8_fallback_kernel(const int8_t* __restrict__ q8,
                                                                   const float* __restrict__ qs, int64_t nq,
-                                                                  const int8_t* __restrict__ d8,
+                                                                  DocSrc dsrc,
                                                                   const float* __restrict__ ds, int64_t n, int32_t d,
                                                                   int32_t R, const uint32_t* __restrict__ cnt,
                                                                   int32_t cap, float* __restrict__ slots,
@@ -563,11 +606,10 @@ __global__ __launch_bounds__(kSqThreads) void sq8_fallback_kernel(const int8_t* 
         const int8_t* qr = q8 + q * d;
         const float sq = qs[q];
         for (int64_t i = tid; i < n; i += kSqThreads) {
-            const int8_t* dr = d8 + i * d;
             int32_t dot = 0;
             for (int k = 0; k < d; k += 16) {
                 const v4i a = *reinterpret_cast<const v4i*>(qr + k);
-                const v4i b = *reinterpret_cast<const v4i*>(dr + k);
+                const v4i b = doc_chunk(dsrc, i, d, k);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) dot = __builtin_amdgcn_sdot4(a[j], b[j], dot, false);
             }
@@ -646,7 +688,7 @@ size_t sq8_workspace_bytes(int64_t nq, int64_t n, int32_t d, int32_t R) { return
 // One scoring pass over `units` work units along the documents (256-document
 // tiles, or for the group maxima four sampled groups per unit).
 template <int kMode, int KS>
-static void launch_dstat(const int8_t* q8, const float* qs, int64_t m, const int8_t* d8, const float* ds, int64_t n,
+static void launch_dstat(const int8_t* q8, const float* qs, int64_t m, const DocSrc& d8, const float* ds, int64_t n,
                          int32_t d, const SqOut& o, hipStream_t stream) {
     const int64_t units = kMode == kSqGroupMax ? (o.G0 + kDsW - 1) / kDsW : (n + kDsDocs - 1) / kDsDocs;
     const int64_t nqb = (m + kDsQB - 1) / kDsQB;
@@ -655,12 +697,16 @@ static void launch_dstat(const int8_t* q8, const float* qs, int64_t m, const int
     split = split < most ? split : most;
     const int64_t per = (nqb + split - 1) / split;
     split = (nqb + per - 1) / per;
-    hipLaunchKernelGGL((sq8_dstat_kernel<KS, kMode>), dim3((unsigned)(units * split)), dim3(kDsThreads), 0, stream,
-                       q8, qs, m, d8, ds, n, d, units, per, o);
+    if (d8.d4)
+        hipLaunchKernelGGL((sq8_dstat_kernel<KS, kMode, true>), dim3((unsigned)(units * split)), dim3(kDsThreads), 0,
+                           stream, q8, qs, m, DocArg<true>{d8}, ds, n, d, units, per, o);
+    else
+        hipLaunchKernelGGL((sq8_dstat_kernel<KS, kMode, false>), dim3((unsigned)(units * split)), dim3(kDsThreads), 0,
+                           stream, q8, qs, m, DocArg<false>{d8.d8}, ds, n, d, units, per, o);
 }
 
 template <int kMode>
-static hipError_t launch_scores(const int8_t* q8, const float* qs, int64_t m, const int8_t* d8, const float* ds,
+static hipError_t launch_scores(const int8_t* q8, const float* qs, int64_t m, const DocSrc& d8, const float* ds,
                                 int64_t n, int32_t d, const SqOut& o, hipStream_t stream) {
     switch ((d + 63) / 64) {
         case 1: launch_dstat<kMode, 1>(q8, qs, m, d8, ds, n, d, o, stream); break;
@@ -681,9 +727,12 @@ static hipError_t launch_scores(const int8_t* q8, const float* qs, int64_t m, co
     return hipGetLastError();
 }
 
-hipError_t launch_sq8_topk(const int8_t* q8, const float* qs, int64_t nq, const int8_t* d8, const float* ds,
+hipError_t launch_sq8_topk(const int8_t* q8, const float* qs, int64_t nq, const int8_t* d8_rows, const float* ds,
                            int64_t n, int32_t d, int32_t R, int32_t* ids, float* scores, void* ws,
-                           hipStream_t stream) {
+                           hipStream_t stream, const uint8_t* d4, const int8_t* levels) {
+    DocSrc d8{d8_rows, d4, {0, 0, 0, 0}};
+    if (d4)
+        for (int c = 0; c < 16; ++c) d8.lv[c >> 2] |= (uint32_t)(uint8_t)levels[c] << (8 * (c & 3));
     if (nq == 0) return hipSuccess;
     const SqPlan p = sq8_plan(nq, n, d, R);
     char* base = reinterpret_cast<char*>(ws);

@@ -180,3 +180,12 @@ def gpu_normal_rows(torch, n: int, d: int, seed: int, dtype, chunk_rows: int = 1
         b = min(n, a + chunk_rows)
         out[a:b] = torch.randn((b - a, d), generator=g, device="cuda").to(dtype)
     return out
+
+
+def rotation_draws(d: int, seed: int):
+    """The random draws of the training-free rotation: signs float32 [d] (+-1)
+    and a permutation int32 [d]."""
+    rng = np.random.default_rng([7000, seed])
+    signs = rng.choice(np.array([-1.0, 1.0], dtype=np.float32), size=d)
+    perm = rng.permutation(d).astype(np.int32)
+    return signs, perm

@@ -184,3 +184,32 @@ def test_residual_validation(lib):
                                      16, None) == -4
     assert lib.ah_scan_topk_residual(None, 0, 8, None, 4, 100, None, None, 4, None, 2, None, 10, 5, None, None, None,
                                      0, None) == 0
+
+
+def test_rslm_validation(lib):
+    vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    lib.ah_rslm_rotate.argtypes = [vp, i64, i32, vp, vp, vp, vp]
+    lib.ah_rslm_encode.argtypes = [vp, i64, i32, vp, vp, vp, vp]
+    lib.ah_rslm_scan_topk.argtypes = [vp, vp, i64, vp, vp, i64, i32, vp, i32, vp, vp, vp, sz, vp]
+    fake = vp(4096)  # device pointers are never dereferenced: every case fails validation first
+    assert lib.ah_rslm_rotate(fake, 10, 0, fake, fake, fake, None) == -2
+    assert lib.ah_rslm_rotate(fake, 10, 20000, fake, fake, fake, None) == -3
+    assert lib.ah_rslm_rotate(None, 10, 8, fake, fake, fake, None) == -1
+    assert lib.ah_rslm_rotate(None, 0, 8, None, None, None, None) == 0
+    good = (C.c_float * 16)(*[float(c) - 7.5 for c in range(16)])
+    flat = (C.c_float * 16)(*([0.0] * 16))
+    assert lib.ah_rslm_encode(fake, 10, 8, C.cast(flat, vp), fake, fake, None) == -2  # not increasing
+    assert lib.ah_rslm_encode(fake, 10, 8, None, fake, fake, None) == -1
+    assert lib.ah_rslm_encode(None, 10, 8, C.cast(good, vp), fake, fake, None) == -1
+    assert lib.ah_rslm_encode(None, 0, 8, C.cast(good, vp), None, None, None) == 0
+    lv = (C.c_int8 * 16)(*range(-8, 8))
+    big = 1 << 40
+    assert lib.ah_rslm_scan_topk(fake, fake, 4, fake, fake, 100, 40, C.cast(lv, vp), 10, fake, None, fake, big,
+                                 None) == -3  # d % 16
+    assert lib.ah_rslm_scan_topk(fake, fake, 4, vp(4100), fake, 100, 64, C.cast(lv, vp), 10, fake, None, fake, big,
+                                 None) == -3  # codes not 8-byte aligned
+    assert lib.ah_rslm_scan_topk(fake, fake, 4, fake, fake, 100, 64, None, 10, fake, None, fake, big, None) == -1
+    assert lib.ah_rslm_scan_topk(fake, fake, 4, fake, fake, 100, 64, C.cast(lv, vp), 101, fake, None, fake, big,
+                                 None) == -2
+    assert lib.ah_rslm_scan_topk(fake, fake, 4, fake, fake, 100, 64, C.cast(lv, vp), 10, fake, None, fake, 16,
+                                 None) == -4
