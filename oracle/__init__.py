@@ -71,6 +71,7 @@ def lib() -> C.CDLL:
         L.oracle_sq8_topk.argtypes = [_i8p, _f32p, C.c_int64, _i8p, _f32p, C.c_int64, C.c_int32, C.c_int32,
                                       _i32p, _f32p]
         L.oracle_nearest.argtypes = [_f32p, C.c_int64, C.c_int32, _f32p, C.c_int32, _i32p, _f64p]
+        L.oracle_kmeans_update.argtypes = [_f32p, C.c_int64, C.c_int32, _i32p, C.c_int32, _f32p, _i32p]
         L.oracle_encode.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_int32, _f32p, C.c_int32, C.c_int32,
                                     C.c_double, C.c_int32, _u8p, C.c_int32]
         _LIB = L
@@ -243,6 +244,18 @@ def nearest(X, centroids):
     dist = np.empty(n, dtype=np.float64)
     lib().oracle_nearest(X, n, d, Cn, Cn.shape[0], ids, dist)
     return ids, dist
+
+
+def kmeans_update(X, leaf, centroids):
+    """The k-means update: each leaf's centroid becomes the float64 mean of its
+    rows (in row order), rounded to float32; empty leaves keep theirs.
+    Returns (centroids float32 [L, d], counts int32 [L])."""
+    X = _c(X, np.float32)
+    lf = _c(leaf, np.int32)
+    Cn = np.array(centroids, dtype=np.float32, copy=True, order="C")
+    cnt = np.empty(Cn.shape[0], dtype=np.int32)
+    lib().oracle_kmeans_update(X, X.shape[0], X.shape[1], lf, Cn.shape[0], Cn, cnt)
+    return Cn, cnt
 
 
 def encode(rows, codebooks, eta, sweeps=2, stride=None):

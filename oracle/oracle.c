@@ -386,6 +386,29 @@ void oracle_nearest(const float* x, int64_t n, int32_t d, const float* cent, int
     }
 }
 
+/* The update step of the partitioning's k-means (the ScaNN page's partition
+ * groups rows under centroids; a centroid is the mean of its rows, the
+ * textbook Lloyd step the anisotropic trainer reduces to at eta = 1): per leaf,
+ * the float64 sum of its rows in row order divided by their count, rounded to
+ * float32; a leaf with no rows keeps its previous centroid.  counts may be NULL. */
+void oracle_kmeans_update(const float* x, int64_t n, int32_t d, const int32_t* leaf, int32_t L,
+                          float* cent, int32_t* counts) {
+    double* sum = (double*)calloc((size_t)L * (size_t)d, sizeof(double));
+    int64_t* cnt = (int64_t*)calloc((size_t)L, sizeof(int64_t));
+    for (int64_t i = 0; i < n; ++i) {
+        const int32_t l = leaf[i];
+        cnt[l] += 1;
+        for (int32_t t = 0; t < d; ++t) sum[(int64_t)l * d + t] += (double)x[i * d + t];
+    }
+    for (int32_t l = 0; l < L; ++l) {
+        if (counts) counts[l] = (int32_t)cnt[l];
+        if (cnt[l] == 0) continue;
+        for (int32_t t = 0; t < d; ++t) cent[(int64_t)l * d + t] = (float)(sum[(int64_t)l * d + t] / (double)cnt[l]);
+    }
+    free(sum);
+    free(cnt);
+}
+
 /* ----------------------------------------------------------------------------
  * Int8 scalar-quantised flat search (the page "Incoherence-Aware Asymmetric
  * Quantization for Retrieval", sections "A Specialized int8 Retrieval Engine"

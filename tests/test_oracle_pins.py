@@ -651,3 +651,32 @@ def test_rslm_reconstruction_keeps_the_norm():
     rec = (step.astype(np.float64) * lam)[:, None] * L[nib].astype(np.float64)
     assert np.allclose(np.linalg.norm(rec, axis=1), np.linalg.norm(Y.astype(np.float64), axis=1), rtol=1e-6)
     assert lv8[-1] == 127 and lv8[0] == -127 and (lv8 == -lv8[::-1]).all()
+
+
+# ---------------------------------------------------------------- k-means update
+def test_kmeans_update_hand_case_and_empty_leaf():
+    X = np.array([[1, 2], [3, 4], [10, 10], [-1, 0]], np.float32)
+    C0 = np.array([[0, 0], [5, 5], [7, 7]], np.float32)
+    C, cnt = oracle.kmeans_update(X, np.array([0, 0, 1, 0]), C0)
+    # leaf 0: mean of (1,2), (3,4), (-1,0) = (1, 2); leaf 1: (10, 10); leaf 2 empty: kept
+    assert C.tolist() == [[1.0, 2.0], [10.0, 10.0], [7.0, 7.0]] and cnt.tolist() == [3, 1, 0]
+
+
+def test_kmeans_update_minimises_the_within_leaf_squared_distance():
+    rng = np.random.default_rng(21)
+    X = rng.standard_normal((3000, 8)).astype(np.float32) * 3
+    C0 = X[rng.choice(3000, 40, replace=False)]
+    lf, _ = oracle.nearest(X, C0)
+    C, cnt = oracle.kmeans_update(X, lf, C0)
+    Xd = X.astype(np.float64)
+    for l in range(40):
+        m = lf == l
+        if not m.any():
+            continue
+        # the gradient of sum |x - c|^2 vanishes (up to the float32 rounding of c)
+        g = 2 * (C[l].astype(np.float64) * m.sum() - Xd[m].sum(0))
+        assert np.abs(g).max() <= 1e-6 * m.sum() * (np.abs(Xd[m]).max() + 1)
+    # a Lloyd step never raises the objective
+    before = ((Xd - C0[lf]) ** 2).sum()
+    after = ((Xd - C[lf].astype(np.float64)) ** 2).sum()
+    assert after <= before
