@@ -336,6 +336,15 @@ def stage_probes(torch, ahlib):
     tf = 2.0 * na * w.num_leaves * w.d / (ms / 1e3) / 1e12
     out["assign_wiki20m_4M_rows"] = {"rows": na, "leaves": w.num_leaves, "d": w.d, "ms": ms, "TFLOPs": tf,
                                      "frac_of_fp32_mfma": tf / PEAK_FP32_MFMA_TFLOPS}
+    # the k-means update on the same rows and assignment (one Lloyd iteration = assignment + update):
+    # reads the rows once (n d 4 bytes) plus n d float64 atomic adds into L d sums
+    Cu = C.clone()
+    wsk = torch.empty(ahlib.ah_kmeans_workspace_bytes(w.num_leaves, w.d), dtype=torch.uint8, device="cuda")
+    ms_u = _time_ms(torch, lambda: ahlib.ah_kmeans_update(X, lv, Cu, workspace=wsk), runs=3)
+    out["kmeans_update_wiki20m_4M_rows"] = {"rows": na, "leaves": w.num_leaves, "d": w.d, "ms": ms_u,
+                                            "row_GBps": na * w.d * 4 / (ms_u / 1e3) / 1e9,
+                                            "atomic_adds_per_s": na * w.d / (ms_u / 1e3)}
+    del Cu, wsk
     del X, wsa, lv
     torch.cuda.empty_cache()
     # encoding (the codes the scan reads) at the 20M x 384 shape, bf16 rows, two sweeps:

@@ -236,6 +236,24 @@ int ah_assign_leaves(const float* x, int64_t n, int32_t d, const float* centroid
                      float* score_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * The partition's k-means update step (with ah_assign_leaves, one Lloyd
+ * iteration on the GPU; the ScaNN page's partition groups rows under
+ * centroids, and a centroid is the mean of its rows): for every leaf l with
+ * rows, centroids[l] = float32(sum of its rows in float64 / their number); a
+ * leaf without rows keeps its centroid.  The float64 sums are taken by atomic
+ * adds in no fixed order, so a result may differ from a row-order sum by one
+ * float32 unit.  Rows whose leaf is outside [0, L) are left out.
+ *   x float32 [n][d];  leaf_of_row int32 [n];  centroids float32 [L][d] (in:
+ *   previous, out: updated);  counts_out int32 [L] rows per leaf, or NULL
+ *   workspace >= ah_kmeans_workspace_bytes(L, d) bytes
+ * Errors: AH_ERR_SHAPE (n < 0, d < 1, L < 1), AH_ERR_UNSUPPORTED (d >
+ * AH_MAX_DIM, n >= 2^32), AH_ERR_NULL, AH_ERR_WORKSPACE.
+ */
+size_t ah_kmeans_workspace_bytes(int32_t L, int32_t d);
+int ah_kmeans_update(const float* x, int64_t n, int32_t d, const int32_t* leaf_of_row, int32_t L, float* centroids,
+                     int32_t* counts_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Encoding: the codes the scan reads (ScaNN page, sections "The loss in one
  * paragraph" and "Training an anisotropic codebook yourself": a row's loss is
  * (eta-1)*(u.r)^2 + |r|^2 for its residual r = x - decode(code) and direction

@@ -32,6 +32,7 @@ EXPORTS = (
     "ah_sq8_quantize", "ah_sq8_workspace_bytes", "ah_sq8_scan_topk",
     "ah_rslm_rotate", "ah_rslm_encode", "ah_rslm_scan_topk",
     "ah_assign_workspace_bytes", "ah_assign_leaves",
+    "ah_kmeans_workspace_bytes", "ah_kmeans_update",
     "ah_encode", "ah_tiled_codes_bytes", "ah_tile_codes",
     "ah_reorder_exact",
 )
@@ -79,6 +80,10 @@ def lib() -> C.CDLL:
         L.ah_rslm_encode.argtypes = [vp, i64, i32, vp, vp, vp, vp]
         L.ah_rslm_scan_topk.restype = C.c_int
         L.ah_rslm_scan_topk.argtypes = [vp, vp, i64, vp, vp, i64, i32, vp, i32, vp, vp, vp, sz, vp]
+        L.ah_kmeans_workspace_bytes.restype = sz
+        L.ah_kmeans_workspace_bytes.argtypes = [i32, i32]
+        L.ah_kmeans_update.restype = C.c_int
+        L.ah_kmeans_update.argtypes = [vp, i64, i32, vp, i32, vp, vp, vp, sz, vp]
         L.ah_sq8_quantize.restype = C.c_int
         L.ah_sq8_quantize.argtypes = [vp, i64, i32, C.c_double, vp, vp, vp]
         L.ah_sq8_workspace_bytes.restype = sz
@@ -292,6 +297,30 @@ def ah_rslm_scan_topk(q8, q_scale, codes, step, d, levels_i8, R, ids_out=None, s
                                    lv.ctypes.data_as(C.c_void_p), int(R), _ptr(ids_out), _ptr(scores_out),
                                    _ptr(workspace), workspace.numel(), _stream(stream)), "ah_rslm_scan_topk")
     return ids_out, scores_out
+
+
+def ah_kmeans_update(x, leaf_of_row, centroids, counts_out=None, workspace=None, stream=None):
+    """In place: each leaf's centroid becomes the mean of its rows (empty leaves keep theirs).
+    Returns (centroids, counts int32 [L])."""
+    x = _dev(x, torch.float32, "x", 2)
+    leaf_of_row = _dev(leaf_of_row, torch.int32, "leaf_of_row", 1)
+    centroids = _dev(centroids, torch.float32, "centroids", 2)
+    n, d = x.shape
+    L = centroids.shape[0]
+    if centroids.shape[1] != d or leaf_of_row.numel() != n:
+        raise ValueError("shapes")
+    if counts_out is None:
+        counts_out = torch.empty(L, dtype=torch.int32, device=x.device)
+    need = int(lib().ah_kmeans_workspace_bytes(L, d))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().ah_kmeans_update(_ptr(x), n, d, _ptr(leaf_of_row), L, _ptr(centroids), _ptr(counts_out),
+                                  _ptr(workspace), workspace.numel(), _stream(stream)), "ah_kmeans_update")
+    return centroids, counts_out
+
+
+def ah_kmeans_workspace_bytes(L: int, d: int) -> int:
+    return int(lib().ah_kmeans_workspace_bytes(L, d))
 
 
 def ah_assign_workspace_bytes(n: int, L: int) -> int:

@@ -194,6 +194,21 @@ int ah_rslm_scan_topk(const int8_t* q8, const float* q_scale, int64_t nq, const 
                                           static_cast<hipStream_t>(stream), codes, levels_i8));
 }
 
+size_t ah_kmeans_workspace_bytes(int32_t L, int32_t d) {
+    if (L < 1 || d < 1) return 0;
+    return ah::kmeans_workspace_bytes(L, d);
+}
+
+int ah_kmeans_update(const float* x, int64_t n, int32_t d, const int32_t* leaf_of_row, int32_t L, float* centroids,
+                     int32_t* counts_out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (n < 0 || d < 1 || L < 1) return AH_ERR_SHAPE;
+    if (d > AH_MAX_DIM || n >= ((int64_t)1 << 32)) return AH_ERR_UNSUPPORTED;
+    if (!centroids || (n > 0 && (!x || !leaf_of_row))) return AH_ERR_NULL;
+    if (!workspace || workspace_bytes < ah::kmeans_workspace_bytes(L, d)) return AH_ERR_WORKSPACE;
+    return hip_status(ah::launch_kmeans_update(x, n, d, leaf_of_row, L, centroids, counts_out, workspace,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 size_t ah_assign_workspace_bytes(int64_t n, int32_t L) {
     if (n < 0 || L < 1) return 0;
     return ah::assign_workspace_bytes(n, L);

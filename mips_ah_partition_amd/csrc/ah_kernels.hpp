@@ -46,6 +46,10 @@ hipError_t launch_rows_topk(const float* S, int64_t rows, int32_t L, int32_t k, 
 // Best k of each row of a candidate list: row r holds rowcnt[r] scores S[r * cap
 // + j] with ids idmap[r * cap + j]; rows with rowcnt[r] > cap are skipped.
 // cap <= 4096, k <= 512.
+// k-means update: centroids[l] = float64 mean of the rows with leaf l (float32), kept when empty.
+size_t kmeans_workspace_bytes(int32_t L, int32_t d);
+hipError_t launch_kmeans_update(const float* x, int64_t n, int32_t d, const int32_t* leaf, int32_t L, float* cent,
+                                int32_t* counts, void* ws, hipStream_t stream);
 // Residual variant's per-leaf term: clip(rint((s[q][j] - s[q][0]) / step[q]), -bound, bound), 0 when step is 0.
 hipError_t launch_residual_bias(const float* scores, const float* step, int64_t nq, int32_t nl, int32_t bound,
                                 int32_t* bias, hipStream_t stream);

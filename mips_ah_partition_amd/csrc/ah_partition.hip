@@ -592,9 +592,65 @@ hipError_t launch_assign(const float* x, int64_t n, int32_t d, const float* cent
     return hipSuccess;
 }
 
-// The best k columns of each row of a score block [rows][L] by (score desc,
-// column asc): the one-wave selection for L <= kWaveLeaves and k <= kLeafSort,
-// else the workgroup selection.
+// ------------------------------------------------------------------ k-means update
+// The update step of the partitioning's k-means: each leaf's centroid becomes
+// the mean of its rows (float64 sums, float32 result); a leaf with no rows
+// keeps its centroid.  Sums by float64 atomic adds (a wave per row, one lane
+// per dimension), so their order is not fixed: results agree with a row-order
+// sum to float64 rounding, i.e. to within one float32 unit.
+__global__ void kmeans_zero_kernel(double* __restrict__ sum, int64_t count, uint32_t* __restrict__ cnt, int32_t L) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
+        sum[i] = 0.0;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < L; i += (int64_t)gridDim.x * blockDim.x)
+        cnt[i] = 0;
+}
+
+__global__ __launch_bounds__(256) void kmeans_accumulate_kernel(const float* __restrict__ x, int64_t n, int32_t d,
+                                                                const int32_t* __restrict__ leaf, int32_t L,
+                                                                double* __restrict__ sum, uint32_t* __restrict__ cnt) {
+    const int lane = lane_id();
+    const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
+    for (int64_t i = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; i < n; i += waves) {
+        const int32_t l = leaf[i];
+        if (l < 0 || l >= L) continue;  // rows without a valid leaf are left out
+        if (lane == 0) atomicAdd(&cnt[l], 1u);
+        const float* xr = x + i * d;
+        double* sr = sum + (int64_t)l * d;
+        for (int t = lane; t < d; t += kWave) unsafeAtomicAdd(&sr[t], (double)xr[t]);
+    }
+}
+
+__global__ void kmeans_finish_kernel(const double* __restrict__ sum, const uint32_t* __restrict__ cnt, int32_t L,
+                                     int32_t d, float* __restrict__ cent, int32_t* __restrict__ counts) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= (int64_t)L * d) return;
+    const int32_t l = (int32_t)(e / d);
+    const uint32_t c = cnt[l];
+    if (counts && e % d == 0) counts[l] = (int32_t)c;
+    if (c > 0) cent[e] = (float)(sum[e] / (double)c);
+}
+
+size_t kmeans_workspace_bytes(int32_t L, int32_t d) {
+    return (((size_t)L * d * 8 + 255) & ~(size_t)255) + (size_t)L * 4;
+}
+
+hipError_t launch_kmeans_update(const float* x, int64_t n, int32_t d, const int32_t* leaf, int32_t L, float* cent,
+                                int32_t* counts, void* ws, hipStream_t stream) {
+    double* sum = reinterpret_cast<double*>(ws);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + (((size_t)L * d * 8 + 255) & ~(size_t)255));
+    const int64_t cells = (int64_t)L * d;
+    hipLaunchKernelGGL(kmeans_zero_kernel, dim3((unsigned)((cells + 255) / 256 < 4096 ? (cells + 255) / 256 : 4096)),
+                       dim3(256), 0, stream, sum, cells, cnt, L);
+    if (n > 0) {
+        const int64_t blocks = (n + 3) / 4;
+        hipLaunchKernelGGL(kmeans_accumulate_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0,
+                           stream, x, n, d, leaf, L, sum, cnt);
+    }
+    hipLaunchKernelGGL(kmeans_finish_kernel, dim3((unsigned)((cells + 255) / 256)), dim3(256), 0, stream, sum, cnt, L, d,
+                       cent, counts);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ residual leaf terms
 // The residual (leaf-relative) variant scores a row as q.c_leaf + q.residual; the
 // int8 table approximates q.residual as bias + step * sum, so, in table units,
@@ -626,6 +682,10 @@ hipError_t launch_residual_bias(const float* scores, const float* step, int64_t 
     return hipGetLastError();
 }
 
+// The best k columns of each row of a score block [rows][L] by (score desc,
+// column asc): the one-wave selection for L <= kWaveLeaves and k <= kLeafSort,
+// else the workgroup selection (launch_rows_topk); launch_list_topk does the
+// same for candidate lists with their own ids and lengths.
 hipError_t launch_list_topk(const float* S, const int32_t* idmap, const uint32_t* rowcnt, int64_t rows, int32_t cap,
                             int32_t k, int32_t* ids, float* scores, hipStream_t stream) {
     if (rows == 0) return hipSuccess;

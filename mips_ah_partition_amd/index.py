@@ -157,6 +157,28 @@ def kmeans(X: np.ndarray, k: int, iters: int = ITERS, seed=0, init_rows=None):
     return Cn, assign
 
 
+def kmeans_gpu(X, k: int, iters: int = ITERS, seed=0, init_rows=None):
+    """The same Lloyd iterations as kmeans() on the GPU (ah_assign_leaves, then
+    ah_kmeans_update).  X: float32 device tensor [n, d].  Returns (centroids
+    float32 device tensor [k, d], assignment int32 device tensor [n])."""
+    from . import ahlib
+    n = X.shape[0]
+    if init_rows is None:
+        init_rows = np.random.default_rng(seed).choice(n, k, replace=False)
+    import torch
+    C = X[torch.as_tensor(np.asarray(init_rows), device=X.device, dtype=torch.long)].clone()
+    ws_a = ws_k = None
+    leaf = None
+    for _ in range(iters):
+        if ws_a is None:
+            ws_a = torch.empty(ahlib.ah_assign_workspace_bytes(n, k), dtype=torch.uint8, device=X.device)
+            ws_k = torch.empty(ahlib.ah_kmeans_workspace_bytes(k, X.shape[1]), dtype=torch.uint8, device=X.device)
+        leaf, _ = ahlib.ah_assign_leaves(X, C, workspace=ws_a)
+        ahlib.ah_kmeans_update(X, leaf, C, workspace=ws_k)
+    leaf, _ = ahlib.ah_assign_leaves(X, C, workspace=ws_a) if iters else ahlib.ah_assign_leaves(X, C)
+    return C, leaf
+
+
 def leaf_sort(assign: np.ndarray, num_leaves: int):
     """Rows grouped by leaf, ascending id inside each leaf.
     Returns (ids int32 [n] original row of each position, leaf_offsets int64 [L+1])."""

@@ -543,3 +543,50 @@ def test_sq8_topk_parity(gpu, nq, n, d, R, dup):
     o_ids, o_sc = oracle.sq8_topk(_np(q8), _np(qs), _np(d8), _np(ds), R)
     assert np.array_equal(_np(ids), o_ids)
     assert np.array_equal(_np(sc), o_sc)
+
+
+# ----------------------------------------------------------------------------- k-means update
+@pytest.mark.parametrize("n,d,L", [(20000, 100, 300), (5000, 384, 4000), (1, 3, 2), (0, 8, 5)])
+def test_kmeans_update_parity(gpu, n, d, L):
+    """Stage-chained: the GPU's assignment of the rows to the centroids, then the
+    update on both sides; float64 sums in another order, so one float32 unit."""
+    torch, ah = gpu
+    rng = np.random.default_rng(n + d + L)
+    X = (rng.standard_normal((n, d)) * 4).astype(np.float32)
+    C0 = rng.standard_normal((L, d)).astype(np.float32)
+    if n:
+        leaf, _ = ah.ah_assign_leaves(_t(torch, X), _t(torch, C0))
+        lf = leaf.clone()
+        lf[:: 97] = -1  # rows outside every leaf are left out
+        lf_np = _np(lf)
+    else:
+        lf = torch.zeros(0, dtype=torch.int32, device="cuda")
+        lf_np = np.zeros(0, np.int32)
+    Cg, cnt = ah.ah_kmeans_update(_t(torch, X), lf, _t(torch, C0))
+    torch.cuda.synchronize()
+    keep = lf_np >= 0
+    Co, cnto = oracle.kmeans_update(X[keep], lf_np[keep], C0)
+    assert np.array_equal(_np(cnt), cnto)
+    g = _np(Cg).astype(np.float64)
+    o = Co.astype(np.float64)
+    scale = np.abs(X).max() if n else 1.0
+    ulp = np.spacing(np.abs(Co)).astype(np.float64)
+    assert (np.abs(g - o) <= np.maximum(ulp, 1e-12 * scale)).all()
+
+
+def test_kmeans_gpu_lloyd_objective_never_rises(gpu):
+    """Lloyd iterations on the GPU (assignment, then update) never raise the
+    within-leaf squared distance (float64, measured on the host)."""
+    torch, ah = gpu
+    from mips_ah_partition_amd import index as hix
+    rng = np.random.default_rng(5)
+    X = (rng.standard_normal((30000, 32)) + rng.integers(0, 5, (30000, 1))).astype(np.float32)
+    Xd = _t(torch, X)
+    init = rng.choice(30000, 100, replace=False)
+    prev = np.inf
+    for it in (1, 2, 4, 8):
+        C, leaf = hix.kmeans_gpu(Xd, 100, iters=it, init_rows=init)
+        torch.cuda.synchronize()
+        obj = ((X.astype(np.float64) - _np(C).astype(np.float64)[_np(leaf)]) ** 2).sum()
+        assert obj <= prev * (1 + 1e-6)
+        prev = obj
