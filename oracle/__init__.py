@@ -73,7 +73,9 @@ def lib() -> C.CDLL:
         L.oracle_nearest.argtypes = [_f32p, C.c_int64, C.c_int32, _f32p, C.c_int32, _i32p, _f64p]
         L.oracle_kmeans_update.argtypes = [_f32p, C.c_int64, C.c_int32, _i32p, C.c_int32, _f32p, _i32p]
         L.oracle_encode.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_int32, _f32p, C.c_int32, C.c_int32,
-                                    C.c_double, C.c_int32, _u8p, C.c_int32]
+                                    C.c_double, C.c_int32, _u8p, C.c_int32, C.c_void_p]
+        L.oracle_pq_update.argtypes = [_f32p, C.c_int64, C.c_int32, _u8p, C.c_int32, C.c_int32, C.c_int32,
+                                       C.c_double, _f32p]
         _LIB = L
     return _LIB
 
@@ -258,10 +260,22 @@ def kmeans_update(X, leaf, centroids):
     return Cn, cnt
 
 
-def encode(rows, codebooks, eta, sweeps=2, stride=None):
+def pq_update(X, codes, codebooks, eta):
+    """One block-by-block closed-form center update of anisotropic codebook
+    training at fixed codes; returns the new codebooks float32 [B, 16, dpb]."""
+    X = _c(X, np.float32)
+    cd = _c(codes, np.uint8)
+    cb = np.array(codebooks, dtype=np.float32, copy=True, order="C")
+    B, _, dpb = cb.shape
+    lib().oracle_pq_update(X, X.shape[0], X.shape[1], cd, cd.shape[1], B, dpb, float(eta), cb)
+    return cb
+
+
+def encode(rows, codebooks, eta, sweeps=2, stride=None, init_codes=None):
     """Anisotropic coupled encoding (block-coordinate descent from the per-block
-    nearest centers).  rows: float32 [n, d] or bfloat16 bits as uint16 [n, d];
-    codebooks float32 [B, 16, dpb].  Returns uint8 [n, stride] nibble codes."""
+    nearest centers, or from init_codes).  rows: float32 [n, d] or bfloat16 bits
+    as uint16 [n, d]; codebooks float32 [B, 16, dpb].  Returns uint8 [n, stride]
+    nibble codes."""
     b, dt = _base_args(rows)
     cb = _c(codebooks, np.float32)
     B, _, dpb = cb.shape
@@ -270,7 +284,10 @@ def encode(rows, codebooks, eta, sweeps=2, stride=None):
         raise ValueError("rows do not have B * dpb columns")
     stride = (B + 1) // 2 if stride is None else int(stride)
     out = np.zeros((n, stride), dtype=np.uint8)
-    lib().oracle_encode(_ptr(b), dt, n, d, cb, B, dpb, float(eta), int(sweeps), out, stride)
+    ic = None if init_codes is None else _c(init_codes, np.uint8)
+    if ic is not None and ic.shape != (n, stride):
+        raise ValueError("init_codes must be [n, stride]")
+    lib().oracle_encode(_ptr(b), dt, n, d, cb, B, dpb, float(eta), int(sweeps), out, stride, _ptr(ic))
     return out
 
 

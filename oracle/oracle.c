@@ -303,8 +303,11 @@ static double oracle_pb(const double* xv, double invn, const float* cen, int32_t
     return p;
 }
 
+/* init: when non-NULL, the sweeps start from these codes ([n][stride], the
+ * training loop's current assignment) instead of the per-block nearest centers. */
 void oracle_encode(const void* rows, int32_t dtype, int64_t n, int32_t d, const float* cb, int32_t B,
-                   int32_t dpb, double eta, int32_t sweeps, uint8_t* codes, int32_t stride) {
+                   int32_t dpb, double eta, int32_t sweeps, uint8_t* codes, int32_t stride,
+                   const uint8_t* init) {
     #pragma omp parallel
     {
         double* xv = (double*)malloc(sizeof(double) * (size_t)d);
@@ -318,6 +321,10 @@ void oracle_encode(const void* rows, int32_t dtype, int64_t n, int32_t d, const 
             }
             const double invn = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
             for (int32_t b = 0; b < B; ++b) {
+                if (init) {
+                    code[b] = (init[i * (int64_t)stride + (b >> 1)] >> (4 * (b & 1))) & 15;
+                    continue;
+                }
                 double best = INFINITY;
                 int bc = 0;
                 for (int c = 0; c < 16; ++c) {
@@ -384,6 +391,100 @@ void oracle_nearest(const float* x, int64_t n, int32_t d, const float* cent, int
         out[i] = bl;
         if (dist2) dist2[i] = best;
     }
+}
+
+/* The center update of anisotropic codebook training (the ScaNN page,
+ * "Training an anisotropic codebook yourself": a closed-form per-center solve;
+ * with the block coupling, block by block in order, each with the other
+ * blocks' current centers): for block b and center c over the rows coded c,
+ *   sum_i [(eta-1) u_ib u_ib^T + I] c = sum_i [x_ib + (eta-1)(s_i - p_ib + u_ib.x_ib) u_ib]
+ * with u = x/|x|, p_ib = u_ib.(x_ib - center) and s_i = sum_b p_ib at the
+ * current centers; the solve is Gaussian elimination with partial pivoting in
+ * float64; a center with no rows, or a singular system, keeps its value; after
+ * block b, its p_ib and s_i are refreshed with the new centers.  Float32 rows;
+ * codes [n][stride] nibble-packed; cb [B][16][dpb] updated in place. */
+void oracle_pq_update(const float* X, int64_t n, int32_t d, const uint8_t* codes, int32_t stride, int32_t B,
+                      int32_t dpb, double eta, float* cb) {
+    double* invn = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    double* p = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * (size_t)B);
+    double* s = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    for (int64_t i = 0; i < n; ++i) {
+        double ss = 0.0;
+        for (int32_t j = 0; j < d; ++j) ss += (double)X[i * d + j] * (double)X[i * d + j];
+        invn[i] = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+        s[i] = 0.0;
+        for (int32_t b = 0; b < B; ++b) {
+            const int c = (codes[i * (int64_t)stride + (b >> 1)] >> (4 * (b & 1))) & 15;
+            double pr = 0.0;
+            for (int32_t t = 0; t < dpb; ++t) {
+                const double x = X[i * d + b * dpb + t];
+                pr += (x * invn[i]) * (x - (double)cb[((int64_t)b * 16 + c) * dpb + t]);
+            }
+            p[i * B + b] = pr;
+            s[i] += pr;
+        }
+    }
+    double A[16 * 16], r[16];
+    for (int32_t b = 0; b < B; ++b) {
+        for (int c = 0; c < 16; ++c) {
+            for (int e = 0; e < dpb * dpb; ++e) A[e] = 0.0;
+            for (int e = 0; e < dpb; ++e) r[e] = 0.0;
+            int64_t cnt = 0;
+            for (int64_t i = 0; i < n; ++i) {
+                if (((codes[i * (int64_t)stride + (b >> 1)] >> (4 * (b & 1))) & 15) != c) continue;
+                ++cnt;
+                double u[16], ux = 0.0;
+                for (int32_t t = 0; t < dpb; ++t) {
+                    u[t] = (double)X[i * d + b * dpb + t] * invn[i];
+                    ux += u[t] * (double)X[i * d + b * dpb + t];
+                }
+                const double w = (eta - 1.0) * (s[i] - p[i * B + b] + ux);
+                for (int32_t a = 0; a < dpb; ++a) {
+                    for (int32_t t = 0; t < dpb; ++t) A[a * dpb + t] += (eta - 1.0) * u[a] * u[t];
+                    A[a * dpb + a] += 1.0;
+                    r[a] += (double)X[i * d + b * dpb + a] + w * u[a];
+                }
+            }
+            if (cnt == 0) continue;
+            /* Gaussian elimination with partial pivoting */
+            int ok = 1;
+            for (int32_t k = 0; k < dpb && ok; ++k) {
+                int32_t piv = k;
+                for (int32_t a = k + 1; a < dpb; ++a)
+                    if (fabs(A[a * dpb + k]) > fabs(A[piv * dpb + k])) piv = a;
+                if (A[piv * dpb + k] == 0.0) { ok = 0; break; }
+                if (piv != k) {
+                    for (int32_t t = 0; t < dpb; ++t) { double tmp = A[k * dpb + t]; A[k * dpb + t] = A[piv * dpb + t]; A[piv * dpb + t] = tmp; }
+                    double tmp = r[k]; r[k] = r[piv]; r[piv] = tmp;
+                }
+                for (int32_t a = k + 1; a < dpb; ++a) {
+                    const double f = A[a * dpb + k] / A[k * dpb + k];
+                    for (int32_t t = k; t < dpb; ++t) A[a * dpb + t] -= f * A[k * dpb + t];
+                    r[a] -= f * r[k];
+                }
+            }
+            if (!ok) continue;
+            for (int32_t k = dpb - 1; k >= 0; --k) {
+                double v = r[k];
+                for (int32_t t = k + 1; t < dpb; ++t) v -= A[k * dpb + t] * r[t];
+                r[k] = v / A[k * dpb + k];
+            }
+            for (int32_t t = 0; t < dpb; ++t) cb[((int64_t)b * 16 + c) * dpb + t] = (float)r[t];
+        }
+        for (int64_t i = 0; i < n; ++i) {
+            const int c = (codes[i * (int64_t)stride + (b >> 1)] >> (4 * (b & 1))) & 15;
+            double pr = 0.0;
+            for (int32_t t = 0; t < dpb; ++t) {
+                const double x = X[i * d + b * dpb + t];
+                pr += (x * invn[i]) * (x - (double)cb[((int64_t)b * 16 + c) * dpb + t]);
+            }
+            s[i] += pr - p[i * B + b];
+            p[i * B + b] = pr;
+        }
+    }
+    free(invn);
+    free(p);
+    free(s);
 }
 
 /* The update step of the partitioning's k-means (the ScaNN page's partition

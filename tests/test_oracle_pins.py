@@ -680,3 +680,69 @@ def test_kmeans_update_minimises_the_within_leaf_squared_distance():
     before = ((Xd - C0[lf]) ** 2).sum()
     after = ((Xd - C[lf].astype(np.float64)) ** 2).sum()
     assert after <= before
+
+
+# ---------------------------------------------------------------- codebook training update
+def test_pq_update_at_eta_one_is_the_per_block_mean():
+    rng = np.random.default_rng(41)
+    B, dpb, n = 5, 2, 800
+    X = rng.standard_normal((n, B * dpb)).astype(np.float32)
+    cb = rng.standard_normal((B, 16, dpb)).astype(np.float32)
+    codes = synth.random_codes(rng, n, B)
+    new = oracle.pq_update(X, codes, cb, 1.0)
+    nib = _decode_nibbles(codes, B)
+    for b in range(B):
+        for c in range(16):
+            m = nib[:, b] == c
+            want = X[m, b * dpb:(b + 1) * dpb].astype(np.float64).mean(0) if m.any() else cb[b, c]
+            assert np.allclose(new[b, c], want, rtol=1e-6, atol=1e-7)
+
+
+def test_pq_update_one_block_is_the_stationary_vq_solution():
+    # one block: s_i - p_ib = 0, so each center solves (sum (eta-1) u u^T + m I) c = sum eta... form
+    rng = np.random.default_rng(42)
+    d, eta, n = 4, 3.0, 600
+    X = (rng.standard_normal((n, d)) + 1.5).astype(np.float32)
+    cb = rng.standard_normal((1, 16, d)).astype(np.float32)
+    codes = synth.random_codes(rng, n, 1)
+    new = oracle.pq_update(X, codes, cb, eta)
+    U = X / np.linalg.norm(X, axis=1, keepdims=True)
+    for c in range(16):
+        m = (codes[:, 0] & 15) == c
+        if not m.any():
+            assert np.array_equal(new[0, c], cb[0, c])
+            continue
+        Xm, Um = X[m].astype(np.float64), U[m].astype(np.float64)
+        A = (eta - 1) * Um.T @ Um + m.sum() * np.eye(d)
+        rhs = (Xm + (eta - 1) * (Um * Xm).sum(1, keepdims=True) * Um).sum(0)
+        assert np.allclose(new[0, c], np.linalg.solve(A, rhs), rtol=1e-5, atol=1e-6)
+
+
+def test_pq_training_step_never_raises_the_loss():
+    rng = np.random.default_rng(43)
+    B, dpb, n, eta = 6, 2, 1500, 4.0
+    X = rng.standard_normal((n, B * dpb)).astype(np.float32)
+    cb = X[rng.choice(n, 16, replace=False)].reshape(16, B, dpb).transpose(1, 0, 2).copy()
+    def loss(codes, cbk):
+        nib = _decode_nibbles(codes, B)
+        rec = np.stack([cbk[b, nib[:, b]] for b in range(B)], 1).reshape(n, -1).astype(np.float64)
+        R = X.astype(np.float64) - rec
+        u = X.astype(np.float64) / np.linalg.norm(X.astype(np.float64), axis=1, keepdims=True)
+        return ((eta - 1) * (R * u).sum(1) ** 2 + (R * R).sum(1)).sum()
+    codes = oracle.encode(X, cb, eta, sweeps=1)
+    prev = loss(codes, cb)
+    for _ in range(3):
+        cb = oracle.pq_update(X, codes, cb, eta)
+        l1 = loss(codes, cb)
+        codes = oracle.encode(X, cb, eta, sweeps=1, init_codes=codes)
+        l2 = loss(codes, cb)
+        assert l1 <= prev * (1 + 1e-9) and l2 <= l1 * (1 + 1e-9)
+        prev = l2
+
+
+def test_encode_from_given_codes_with_zero_sweeps_returns_them():
+    rng = np.random.default_rng(44)
+    X = rng.standard_normal((50, 8)).astype(np.float32)
+    cb = rng.standard_normal((4, 16, 2)).astype(np.float32)
+    init = synth.random_codes(rng, 50, 4)
+    assert np.array_equal(oracle.encode(X, cb, 4.0, sweeps=0, init_codes=init), init)
