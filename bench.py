@@ -347,6 +347,21 @@ def stage_probes(torch, ahlib):
     del Cu, wsk
     del X, wsa, lv
     torch.cuda.empty_cache()
+    # anisotropic codebook training on the GPU at the 20M x 384 shape's training sample:
+    # 250,000 rows, 192 blocks x 2 dims, eta = 4, 10 iterations (sweep + block-by-block update)
+    from mips_ah_partition_amd import index as hix
+    Xt = synth.gpu_normal_rows(torch, 250_000, w.d, 6060, torch.float32)
+    init = np.random.default_rng(60).choice(250_000, 16, replace=False)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    hix.train_codebooks_gpu(Xt, w.dpb, w.eta, iters=1, init_rows=init)
+    t0.record()
+    hix.train_codebooks_gpu(Xt, w.dpb, w.eta, iters=10, init_rows=init)
+    t1.record()
+    torch.cuda.synchronize()
+    out["train_codebooks_wiki20m_sample"] = {"rows": 250_000, "d": w.d, "blocks": w.blocks, "iters": 10,
+                                             "ms": t0.elapsed_time(t1)}
+    del Xt
     # encoding (the codes the scan reads) at the 20M x 384 shape, bf16 rows, two sweeps:
     # a float64 vector-ALU kernel, counted by costs.encode_flops_per_row
     w = synth.WORKLOADS["wiki20m"]

@@ -276,6 +276,32 @@ int ah_kmeans_update(const float* x, int64_t n, int32_t d, const int32_t* leaf_o
 int ah_encode(const void* rows, int32_t rows_dtype, int64_t n, int32_t d, const float* codebooks, int32_t B,
               int32_t dpb, double eta, int32_t sweeps, uint8_t* codes_out, int32_t code_stride, void* stream);
 
+/* The same descent started from the codes already in codes_inout (no nearest-
+ * center start): `sweeps` sweeps, results written back in place.  With
+ * ah_pq_update this is one iteration of anisotropic codebook training (ScaNN
+ * page, "Training an anisotropic codebook yourself": assign by the loss,
+ * update each center in closed form).  Arguments and errors as ah_encode. */
+int ah_encode_sweep(const void* rows, int32_t rows_dtype, int64_t n, int32_t d, const float* codebooks, int32_t B,
+                    int32_t dpb, double eta, int32_t sweeps, uint8_t* codes_inout, int32_t code_stride, void* stream);
+
+/* Center update of anisotropic codebook training at fixed codes, block by block
+ * in order, each with the other blocks' current centers: block b's center c
+ * solves  sum_i [(eta-1) u u^T + I] c = sum_i [x_ib + (eta-1)(s_i - p_ib + u.x_ib) u]
+ * over the rows coded c (u = x_ib/|x|, p_ib = u.(x_ib - center), s_i = sum_b
+ * p_ib at the current centers), by Gaussian elimination with partial pivoting
+ * in float64; a center with no rows, or a singular system, keeps its value;
+ * block b's p_ib and s_i are refreshed before block b+1.  The float64 sums are
+ * taken in no fixed order (results agree with a row-order sum to rounding).
+ *   x float32 [n][d] (d == B * dpb);  codes uint8 [n][code_stride];
+ *   codebooks float32 [B][16][dpb] (in: current, out: updated)
+ *   workspace >= ah_pq_update_workspace_bytes(n, B, dpb) bytes
+ * Errors: AH_ERR_SHAPE (n < 0, B < 1, dpb < 1, d != B*dpb, code_stride <
+ * ceil(B/2), eta < 0 or not finite), AH_ERR_UNSUPPORTED (dpb > AH_MAX_DPB,
+ * B > AH_MAX_BLOCKS), AH_ERR_NULL, AH_ERR_WORKSPACE. */
+size_t ah_pq_update_workspace_bytes(int64_t n, int32_t B, int32_t dpb);
+int ah_pq_update(const float* x, int64_t n, int32_t d, const uint8_t* codes, int32_t code_stride, int32_t B,
+                 int32_t dpb, double eta, float* codebooks, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Code layout for the scan (same page and section as the scan: the codes are
  * read once per query batch, so their layout decides how well the reads

@@ -33,7 +33,8 @@ EXPORTS = (
     "ah_rslm_rotate", "ah_rslm_encode", "ah_rslm_scan_topk",
     "ah_assign_workspace_bytes", "ah_assign_leaves",
     "ah_kmeans_workspace_bytes", "ah_kmeans_update",
-    "ah_encode", "ah_tiled_codes_bytes", "ah_tile_codes",
+    "ah_encode", "ah_encode_sweep", "ah_pq_update_workspace_bytes", "ah_pq_update",
+    "ah_tiled_codes_bytes", "ah_tile_codes",
     "ah_reorder_exact",
 )
 
@@ -84,6 +85,12 @@ def lib() -> C.CDLL:
         L.ah_kmeans_workspace_bytes.argtypes = [i32, i32]
         L.ah_kmeans_update.restype = C.c_int
         L.ah_kmeans_update.argtypes = [vp, i64, i32, vp, i32, vp, vp, vp, sz, vp]
+        L.ah_encode_sweep.restype = C.c_int
+        L.ah_encode_sweep.argtypes = [vp, i32, i64, i32, vp, i32, i32, C.c_double, i32, vp, i32, vp]
+        L.ah_pq_update_workspace_bytes.restype = sz
+        L.ah_pq_update_workspace_bytes.argtypes = [i64, i32, i32]
+        L.ah_pq_update.restype = C.c_int
+        L.ah_pq_update.argtypes = [vp, i64, i32, vp, i32, i32, i32, C.c_double, vp, vp, sz, vp]
         L.ah_sq8_quantize.restype = C.c_int
         L.ah_sq8_quantize.argtypes = [vp, i64, i32, C.c_double, vp, vp, vp]
         L.ah_sq8_workspace_bytes.restype = sz
@@ -321,6 +328,41 @@ def ah_kmeans_update(x, leaf_of_row, centroids, counts_out=None, workspace=None,
 
 def ah_kmeans_workspace_bytes(L: int, d: int) -> int:
     return int(lib().ah_kmeans_workspace_bytes(L, d))
+
+
+def ah_encode_sweep(rows, codebooks, eta, codes_inout, sweeps=1, stream=None):
+    """Coupled-encoding sweeps started from the codes in codes_inout (updated in place)."""
+    codebooks = _dev(codebooks, torch.float32, "codebooks", 3)
+    B, _, dpb = codebooks.shape
+    if rows.dtype == torch.bfloat16:
+        dt = AH_BF16
+    else:
+        rows = _dev(rows, torch.float32, "rows", 2)
+        dt = AH_F32
+    n, d = rows.shape
+    _dev(codes_inout, torch.uint8, "codes_inout", 2)
+    _check(lib().ah_encode_sweep(_ptr(rows), dt, n, d, _ptr(codebooks), B, dpb, float(eta), int(sweeps),
+                                 _ptr(codes_inout), codes_inout.shape[1], _stream(stream)), "ah_encode_sweep")
+    return codes_inout
+
+
+def ah_pq_update(x, codes, codebooks, eta, workspace=None, stream=None):
+    """Block-by-block closed-form center update at fixed codes (codebooks updated in place)."""
+    x = _dev(x, torch.float32, "x", 2)
+    codes = _dev(codes, torch.uint8, "codes", 2)
+    codebooks = _dev(codebooks, torch.float32, "codebooks", 3)
+    n, d = x.shape
+    B, _, dpb = codebooks.shape
+    need = int(lib().ah_pq_update_workspace_bytes(n, B, dpb))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().ah_pq_update(_ptr(x), n, d, _ptr(codes), codes.shape[1], B, dpb, float(eta), _ptr(codebooks),
+                              _ptr(workspace), workspace.numel(), _stream(stream)), "ah_pq_update")
+    return codebooks
+
+
+def ah_pq_update_workspace_bytes(n: int, B: int, dpb: int) -> int:
+    return int(lib().ah_pq_update_workspace_bytes(n, B, dpb))
 
 
 def ah_assign_workspace_bytes(n: int, L: int) -> int:

@@ -238,6 +238,36 @@ int ah_encode(const void* rows, int32_t rows_dtype, int64_t n, int32_t d, const 
                                         code_stride, static_cast<hipStream_t>(stream)));
 }
 
+int ah_encode_sweep(const void* rows, int32_t rows_dtype, int64_t n, int32_t d, const float* codebooks, int32_t B,
+                    int32_t dpb, double eta, int32_t sweeps, uint8_t* codes_inout, int32_t code_stride, void* stream) {
+    if (n < 0 || B < 1 || dpb < 1 || (int64_t)B * dpb != d || code_stride < (B + 1) / 2 || sweeps < 0 ||
+        sweeps > 64 || !(eta >= 0.0) || !(eta < 1e300))
+        return AH_ERR_SHAPE;
+    if ((rows_dtype != AH_F32 && rows_dtype != AH_BF16) || dpb > AH_MAX_DPB || B > AH_MAX_BLOCKS)
+        return AH_ERR_UNSUPPORTED;
+    if (n == 0) return AH_OK;
+    if (!rows || !codebooks || !codes_inout) return AH_ERR_NULL;
+    return hip_status(ah::launch_encode(rows, rows_dtype, n, d, codebooks, B, dpb, eta, sweeps, codes_inout,
+                                        code_stride, static_cast<hipStream_t>(stream), true));
+}
+
+size_t ah_pq_update_workspace_bytes(int64_t n, int32_t B, int32_t dpb) {
+    if (n < 0 || B < 1 || dpb < 1 || dpb > AH_MAX_DPB) return 0;
+    return ah::pq_update_workspace_bytes(n, B, dpb);
+}
+
+int ah_pq_update(const float* x, int64_t n, int32_t d, const uint8_t* codes, int32_t code_stride, int32_t B,
+                 int32_t dpb, double eta, float* codebooks, void* workspace, size_t workspace_bytes, void* stream) {
+    if (n < 0 || B < 1 || dpb < 1 || (int64_t)B * dpb != d || code_stride < (B + 1) / 2 || !(eta >= 0.0) ||
+        !(eta < 1e300))
+        return AH_ERR_SHAPE;
+    if (dpb > AH_MAX_DPB || B > AH_MAX_BLOCKS) return AH_ERR_UNSUPPORTED;
+    if (!codebooks || (n > 0 && (!x || !codes))) return AH_ERR_NULL;
+    if (!workspace || workspace_bytes < ah::pq_update_workspace_bytes(n, B, dpb)) return AH_ERR_WORKSPACE;
+    return hip_status(ah::launch_pq_update(x, n, d, codes, code_stride, B, dpb, eta, codebooks, workspace,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 size_t ah_tiled_codes_bytes(int64_t n, int32_t B) {
     if (n < 0 || B < 1) return 0;
     return ah::tiled_codes_bytes(n, B);

@@ -38,7 +38,7 @@ template <int kDpb, bool kBf16>
 __global__ __launch_bounds__(kEncThreads) void encode_kernel(const void* __restrict__ rows, int64_t n, int32_t d,
                                                              const float* __restrict__ cb, int32_t B, int32_t dpb_rt,
                                                              double eta, int32_t sweeps, uint8_t* __restrict__ codes,
-                                                             int32_t stride, bool vec_rows) {
+                                                             int32_t stride, bool vec_rows, bool from_codes) {
 #pragma clang fp contract(off)
     constexpr int kMaxDpb = 16;
     const int64_t i = (int64_t)blockIdx.x * kEncThreads + threadIdx.x;
@@ -129,9 +129,10 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(const void* __restr
     };
     auto get_code = [&](int b) -> int { return (row[b >> 1] >> (4 * (b & 1))) & 15; };
 
-    // per-block nearest centers; a byte is written once both of its nibbles are known
+    // per-block nearest centers (unless the sweeps start from the given codes);
+    // a byte is written once both of its nibbles are known
     uint32_t pend = 0;
-    for (int b = 0; b < B; ++b) {
+    for (int b = 0; b < (from_codes ? 0 : B); ++b) {
         load_block(b);
         double best = __builtin_huge_val();
         int bc = 0;
@@ -187,22 +188,23 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(const void* __restr
 
 template <int kDpb, bool kBf16>
 static void launch_enc(const void* rows, int64_t n, int32_t d, const float* cb, int32_t B, int32_t dpb, double eta,
-                       int32_t sweeps, uint8_t* codes, int32_t stride, hipStream_t stream) {
+                       int32_t sweeps, uint8_t* codes, int32_t stride, bool from_codes, hipStream_t stream) {
     // chunked row reads: 16-byte aligned rows
     const bool vec_rows = (reinterpret_cast<uintptr_t>(rows) & 15) == 0 && ((size_t)d * (kBf16 ? 2 : 4)) % 16 == 0;
     hipLaunchKernelGGL((encode_kernel<kDpb, kBf16>), dim3((unsigned)((n + kEncThreads - 1) / kEncThreads)),
-                       dim3(kEncThreads), 0, stream, rows, n, d, cb, B, dpb, eta, sweeps, codes, stride, vec_rows);
+                       dim3(kEncThreads), 0, stream, rows, n, d, cb, B, dpb, eta, sweeps, codes, stride, vec_rows,
+                       from_codes);
 }
 
 hipError_t launch_encode(const void* rows, int32_t dtype, int64_t n, int32_t d, const float* cb, int32_t B,
                          int32_t dpb, double eta, int32_t sweeps, uint8_t* codes, int32_t stride,
-                         hipStream_t stream) {
+                         hipStream_t stream, bool from_codes) {
     if (n == 0) return hipSuccess;
     const bool bf = dtype != 0;
-#define AH_ENC(D)                                                                               \
-    do {                                                                                        \
-        if (bf) launch_enc<D, true>(rows, n, d, cb, B, dpb, eta, sweeps, codes, stride, stream); \
-        else launch_enc<D, false>(rows, n, d, cb, B, dpb, eta, sweeps, codes, stride, stream);  \
+#define AH_ENC(D)                                                                                           \
+    do {                                                                                                    \
+        if (bf) launch_enc<D, true>(rows, n, d, cb, B, dpb, eta, sweeps, codes, stride, from_codes, stream); \
+        else launch_enc<D, false>(rows, n, d, cb, B, dpb, eta, sweeps, codes, stride, from_codes, stream);  \
     } while (0)
     if (dpb == 1) AH_ENC(1);
     else if (dpb == 2) AH_ENC(2);

@@ -78,7 +78,12 @@ hipError_t launch_assign(const float* x, int64_t n, int32_t d, const float* cent
 
 hipError_t launch_encode(const void* rows, int32_t dtype, int64_t n, int32_t d, const float* cb, int32_t B,
                          int32_t dpb, double eta, int32_t sweeps, uint8_t* codes, int32_t stride,
-                         hipStream_t stream);
+                         hipStream_t stream, bool from_codes = false);
+
+// Anisotropic codebook training: the block-by-block closed-form center update at fixed codes.
+size_t pq_update_workspace_bytes(int64_t n, int32_t B, int32_t dpb);
+hipError_t launch_pq_update(const float* x, int64_t n, int32_t d, const uint8_t* codes, int32_t stride, int32_t B,
+                            int32_t dpb, double eta, float* cb, void* ws, hipStream_t stream);
 
 size_t tiled_codes_bytes(int64_t n, int32_t B);
 hipError_t launch_tile_codes(const uint8_t* codes, int32_t stride, int64_t n, int32_t B, uint8_t* tiled,

@@ -157,6 +157,33 @@ def kmeans(X: np.ndarray, k: int, iters: int = ITERS, seed=0, init_rows=None):
     return Cn, assign
 
 
+def train_codebooks_gpu(X, dpb: int, eta: float, iters: int = ITERS, seed=0, init_rows=None):
+    """The same training iterations as train_codebooks on the GPU: codebooks
+    seeded from 16 rows, then per iteration one coupled-encoding sweep (from
+    the per-block nearest centers the first time, else from the current codes)
+    and the block-by-block center update.  X: float32 device tensor [m, d].
+    Returns (codebooks float32 device tensor [B, 16, dpb], codes uint8 [m, ceil(B/2)])."""
+    from . import ahlib
+    import torch
+    m, d = X.shape
+    B = d // dpb
+    if init_rows is None:
+        init_rows = np.random.default_rng(seed).choice(m, 16, replace=False)
+    rows = X[torch.as_tensor(np.asarray(init_rows), device=X.device, dtype=torch.long)]  # [16, d]
+    cb = rows.view(16, B, dpb).permute(1, 0, 2).contiguous()
+    ws = torch.empty(max(ahlib.ah_pq_update_workspace_bytes(m, B, dpb), 1), dtype=torch.uint8, device=X.device)
+    codes = None
+    for it in range(iters):
+        if codes is None:
+            codes = ahlib.ah_encode(X, cb, eta, sweeps=1)
+        else:
+            ahlib.ah_encode_sweep(X, cb, eta, codes, sweeps=1)
+        ahlib.ah_pq_update(X, codes, cb, eta, workspace=ws)
+    if codes is None:
+        codes = ahlib.ah_encode(X, cb, eta, sweeps=0)
+    return cb, codes
+
+
 def kmeans_gpu(X, k: int, iters: int = ITERS, seed=0, init_rows=None):
     """The same Lloyd iterations as kmeans() on the GPU (ah_assign_leaves, then
     ah_kmeans_update).  X: float32 device tensor [n, d].  Returns (centroids

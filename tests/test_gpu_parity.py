@@ -590,3 +590,60 @@ def test_kmeans_gpu_lloyd_objective_never_rises(gpu):
         obj = ((X.astype(np.float64) - _np(C).astype(np.float64)[_np(leaf)]) ** 2).sum()
         assert obj <= prev * (1 + 1e-6)
         prev = obj
+
+
+# ----------------------------------------------------------------------------- codebook training
+@pytest.mark.parametrize("n,B,dpb,eta,few", [(5000, 8, 2, 4.0, False), (3000, 3, 4, 2.5, False),
+                                              (4000, 16, 1, 1.0, False), (2000, 6, 2, 4.0, True), (1, 2, 2, 4.0, False)])
+def test_pq_update_parity(gpu, n, B, dpb, eta, few):
+    """Stage-chained: the same codes and codebooks on both sides; float64 sums
+    in another order, so the new centers agree to float32 rounding."""
+    torch, ah = gpu
+    rng = np.random.default_rng(n + B + dpb)
+    X = (rng.standard_normal((n, B * dpb)) + 0.5).astype(np.float32)
+    cb = rng.standard_normal((B, 16, dpb)).astype(np.float32)
+    codes = synth.random_codes(rng, n, B)
+    if few:  # most centers get no rows and keep their values
+        codes &= np.uint8(0x11)
+    got = ah.ah_pq_update(_t(torch, X), _t(torch, codes), _t(torch, cb), eta)
+    torch.cuda.synchronize()
+    want = oracle.pq_update(X, codes, cb, eta)
+    assert np.allclose(_np(got), want, rtol=1e-5, atol=1e-6 * max(1.0, np.abs(want).max()))
+
+
+@pytest.mark.parametrize("dpb,B,dtype", [(2, 24, "f32"), (4, 5, "f32"), (2, 48, "bf16"), (3, 7, "f32")])
+def test_encode_sweep_from_codes_parity(gpu, dpb, B, dtype):
+    torch, ah = gpu
+    rng = np.random.default_rng(dpb * 100 + B)
+    n = 1500
+    X = rng.standard_normal((n, B * dpb)).astype(np.float32)
+    cb = (0.7 * rng.standard_normal((B, 16, dpb))).astype(np.float32)
+    init = synth.random_codes(rng, n, B)
+    if dtype == "bf16":
+        bits = synth.to_bf16_bits(X)
+        rows = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+        ref_rows = bits
+    else:
+        rows = _t(torch, X)
+        ref_rows = X
+    codes = _t(torch, init.copy())
+    ah.ah_encode_sweep(rows, _t(torch, cb), 4.0, codes, sweeps=2)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(codes), oracle.encode(ref_rows, cb, 4.0, sweeps=2, init_codes=init))
+
+
+def test_train_codebooks_gpu_loss_never_rises(gpu):
+    torch, ah = gpu
+    from mips_ah_partition_amd import index as hix
+    rng = np.random.default_rng(8)
+    X = rng.integers(0, 256, size=(20000, 16)).astype(np.float32)
+    init = rng.choice(20000, 16, replace=False)
+    prev = np.inf
+    for it in (1, 2, 4, 6):
+        cb, codes = hix.train_codebooks_gpu(_t(torch, X), 2, 4.0, iters=it, init_rows=init)
+        torch.cuda.synchronize()
+        loss = hix.pq_loss(X, _np(cb), _np(codes), 4.0)
+        assert loss <= prev * (1 + 1e-6)
+        prev = loss
+    host_cb, host_loss = hix.train_codebooks(X, 2, 4.0, iters=6, init_rows=init, return_loss=True)
+    assert prev <= host_loss[-1] * 1.01  # the same iterations as the host trainer, to float rounding
