@@ -267,3 +267,31 @@ def test_sq8_flat_fullsize_sampled(gpu):
     assert np.array_equal(sc[idx].cpu().numpy(), o_sc)
     del d8, q8
     torch.cuda.empty_cache()
+
+
+def test_rslm_flat_fullsize_sampled(gpu):
+    """The rotation quantiser at 1M x 512 with 10,000 queries and R = 100, in
+    the configuration the benchmark times; sampled queries ranked by the
+    oracle over the GPU's own codes, steps and query codes must match exactly."""
+    torch, ah = gpu
+    from mips_ah_partition_amd.rslm import RSLMIndex
+    from oracle import rslm as orslm
+    nd, dd, nqs, R = 1_000_000, 512, 10_000, 100
+    _log("rslm: generating, rotating and encoding 1M x 512 documents")
+    Dv = synth.gpu_normal_rows(torch, nd, dd, 6464, torch.float32)
+    Qv = synth.gpu_normal_rows(torch, nqs, dd, 6465, torch.float32)
+    signs, perm = synth.rotation_draws(dd, 1)
+    rix = RSLMIndex(Dv, signs, perm)
+    ids, sc = rix.search(Qv, R)
+    Qr = ah.ah_rslm_rotate(Qv, rix.signs, rix.perm)
+    q8, qs = ah.ah_sq8_quantize(Qr)
+    torch.cuda.synchronize()
+    _log("rslm: done; checking sampled queries")
+    idx = _sample(nqs) + [4097]
+    lv8, _ = orslm.int8_levels(orslm.lloyd_max_gaussian(16).astype(np.float32))
+    d8 = orslm.expand(rix.codes.cpu().numpy(), dd, lv8)
+    o_ids, o_sc = oracle.sq8_topk(q8[idx].cpu().numpy(), qs[idx].cpu().numpy(), d8, rix.step.cpu().numpy(), R)
+    assert np.array_equal(ids[idx].cpu().numpy(), o_ids)
+    assert np.array_equal(sc[idx].cpu().numpy(), o_sc)
+    del Dv, rix
+    torch.cuda.empty_cache()
