@@ -781,34 +781,50 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
 #pragma unroll
             for (int m = 0; m < 4; ++m)
                 aA[m] = *reinterpret_cast<const v4i*>(onehot_s + __builtin_amdgcn_ubfe(cw[m], 4 * g, 4) * 4);
+            // LDS reads only (lgkmcnt 0; vmcnt and expcnt at their maxima, so the
+            // code loads in flight are not waited for): the loop is entered with
+            // no LDS read pending, and the waits inside it follow its own order
+            __builtin_amdgcn_s_waitcnt(0xC07F);
             for (int j = 0; j < (ks >> 1); ++j) {
                 const int s1 = 2 * j + 1;
+                // the next pair's operands are fetched unconditionally (the last
+                // pair re-reads its own: same addresses, unused), so the loop has
+                // one path.  The reads are spread over the pair so that at most
+                // 14 are in flight (the LDS counter holds 15): second-half B and
+                // the next code words, first-half products m = 0-1, second-half
+                // A, products m = 2-3, then the next pair's first-half operands.
+                const int jn = j + 1 < (ks >> 1) ? j + 1 : j;
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt)
                     bB[nt] = *reinterpret_cast<const v4i*>(lutw + (s1 * 4 + nt) * kWave * 16);
 #pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    aB[m] = *reinterpret_cast<const v4i*>(onehot_s + __builtin_amdgcn_ubfe(cw[m], 16 + 4 * g, 4) * 4);
-                const bool more = j + 1 < (ks >> 1);
-                if (more) {
+                for (int m = 0; m < 4; ++m) cwn[m] = crow[m * 16 * kCodeStride + jn];
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) cwn[m] = crow[m * 16 * kCodeStride + j + 1];
-                }
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
+                for (int m = 0; m < 2; ++m)
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt)
                         acc[m][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aA[m], bA[nt], acc[m][nt], 0, 0, 0);
-                if (more) {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    aB[m] = *reinterpret_cast<const v4i*>(onehot_s + __builtin_amdgcn_ubfe(cw[m], 16 + 4 * g, 4) * 4);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int m = 2; m < 4; ++m)
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt)
-                        bA[nt] = *reinterpret_cast<const v4i*>(lutw + ((s1 + 1) * 4 + nt) * kWave * 16);
+                        acc[m][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aA[m], bA[nt], acc[m][nt], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        cw[m] = cwn[m];
-                        aA[m] = *reinterpret_cast<const v4i*>(onehot_s + __builtin_amdgcn_ubfe(cw[m], 4 * g, 4) * 4);
-                    }
+                for (int nt = 0; nt < 4; ++nt)
+                    bA[nt] = *reinterpret_cast<const v4i*>(lutw + ((2 * jn) * 4 + nt) * kWave * 16);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    cw[m] = cwn[m];
+                    aA[m] = *reinterpret_cast<const v4i*>(onehot_s + __builtin_amdgcn_ubfe(cw[m], 4 * g, 4) * 4);
                 }
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
 #pragma unroll
