@@ -492,7 +492,7 @@ static void launch_leaf_wave(const float* S, int64_t nq, int32_t L, int32_t nl, 
 // up to four splits bring it to about 512 workgroups.
 static int max_splits(int64_t nq, int32_t L) {
     const int64_t tiles = ((nq + kGT - 1) / kGT) * ((L + kGT - 1) / kGT);
-    if (L > kWaveLeaves || tiles >= 256) return 1;
+    if (L > kWaveLeaves || tiles >= 256 || tiles == 0) return 1;  // tiles == 0: no queries or no leaves
     const int64_t want = (512 + tiles - 1) / tiles;
     return (int)(want < 4 ? want : 4);
 }

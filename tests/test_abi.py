@@ -213,3 +213,23 @@ def test_rslm_validation(lib):
                                  None) == -2
     assert lib.ah_rslm_scan_topk(fake, fake, 4, fake, fake, 100, 64, C.cast(lv, vp), 10, fake, None, fake, 16,
                                  None) == -4
+
+
+def test_workspace_sizes_zero_shapes(lib):
+    """Every size query is host arithmetic and accepts empty shapes (no queries,
+    no rows, no leaves) without faulting."""
+    i32, i64 = C.c_int32, C.c_int64
+    sig = {"ah_partition_workspace_bytes": [i64, i32], "ah_scan_workspace_bytes": [i64, i32, i64, i32, i32, i32],
+           "ah_sq8_workspace_bytes": [i64, i64, i32, i32], "ah_kmeans_workspace_bytes": [i32, i32],
+           "ah_pq_update_workspace_bytes": [i64, i32, i32], "ah_assign_workspace_bytes": [i64, i32],
+           "ah_tiled_codes_bytes": [i64, i32]}
+    for fn, args in (("ah_partition_workspace_bytes", (0, 5)), ("ah_partition_workspace_bytes", (3, 0)),
+                     ("ah_partition_workspace_bytes", (0, 0)), ("ah_scan_workspace_bytes", (0, 8, 10, 0, 0, 5)),
+                     ("ah_scan_workspace_bytes", (3, 8, 0, 0, 0, 5)), ("ah_scan_workspace_bytes", (0, 8, 10, 4, 2, 5)),
+                     ("ah_sq8_workspace_bytes", (0, 10, 16, 5)), ("ah_sq8_workspace_bytes", (3, 0, 16, 5)),
+                     ("ah_kmeans_workspace_bytes", (0, 16)), ("ah_pq_update_workspace_bytes", (0, 8, 2)),
+                     ("ah_assign_workspace_bytes", (0, 5)), ("ah_assign_workspace_bytes", (5, 0)),
+                     ("ah_tiled_codes_bytes", (0, 8))):
+        f = getattr(lib, fn)
+        f.argtypes, f.restype = sig[fn], C.c_size_t
+        assert f(*args) < (1 << 40), (fn, args)

@@ -120,6 +120,7 @@ def _scan_check(torch, ah, lut, codes, R, ids=None, offs=None, leaves=None):
     (33, 1234, 5, 10, 7),       # odd B, padded rows
     (16, 20000, 10, 1500, 0),   # R > 1024: the workgroup final selection
     (300, 3000, 6, 40, 0),      # 300 blocks: the workgroup warm-up
+    (64, 12000, 70, 4096, 0),   # R at its maximum (AH_MAX_R)
 ])
 def test_scan_full_parity(gpu, B, n, nq, R, stride_pad):
     torch, ah = gpu
@@ -148,6 +149,36 @@ def test_scan_empty_database(gpu):
     ids, sc = ah.ah_scan_topk(_t(torch, lut), _t(torch, codes), 5)
     torch.cuda.synchronize()
     assert (_np(ids) == -1).all() and (_np(sc) == np.iinfo(np.int32).min).all()
+
+
+def test_zero_queries_every_query_entry(gpu):
+    """An empty query batch is valid at every query-side call (partition, tables,
+    plain and partitioned and residual scans, reorder, int8 flat search, rotation
+    quantiser): each returns empty outputs without an error."""
+    torch, ah = gpu
+    rng = np.random.default_rng(9)
+    d, B, dpb, L, nl, n, R, k = 16, 8, 2, 6, 3, 60, 10, 4
+    Q0 = torch.empty((0, d), dtype=torch.float32, device="cuda")
+    X = rng.standard_normal((n, d)).astype(np.float32)
+    leaves, lsc = ah.ah_partition_score(Q0, _t(torch, rng.standard_normal((L, d)).astype(np.float32)), nl)
+    t8, step, _, _ = ah.ah_build_lut(Q0, _t(torch, rng.standard_normal((B, 16, dpb)).astype(np.float32)))
+    codes = _t(torch, synth.random_codes(rng, n, B))
+    offs = _t(torch, np.array([0, 10, 10, 25, 40, 55, 60], dtype=np.int64))
+    ids, sc = ah.ah_scan_topk(t8, codes, R)
+    pids, psc = ah.ah_scan_topk(t8, codes, R, leaf_offsets=offs, leaves=leaves)
+    bias = ah.ah_residual_leaf_bias(lsc, step, 1000)
+    rids, rsc = ah.ah_scan_topk(t8, codes, R, leaf_offsets=offs, leaves=leaves, leaf_bias=bias, bias_bound=1000)
+    fid, fsc = ah.ah_reorder_exact(Q0, _t(torch, X), ids, k)
+    q8, qs = ah.ah_sq8_quantize(Q0)
+    d8, dsc = ah.ah_sq8_quantize(_t(torch, X))
+    sid, ssc = ah.ah_sq8_scan_topk(q8, qs, d8, dsc, R)
+    signs, perm = synth.rotation_draws(d, 1)
+    y0 = ah.ah_rslm_rotate(Q0, _t(torch, signs), _t(torch, perm))
+    torch.cuda.synchronize()
+    for t, shape in ((leaves, (0, nl)), (lsc, (0, nl)), (t8, (0, B, 16)), (step, (0,)), (ids, (0, R)), (sc, (0, R)),
+                     (pids, (0, R)), (bias, (0, nl)), (rids, (0, R)), (rsc, (0, R)), (fid, (0, k)), (fsc, (0, k)),
+                     (q8, (0, d)), (sid, (0, R)), (ssc, (0, R)), (y0, (0, d))):
+        assert tuple(t.shape) == shape
 
 
 def test_scan_partitioned_parity(gpu):
@@ -193,6 +224,7 @@ def test_scan_partitioned_parity(gpu):
     (500, 4000, 1, 100, 6),     # one query, nibble table, partial last segment
     (1001, 3000, 1, 64, 11),    # odd B in 512 B rows
     (1536, 2000, 1, 50, 0),     # 768 B rows
+    (64, 9000, 3, 4096, 0),     # R at its maximum (AH_MAX_R)
 ])
 def test_scan_stream_parity(gpu, B, n, nq, R, stride_pad):
     torch, ah = gpu
@@ -352,11 +384,11 @@ def _check_ranked(g_ids, g_sc, o_ids, o_sc, ref_fn, denom_fn):
 # 4 x 64 chunks (several passes), and rows not in whole chunks (element path).
 @pytest.mark.parametrize("dtype,d,R,k", [("f32", 128, 200, 10), ("f32", 100, 37, 37), ("bf16", 384, 300, 10),
                                          ("bf16", 1536, 64, 10), ("f32", 7, 10, 3), ("f32", 512, 50, 5),
-                                         ("bf16", 4096, 40, 8), ("f32", 2048, 30, 30)])
+                                         ("bf16", 4096, 40, 8), ("f32", 2048, 30, 30), ("f32", 32, 4096, 4096)])
 def test_reorder_parity(gpu, dtype, d, R, k):
     torch, ah = gpu
     rng = np.random.default_rng(d + R)
-    n, nq = 3000, 45
+    n, nq = max(3000, R + 500), 45
     X = rng.standard_normal((n, d)).astype(np.float32)
     Q = rng.standard_normal((nq, d)).astype(np.float32)
     cand = np.stack([rng.permutation(n)[:R] for _ in range(nq)]).astype(np.int32)
