@@ -132,6 +132,36 @@ def test_scan_full_parity(gpu, B, n, nq, R, stride_pad):
     _scan_check(torch, ah, lut, codes, R)
 
 
+
+def test_zero_rows_every_row_entry(gpu):
+    """An empty set of rows is valid at every row-side call: assignment, the
+    k-means update (counts 0, centroids kept, as for empty leaves), coupled
+    encoding and sweeps, the codebook update (codebooks kept), the rotation
+    quantiser, tiling and int8 quantisation."""
+    torch, ah = gpu
+    rng = np.random.default_rng(10)
+    d, B, dpb, L = 16, 8, 2, 5
+    X0 = torch.empty((0, d), dtype=torch.float32, device="cuda")
+    C = rng.standard_normal((L, d)).astype(np.float32)
+    cb = rng.standard_normal((B, 16, dpb)).astype(np.float32)
+    leaf, _ = ah.ah_assign_leaves(X0, _t(torch, C))
+    cent, counts = ah.ah_kmeans_update(X0, torch.empty(0, dtype=torch.int32, device="cuda"), _t(torch, C))
+    codes = ah.ah_encode(X0, _t(torch, cb), 4.0)
+    ah.ah_encode_sweep(X0, _t(torch, cb), 4.0, codes)
+    cbt = _t(torch, cb)
+    ah.ah_pq_update(X0, codes, cbt, 4.0)
+    signs, perm = synth.rotation_draws(d, 2)
+    y = ah.ah_rslm_rotate(X0, _t(torch, signs), _t(torch, perm))
+    from mips_ah_partition_amd import rslm
+    rc, rs = ah.ah_rslm_encode(y, rslm.gaussian_levels())
+    tc = ah.ah_tile_codes(codes, B)
+    c8, s8 = ah.ah_sq8_quantize(X0)
+    torch.cuda.synchronize()
+    assert tuple(leaf.shape) == (0,) and tuple(codes.shape) == (0, B // 2) and tuple(rc.shape) == (0, d // 2)
+    assert tuple(rs.shape) == (0,) and tc.n == 0 and tuple(c8.shape) == (0, d) and tuple(s8.shape) == (0,)
+    assert (_np(counts) == 0).all() and np.array_equal(_np(cent), C)
+    assert np.array_equal(_np(cbt), cb)
+
 @pytest.mark.parametrize("seed", range(3))
 def test_scan_heavy_ties(gpu, seed):
     torch, ah = gpu
