@@ -405,8 +405,8 @@ def main():
                     help="only copy 1 GiB device-to-device 5 times (calibrates FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(the multi-GPU sharding is a design note, not a code path)"}))
+        print(json.dumps({"error": "the search runs on one GPU only; --gpus must be 1 "
+                                   "(sharding across GPUs is not implemented)"}))
         sys.exit(2)
 
     if args.copy_calibration:
