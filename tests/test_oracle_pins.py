@@ -740,6 +740,92 @@ def test_pq_training_step_never_raises_the_loss():
         prev = l2
 
 
+def _pack_nibbles(nib):
+    """uint8 [n, ceil(B/2)] from nibbles [n, B] (low nibble = even block)."""
+    n, B = nib.shape
+    full = np.zeros((n, B + (B & 1)), dtype=np.uint8)
+    full[:, :B] = nib
+    return (full[:, 0::2] | (full[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _aniso_grad_last_block(X, codes, cb, eta):
+    """Gradient of sum_i (eta-1)(u_i.r_i)^2 + |r_i|^2 with respect to the last
+    block's 16 centers, written from the loss's definition in float64 (r_i is the
+    row minus its decoded codes, u_i the row's unit direction).  Also returns the
+    scale of each center's gradient terms (sum of their magnitudes) and counts."""
+    B, _, dpb = cb.shape
+    Xd = X.astype(np.float64)
+    r = Xd - _decode(codes, cb)
+    u = Xd / np.linalg.norm(Xd, axis=1, keepdims=True)
+    par = np.sum(u * r, axis=1, keepdims=True)
+    sl = slice((B - 1) * dpb, B * dpb)
+    term = -2.0 * ((eta - 1.0) * par * u[:, sl] + r[:, sl])
+    nib = _decode_nibbles(codes, B)[:, B - 1]
+    grad = np.zeros((16, dpb))
+    scale = np.zeros(16)
+    np.add.at(grad, nib, term)
+    np.add.at(scale, nib, np.abs(term).sum(1))
+    return grad, scale, np.bincount(nib, minlength=16)
+
+
+def _rotate_blocks(X, nib, cb, j):
+    """Move block j to the last position (blocks j+1.. move down by one)."""
+    B, _, dpb = cb.shape
+    order = [b for b in range(B) if b != j] + [j]
+    cols = np.concatenate([np.arange(b * dpb, (b + 1) * dpb) for b in order])
+    return np.ascontiguousarray(X[:, cols]), _pack_nibbles(nib[:, order]), np.ascontiguousarray(cb[order])
+
+
+def _uncoupled_update(X, codes, cb, eta):
+    """A plausible mistake, planted here on the CPU: each block's center solved
+    as if the other blocks' parallel errors were zero (the coupling term dropped)."""
+    B, _, dpb = cb.shape
+    Xd = X.astype(np.float64)
+    U = Xd / np.linalg.norm(Xd, axis=1, keepdims=True)
+    nib = _decode_nibbles(codes, B)
+    out = cb.astype(np.float64).copy()
+    for b in range(B):
+        sl = slice(b * dpb, (b + 1) * dpb)
+        for c in range(16):
+            m = nib[:, b] == c
+            if not m.any():
+                continue
+            Ub, Xb = U[m, sl], Xd[m, sl]
+            A = (eta - 1.0) * Ub.T @ Ub + m.sum() * np.eye(dpb)
+            rhs = (Xb + (eta - 1.0) * np.sum(Ub * Xb, axis=1, keepdims=True) * Ub).sum(0)
+            out[b, c] = np.linalg.solve(A, rhs)
+    return out.astype(np.float32)
+
+
+@pytest.mark.parametrize("B,dpb,eta", [(3, 2, 4.0), (4, 2, 0.5), (3, 3, 6.0), (2, 4, 2.5)])
+def test_pq_update_last_block_is_stationary_with_coupling(B, dpb, eta):
+    # ScaNN page, "Training an anisotropic codebook yourself": each center solves
+    # the closed-form minimiser of the anisotropic loss, and with blocks the
+    # parallel error couples them.  The update goes block by block (0 .. B-1), so
+    # after it the last block's centers minimise the whole loss with every other
+    # block at its new value: the gradient of the loss, written from its
+    # definition, vanishes there.  Rotating the block order puts each block last.
+    rng = np.random.default_rng(4500 + 10 * B + dpb)
+    n = 1200
+    X = (rng.standard_normal((n, B * dpb)) + 0.7).astype(np.float32)
+    cb = rng.standard_normal((B, 16, dpb)).astype(np.float32)
+    nib = _decode_nibbles(synth.random_codes(rng, n, B), B)
+    nib[:5, :] = 3  # center 3 of every block has rows; some centers may be empty
+    for j in range(B):
+        Xr, cr, cbr = _rotate_blocks(X, nib, cb, j)
+        new = oracle.pq_update(Xr, cr, cbr, eta)
+        grad, scale, cnt = _aniso_grad_last_block(Xr, cr, new, eta)
+        # the solve is float64; the stored center is float32, so the gradient is
+        # the float32 rounding of each center times the loss's curvature
+        tol = 2.0 * max(eta, 1.0) * cnt[:, None] * np.abs(new[-1]).max() * 2.0 ** -22 + 1e-9 * scale[:, None]
+        assert (np.abs(grad) <= tol).all(), (j, np.abs(grad).max())
+        assert np.array_equal(new[-1][cnt == 0], cbr[-1][cnt == 0])
+        # the same check rejects an update that drops the coupling term
+        bad = _uncoupled_update(Xr, cr, cbr, eta)
+        gbad, _, _ = _aniso_grad_last_block(Xr, cr, bad, eta)
+        assert (np.abs(gbad) > tol).any()
+
+
 def test_encode_from_given_codes_with_zero_sweeps_returns_them():
     rng = np.random.default_rng(44)
     X = rng.standard_normal((50, 8)).astype(np.float32)
