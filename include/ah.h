@@ -60,8 +60,10 @@ enum { AH_F32 = 0, AH_BF16 = 1 };
 #define AH_MAX_ASSIGN_LEAVES 4096 /* L for ah_assign_leaves */
 #define AH_MAX_LEAF_BIAS (1 << 24) /* bias_bound of the residual scan */
 
-/* code_stride value selecting the tiled code layout (see ah_tile_codes). */
-#define AH_CODES_TILED 0
+/* code_stride value selecting the tiled code layout (see ah_tile_codes); a
+ * negative sentinel, so that a zero stride is rejected rather than taken as
+ * the tiled layout. */
+#define AH_CODES_TILED (-1)
 
 const char* ah_status_string(int status);
 int ah_version(void);
@@ -92,7 +94,10 @@ int ah_partition_score(const float* q, int64_t nq, int32_t d, const float* centr
  *
  *   q          float32 [nq][d]
  *   codebooks  float32 [B][16][dpb]   (d == B*dpb)
- *   lut_f32_out float32 [nq][B][16]   T[q][b][c] = sum_t q[b*dpb+t]*cb[b][c][t], or NULL
+ *   lut_f32_out float32 [nq][B][16]   T[q][b][c] = sum_t q[b*dpb+t]*cb[b][c][t], or NULL;
+ *                                     the sum is taken in float64 in t order and rounded
+ *                                     once to float32 (so T is the float32 rounding of a
+ *                                     float64 left-to-right sum of exact products)
  *   lut_i8_out  int8    [nq][B][16]   int8 table
  *   scale_out   float32 [nq]          per-query step s
  *   bias_out    float32 [nq]          per-query bias beta
@@ -323,18 +328,6 @@ int ah_pq_update(const float* x, int64_t n, int32_t d, const uint8_t* codes, int
 size_t ah_tiled_codes_bytes(int64_t n, int32_t B);
 int ah_tile_codes(const uint8_t* codes, int32_t code_stride, int64_t n, int32_t B, uint8_t* tiled_out,
                   size_t tiled_bytes, void* stream);
-
-/* Same as ah_scan_topk.  When main_start_event / main_stop_event are non-NULL
- * hipEvent_t handles (created by the caller), they are recorded on `stream`
- * immediately before and after the main scan kernel, so the caller can time
- * that kernel alone (the leaf inversion, threshold warm-up and final selection
- * run outside the pair). */
-int ah_scan_topk_timed(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* codes,
-                       int32_t code_stride, int64_t n, const int32_t* ids,
-                       const int64_t* leaf_offsets, int32_t L, const int32_t* leaves, int32_t nl,
-                       int32_t R, int32_t* cand_ids_out, int32_t* cand_scores_out, void* workspace,
-                       size_t workspace_bytes, void* stream, void* main_start_event,
-                       void* main_stop_event);
 
 /* ---------------------------------------------------------------------------
  * Residual (leaf-relative) variant of steps 3+4 (page "RSLM: Training-Free

@@ -27,15 +27,20 @@ namespace ah {
 // Group values for dims_per_block = kDpb (1, 2 or 4; 0 = any, loaded one float
 // at a time): a group's four centres are 4 kDpb consecutive floats of the
 // codebook (kDpb 16-byte loads) and its query slice kDpb consecutive floats.
+// Each value is summed in float64 in t order (every product of two floats is
+// exact in float64, so a fused multiply-add rounds only the sum) and rounded
+// once to float32: the table is then a fixed function of q and the codebook,
+// independent of any float32 operation order.
 template <int kDpb>
 __device__ __forceinline__ void group_values(const float* __restrict__ qrow, const float* __restrict__ cb, int b,
                                              int c0, int dpb, float (&v)[4]) {
     const float* cen = cb + ((int64_t)b * 16 + c0) * (kDpb ? kDpb : dpb);
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
     if constexpr (kDpb == 0) {
         for (int t = 0; t < dpb; ++t) {
-            const float qv = qrow[b * dpb + t];
+            const double qv = qrow[b * dpb + t];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = __fmaf_rn(qv, cen[j * dpb + t], v[j]);
+            for (int j = 0; j < 4; ++j) acc[j] = __fma_rn(qv, (double)cen[j * dpb + t], acc[j]);
         }
     } else {
         float c[4 * kDpb], qq[kDpb];
@@ -63,8 +68,10 @@ __device__ __forceinline__ void group_values(const float* __restrict__ qrow, con
 #pragma unroll
         for (int t = 0; t < kDpb; ++t)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = __fmaf_rn(qq[t], c[j * kDpb + t], v[j]);
+            for (int j = 0; j < 4; ++j) acc[j] = __fma_rn((double)qq[t], (double)c[j * kDpb + t], acc[j]);
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = __double2float_rn(acc[j]);
 }
 
 // kWq waves per query (1, 4 or 16), kIt groups of four centres per thread; a
@@ -92,7 +99,7 @@ __global__ __launch_bounds__(kWq >= 4 ? kWq * kWave : 4 * kWave) void build_lut_
     for (int i = 0; i < kIt; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[i][j] = 0.0f;
-    // table values: v[i][j] = sum_t q[b*dpb + t] * cb[b][c0 + j][t], fma in t order
+    // table values: v[i][j] = sum_t q[b*dpb + t] * cb[b][c0 + j][t] (float64 in t order, rounded once)
 #pragma unroll
     for (int i = 0; i < kIt; ++i) {
         const int g = tq + i * kTq;

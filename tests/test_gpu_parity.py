@@ -54,7 +54,11 @@ def test_build_lut_parity(gpu, dpb, B, nq):
     denom = np.maximum(np.abs(ref), np.einsum("qbt,bct->qbc", np.abs(Q.reshape(nq, B, dpb)).astype(np.float64),
                                                np.abs(cb).astype(np.float64)))
     assert (np.abs(l32 - ref) <= TOL * denom + 1e-30).all()
-    o8, os_, ob = oracle.quantize_lut(l32)
+    # the table is the float32 rounding of the float64 sum (include/ah.h), so it
+    # equals the oracle's table rounded to float32 bit for bit, and the int8 table
+    # follows from the oracle's own float32 table without chaining
+    assert np.array_equal(l32, ref.astype(np.float32))
+    o8, os_, ob = oracle.quantize_lut(ref.astype(np.float32))
     assert np.array_equal(_np(t8), o8)
     assert np.array_equal(_np(s), os_)
     assert np.array_equal(_np(beta), ob)
