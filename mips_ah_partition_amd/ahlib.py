@@ -20,14 +20,14 @@ LIB_PATH = os.path.join(_HERE, "libah.so")
 
 AH_OK, AH_ERR_NULL, AH_ERR_SHAPE, AH_ERR_UNSUPPORTED, AH_ERR_WORKSPACE, AH_ERR_HIP = 0, -1, -2, -3, -4, -5
 AH_F32, AH_BF16 = 0, 1
-AH_CODES_TILED = 0
+AH_CODES_TILED = -1
 
 # every symbol include/ah.h declares
 EXPORTS = (
     "ah_status_string", "ah_version",
     "ah_partition_workspace_bytes", "ah_partition_score",
     "ah_build_lut",
-    "ah_scan_workspace_bytes", "ah_scan_topk", "ah_scan_topk_timed",
+    "ah_scan_workspace_bytes", "ah_scan_topk",
     "ah_residual_leaf_bias", "ah_scan_topk_residual",
     "ah_sq8_quantize", "ah_sq8_workspace_bytes", "ah_sq8_scan_topk",
     "ah_rslm_rotate", "ah_rslm_encode", "ah_rslm_scan_topk",
@@ -37,6 +37,8 @@ EXPORTS = (
     "ah_tiled_codes_bytes", "ah_tile_codes",
     "ah_reorder_exact",
 )
+# every symbol include/ah_instrument.h declares (measurement hooks)
+INSTRUMENT_EXPORTS = ("ah_scan_topk_timed", "ah_scan_workspace_counters", "ah_hbm_read_probe")
 
 _lib = None
 
@@ -109,6 +111,10 @@ def lib() -> C.CDLL:
         L.ah_tile_codes.argtypes = [vp, i32, i64, i32, vp, sz, vp]
         L.ah_reorder_exact.restype = C.c_int
         L.ah_reorder_exact.argtypes = [vp, i64, i32, vp, i32, i64, vp, i32, i32, vp, vp, vp]
+        L.ah_scan_workspace_counters.restype = C.c_int
+        L.ah_scan_workspace_counters.argtypes = [i64, i32, i64, i32, i32, i32, C.POINTER(sz), C.POINTER(sz)]
+        L.ah_hbm_read_probe.restype = C.c_int
+        L.ah_hbm_read_probe.argtypes = [vp, sz, i32, vp, vp]
         _lib = L
     return _lib
 
@@ -527,3 +533,34 @@ def ah_reorder_exact(q, base, cand_ids, k, ids_out=None, scores_out=None, stream
     _check(lib().ah_reorder_exact(_ptr(q), nq, d, _ptr(base), dt, n, _ptr(cand_ids), R, k, _ptr(ids_out),
                                   _ptr(scores_out), _stream(stream)), "ah_reorder_exact")
     return ids_out, scores_out
+
+
+# ----------------------------------------------------------------------------- measurement hooks
+def ah_scan_workspace_counters(nq: int, B: int, n: int, L: int, nl: int, R: int):
+    """(appended_offset, control_offset): byte offsets of the scan's counters in its workspace."""
+    a, c = C.c_size_t(), C.c_size_t()
+    _check(lib().ah_scan_workspace_counters(nq, B, n, L, nl, R, C.byref(a), C.byref(c)), "ah_scan_workspace_counters")
+    return a.value, c.value
+
+
+def scan_counters(workspace, nq: int, B: int, n: int, L: int, nl: int, R: int):
+    """(appended rows per query int64 [nq], overflowed queries) as the last scan
+    call on `workspace` left them (synchronises the device)."""
+    a, c = ah_scan_workspace_counters(nq, B, n, L, nl, R)
+    torch.cuda.synchronize()
+    appended = workspace[a:a + 4 * nq].view(torch.int32).cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+    ctrl = workspace[c:c + 64].view(torch.int32).cpu().numpy()
+    return appended, int(ctrl[1])
+
+
+def ah_hbm_read_probe(data, blocks_per_cu=8, sink=None, stream=None):
+    """Plain-stream read of every byte of the device tensor `data` (16-byte loads)."""
+    if not data.is_cuda or not data.is_contiguous():
+        raise ValueError("data must be a contiguous device tensor")
+    nbytes = data.numel() * data.element_size()
+    if sink is None:
+        sink = torch.zeros(4, dtype=torch.int32, device=data.device)
+    _check(lib().ah_hbm_read_probe(_ptr(data), nbytes, int(blocks_per_cu), _ptr(sink), _stream(stream)),
+           "ah_hbm_read_probe")
+    return sink
+

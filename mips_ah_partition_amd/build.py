@@ -1,7 +1,8 @@
 """Build the gfx950 HIP library behind include/ah.h (libah.so, in-tree) and the
 host index builder behind include/ah_index.h (libah_index.so).
 
-One hipcc invocation compiles every source under csrc/ for gfx950 only.  Device
+Every source under csrc/ is compiled for gfx950 only, one hipcc process per
+source (in parallel), then linked.  Device
 code is built without fast-math (IEEE division and rint are part of the int8
 table definition) and with packed-fp32 instruction selection disabled.
 """
@@ -23,13 +24,7 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-fno-fast-math", "-ffp-contract=on", "-Wall", "-Wno-unused-function",
-           "-I", os.path.join(HERE, "..", "include"), "-o", tmp] + sources()
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd))
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -39,6 +34,26 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every csrc/*.hip to its own object in parallel (each source is a
+    self-contained translation unit), then link libah.so."""
+    from concurrent.futures import ThreadPoolExecutor
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-fno-fast-math", "-ffp-contract=on", "-Wall", "-Wno-unused-function",
+             "-I", os.path.join(HERE, "..", "include")]
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(objdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(lambda so: _run([hipcc] + flags + ["-c", so[0], "-o", so[1]], verbose), zip(srcs, objs)))
+    tmp = LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB)
     build_host(verbose)
     return LIB

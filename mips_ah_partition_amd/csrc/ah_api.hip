@@ -2,6 +2,7 @@
 // host, workspace sizing, and the kernel launches.  Nothing here allocates,
 // synchronises or keeps state between calls.
 #include "../../include/ah.h"
+#include "../../include/ah_instrument.h"
 #include "ah_kernels.hpp"
 
 namespace {
@@ -94,6 +95,23 @@ int ah_scan_topk_timed(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_
     return scan_impl(lut_i8, nq, B, codes, code_stride, n, ids, leaf_offsets, L, leaves, nl, nullptr, 0, R,
                      cand_ids_out, cand_scores_out, workspace, workspace_bytes, stream, main_start_event,
                      main_stop_event);
+}
+
+int ah_scan_workspace_counters(int64_t nq, int32_t B, int64_t n, int32_t L, int32_t nl, int32_t R,
+                               size_t* appended_offset, size_t* control_offset) {
+    if (!appended_offset || !control_offset) return AH_ERR_NULL;
+    if (nq < 0 || n < 0 || B < 1 || R < 1) return AH_ERR_SHAPE;
+    ah::scan_counter_offsets(nq, B, n, L, nl, R, appended_offset, control_offset);
+    return AH_OK;
+}
+
+int ah_hbm_read_probe(const void* data, size_t bytes, int32_t blocks_per_cu, uint32_t* sink, void* stream) {
+    if ((bytes & 15) != 0 || blocks_per_cu < 1 || blocks_per_cu > 64) return AH_ERR_SHAPE;
+    if (bytes == 0) return AH_OK;
+    if (!data || !sink) return AH_ERR_NULL;
+    if (!a16(data)) return AH_ERR_UNSUPPORTED;
+    return hip_status(ah::launch_read_probe(data, (int64_t)(bytes / 16), blocks_per_cu, sink,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 int ah_scan_topk(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* codes,

@@ -38,6 +38,11 @@ struct ScanProblem {
     int32_t bias_bound = 0;              // every bias is clipped to [-bias_bound, bias_bound]
 };
 size_t scan_workspace_bytes(int64_t nq, int32_t B, int64_t n, int32_t L, int32_t nl, int32_t R);
+// Offsets of the per-query append counters and the control words inside the scan workspace.
+void scan_counter_offsets(int64_t nq, int32_t B, int64_t n, int32_t L, int32_t nl, int32_t R, size_t* appended,
+                          size_t* control);
+// Plain-stream HBM read of n16 16-byte words (measurement hook).
+hipError_t launch_read_probe(const void* data, int64_t n16, int32_t blocks_per_cu, uint32_t* sink, hipStream_t stream);
 hipError_t launch_scan(const ScanProblem& p, void* ws, size_t ws_bytes, hipStream_t stream,
                        hipEvent_t main_start = nullptr, hipEvent_t main_stop = nullptr);
 

@@ -101,6 +101,13 @@ size_t scan_workspace_bytes(int64_t nq, int32_t B, int64_t n, int32_t L, int32_t
     return scan_layout(nq, B, n, L, nl, R).total;
 }
 
+void scan_counter_offsets(int64_t nq, int32_t B, int64_t n, int32_t L, int32_t nl, int32_t R, size_t* appended,
+                          size_t* control) {
+    const ScanLayout s = scan_layout(nq, B, n, L, nl, R);
+    *appended = s.cnt;
+    *control = s.ctrl;
+}
+
 struct ScanState {
     int32_t* tau;
     uint32_t* cnt;

@@ -7,10 +7,16 @@ Product Search": "The loss in one paragraph" (eta and its large-d limit),
 search" (partition into leaves; blocks of dimensions_per_block dims, 16 centers
 each) and "Using the library" (training on a sample of up to 250,000 rows).
 
-The codebook training and encoding run in the C++ host library
-(include/ah_index.h, libah_index.so); the partition k-means uses numpy BLAS.
-Nothing here runs on the GPU: the index is built once on the host and its
-arrays are passed to the C ABI of include/ah.h.
+Two builders of the same index:
+- build(): on the host -- codebook training and encoding in the C++ host
+  library (include/ah_index.h, libah_index.so), the partition k-means with
+  numpy BLAS;
+- build_gpu(): every step on the GPU through include/ah.h (ah_assign_leaves +
+  ah_kmeans_update for the partition, ah_encode / ah_encode_sweep +
+  ah_pq_update for the codebooks, ah_assign_leaves + ah_encode over all rows),
+  for databases whose host build would take minutes (20M x 384).
+Either way the index arrays are then passed to the search calls of
+include/ah.h.
 """
 from __future__ import annotations
 
@@ -256,6 +262,83 @@ def build(X: np.ndarray, dpb: int, eta: float, num_leaves: int = 0, seed: int = 
     if ids is not None:
         codes = np.ascontiguousarray(codes[ids])
     return HostIndex(cb, codes, ids, centroids, leaf_offsets, eta, residual)
+
+
+@dataclasses.dataclass
+class DeviceIndex:
+    """The index arrays as torch device tensors (same layout as HostIndex)."""
+    codebooks: object                # float32 [B, 16, dpb]
+    codes: object                    # uint8 [n, stride], leaf-sorted when partitioned
+    ids: object | None               # int32 [n]
+    centroids: object | None         # float32 [L, d]
+    leaf_offsets: object | None      # int64 [L+1]
+    eta: float
+    residual: bool = False
+
+    def to_host(self) -> HostIndex:
+        g = lambda t: None if t is None else t.cpu().numpy()  # noqa: E731
+        return HostIndex(g(self.codebooks), g(self.codes), g(self.ids), g(self.centroids), g(self.leaf_offsets),
+                         self.eta, self.residual)
+
+
+def build_gpu(X, dpb: int, eta: float, num_leaves: int = 0, seed=0, sample_rows: int = SAMPLE_ROWS,
+              iters: int = ITERS, sweeps: int = 2, chunk_rows: int = 1 << 21, timings: dict | None = None):
+    """The steps of build() on the GPU.  X: device tensor [n, d], float32 or
+    bfloat16 (the stored rows; training sees them widened exactly to float32).
+    Partition: Lloyd k-means on a sample of up to sample_rows rows (init = L
+    distinct sample rows), then every row's nearest centroid; codebooks:
+    anisotropic training on the same sample (train_codebooks_gpu); codes: the
+    coupled encoding of every row; leaf sort: rows grouped by leaf, ascending
+    row id inside a leaf.  The random draws (sample, initial rows) come from
+    numpy's default_rng(seed) in the same order as build().  timings, if given,
+    receives each step's wall time in seconds (device-synchronised).
+    Returns a DeviceIndex."""
+    import time
+    import torch
+    from . import ahlib
+    n, d = X.shape
+    dev = X.device
+    rng = np.random.default_rng(seed)
+    t = {} if timings is None else timings
+
+    def mark(name, t0):
+        torch.cuda.synchronize()
+        t[name] = time.perf_counter() - t0
+        return time.perf_counter()
+
+    t0 = time.perf_counter()
+    sample = np.sort(rng.choice(n, min(n, sample_rows), replace=False)) if n > sample_rows else np.arange(n)
+    Xs = X[torch.as_tensor(sample, device=dev, dtype=torch.long)].to(torch.float32).contiguous()
+    m = Xs.shape[0]
+    centroids = ids = offsets = None
+    if num_leaves > 0:
+        centroids, _ = kmeans_gpu(Xs, num_leaves, iters, init_rows=rng.choice(m, num_leaves, replace=False))
+        t0 = mark("partition_kmeans", t0)
+        leaf = torch.empty(n, dtype=torch.int32, device=dev)
+        ws = torch.empty(ahlib.ah_assign_workspace_bytes(min(n, chunk_rows), num_leaves), dtype=torch.uint8,
+                         device=dev)
+        for a in range(0, n, chunk_rows):
+            b = min(n, a + chunk_rows)
+            ahlib.ah_assign_leaves(X[a:b].to(torch.float32).contiguous(), centroids, leaf_out=leaf[a:b],
+                                   workspace=ws)
+        del ws
+        t0 = mark("partition_assign", t0)
+    cb, _ = train_codebooks_gpu(Xs, dpb, eta, iters, init_rows=rng.choice(m, 16, replace=False))
+    del Xs
+    t0 = mark("codebook_training", t0)
+    codes = ahlib.ah_encode(X if X.dtype in (torch.float32, torch.bfloat16) else X.to(torch.float32), cb, eta,
+                            sweeps=sweeps)
+    t0 = mark("encode", t0)
+    if num_leaves > 0:
+        order = torch.sort(leaf, stable=True).indices
+        ids = order.to(torch.int32)
+        counts = torch.bincount(leaf, minlength=num_leaves)
+        offsets = torch.zeros(num_leaves + 1, dtype=torch.int64, device=dev)
+        offsets[1:] = torch.cumsum(counts, 0)
+        codes = codes[order].contiguous()
+        del order, leaf
+        t0 = mark("leaf_sort", t0)
+    return DeviceIndex(cb, codes, ids, centroids, offsets, float(eta))
 
 
 def save(path: str, ix: HostIndex) -> None:

@@ -43,6 +43,24 @@ class AHIndex:
         self.final_num_neighbors = final_num_neighbors
         self._ws = {}
 
+    @classmethod
+    def from_device(cls, dix, base, num_leaves_to_search: int = 0, reorder: int = 100,
+                    final_num_neighbors: int = 10):
+        """An index whose arrays are already on the GPU (index.DeviceIndex) and
+        base rows as a float32 or bfloat16 device tensor [n, d]."""
+        self = cls.__new__(cls)
+        self.device = base.device
+        self.codebooks, self.codes, self.ids = dix.codebooks, dix.codes, dix.ids
+        self.centroids, self.leaf_offsets = dix.centroids, dix.leaf_offsets
+        self.base = base
+        self.residual = bool(dix.residual) and self.centroids is not None
+        self.bias_bound = min(2 * 255 * int(dix.codebooks.shape[0]), 1 << 24)
+        self.num_leaves_to_search = num_leaves_to_search
+        self.reorder = reorder
+        self.final_num_neighbors = final_num_neighbors
+        self._ws = {}
+        return self
+
     @property
     def partitioned(self) -> bool:
         return self.centroids is not None and self.num_leaves_to_search > 0

@@ -182,6 +182,36 @@ def gpu_normal_rows(torch, n: int, d: int, seed: int, dtype, chunk_rows: int = 1
     return out
 
 
+def gpu_database(torch, w: Workload, n: int | None = None, chunk_rows: int = CHUNK):
+    """The workload's database rows generated on the GPU, stored as the
+    workload's originals dtype (float32, or bfloat16 rounded to nearest even).
+    Same laws as ``rows`` (mixture: component uniform, mean + sigma N(0, I),
+    L2-normalised; gauss_unit: N(0, I) normalised; uint8_grid: integers in
+    [0, 255]); the mixture means are the host ones (``mixture_means``), the
+    per-row draws come from torch's GPU generator seeded per chunk with
+    1000*index + role and the chunk number, so any chunk can be rebuilt alone."""
+    n = w.n if n is None else n
+    dt = torch.bfloat16 if w.originals == "bf16" else torch.float32
+    out = torch.empty((n, w.d), dtype=dt, device="cuda")
+    means = torch.from_numpy(mixture_means(w)).cuda() if w.kind == "mixture_unit" else None
+    for c, a in enumerate(range(0, n, chunk_rows)):
+        b = min(n, a + chunk_rows)
+        g = torch.Generator(device="cuda")
+        g.manual_seed((1000 * w.index + ROLE_DATA) * 1_000_003 + c)
+        if w.kind == "uint8_grid":
+            x = torch.randint(0, 256, (b - a, w.d), generator=g, device="cuda").to(torch.float32)
+        else:
+            x = torch.randn((b - a, w.d), generator=g, device="cuda", dtype=torch.float32)
+            if w.kind == "mixture_unit":
+                comp = torch.randint(0, w.components, (b - a,), generator=g, device="cuda")
+                x = means[comp] + np.float32(w.sigma) * x
+            nrm = torch.linalg.vector_norm(x.double(), dim=1, keepdim=True)
+            nrm[nrm == 0] = 1.0
+            x = (x.double() / nrm).to(torch.float32)
+        out[a:b] = x.to(dt)
+    return out
+
+
 def rotation_draws(d: int, seed: int):
     """The random draws of the training-free rotation: signs float32 [d] (+-1)
     and a permutation int32 [d]."""

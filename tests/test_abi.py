@@ -1,4 +1,5 @@
-"""The C-ABI library loads, exports every symbol include/ah.h declares, and
+"""The C-ABI library loads, exports every symbol include/ah.h and
+include/ah_instrument.h declare, and
 rejects bad arguments on the host before enqueueing anything (no GPU needed:
 these calls return before any HIP API is touched)."""
 import ctypes as C
@@ -9,11 +10,12 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ah.h")
+INSTRUMENT_HEADER = os.path.join(ROOT, "include", "ah_instrument.h")
 LIB = os.path.join(ROOT, "mips_ah_partition_amd", "libah.so")
 
 
-def _declared():
-    txt = open(HEADER).read()
+def _declared(header=HEADER):
+    txt = open(header).read()
     return sorted(set(re.findall(r"^(?:const char\*|int|size_t)\s+(ah_\w+)\(", txt, flags=re.M)))
 
 
@@ -35,8 +37,31 @@ def test_library_exports_every_declared_symbol(lib):
     from mips_ah_partition_amd import ahlib
     names = _declared()
     assert sorted(ahlib.EXPORTS) == names
-    for n in names:
+    inst = _declared(INSTRUMENT_HEADER)
+    assert sorted(ahlib.INSTRUMENT_EXPORTS) == inst and not set(inst) & set(names)
+    for n in names + inst:
         assert hasattr(lib, n), n
+
+
+def test_instrument_hooks_validate_on_the_host(lib):
+    vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    lib.ah_hbm_read_probe.argtypes = [vp, sz, i32, vp, vp]
+    lib.ah_scan_workspace_counters.argtypes = [i64, i32, i64, i32, i32, i32, C.POINTER(sz), C.POINTER(sz)]
+    fake, odd = vp(4096), vp(4097)  # never dereferenced: every case below fails validation first
+    assert lib.ah_hbm_read_probe(fake, 100, 8, fake, None) == -2      # not a multiple of 16
+    assert lib.ah_hbm_read_probe(fake, 1024, 0, fake, None) == -2     # blocks per CU out of range
+    assert lib.ah_hbm_read_probe(fake, 1024, 65, fake, None) == -2
+    assert lib.ah_hbm_read_probe(None, 1024, 8, fake, None) == -1
+    assert lib.ah_hbm_read_probe(odd, 1024, 8, fake, None) == -3
+    assert lib.ah_hbm_read_probe(None, 0, 8, None, None) == 0         # nothing to read
+    a, c = sz(), sz()
+    assert lib.ah_scan_workspace_counters(10, 64, 1000, 0, 0, 50, C.byref(a), C.byref(c)) == 0
+    lib.ah_scan_workspace_bytes.restype = sz
+    lib.ah_scan_workspace_bytes.argtypes = [i64, i32, i64, i32, i32, i32]
+    total = lib.ah_scan_workspace_bytes(10, 64, 1000, 0, 0, 50)
+    assert a.value + 40 <= total and c.value + 64 <= total and a.value != c.value
+    assert lib.ah_scan_workspace_counters(10, 64, 1000, 0, 0, 0, C.byref(a), C.byref(c)) == -2
+    assert lib.ah_scan_workspace_counters(10, 64, 1000, 0, 0, 50, None, C.byref(c)) == -1
 
 
 def test_status_strings(lib):
@@ -99,9 +124,11 @@ def test_tiled_layout_validation(lib):
     assert lib.ah_tile_codes(None, 32, 100, 64, fake, need, None) == -1
     assert lib.ah_tile_codes(fake, 32, 100, 64, odd, need, None) == -3       # output not 16-byte aligned
     assert lib.ah_tile_codes(None, 32, 0, 64, None, 0, None) == 0            # n == 0: no-op
-    # scan on tiled codes (code_stride 0) needs 16-byte aligned codes
-    assert lib.ah_scan_topk(fake, 2, 8, odd, 0, 10, None, None, 0, None, 0, 5, fake, fake, fake, 1 << 30, None) == -3
-    assert lib.ah_scan_topk(fake, 2, 8, fake, -1, 10, None, None, 0, None, 0, 5, fake, fake, fake, 1 << 30, None) == -2
+    # scan on tiled codes (code_stride AH_CODES_TILED) needs 16-byte aligned codes
+    assert lib.ah_scan_topk(fake, 2, 8, odd, -1, 10, None, None, 0, None, 0, 5, fake, fake, fake, 1 << 30, None) == -3
+    # a zero (or any other negative) stride is a caller error, not the tiled layout
+    assert lib.ah_scan_topk(fake, 2, 8, fake, 0, 10, None, None, 0, None, 0, 5, fake, fake, fake, 1 << 30, None) == -2
+    assert lib.ah_scan_topk(fake, 2, 8, fake, -2, 10, None, None, 0, None, 0, 5, fake, fake, fake, 1 << 30, None) == -2
 
 
 def test_encode_validation(lib):

@@ -1,10 +1,11 @@
 """Parity at the workloads' full sizes, in the launch configuration the benchmark
 uses, checked on sampled queries that the oracle computes one by one.
 
-Stage-chained like tests/test_gpu_parity.py: the oracle receives, for each sampled
-query, the same int8 table, leaves and candidates the GPU stage received.  Integer
-results must match exactly; float scores within 1e-4 relative (float64 reference,
-denominator max(|ref|, sum |a_j b_j|)).
+On trained (GPU-built) indexes the oracle computes each sampled query from its
+own intermediates (tables, top-R), only the leaves being chained when two leaf
+scores tie within the tolerance; on the random-structure shapes it receives the
+GPU stage's inputs.  Integer results must match exactly; float scores within
+1e-4 relative (float64 reference, denominator max(|ref|, sum |a_j b_j|)).
 """
 import time
 
@@ -59,41 +60,98 @@ def _check_reorder(Qs, rows_of, cand, k, g_ids, g_sc):
         assert (np.abs(gref - ref[order]) <= 2 * TOL * np.maximum(np.abs(gref), gden)).all()
 
 
-def test_sift1m_bench_configuration(gpu):
-    """1,000,000 x 128 integer rows, 64 blocks x 2 dims, 10,000 queries, R=200,
-    k=10: the benchmark's configuration with its trained index."""
-    torch, ah = gpu
+def _trained(torch, w):
+    """The benchmark's inputs and GPU-built index for workload w."""
     import bench
+    from mips_ah_partition_amd import index as ixm
     from mips_ah_partition_amd.search import AHIndex
-    w = synth.WORKLOADS["sift1m"]
-    X, Q = bench.workload_arrays(w)
-    ix = bench.load_index(w, X)
-    _log("index ready")
-    index = AHIndex(ix, X, reorder=w.reorder, final_num_neighbors=w.k)
-    Qd = torch.from_numpy(Q).cuda()
-    t8, s, beta, l32 = ah.ah_build_lut(Qd, index.codebooks, want_f32=True)
-    cand, csum = ah.ah_scan_topk(t8, index.codes, w.reorder)
-    fid, fsc = ah.ah_reorder_exact(Qd, index.base, cand, w.k)
+    base, X, Q = bench.make_inputs(w, torch)
+    _log(f"{w.name}: rows ready; building the index on the GPU")
+    dix = ixm.build_gpu(base, w.dpb, w.eta, num_leaves=w.num_leaves, seed=1000 * w.index + synth.ROLE_CODEBOOK)
+    index = AHIndex.from_device(dix, base, num_leaves_to_search=w.leaves_to_search, reorder=w.reorder,
+                                final_num_neighbors=w.k)
     torch.cuda.synchronize()
-    _log("gpu path done")
+    _log(f"{w.name}: index ready")
+    return base, X, Q, dix, index
+
+
+def _trained_case(gpu, name):
+    """Whole path at a workload's full size on its trained (GPU-built) index, in
+    the launch configuration the benchmark times.  Sampled queries are checked
+    stage by stage against the oracle on its own intermediates: leaves (near
+    ties accepted, then the GPU's leaves are chained), the float32 and int8
+    tables bit for bit, top-R ids and sums bit for bit, reorder within 1e-4.
+    No query's candidate list may overflow (the exact fallback is not needed)."""
+    torch, ah = gpu
+    w = synth.WORKLOADS[name]
+    base, X, Q, dix, index = _trained(torch, w)
+    Qd = torch.from_numpy(Q).cuda()
+    fid, fsc = index.search_batched(Qd)
+    L = w.num_leaves if index.partitioned else 0
+    nl = w.leaves_to_search if index.partitioned else 0
+    appended, overflowed = ah.scan_counters(index._ws["scan"], w.nq, w.blocks, w.n, L, nl, w.reorder)
+    _log(f"{name}: search done; {appended.mean():.0f} candidates appended per query, {overflowed} overflowed")
+    assert overflowed == 0
+    leaves = None
+    if index.partitioned:
+        leaves, lsc = ah.ah_partition_score(Qd, dix.centroids, nl)
+    t8, s, beta, l32 = ah.ah_build_lut(Qd, dix.codebooks, want_f32=True)
+    cand, csum = ah.ah_scan_topk(t8, dix.codes, w.reorder, ids=dix.ids,
+                                 leaf_offsets=dix.leaf_offsets if leaves is not None else None, leaves=leaves)
+    fid2, _ = ah.ah_reorder_exact(Qd, index.base, cand, w.k)
+    torch.cuda.synchronize()
+    assert torch.equal(fid, fid2), "search_batched differs from the same calls made one by one"
     S = _sample(w.nq)
-    l32s, t8s = l32[S].cpu().numpy(), t8[S].cpu().numpy()
-    o8, os_, ob = oracle.quantize_lut(l32s)
-    assert np.array_equal(t8s, o8)
+    hix = dix.to_host()
+    lv = None
+    if leaves is not None:
+        lv = leaves[S].cpu().numpy()
+        o_lv, o_ls = oracle.partition(Q[S], hix.centroids, nl)
+        Cd, Qs = hix.centroids.astype(np.float64), Q[S].astype(np.float64)
+        for i in range(len(S)):
+            ref = Cd[lv[i]] @ Qs[i]
+            den = np.abs(Cd[lv[i]]) @ np.abs(Qs[i])
+            assert (np.abs(ref - o_ls[i]) <= 2 * TOL * np.maximum(np.abs(ref), den)).all()
+    l32o = oracle.lut_f64(Q[S], hix.codebooks).astype(np.float32)
+    assert np.array_equal(l32[S].cpu().numpy(), l32o)
+    o8, os_, ob = oracle.quantize_lut(l32o)
+    assert np.array_equal(t8[S].cpu().numpy(), o8)
     assert np.array_equal(s[S].cpu().numpy(), os_) and np.array_equal(beta[S].cpu().numpy(), ob)
-    ref = oracle.lut_f64(Q[S], ix.codebooks)
-    B, dpb = ix.codebooks.shape[0], ix.codebooks.shape[2]
-    den = np.einsum("qbt,bct->qbc", np.abs(Q[S].reshape(len(S), B, dpb)).astype(np.float64),
-                    np.abs(ix.codebooks).astype(np.float64))
-    assert (np.abs(l32s - ref) <= TOL * np.maximum(np.abs(ref), den)).all()
-    _check_scan(t8s, ix.codes, w.reorder, cand[S].cpu().numpy(), csum[S].cpu().numpy())
-    _log("scan sampled parity ok")
-    _check_reorder(Q[S], lambda c: X[c].astype(np.float64), cand[S].cpu().numpy(), w.k,
-                   fid[S].cpu().numpy(), fsc[S].cpu().numpy())
-    # property over every query: candidate sums are non-increasing, ids unique
-    c_all, s_all = cand.cpu().numpy(), csum.cpu().numpy()
+    _check_scan(o8, hix.codes, w.reorder, cand[S].cpu().numpy(), csum[S].cpu().numpy(), ids=hix.ids,
+                offs=hix.leaf_offsets if lv is not None else None, leaves_q=lv)
+    _log(f"{name}: sampled stage parity ok")
+    cs = cand[S].cpu().numpy()
+    rows = {}
+    for i in range(len(S)):
+        c = cs[i][cs[i] >= 0]
+        r = index.base[torch.from_numpy(c.astype(np.int64)).cuda()].float().cpu().numpy().astype(np.float64)
+        rows.update({int(x): r[j] for j, x in enumerate(c)})
+    _check_reorder(Q[S], lambda c: np.stack([rows[int(x)] for x in c]), cs, w.k, fid[S].cpu().numpy(),
+                   fsc[S].cpu().numpy())
+    s_all = csum.cpu().numpy()
     assert (np.diff(s_all, axis=1) <= 0).all()
-    assert all(len(set(r.tolist())) == w.reorder for r in c_all[:: max(1, w.nq // 500)])
+    del base, X, dix, index, cand, csum, fid, fid2
+    torch.cuda.empty_cache()
+
+
+def test_sift1m_trained_full_size(gpu):
+    """1,000,000 x 128 integer rows, 64 blocks x 2 dims, eta = 4, 10,000 queries, R=200, k=10."""
+    _trained_case(gpu, "sift1m")
+
+
+def test_glove1m_trained_full_size(gpu):
+    """1,000,000 x 100 mixture rows, 1,000 leaves / 50 searched, 50 blocks x 2 dims, R=200."""
+    _trained_case(gpu, "glove1m")
+
+
+def test_openai2m_trained_full_size(gpu):
+    """2,000,000 x 1536 bf16 mixture rows, 2,000 leaves / 100 searched, 768 blocks, 1,000 queries, R=400."""
+    _trained_case(gpu, "openai2m")
+
+
+def test_wiki20m_trained_full_size(gpu):
+    """20,000,000 x 384 bf16 mixture rows, 4,000 leaves / 200 searched, 192 blocks, 10,000 queries, R=300."""
+    _trained_case(gpu, "wiki20m")
 
 
 def test_tiny_whole_path_every_query(gpu):
@@ -112,13 +170,17 @@ def test_tiny_whole_path_every_query(gpu):
     fid, fsc = ah.ah_reorder_exact(Qd, T(X), cand, w.k)
     torch.cuda.synchronize()
     l32, t8 = l32.cpu().numpy(), t8.cpu().numpy()
+    assert np.array_equal(l32, oracle.lut_f64(Q, ix.codebooks).astype(np.float32))
     assert np.array_equal(t8, oracle.quantize_lut(l32)[0])
     _check_scan(t8, ix.codes, w.reorder, cand.cpu().numpy(), csum.cpu().numpy())
     _check_reorder(Q, lambda c: X[c].astype(np.float64), cand.cpu().numpy(), w.k, fid.cpu().numpy(),
                    fsc.cpu().numpy())
     gt, _ = oracle.brute_force(Q, X, w.k)
     res = oracle.search(Q, ix.codebooks, ix.codes, X, w.reorder, w.k)
-    assert oracle.recall_at_k(fid.cpu().numpy(), gt) >= oracle.recall_at_k(res["ids"], gt) - 0.01
+    # the oracle's own whole path (its own tables, candidates and float64 reorder):
+    # tables and candidates equal the GPU's bit for bit, and recall@10 is at least the oracle's
+    assert np.array_equal(res["lut_i8"], t8) and np.array_equal(res["cand_ids"], cand.cpu().numpy())
+    assert oracle.recall_at_k(fid.cpu().numpy(), gt) >= oracle.recall_at_k(res["ids"], gt)
 
 
 def _partitioned_case(gpu, name, generate_originals_on_gpu):
