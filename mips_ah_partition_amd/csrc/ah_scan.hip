@@ -42,6 +42,7 @@
 #include "ah_kernels.hpp"
 
 #include <limits.h>
+#include <type_traits>
 
 namespace ah {
 
@@ -49,7 +50,8 @@ constexpr int kScanWaves = 8;
 constexpr int kScanThreads = kScanWaves * kWave;  // 512
 constexpr int kTilePts = 64 * kScanWaves;         // rows per tile
 constexpr int kQG = 64;                           // queries per item
-constexpr int kKC = 16;                           // k-steps (x4 blocks) per chunk
+constexpr int kKC = 16;                           // k-steps (x4 blocks) of a resident table (B <= 64)
+constexpr int kKCS = 8;                           // k-steps of one staged chunk (B > 64): half of lut_s
 constexpr int kCodeStride = 9;                    // LDS row stride (dwords) for a chunk's 8 code dwords
 constexpr int kNB = 1024;                         // histogram bins per query
 constexpr int kLB = 64;                           // an item's LDS histogram bins per query
@@ -331,11 +333,24 @@ __global__ __launch_bounds__(kSelThreads) void warmup_kernel(Problem p, ScanStat
 }
 
 // ------------------------------------------------------------------ main scan
+// Source of the zero table entries a staged chunk holds for blocks past B.
+__device__ __align__(16) int8_t g_zero16[16];
+
+// One wave's direct global-to-LDS copy: lane l's 16 bytes at src land at
+// lds_base + 16 l (lds_base is wave-uniform).  Completion is counted by vmcnt.
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+template <int V>
+__device__ __forceinline__ constexpr int buf_value(std::integral_constant<int, V>) { return V; }
+__device__ __forceinline__ int buf_value(int b) { return b; }
+
 struct MainArgs {
     Problem p;
     ScanState st;
     int32_t nkstep;   // k-steps of 4 blocks (blocks rounded up to 8)
-    int32_t nchunk;   // 64-block chunks
+    int32_t nchunk;   // 1: the table is resident (B <= 64); else staged chunks of 32 blocks
     int32_t qg;       // queries per item
     int32_t item_pts; // rows per item (at most kItemPts)
     int32_t nqg;      // query groups (full scan)
@@ -594,9 +609,19 @@ __device__ __forceinline__ void refresh_tau_wave(const ScanState& st, const int3
 }
 
 // kBias: the residual variant (a.qbias set); the plain scan compiles without it.
-template <bool kBias>
+// kStaged: tables of more than 64 blocks, staged 32 blocks at a time (a.nchunk
+// chunks); else the table is resident for the item (a.nchunk == 1).  kFast
+// (staged only): rows 16-byte aligned, one 16-byte code load per row and step
+// (a separate instantiation, so the byte-wise loads of unaligned rows leave
+// no pending loads in the aligned loop).
+template <bool kBias, bool kStaged, bool kFast>
 __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) {
-    __shared__ __align__(16) int8_t lut_s[kKC * 4 * kWave * 16];  // [kstep][ntile][lane][16]
+    // resident table: lut_s, 64 blocks [kstep][ntile][lane][16]; staged: lut_s
+    // and lut_t hold alternate 32-block chunks.  Two objects, so that the
+    // compiler sees a chunk's copy and the other chunk's reads as disjoint and
+    // does not wait for the copy before those reads.
+    __shared__ __align__(16) int8_t lut_s[(kStaged ? kKCS : kKC) * 4 * kWave * 16];
+    __shared__ __align__(16) int8_t lut_t[kStaged ? kKCS * 4 * kWave * 16 : 16];
     __shared__ __align__(16) uint32_t code_s[2][kTilePts * kCodeStride];
     __shared__ uint64_t log_s[kScanWaves * kLogCap];
     __shared__ __align__(16) uint32_t onehot_s[16 * 4];           // onehot_s[c] = 16 bytes, byte c = 1
@@ -616,6 +641,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
     const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
     const int r16 = lane & 15, g = lane >> 4;
     const int64_t n_items = p.leaves ? a.itemoff[p.L] : a.n_items;
+    constexpr bool dyn = !kStaged;  // resident table; else staged 32-block chunks
     uint64_t* mylog = log_s + w * kLogCap;
     uint32_t* mywq = fl_s + w * 2 * kWave;
     if (tid < 16) {
@@ -660,7 +686,23 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
         for (int e = tid; e < kQG * kLB; e += kScanThreads) lh[e] = 0;
         __syncthreads();
 
-        // table staging: B operand layout [kstep][ntile][lane][16 bytes]
+        // staged tables (B > 64): chunk c (blocks 32c .. 32c+31) into dst (lut_s
+        // or lut_t) by direct global-to-LDS copies, four 1 KB slices per wave,
+        // in the B-operand layout [kstep][ntile][lane][16 bytes]; blocks past B
+        // copy zeros, padded query slots copy query 0's (never passed by the filter)
+        auto dma_lut = [&](int c, int8_t* dst) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int idx = w * 4 + i, s = idx >> 2, nt = idx & 3;
+                const int ql = 16 * nt + r16;
+                const int blk = c * 32 + 4 * s + g;
+                // an integer select keeps the copy a single unmasked instruction
+                const uintptr_t tab = reinterpret_cast<uintptr_t>(p.lut + ((int64_t)qid_s[ql] * p.B + blk) * 16);
+                const uintptr_t src = blk < p.B ? tab : reinterpret_cast<uintptr_t>(g_zero16);
+                dma16(reinterpret_cast<const void*>(src), dst + idx * (kWave * 16));
+            }
+        };
+        // resident table (B <= 64): B operand layout [kstep][ntile][lane][16 bytes]
         auto stage_lut = [&](int c) {
             for (int e = tid; e < kKC * 4 * kWave; e += kScanThreads) {
                 const int s = e >> 8, nt = (e >> 6) & 3, ln = e & 63;
@@ -679,6 +721,33 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
         auto load_codes = [&](int64_t rowbase, int c, uint4& x0, uint4& x1, uint32_t& keep) {
             const int64_t row = rowbase + lane;
             const bool live = row < p1;
+            if (!dyn) {
+                // staged chunk c: code bytes [16c, 16c + 16), one 16-byte load
+                x1 = make_uint4(0, 0, 0, 0);
+                if (kFast) {
+                    const int64_t r = live ? row : p1 - 1;
+                    const int avail = p.stride - 16 * c;
+                    x0 = *reinterpret_cast<const uint4*>(code_row(p, r) + (avail >= 16 ? c * seg_step(p) : 0));
+                    keep = live && avail >= 16 ? 1u : 0u;
+                } else {
+                    keep = 1u;
+                    x0 = make_uint4(0, 0, 0, 0);
+                    if (!live) return;
+                    const uint8_t* src = p.codes + row * p.stride + 16 * c;
+                    const int cb = (p.B + 1) / 2 - 16 * c;
+                    uint32_t wd[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        uint32_t v = 0;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * k + e < cb) v |= (uint32_t)src[4 * k + e] << (8 * e);
+                        wd[k] = v;
+                    }
+                    x0 = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                }
+                return;
+            }
             if (a.fast_codes) {
                 // always exactly two 16-byte loads from an in-bounds address (the
                 // row itself, or the item's last row), so the number of loads in
@@ -717,12 +786,13 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
             d[4] = x1.x & k1; d[5] = x1.y & k1; d[6] = x1.z & k1; d[7] = x1.w & k1;
         };
 
-        // A wave's steps.  With one 64-block chunk, each step is a 64-row slab
-        // that the wave claims from the item's LDS counter, so the waves of an
-        // item finish within one slab of each other.  With several chunks, the
-        // waves share each chunk's table and step through the 512-row tiles in
-        // lockstep: step = tile * nchunk + c, rows tile * 512 + 64 w onwards.
-        const bool dyn = a.nchunk == 1;
+        // A wave's steps.  With a resident table (one chunk), each step is a
+        // 64-row slab that the wave claims from the item's LDS counter, so the
+        // waves of an item finish within one slab of each other.  With staged
+        // chunks, the waves share each chunk's table and step through the
+        // 512-row tiles in lockstep: step = tile * nchunk + c, rows tile * 512
+        // + 64 w onwards; chunk c's table is copied into one half of lut_s
+        // while the previous chunk is computed from the other half.
         const int64_t nslabs = (p1 - p0 + 63) / 64;
         const int64_t nsteps = ((p1 - p0 + kTilePts - 1) / kTilePts) * a.nchunk;
         auto claim = [&]() -> int64_t {
@@ -744,19 +814,23 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
         step_after(nu, nc);
         uint4 px0, px1;
         uint32_t pkeep;
+        if (!dyn && cu < nunits) dma_lut(cc, lut_s);
         if (cu < nunits) {
             load_codes(rowbase_of(cu), cc, px0, px1, pkeep);
             store_codes(0, px0, px1, pkeep);
         }
         if (nu < nunits) load_codes(rowbase_of(nu), nc, px0, px1, pkeep);
-        if (a.nchunk == 1) stage_lut(0);
-        __syncthreads();  // lut_s, qid_s and the first codes for this item are complete
+        if (dyn) stage_lut(0);
+        __syncthreads();  // lut_s (its first chunk), qid_s and the first codes for this item are complete
 
         v4i acc[4][4];
         int32_t tq[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
         int log_n = 0;
 
-        for (int buf = 0; cu < nunits; buf ^= 1) {
+        // one step; buf (0 or 1) selects the code buffer and, when staged, the
+        // table half read by this step (a compile-time constant there)
+        auto step = [&](auto buf_tag) {
+            const int buf = buf_value(buf_tag);
             const int c = cc;
             if (c == 0) {
 #pragma unroll
@@ -764,18 +838,20 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt) acc[m][nt] = v4i{0, 0, 0, 0};
             }
-            // thresholds for this step's filter, loaded every step (padded
-            // query slots read query 0 and are disabled in the filter)
+            // thresholds for this step's filter (padded query slots read query
+            // 0 and are disabled in the filter), issued before the next chunk's
+            // table copies so that the filter's wait does not include them
+            if (c == a.nchunk - 1) {
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) tq[nt] = ld_coherent(st.tau + qid_s[16 * nt + r16]);
-            if (!dyn) {  // every wave is past the previous step's reads of lut_s
-                if (c > 0 || cu > 0) __syncthreads();
-                stage_lut(c);
-                __syncthreads();
+                for (int nt = 0; nt < 4; ++nt) tq[nt] = ld_coherent(st.tau + qid_s[16 * nt + r16]);
             }
-            const int ks = a.nkstep - c * kKC < kKC ? a.nkstep - c * kKC : kKC;  // even
+            // staged: every wave has passed the previous step's barrier, so the
+            // half read one step ago is free for the next step's chunk
+            if (!dyn) dma_lut(nu < nunits ? nc : cc, buf ? lut_s : lut_t);  // past the last step: an unused copy
+            const int kc = dyn ? kKC : kKCS;
+            const int ks = a.nkstep - c * kc < kc ? a.nkstep - c * kc : kc;  // even
             const uint32_t* crow = code_s[buf] + (w * 64 + r16) * kCodeStride;
-            const int8_t* lutw = lut_s + lane * 16;
+            const int8_t* lutw = (dyn || buf == 0 ? lut_s : lut_t) + lane * 16;
             // k-steps go in pairs sharing one code dword per row tile (blocks
             // 8j..8j+7); each step's A and B fragments are fetched from LDS one
             // step ahead into alternating registers.
@@ -897,20 +973,47 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                     }
                 }
             }
-            // Each wave stages and reads only its own 64 code rows, so with one
-            // chunk the waves need no workgroup barrier inside an item: a
-            // wave-scope fence orders this wave's reads of buf^1 (one step ago)
-            // before its new writes.  Several chunks share lut_s, which is
-            // restaged every step.  The next step's loads are issued after the
-            // filter, whose wait for the thresholds would otherwise wait for them.
-            if (!dyn) __syncthreads();
+            // Each wave stages and reads only its own 64 code rows, so with a
+            // resident table the waves need no workgroup barrier inside an
+            // item: a wave-scope fence orders this wave's reads of buf^1 (one
+            // step ago) before its new writes.  Staged chunks are shared by
+            // all waves (the barrier below).  The next step's loads are issued
+            // after the filter, whose wait for the thresholds would otherwise
+            // wait for them.
             wave_fence();
             if (nu < nunits) store_codes(buf ^ 1, px0, px1, pkeep);  // buf^1 was last read one step ago
             cu = nu;
             cc = nc;
             step_after(nu, nc);
-            if (nu < nunits) load_codes(rowbase_of(nu), nc, px0, px1, pkeep);
+            const bool more = nu < nunits;
+            if (more) load_codes(rowbase_of(nu), nc, px0, px1, pkeep);
+            if (!dyn) {
+                // this wave's copies of the next chunk have landed (only the
+                // code load just issued may still be in flight; with byte-wise
+                // code loads, everything) and its LDS writes are done; after
+                // the barrier every wave's copies are visible and every wave is
+                // past this step's reads
+                if (more && kFast) __builtin_amdgcn_s_waitcnt(0x0071);  // vmcnt(1) lgkmcnt(0)
+                else __builtin_amdgcn_s_waitcnt(0x0070);                       // vmcnt(0) lgkmcnt(0)
+                wave_fence();
+                __builtin_amdgcn_s_barrier();
+            }
             wave_fence();
+        };
+        if constexpr (kStaged) {
+            using I0 = std::integral_constant<int, 0>;
+            using I1 = std::integral_constant<int, 1>;
+            while (cu < nunits) {
+                step(I0{});
+                if (!(cu < nunits)) break;
+                step(I1{});
+            }
+        } else {
+            int buf = 0;
+            while (cu < nunits) {
+                step(buf);
+                buf ^= 1;
+            }
         }
         if (log_n > 0) flush_log<true>(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave, lh, jb_s);
         __syncthreads();
@@ -1572,7 +1675,9 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     ma.st = st;
     const int32_t B8 = (sp.B + 7) & ~7;
     ma.nkstep = B8 / 4;
-    ma.nchunk = (ma.nkstep + kKC - 1) / kKC;
+    // tables up to 64 blocks stay resident for an item; larger ones are staged
+    // through LDS 32 blocks at a time
+    ma.nchunk = ma.nkstep <= kKC ? 1 : (ma.nkstep + kKCS - 1) / kKCS;
     // small batches stream the codes through VALU lookups: one query, or two
     // per item, by byte-pair tables; else one or four per item by nibble
     // tables; larger batches use the MFMA kernel with 64 queries per item
@@ -1644,8 +1749,20 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     if (max_items < grid) grid = (int)(max_items > 0 ? max_items : 1);
     if (main_start && (e = hipEventRecord(main_start, stream)) != hipSuccess) return e;
     if (!streaming) {
-        if (ma.qbias) hipLaunchKernelGGL(scan_main_kernel<true>, dim3(grid), dim3(kScanThreads), 0, stream, ma);
-        else hipLaunchKernelGGL(scan_main_kernel<false>, dim3(grid), dim3(kScanThreads), 0, stream, ma);
+        const bool staged = ma.nchunk > 1;
+        const bool fast = ma.fast_codes != 0;
+#define AH_MAIN(BIAS, ST, FAST) \
+    hipLaunchKernelGGL((scan_main_kernel<BIAS, ST, FAST>), dim3(grid), dim3(kScanThreads), 0, stream, ma)
+        if (ma.qbias) {
+            if (!staged) AH_MAIN(true, false, false);
+            else if (fast) AH_MAIN(true, true, true);
+            else AH_MAIN(true, true, false);
+        } else {
+            if (!staged) AH_MAIN(false, false, false);
+            else if (fast) AH_MAIN(false, true, true);
+            else AH_MAIN(false, true, false);
+        }
+#undef AH_MAIN
     } else {
         const int nseg = ((sp.B + 1) / 2 + 15) / 16;
         if (spair && sg == 1) launch_stream<1, true>(nseg, grid, stbl, stream, ma);
