@@ -14,7 +14,9 @@
  * Conventions shared by every call
  *  - Every array pointer is a DEVICE pointer to row-major, contiguous memory
  *    owned by the caller; the library keeps no pointer after a call returns and
- *    holds no global mutable state, so calls on distinct streams are safe.
+ *    holds no global mutable state, so calls on distinct streams are safe (the
+ *    one exception, ah_scan_topk_noalloc, keeps its scratch in a static array
+ *    per GPU; see there).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on that stream and returns; device faults surface at the
  *    caller's next synchronisation.  The caller keeps inputs, outputs and
@@ -143,6 +145,25 @@ int ah_scan_topk(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* cod
                  int32_t code_stride, int64_t n, const int32_t* ids, const int64_t* leaf_offsets,
                  int32_t L, const int32_t* leaves, int32_t nl, int32_t R, int32_t* cand_ids_out,
                  int32_t* cand_scores_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ah_scan_topk without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  The scan's scratch (thresholds, counters,
+ * histograms, candidate lists, fallback slots, leaf inversion) lives in one
+ * static device array of AH_SCAN_SCRATCH_BYTES per GPU, held by every GPU the
+ * library runs on until the process ends; its address is looked up once per
+ * device on the first call.  The call allocates nothing and clears, with its
+ * own kernels, everything the scan needs to start from zero.  Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other threads) race and give wrong results; serialise them.
+ * Arguments, results and errors are those of ah_scan_topk, plus
+ * AH_ERR_UNSUPPORTED when ah_scan_workspace_bytes(nq, B, n, L, nl, R) exceeds
+ * AH_SCAN_SCRATCH_BYTES, and AH_ERR_HIP if the array's address cannot be had. */
+#define AH_SCAN_SCRATCH_BYTES (128u << 20)
+int ah_scan_topk_noalloc(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* codes,
+                         int32_t code_stride, int64_t n, const int32_t* ids, const int64_t* leaf_offsets,
+                         int32_t L, const int32_t* leaves, int32_t nl, int32_t R, int32_t* cand_ids_out,
+                         int32_t* cand_scores_out, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Int8 scalar-quantised flat search (a second workload; page "Incoherence-Aware

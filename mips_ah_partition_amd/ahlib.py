@@ -27,7 +27,7 @@ EXPORTS = (
     "ah_status_string", "ah_version",
     "ah_partition_workspace_bytes", "ah_partition_score",
     "ah_build_lut",
-    "ah_scan_workspace_bytes", "ah_scan_topk",
+    "ah_scan_workspace_bytes", "ah_scan_topk", "ah_scan_topk_noalloc",
     "ah_residual_leaf_bias", "ah_scan_topk_residual",
     "ah_sq8_quantize", "ah_sq8_workspace_bytes", "ah_sq8_scan_topk",
     "ah_rslm_rotate", "ah_rslm_encode", "ah_rslm_scan_topk",
@@ -111,6 +111,8 @@ def lib() -> C.CDLL:
         L.ah_tile_codes.argtypes = [vp, i32, i64, i32, vp, sz, vp]
         L.ah_reorder_exact.restype = C.c_int
         L.ah_reorder_exact.argtypes = [vp, i64, i32, vp, i32, i64, vp, i32, i32, vp, vp, vp]
+        L.ah_scan_topk_noalloc.restype = C.c_int
+        L.ah_scan_topk_noalloc.argtypes = [vp, i64, i32, vp, i32, i64, vp, vp, i32, vp, i32, i32, vp, vp, vp]
         L.ah_scan_workspace_counters.restype = C.c_int
         L.ah_scan_workspace_counters.argtypes = [i64, i32, i64, i32, i32, i32, C.POINTER(sz), C.POINTER(sz)]
         L.ah_hbm_read_probe.restype = C.c_int
@@ -491,6 +493,40 @@ def ah_scan_topk(lut_i8, codes, R, ids=None, leaf_offsets=None, leaves=None, can
     else:  # (start, stop) raw hipEvent_t handles bracketing the main scan kernel
         _check(lib().ah_scan_topk_timed(*args, C.c_void_p(main_events[0]), C.c_void_p(main_events[1])),
                "ah_scan_topk_timed")
+    return cand_ids_out, cand_scores_out
+
+
+AH_SCAN_SCRATCH_BYTES = 128 << 20
+
+
+def ah_scan_topk_noalloc(lut_i8, codes, R, ids=None, leaf_offsets=None, leaves=None, cand_ids_out=None,
+                         cand_scores_out=None, stream=None):
+    """ah_scan_topk on the library's static per-GPU scratch (no workspace);
+    the outputs are allocated here only when not given."""
+    lut_i8 = _dev(lut_i8, torch.int8, "lut_i8", 3)
+    _dev(ids, torch.int32, "ids")
+    _dev(leaf_offsets, torch.int64, "leaf_offsets")
+    _dev(leaves, torch.int32, "leaves")
+    nq, B, _ = lut_i8.shape
+    if isinstance(codes, TiledCodes):
+        if codes.blocks != B:
+            raise ValueError("tiled codes were made for another number of blocks")
+        n, stride = codes.n, AH_CODES_TILED
+        codes = _dev(codes.data, torch.uint8, "codes", 1)
+    else:
+        codes = _dev(codes, torch.uint8, "codes", 2)
+        n, stride = codes.shape
+    L = 0 if leaf_offsets is None else leaf_offsets.numel() - 1
+    nl = 0 if leaves is None else leaves.shape[1]
+    if cand_ids_out is None:
+        cand_ids_out = torch.empty((nq, R), dtype=torch.int32, device=lut_i8.device)
+    if cand_scores_out is None:
+        cand_scores_out = torch.empty((nq, R), dtype=torch.int32, device=lut_i8.device)
+    _dev(cand_ids_out, torch.int32, "cand_ids_out")
+    _dev(cand_scores_out, torch.int32, "cand_scores_out")
+    _check(lib().ah_scan_topk_noalloc(_ptr(lut_i8), nq, B, _ptr(codes), stride, n, _ptr(ids), _ptr(leaf_offsets), L,
+                                      _ptr(leaves), nl, int(R), _ptr(cand_ids_out), _ptr(cand_scores_out),
+                                      _stream(stream)), "ah_scan_topk_noalloc")
     return cand_ids_out, cand_scores_out
 
 

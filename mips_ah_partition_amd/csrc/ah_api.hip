@@ -5,7 +5,35 @@
 #include "../../include/ah_instrument.h"
 #include "ah_kernels.hpp"
 
+#include <mutex>
+
+// Scan scratch of ah_scan_topk_noalloc: every GPU that runs the library holds
+// one copy of this array for the life of the process.  In host code the name
+// is only a stand-in; the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device and kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[AH_SCAN_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up on the first call on that
+// device, with the device current).
+int current_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return AH_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return AH_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return AH_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return AH_OK;
+}
 
 inline bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -62,11 +90,12 @@ size_t ah_scan_workspace_bytes(int64_t nq, int32_t B, int64_t n, int32_t L, int3
     return ah::scan_workspace_bytes(nq, B, n, L, nl, R);
 }
 
-static int scan_impl(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* codes, int32_t code_stride,
-                     int64_t n, const int32_t* ids, const int64_t* leaf_offsets, int32_t L, const int32_t* leaves,
-                     int32_t nl, const int32_t* leaf_bias, int32_t bias_bound, int32_t R, int32_t* cand_ids_out,
-                     int32_t* cand_scores_out, void* workspace, size_t workspace_bytes, void* stream,
-                     void* main_start_event, void* main_stop_event) {
+// The argument checks of ah_scan_topk that come before the workspace (AH_OK
+// also when nq == 0, which needs no workspace).
+static int scan_check(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* codes, int32_t code_stride,
+                      int64_t n, const int64_t* leaf_offsets, int32_t L, const int32_t* leaves, int32_t nl,
+                      const int32_t* leaf_bias, int32_t bias_bound, int32_t R, const int32_t* cand_ids_out,
+                      const int32_t* cand_scores_out) {
     const bool tiled = code_stride == AH_CODES_TILED;
     if (nq < 0 || n < 0 || B < 1 || R < 1 || (!tiled && code_stride < (B + 1) / 2)) return AH_ERR_SHAPE;
     if (leaves && (L < 1 || nl < 1 || nl > L || !leaf_offsets)) return AH_ERR_SHAPE;
@@ -76,6 +105,18 @@ static int scan_impl(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t*
     if (nq == 0) return AH_OK;
     if (!lut_i8 || !cand_ids_out || !cand_scores_out || (n > 0 && !codes)) return AH_ERR_NULL;
     if (!a16(lut_i8) || (tiled && !a16(codes))) return AH_ERR_UNSUPPORTED;
+    return AH_OK;
+}
+
+static int scan_impl(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* codes, int32_t code_stride,
+                     int64_t n, const int32_t* ids, const int64_t* leaf_offsets, int32_t L, const int32_t* leaves,
+                     int32_t nl, const int32_t* leaf_bias, int32_t bias_bound, int32_t R, int32_t* cand_ids_out,
+                     int32_t* cand_scores_out, void* workspace, size_t workspace_bytes, void* stream,
+                     void* main_start_event, void* main_stop_event) {
+    const int chk = scan_check(lut_i8, nq, B, codes, code_stride, n, leaf_offsets, L, leaves, nl, leaf_bias,
+                               bias_bound, R, cand_ids_out, cand_scores_out);
+    if (chk != AH_OK || nq == 0) return chk;
+    const bool tiled = code_stride == AH_CODES_TILED;
     const int32_t Lw = leaves ? L : 0, nlw = leaves ? nl : 0;
     if (!workspace || workspace_bytes < ah::scan_workspace_bytes(nq, B, n, Lw, nlw, R)) return AH_ERR_WORKSPACE;
     const int32_t seg16 = ((B + 1) / 2 + 15) / 16;  // 16-byte segments per row
@@ -95,6 +136,23 @@ int ah_scan_topk_timed(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_
     return scan_impl(lut_i8, nq, B, codes, code_stride, n, ids, leaf_offsets, L, leaves, nl, nullptr, 0, R,
                      cand_ids_out, cand_scores_out, workspace, workspace_bytes, stream, main_start_event,
                      main_stop_event);
+}
+
+int ah_scan_topk_noalloc(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_t* codes,
+                         int32_t code_stride, int64_t n, const int32_t* ids, const int64_t* leaf_offsets,
+                         int32_t L, const int32_t* leaves, int32_t nl, int32_t R, int32_t* cand_ids_out,
+                         int32_t* cand_scores_out, void* stream) {
+    // the checks of ah_scan_topk, then the scratch it needs against the array
+    const int chk = scan_check(lut_i8, nq, B, codes, code_stride, n, leaf_offsets, L, leaves, nl, nullptr, 0, R,
+                               cand_ids_out, cand_scores_out);
+    if (chk != AH_OK || nq == 0) return chk;
+    const int32_t Lw = leaves ? L : 0, nlw = leaves ? nl : 0;
+    if (ah::scan_workspace_bytes(nq, B, n, Lw, nlw, R) > (size_t)AH_SCAN_SCRATCH_BYTES) return AH_ERR_UNSUPPORTED;
+    void* ws = nullptr;
+    const int st = current_scratch(&ws);
+    if (st != AH_OK) return st;
+    return scan_impl(lut_i8, nq, B, codes, code_stride, n, ids, leaf_offsets, L, leaves, nl, nullptr, 0, R,
+                     cand_ids_out, cand_scores_out, ws, (size_t)AH_SCAN_SCRATCH_BYTES, stream, nullptr, nullptr);
 }
 
 int ah_scan_workspace_counters(int64_t nq, int32_t B, int64_t n, int32_t L, int32_t nl, int32_t R,

@@ -260,3 +260,18 @@ def test_workspace_sizes_zero_shapes(lib):
         f = getattr(lib, fn)
         f.argtypes, f.restype = sig[fn], C.c_size_t
         assert f(*args) < (1 << 40), (fn, args)
+
+
+def test_noalloc_scan_rejects_on_the_host(lib):
+    """ah_scan_topk_noalloc validates like ah_scan_topk and rejects a batch whose
+    scratch exceeds AH_SCAN_SCRATCH_BYTES before touching the GPU."""
+    vp, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
+    lib.ah_scan_topk_noalloc.argtypes = [vp, i64, i32, vp, i32, i64, vp, vp, i32, vp, i32, i32, vp, vp, vp]
+    fake = vp(4096)  # never dereferenced: every case below fails validation first
+    assert lib.ah_scan_topk_noalloc(fake, 16, 64, fake, 32, 20_000_000, None, None, 0, None, 0, 100,
+                                    fake, fake, None) == -3           # 640 MB of fallback slots alone
+    assert lib.ah_scan_topk_noalloc(fake, 2, 8, fake, 3, 10, None, None, 0, None, 0, 5, fake, fake, None) == -2
+    assert lib.ah_scan_topk_noalloc(fake, 2, 8, fake, 4, 10, None, None, 0, None, 0, 0, fake, fake, None) == -2
+    assert lib.ah_scan_topk_noalloc(None, 2, 8, fake, 4, 10, None, None, 0, None, 0, 5, fake, fake, None) == -1
+    assert lib.ah_scan_topk_noalloc(None, 0, 8, None, 4, 10, None, None, 0, None, 0, 5, None, None, None) == 0
+
