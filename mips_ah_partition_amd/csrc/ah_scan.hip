@@ -52,6 +52,10 @@ constexpr int kTilePts = 64 * kScanWaves;         // rows per tile
 constexpr int kQG = 64;                           // queries per item
 constexpr int kKC = 16;                           // k-steps (x4 blocks) of a resident table (B <= 64)
 constexpr int kKCS = 8;                           // k-steps of one staged chunk (B > 64): half of lut_s
+// The one-hot contraction runs on the sparse int8 matrix instruction (2:4
+// structured sparsity, twice the k of the dense one per instruction); false
+// selects the dense instruction with one-hot operands from an LDS table.
+constexpr bool kSparseScan = true;
 constexpr int kCodeStride = 9;                    // LDS row stride (dwords) for a chunk's 8 code dwords
 constexpr int kNB = 1024;                         // histogram bins per query
 constexpr int kLB = 64;                           // an item's LDS histogram bins per query
@@ -529,6 +533,30 @@ __device__ __forceinline__ void merge_flush(const ScanState& st, uint32_t* fh, c
     }
 }
 
+// Adds the item's LDS histograms (lh: kLB bins per local query from jb_s, the
+// top bin holding everything above) of one wave's queries (ql = w, w+8, ...)
+// to the global histograms, with a bin past the global range merged into the
+// last one (both can only undercount higher bins, so every threshold drawn
+// from the global histograms stays a valid bound), and raises hmax to the
+// highest bin added.
+__device__ __forceinline__ void merge_item_hist(const ScanState& st, const uint32_t* lh, const int32_t* jb_s,
+                                                const int32_t* qid_s, int qn, int w) {
+    const int lane = lane_id();
+#pragma unroll 1
+    for (int ql = w; ql < qn; ql += kScanWaves) {
+        const int q = qid_s[ql];
+        const uint32_t c = lh[ql * kLB + lane];
+        int gb = jb_s[ql] + lane;
+        gb = gb >= kNB ? kNB - 1 : gb;
+        if (c) atomicAdd(&st.hist[(int64_t)q * kNB + gb], c);
+        const uint64_t nz = __ballot(c != 0);
+        if (lane == 0 && nz) {
+            const int top = jb_s[ql] + 63 - __clzll((long long)nz);
+            atomicMax(&st.hmax[q], (uint32_t)(top >= kNB ? kNB - 1 : top));
+        }
+    }
+}
+
 // Publishes one wave's queries' item-local thresholds (ql = w, w+8, ...).
 __device__ __forceinline__ void publish_item(const ScanState& st, const int32_t* tau_s, const int32_t* qid_s, int qn,
                                              int w) {
@@ -625,6 +653,8 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
     __shared__ __align__(16) uint32_t code_s[2][kTilePts * kCodeStride];
     __shared__ uint64_t log_s[kScanWaves * kLogCap];
     __shared__ __align__(16) uint32_t onehot_s[16 * 4];           // onehot_s[c] = 16 bytes, byte c = 1
+    __shared__ __align__(16) uint32_t spv_s[16 * 4];  // sparse A values by (c0 >> 2) | (c1 >> 2) << 2
+    __shared__ uint32_t spi_s[256];                   // sparse A index word by code byte
     __shared__ int32_t qid_s[kQG];
     __shared__ uint32_t qapp_s[kQG];
     __shared__ uint32_t lh[kQG * kLB];  // this item's appended sums per query, bins from jb_s
@@ -644,6 +674,22 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
     constexpr bool dyn = !kStaged;  // resident table; else staged 32-block chunks
     uint64_t* mylog = log_s + w * kLogCap;
     uint32_t* mywq = fl_s + w * 2 * kWave;
+    // sparse one-hot operands: pair indices (c & 3, (c & 3) ^ 1) of both blocks
+    // of a code byte in every pair of the block (nibble 4 ^ 5 (c & 3)), and the
+    // value patterns with a 1 in the first slot of pair c >> 2 of each block
+    if (tid < 256) {
+        const uint32_t x = (uint32_t)tid;
+        const uint32_t u = (x & 3u) | (((x >> 4) & 3u) << 16);
+        spi_s[tid] = (u * 0x5555u) ^ 0x44444444u;
+    }
+    if (tid < 16) {
+        const uint32_t k0 = (uint32_t)tid & 3u, k1 = (uint32_t)tid >> 2;
+        const uint64_t lo = 1ull << (16 * k0), hi = 1ull << (16 * k1);
+        spv_s[tid * 4 + 0] = (uint32_t)lo;
+        spv_s[tid * 4 + 1] = (uint32_t)(lo >> 32);
+        spv_s[tid * 4 + 2] = (uint32_t)hi;
+        spv_s[tid * 4 + 3] = (uint32_t)(hi >> 32);
+    }
     if (tid < 16) {
         // center c: dword c/4 holds 1 << 8*(c%4), the other three dwords are 0
 #pragma unroll
@@ -852,67 +898,125 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
             const int ks = a.nkstep - c * kc < kc ? a.nkstep - c * kc : kc;  // even
             const uint32_t* crow = code_s[buf] + (w * 64 + r16) * kCodeStride;
             const int8_t* lutw = (dyn || buf == 0 ? lut_s : lut_t) + lane * 16;
-            // k-steps go in pairs sharing one code dword per row tile (blocks
-            // 8j..8j+7); each step's A and B fragments are fetched from LDS one
-            // step ahead into alternating registers.
-            v4i aA[4], aB[4], bA[4], bB[4];
-            uint32_t cw[4], cwn[4];
+            if constexpr (kSparseScan) {
+                // Sparse steps of 8 blocks (a code dword per row tile).  Lane group
+                // g's A operand is the one-hot of the code byte g of its row (blocks
+                // 2g and 2g+1 of the step) in the 2:4 sparse form: value slots 0-7
+                // hold the first block's four center groups as pairs, slots 8-15 the
+                // second's, one pair per group with a 1 in its first slot where the
+                // group holds the center, and each slot's 2-bit index selects the
+                // center inside its group (every pair of a block carries the
+                // center's indices; only the pair with the 1 contributes).  The
+                // values come from spv_s (16 patterns, so lanes share entries
+                // instead of conflicting), the index word from spi_s (one per code
+                // byte).  The matching B fragment of lane group g is the table row
+                // of block g (bytes 0-15) and of block 4 + g (bytes 16-31): the
+                // dense fragments of k-steps 2S and 2S+1.  (Fetching the next
+                // step's A operands a step ahead measured slower: the registers
+                // cost more than the latency that the second wave per SIMD hides.)
+                const int nss = ks >> 1;
+                auto ldB = [&](int S, int nt) {
+                    const v4i lo = *reinterpret_cast<const v4i*>(lutw + ((2 * S) * 4 + nt) * kWave * 16);
+                    const v4i hi = *reinterpret_cast<const v4i*>(lutw + ((2 * S + 1) * 4 + nt) * kWave * 16);
+                    return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                };
+                v8i bq[4];
+                uint32_t cw[4], cwn[4];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) cw[m] = crow[m * 16 * kCodeStride];
+                for (int m = 0; m < 4; ++m) cw[m] = crow[m * 16 * kCodeStride];
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) bA[nt] = *reinterpret_cast<const v4i*>(lutw + nt * kWave * 16);
+                for (int nt = 0; nt < 4; ++nt) bq[nt] = ldB(0, nt);
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // LDS reads only (see below)
+                for (int S = 0; S < nss; ++S) {
+                    // the next step's operands are fetched unconditionally (the last
+                    // step re-reads its own), at most 12 LDS reads in flight
+                    const int Sn = S + 1 < nss ? S + 1 : S;
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-                aA[m] = *reinterpret_cast<const v4i*>(onehot_s + __builtin_amdgcn_ubfe(cw[m], 4 * g, 4) * 4);
-            // LDS reads only (lgkmcnt 0; vmcnt and expcnt at their maxima, so the
-            // code loads in flight are not waited for): the loop is entered with
-            // no LDS read pending, and the waits inside it follow its own order
-            __builtin_amdgcn_s_waitcnt(0xC07F);
-            for (int j = 0; j < (ks >> 1); ++j) {
-                const int s1 = 2 * j + 1;
-                // the next pair's operands are fetched unconditionally (the last
-                // pair re-reads its own: same addresses, unused), so the loop has
-                // one path.  The reads are spread over the pair so that at most
-                // 14 are in flight (the LDS counter holds 15): second-half B and
-                // the next code words, first-half products m = 0-1, second-half
-                // A, products m = 2-3, then the next pair's first-half operands.
-                const int jn = j + 1 < (ks >> 1) ? j + 1 : j;
+                    for (int m = 0; m < 4; ++m) cwn[m] = crow[m * 16 * kCodeStride + Sn];
+                    v4i av[4];
+                    int iv[4];
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
-                    bB[nt] = *reinterpret_cast<const v4i*>(lutw + (s1 * 4 + nt) * kWave * 16);
+                    for (int m = 0; m < 4; ++m) {
+                        const uint32_t x = __builtin_amdgcn_ubfe(cw[m], 8 * g, 8);
+                        const uint32_t va = ((x << 2) & 0x30u) | (x & 0xC0u);
+                        av[m] = *reinterpret_cast<const v4i*>(reinterpret_cast<const unsigned char*>(spv_s) + va);
+                        iv[m] = spi_s[x];
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int m = 0; m < 4; ++m) cwn[m] = crow[m * 16 * kCodeStride + jn];
-                __builtin_amdgcn_sched_barrier(0);
+                    for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
-                for (int m = 0; m < 2; ++m)
+                        for (int m = 0; m < 4; ++m)
+                            acc[m][nt] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(av[m], bq[nt], acc[m][nt], iv[m], 0, 0);
+                        __builtin_amdgcn_sched_barrier(0);
+                        bq[nt] = ldB(Sn, nt);
+                    }
 #pragma unroll
-                    for (int nt = 0; nt < 4; ++nt)
-                        acc[m][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aA[m], bA[nt], acc[m][nt], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    aB[m] = *reinterpret_cast<const v4i*>(onehot_s + __builtin_amdgcn_ubfe(cw[m], 16 + 4 * g, 4) * 4);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int m = 2; m < 4; ++m)
-#pragma unroll
-                    for (int nt = 0; nt < 4; ++nt)
-                        acc[m][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aA[m], bA[nt], acc[m][nt], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
-                    bA[nt] = *reinterpret_cast<const v4i*>(lutw + ((2 * jn) * 4 + nt) * kWave * 16);
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    cw[m] = cwn[m];
-                    aA[m] = *reinterpret_cast<const v4i*>(onehot_s + __builtin_amdgcn_ubfe(cw[m], 4 * g, 4) * 4);
+                    for (int m = 0; m < 4; ++m) cw[m] = cwn[m];
                 }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
+            } else {
+                // k-steps go in pairs sharing one code dword per row tile (blocks
+                // 8j..8j+7); each step's A and B fragments are fetched from LDS one
+                // step ahead into alternating registers.
+                v4i aA[4], aB[4], bA[4], bB[4];
+                uint32_t cw[4], cwn[4];
+    #pragma unroll
+                for (int m = 0; m < 4; ++m) cw[m] = crow[m * 16 * kCodeStride];
+    #pragma unroll
+                for (int nt = 0; nt < 4; ++nt) bA[nt] = *reinterpret_cast<const v4i*>(lutw + nt * kWave * 16);
+    #pragma unroll
                 for (int m = 0; m < 4; ++m)
-#pragma unroll
+                    aA[m] = *reinterpret_cast<const v4i*>(onehot_s + __builtin_amdgcn_ubfe(cw[m], 4 * g, 4) * 4);
+                // LDS reads only (lgkmcnt 0; vmcnt and expcnt at their maxima, so the
+                // code loads in flight are not waited for): the loop is entered with
+                // no LDS read pending, and the waits inside it follow its own order
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+                for (int j = 0; j < (ks >> 1); ++j) {
+                    const int s1 = 2 * j + 1;
+                    // the next pair's operands are fetched unconditionally (the last
+                    // pair re-reads its own: same addresses, unused), so the loop has
+                    // one path.  The reads are spread over the pair so that at most
+                    // 14 are in flight (the LDS counter holds 15): second-half B and
+                    // the next code words, first-half products m = 0-1, second-half
+                    // A, products m = 2-3, then the next pair's first-half operands.
+                    const int jn = j + 1 < (ks >> 1) ? j + 1 : j;
+    #pragma unroll
                     for (int nt = 0; nt < 4; ++nt)
-                        acc[m][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aB[m], bB[nt], acc[m][nt], 0, 0, 0);
+                        bB[nt] = *reinterpret_cast<const v4i*>(lutw + (s1 * 4 + nt) * kWave * 16);
+    #pragma unroll
+                    for (int m = 0; m < 4; ++m) cwn[m] = crow[m * 16 * kCodeStride + jn];
+                    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                    for (int m = 0; m < 2; ++m)
+    #pragma unroll
+                        for (int nt = 0; nt < 4; ++nt)
+                            acc[m][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aA[m], bA[nt], acc[m][nt], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        aB[m] = *reinterpret_cast<const v4i*>(onehot_s + __builtin_amdgcn_ubfe(cw[m], 16 + 4 * g, 4) * 4);
+                    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                    for (int m = 2; m < 4; ++m)
+    #pragma unroll
+                        for (int nt = 0; nt < 4; ++nt)
+                            acc[m][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aA[m], bA[nt], acc[m][nt], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                    for (int nt = 0; nt < 4; ++nt)
+                        bA[nt] = *reinterpret_cast<const v4i*>(lutw + ((2 * jn) * 4 + nt) * kWave * 16);
+    #pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        cw[m] = cwn[m];
+                        aA[m] = *reinterpret_cast<const v4i*>(onehot_s + __builtin_amdgcn_ubfe(cw[m], 4 * g, 4) * 4);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                    for (int m = 0; m < 4; ++m)
+    #pragma unroll
+                        for (int nt = 0; nt < 4; ++nt)
+                            acc[m][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aB[m], bB[nt], acc[m][nt], 0, 0, 0);
+                }
             }
             if (c == a.nchunk - 1) {
                 // filter: tile (m, nt) holds, in register i, the sum of row
@@ -952,7 +1056,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                     for (int m = 0; m < 4; ++m) {
                         if (__ballot(mm[m] >= tq[nt]) == 0) continue;
                         if (log_n > kLogCap - 4 * kWave) {
-                            flush_log<true>(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave, lh, jb_s);
+                            flush_log<false>(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave, lh, jb_s);
                             log_n = 0;
                             local_refresh(lh, tau_s, jb_s, qn, w, p.R, st.hlo, st.hsh);
                         }
@@ -1015,9 +1119,12 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                 buf ^= 1;
             }
         }
-        if (log_n > 0) flush_log<true>(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave, lh, jb_s);
+        if (log_n > 0) flush_log<false>(p, st, mylog, log_n, qid_s, qapp_s, p0, mywq, mywq + kWave, lh, jb_s);
         __syncthreads();
         local_refresh(lh, tau_s, jb_s, qn, w, p.R, st.hlo, st.hsh);
+        // the item's histograms go to the global ones once per item (one atomic
+        // per touched bin), not hit by hit
+        merge_item_hist(st, lh, jb_s, qid_s, qn, w);
         publish_item(st, tau_s, qid_s, qn, w);
         refresh_tau_wave(st, qid_s, qapp_s, qn, w, kScanWaves, p.R);
         __syncthreads();
