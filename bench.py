@@ -304,17 +304,20 @@ def run_workload(w, torch, ev, steps, warmup, cpu_budget, one_core_budget, cores
             "encode_rows_per_s": n / build_t["encode"],
         }
     # the oracle needs the index and the stored rows on the host
-    log(f"[bench] {w.name}: oracle sample ...")
-    hix = ix if w.name == "tiny" else ix.to_host()
-    if X is not None:
-        base_host = X
-    else:
-        base_host = base.view(torch.int16).cpu().numpy().view(np.uint16)
-    res["_cpu"] = oracle_leg(w, hix, base_host, Q, gt, gpu_ids, cpu_budget, cores)
-    if one_core_budget > 0:
-        one = oracle_leg(w, hix, base_host, Q, gt, gpu_ids, one_core_budget, 1)
-        res["_cpu"]["one_core_queries_per_s"] = one["value"]
-        res["_cpu"]["one_core_sample"] = one["sample"]
+    res["_cpu"] = None
+    hix = base_host = None
+    if cpu_budget > 0:
+        log(f"[bench] {w.name}: oracle sample ...")
+        hix = ix if w.name == "tiny" else ix.to_host()
+        if X is not None:
+            base_host = X
+        else:
+            base_host = base.view(torch.int16).cpu().numpy().view(np.uint16)
+        res["_cpu"] = oracle_leg(w, hix, base_host, Q, gt, gpu_ids, cpu_budget, cores)
+        if one_core_budget > 0:
+            one = oracle_leg(w, hix, base_host, Q, gt, gpu_ids, one_core_budget, 1)
+            res["_cpu"]["one_core_queries_per_s"] = one["value"]
+            res["_cpu"]["one_core_sample"] = one["sample"]
     res["_lookups"] = lookups
     res["_t_main"] = t_main
     res["_code_bytes"] = n * w.code_bytes
@@ -531,7 +534,7 @@ def main():
     cores, model = host_cpu()
     w = synth.WORKLOADS[args.workload]
     cpu_budget = 0.0 if args.no_cpu_baseline else args.cpu_budget
-    r = run_workload(w, torch, ev, args.steps, args.warmup, max(cpu_budget, 0.5), 0.0, cores)
+    r = run_workload(w, torch, ev, args.steps, args.warmup, cpu_budget, 0.0, cores)
     lookups, t_main, code_bytes = r.pop("_lookups"), r.pop("_t_main"), r.pop("_code_bytes")
     cpu = r.pop("_cpu")
     achieved = 2.0 * lookups / t_main / 1e12
@@ -568,7 +571,7 @@ def main():
         "host_cpu": {"cores": cores, "model": model},
         "headline": r,
     }
-    if cpu_budget > 0:
+    if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps({"progress": "headline done", "value": out["value"], "recall_at_10": out["recall_at_10"]}),
           file=sys.stderr, flush=True)
@@ -577,12 +580,13 @@ def main():
         wo = synth.WORKLOADS[name]
         one = min(3.0, args.other_cpu_budget) if wo.n <= 1_000_000 and cpu_budget > 0 else 0.0
         ro = run_workload(wo, torch, ev, max(5, args.steps // 2), args.warmup,
-                          max(args.other_cpu_budget if cpu_budget > 0 else 0.5, 0.5), one, cores)
+                          args.other_cpu_budget if cpu_budget > 0 else 0.0, one, cores)
         ro.pop("_lookups"), ro.pop("_t_main"), ro.pop("_code_bytes")
         ro["oracle"] = ro.pop("_cpu")
         others[name] = ro
-        log(f"[bench] {name}: {ro['queries_per_s']:.0f} q/s, recall@10 {ro['recall_at_10']:.4f} "
-            f"(oracle {ro['oracle']['recall_at_10']:.4f} on {ro['oracle']['sample']})")
+        orc = ro["oracle"]
+        log(f"[bench] {name}: {ro['queries_per_s']:.0f} q/s, recall@10 {ro['recall_at_10']:.4f}"
+            + (f" (oracle {orc['recall_at_10']:.4f} on {orc['sample']})" if orc else ""))
     if others:
         out["other_workloads"] = others
     if not args.no_probe:

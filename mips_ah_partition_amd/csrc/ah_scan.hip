@@ -898,7 +898,13 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
             const int ks = a.nkstep - c * kc < kc ? a.nkstep - c * kc : kc;  // even
             const uint32_t* crow = code_s[buf] + (w * 64 + r16) * kCodeStride;
             const int8_t* lutw = (dyn || buf == 0 ? lut_s : lut_t) + lane * 16;
-            if constexpr (kSparseScan) {
+            // a staged wave whose 64 rows all lie past the item's end computes
+            // nothing (it still takes part in the copies and barriers).  (Skipping
+            // 16-query tiles past the item's last query inside the loop measured
+            // slower: the branch breaks the loop's schedule.)
+            const bool wlive = dyn || rowbase_of(cu) < p1;
+            if (!wlive) {
+            } else if constexpr (kSparseScan) {
                 // Sparse steps of 8 blocks (a code dword per row tile).  Lane group
                 // g's A operand is the one-hot of the code byte g of its row (blocks
                 // 2g and 2g+1 of the step) in the 2:4 sparse form: value slots 0-7
@@ -1018,7 +1024,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                             acc[m][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aB[m], bB[nt], acc[m][nt], 0, 0, 0);
                 }
             }
-            if (c == a.nchunk - 1) {
+            if (wlive && c == a.nchunk - 1) {
                 // filter: tile (m, nt) holds, in register i, the sum of row
                 // 16m + 4g + i (of this wave's 64) for query 16nt + r16.  All
                 // accumulator indices are compile-time constants, so the
