@@ -190,19 +190,33 @@ __device__ __forceinline__ void wave_fence() {
 
 __device__ __forceinline__ int nibble(const uint8_t* row, int b) { return (row[b >> 1] >> (4 * (b & 1))) & 15; }
 
-// Sum of one row's table entries; the table is int8 [B][16] in LDS.
+// Tables read by per-lane lookups (warm-up, fallback) are held in LDS center
+// major: entry (b, c) at byte c * S + b with S = tstride(B), a multiple of 4 whose
+// dword count is odd.  Lanes summing different rows read the same block at the
+// same time, so their entries fall in 16 different banks (lanes on the same
+// center share one address); block major, a block's 16 entries would share
+// four banks.
+__host__ __device__ constexpr int32_t tstride(int32_t B) { return 4 * (((B + 3) / 4) | 1); }
+
+__device__ __forceinline__ void stage_table_cm(int8_t* dst, const int8_t* src, int32_t B, int t0, int nt) {
+    const int32_t S = tstride(B);
+    for (int e = t0; e < B * 16; e += nt) dst[(e & 15) * S + (e >> 4)] = src[e];
+}
+
+// Sum of one row's table entries; the table is int8, center major (tstride), in LDS.
 __device__ __forceinline__ int32_t row_sum(const int8_t* lut_s, int32_t B, const uint8_t* row, bool aligned4,
                                            int32_t ss = 16) {
+    const int32_t S = tstride(B);
     int32_t s = 0;
     if (aligned4) {  // dword k of the row: segment k / 4 (ss bytes apart), word k % 4
         for (int b0 = 0; b0 < B; b0 += 8) {
             const int k = b0 >> 3;
             const uint32_t wv = *reinterpret_cast<const uint32_t*>(row + (k >> 2) * ss + (k & 3) * 4);
             const int lim = B - b0 < 8 ? B - b0 : 8;
-            for (int t = 0; t < lim; ++t) s += lut_s[(b0 + t) * 16 + ((wv >> (4 * t)) & 15)];
+            for (int t = 0; t < lim; ++t) s += lut_s[((wv >> (4 * t)) & 15) * S + b0 + t];
         }
     } else {
-        for (int b = 0; b < B; ++b) s += lut_s[b * 16 + nibble(row, b)];
+        for (int b = 0; b < B; ++b) s += lut_s[nibble(row, b) * S + b];
     }
     return s;
 }
@@ -293,8 +307,8 @@ __global__ __launch_bounds__(kSelThreads) void warmup_kernel(Problem p, ScanStat
     const int64_t q = blockIdx.x;
     const int tid = threadIdx.x;
     int8_t* lut_s = reinterpret_cast<int8_t*>(smem);
-    uint64_t* keys = reinterpret_cast<uint64_t*>(smem + (((size_t)p.B * 16 + 15) & ~(size_t)15));
-    for (int e = tid; e < p.B * 16; e += kSelThreads) lut_s[e] = p.lut[q * p.B * 16 + e];
+    uint64_t* keys = reinterpret_cast<uint64_t*>(smem + (((size_t)tstride(p.B) * 16 + 15) & ~(size_t)15));
+    stage_table_cm(lut_s, p.lut + q * p.B * 16, p.B, tid, kSelThreads);
     for (int j = tid; j < kNB; j += kSelThreads) st.hist[q * kNB + j] = 0;
     if (tid == 0) {
         st.cnt[q] = 0;
@@ -1497,7 +1511,8 @@ __global__ __launch_bounds__(kSelThreads) void warmup_wave_kernel(Problem p, Sca
     if (q >= p.nq) return;
     int8_t* lut_s = lut_all[w];
     uint32_t* hw_s = hist_all[w];
-    for (int e = lane; e < p.B * 16; e += kWave) lut_s[e] = p.lut[q * p.B * 16 + e];
+    stage_table_cm(lut_s, p.lut + q * p.B * 16, p.B, lane, kWave);
+    const int32_t S = tstride(p.B);
     for (int j = lane; j < kNB; j += kWave) st.hist[q * kNB + j] = 0;
     if (lane == 0) {
         st.cnt[q] = 0;
@@ -1543,7 +1558,7 @@ __global__ __launch_bounds__(kSelThreads) void warmup_wave_kernel(Problem p, Sca
 #pragma unroll
                     for (int u = 0; u < 32; ++u) {
                         const int blk = 32 * j + u;
-                        if (blk < p.B) sv += lut_s[blk * 16 + (int)((wd[u >> 3] >> (4 * (u & 7))) & 15u)];
+                        if (blk < p.B) sv += lut_s[(int)((wd[u >> 3] >> (4 * (u & 7))) & 15u) * S + blk];
                     }
                 }
             } else {
@@ -1685,7 +1700,7 @@ __global__ __launch_bounds__(kSelThreads) void fallback_kernel(Problem p, ScanSt
         const uint32_t it = item;
         if (it >= ld_coherent(&st.ctrl[1])) break;
         const int64_t q = st.ovf[it];
-        for (int e = tid; e < p.B * 16; e += kSelThreads) lut_s[e] = p.lut[q * p.B * 16 + e];
+        stage_table_cm(lut_s, p.lut + q * p.B * 16, p.B, tid, kSelThreads);
         __syncthreads();
         int64_t m = 0;
         const int nsrc = p.leaves ? p.nl : 1;
@@ -1848,8 +1863,8 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     if (W < 1024) W = 1024;
     if (streaming) W = 8192;  // a few queries: a tighter first bound is cheap and every workgroup starts from it
     if (W > 8192) W = 8192;
-    const size_t lut_bytes = ((size_t)sp.B * 16 + 15) & ~(size_t)15;
-    if ((size_t)sp.B * 16 <= (size_t)kWaveLut) {
+    const size_t lut_bytes = ((size_t)tstride(sp.B) * 16 + 15) & ~(size_t)15;
+    if ((size_t)tstride(sp.B) * 16 <= (size_t)kWaveLut) {
         hipLaunchKernelGGL(warmup_wave_kernel, dim3((unsigned)((sp.nq + 3) / 4)), dim3(kSelThreads), 0, stream, p, st, W);
     } else {
         allow_lds(warmup_kernel, lut_bytes + (size_t)W * 8);
