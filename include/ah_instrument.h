@@ -41,9 +41,9 @@ int ah_scan_topk_timed(const int8_t* lut_i8, int64_t nq, int32_t B, const uint8_
 int ah_scan_workspace_counters(int64_t nq, int32_t B, int64_t n, int32_t L, int32_t nl, int32_t R,
                                size_t* appended_offset, size_t* control_offset);
 
-/* Reads `bytes` of device memory at `data` once, with 16-byte loads in a
- * grid-stride loop (blocks_per_cu x 256 workgroups of 256 threads, four loads
- * in flight per thread), and writes sink[0] only if the XOR of every word read
+/* Reads `bytes` of device memory at `data` once, with nontemporal 16-byte
+ * loads in a grid-stride loop (blocks_per_cu x 256 workgroups of 256 threads,
+ * four loads in flight per thread), and writes sink[0] only if the XOR of every word read
  * equals a fixed improbable value (so the loads cannot be dropped).  Bytes per
  * second of this call are the plain-stream HBM read rate.
  * Errors: AH_ERR_NULL (data or sink with bytes > 0), AH_ERR_SHAPE (bytes not

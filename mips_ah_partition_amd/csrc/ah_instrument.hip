@@ -1,5 +1,5 @@
 // Measurement hook behind include/ah_instrument.h: a plain stream of 16-byte
-// loads over a buffer, the reference for how many bytes per second a kernel
+// nontemporal loads over a buffer, the reference for how many bytes per second a kernel
 // that reads HBM once can reach on this GPU.  Not part of the search path.
 #include "ah_device.hpp"
 #include "ah_kernels.hpp"
@@ -17,7 +17,11 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const uint4* 
     for (; i + (kProbeLoads - 1) * kProbeThreads < n16; i += step) {
         uint4 v[kProbeLoads];
 #pragma unroll
-        for (int j = 0; j < kProbeLoads; ++j) v[j] = p[i + j * kProbeThreads];
+        for (int j = 0; j < kProbeLoads; ++j) {
+            // nontemporal, as a read-once stream should be
+            const v4u32 t = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(p + i + j * kProbeThreads));
+            v[j] = make_uint4(t.x, t.y, t.z, t.w);
+        }
 #pragma unroll
         for (int j = 0; j < kProbeLoads; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
     }

@@ -1165,7 +1165,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
 //    G = 4: a dword of the four queries' entries + 128, the even and odd bytes
 //    accumulated as 16-bit fields (at most 256 blocks between folds).
 // An odd last block leaves the high nibble of its byte out of the pair sums.
-// Absent queries' entries are the bias (value 0).  Items, thresholds, hit logs
+// Absent queries' entries are the bias (value 0).  The tables run on with zero
+// entries up to whole 16-byte code segments, so every segment of a row is
+// summed in full whatever its padding bytes hold.  Items, thresholds, hit logs
 // and flushes are those of the main kernel, with G queries per item; every
 // flush also merges into the global histograms and refreshes the global
 // thresholds, because every workgroup scans rows of the same few queries.
@@ -1176,7 +1178,8 @@ constexpr int kStreamThreads = kStreamWaves * kWave;
 
 // 16 code bytes of a row from src.  The streaming kernel runs only on aligned
 // rows (stride a multiple of 16 bytes), so the whole 16 bytes stay inside the
-// row's stride; entries past the row's blocks are never added.
+// row's stride.  (Nontemporal loads measured no faster on the tiled layout and
+// much slower on row-major rows, whose lines the row's other segments reuse.)
 __device__ __forceinline__ uint4 load_code16(const uint8_t* src) {
     return *reinterpret_cast<const uint4*>(src);
 }
@@ -1200,9 +1203,9 @@ struct StreamAcc {
     int32_t s[G == 1 ? 1 : 4] = {};
     uint32_t f0 = 0, f1 = 0;  // packed 16-bit fields
 
-    // segment j of 16 code bytes: nb blocks (pair tables: nb bytes).  Lookups
-    // are issued sixteen at a time before any is added, so they overlap.
-    __device__ __forceinline__ void add(const unsigned char* tbl, int j, uint4 v, int nb) {
+    // segment j of 16 code bytes (32 blocks, or 16 pairs).  Lookups are issued
+    // sixteen at a time before any is added, so they overlap.
+    __device__ __forceinline__ void add(const unsigned char* tbl, int j, uint4 v) {
         constexpr int N = kPair ? 16 : 32;  // entries per segment
         const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -1213,9 +1216,7 @@ struct StreamAcc {
                 const int u = h + i;
                 const uint32_t w32 = wd[u / (N / 4)];
                 const int e = u % (N / 4);
-                if (u >= nb) {
-                    x[i] = 0;
-                } else if (kPair) {
+                if (kPair) {
                     const int c = (int)((w32 >> (8 * e)) & 255u);
                     x[i] = G == 1 ? (uint32_t)(int32_t)reinterpret_cast<const int16_t*>(tbl)[(16 * j + u) * 256 + c]
                                   : reinterpret_cast<const uint32_t*>(tbl)[(16 * j + u) * 256 + c];
@@ -1236,6 +1237,11 @@ struct StreamAcc {
                     f1 += __builtin_amdgcn_perm(x[i], x[i], 0x0c030c01u);  // bytes 1 and 3 -> 16-bit fields
                 }
             }
+            // sixteen lookups in flight at a time: the empty asm keeps the
+            // compiler from regrouping the adds of a whole row into one tree
+            // (which holds every lookup of the row live and spills them)
+            if (G == 1) asm volatile("" : "+v"(s[0]));
+            else asm volatile("" : "+v"(f0), "+v"(f1));
         }
     }
     __device__ __forceinline__ void fold() {
@@ -1250,7 +1256,7 @@ struct StreamAcc {
     }
 };
 
-// kSegs > 0: rows of at most kSegs 16-byte segments stay whole in registers;
+// kSegs > 0: rows of exactly kSegs 16-byte segments stay whole in registers;
 // kSegs = 0: longer rows stream through a ring of four segments.
 template <int G, bool kPair, int kSegs>
 __global__ __launch_bounds__(kStreamThreads) void scan_stream_kernel(MainArgs a) {
@@ -1277,9 +1283,9 @@ __global__ __launch_bounds__(kStreamThreads) void scan_stream_kernel(MainArgs a)
     uint32_t* myfh = fh_s + w * G * kLB;
     for (int e = lane; e < G * kLB; e += kWave) myfh[e] = 0;
     const int cb = (p.B + 1) / 2;     // code bytes per row (= pairs)
-    const int nseg = (cb + 15) / 16;  // 16-byte segments per row (the last may be partial)
-    const int lastb = cb - 16 * (nseg - 1);
-    const size_t tbl_bytes = kPair ? (size_t)cb * 256 * (G == 1 ? 2 : 4) : (size_t)p.B * 16 * (G == 1 ? 1 : 4);
+    const int nseg = kSegs > 0 ? kSegs : (cb + 15) / 16;  // 16-byte segments per row (the last may be partial)
+    const int nent = kPair ? 16 * nseg : 32 * nseg;  // table rows (pairs or blocks), zero past cb or B
+    const size_t tbl_bytes = kPair ? (size_t)nent * 256 * (G == 1 ? 2 : 4) : (size_t)nent * 16 * (G == 1 ? 1 : 4);
     int8_t* nib_s = reinterpret_cast<int8_t*>(tbl + ((tbl_bytes + 15) & ~(size_t)15));  // pair tables: G x B x 16
 
     int64_t claimed = 0;
@@ -1328,10 +1334,13 @@ __global__ __launch_bounds__(kStreamThreads) void scan_stream_kernel(MainArgs a)
                     nib_s[e] = g < qn ? p.lut[(int64_t)qid_s[g] * p.B * 16 + r] : (int8_t)0;
                 }
                 __syncthreads();
-                for (int e = tid; e < cb * 256; e += kStreamThreads) {
+                for (int e = tid; e < nent * 256; e += kStreamThreads) {
                     const int pr = e >> 8, c = e & 255;
                     const bool hi = 2 * pr + 1 < p.B;
-                    if (G == 1) {
+                    if (pr >= cb) {
+                        if (G == 1) reinterpret_cast<int16_t*>(tbl)[e] = 0;
+                        else reinterpret_cast<uint32_t*>(tbl)[e] = 0u;
+                    } else if (G == 1) {
                         const int v = nib_s[(2 * pr) * 16 + (c & 15)] + (hi ? nib_s[(2 * pr + 1) * 16 + (c >> 4)] : 0);
                         reinterpret_cast<int16_t*>(tbl)[e] = (int16_t)v;
                     } else {
@@ -1347,12 +1356,13 @@ __global__ __launch_bounds__(kStreamThreads) void scan_stream_kernel(MainArgs a)
                 }
             } else if (G == 1) {
                 const int8_t* src = p.lut + (int64_t)qid_s[0] * p.B * 16;
-                for (int e = tid; e < p.B * 16; e += kStreamThreads) tbl[e] = (unsigned char)src[e];
+                for (int e = tid; e < nent * 16; e += kStreamThreads)
+                    tbl[e] = e < p.B * 16 ? (unsigned char)src[e] : (unsigned char)0;
             } else {
-                for (int e = tid; e < p.B * 16; e += kStreamThreads) {
+                for (int e = tid; e < nent * 16; e += kStreamThreads) {
                     uint32_t x = 0;
 #pragma unroll
-                    for (int g = 0; g < G; ++g) {
+                    for (int g = 0; g < G && e < p.B * 16; ++g) {
                         const int32_t t = g < qn ? (int32_t)p.lut[(int64_t)qid_s[g] * p.B * 16 + e] : 0;
                         x |= (uint32_t)(t + 128) << (8 * g);
                     }
@@ -1407,33 +1417,24 @@ __global__ __launch_bounds__(kStreamThreads) void scan_stream_kernel(MainArgs a)
                     }
                 }
         };
-        const int fulln = kPair ? 16 : 32;                                 // entries of a full segment
-        const int lastn = kPair ? lastb : p.B - 32 * (nseg - 1);           // entries of the last one
         const int64_t rb0 = p0 + w * kWave;
         const int32_t ss = seg_step(p);
         if (kSegs > 0) {
             // whole rows in registers; the next batch's rows load while this
             // batch's are summed.  Every load is unconditional (rows past the
-            // item and segments past the row read the last valid ones), so the
-            // compiler can wait for exactly the loads it needs.
+            // item read the last valid one), so the compiler can wait for
+            // exactly the loads it needs.
             auto load_row = [&](int64_t rb, uint4* r) {
                 const int64_t row = rb + lane;
                 const uint8_t* src = code_row(p, row < p1 ? row : p1 - 1);
 #pragma unroll
-                for (int j = 0; j < kSegs; ++j) {
-                    const int jj = j < nseg ? j : nseg - 1;
-                    r[j] = load_code16(src + jj * ss);
-                }
+                for (int j = 0; j < kSegs; ++j) r[j] = load_code16(src + j * ss);
             };
             auto batch = [&](int64_t rb, const uint4* r, uint4* nr) {
                 load_row(rb + kStreamThreads, nr);
                 StreamAcc<G, kPair> acc;
 #pragma unroll
-                for (int j = 0; j < kSegs; ++j) {
-                    if (j >= nseg) break;
-                    if (j < nseg - 1) acc.add(tbl, j, r[j], fulln);
-                    else acc.add(tbl, j, r[j], lastn);
-                }
+                for (int j = 0; j < kSegs; ++j) acc.add(tbl, j, r[j]);
                 acc.fold();
                 finish_row(rb + lane, acc);
             };
@@ -1461,8 +1462,7 @@ __global__ __launch_bounds__(kStreamThreads) void scan_stream_kernel(MainArgs a)
                         if (j >= nseg) break;
                         const uint4 v = ring[k];
                         if (j + 4 < nseg) ring[k] = load_code16(src + (j + 4) * ss);
-                        if (j < nseg - 1) acc.add(tbl, j, v, fulln);
-                        else acc.add(tbl, j, v, lastn);
+                        acc.add(tbl, j, v);
                         if (j % 8 == 7) acc.fold();  // 128 pairs, or 256 blocks
                     }
                 }
@@ -1484,8 +1484,8 @@ __global__ __launch_bounds__(kStreamThreads) void scan_stream_kernel(MainArgs a)
 
 // LDS bytes of the streaming kernel's dynamic area (0: the variant does not fit).
 static size_t stream_lds(int G, bool pair, int32_t B) {
-    const size_t cb = (size_t)(B + 1) / 2;
-    const size_t t = pair ? cb * 256 * (G == 1 ? 2 : 4) : (size_t)B * 16 * (G == 1 ? 1 : 4);
+    const size_t cb = (size_t)(B + 1) / 2, nseg = (cb + 15) / 16;  // tables padded to whole segments
+    const size_t t = pair ? 16 * nseg * 256 * (G == 1 ? 2 : 4) : 32 * nseg * 16 * (G == 1 ? 1 : 4);
     const size_t extra = pair ? (size_t)G * B * 16 : 0;
     const size_t total = ((t + 15) & ~(size_t)15) + extra;
     return total <= kStreamMaxTable ? total : 0;
@@ -1747,13 +1747,20 @@ static void launch_stream1(int grid, size_t lds, hipStream_t stream, const MainA
     hipLaunchKernelGGL((scan_stream_kernel<G, kPair, kSegs>), dim3(grid), dim3(kStreamThreads), lds, stream, ma);
 }
 
-// Row length classes: up to 2 or 6 segments of 16 code bytes whole in
-// registers, longer rows through the ring.
+// Rows of 1 to 6 segments of 16 code bytes whole in registers (the count a
+// compile-time constant, so the loads and their waits follow a fixed pattern),
+// longer rows through the ring.
 template <int G, bool kPair>
 static void launch_stream(int nseg, int grid, size_t lds, hipStream_t stream, const MainArgs& ma) {
-    if (nseg <= 2) launch_stream1<G, kPair, 2>(grid, lds, stream, ma);
-    else if (nseg <= 6) launch_stream1<G, kPair, 6>(grid, lds, stream, ma);
-    else launch_stream1<G, kPair, 0>(grid, lds, stream, ma);
+    switch (nseg) {
+        case 1: launch_stream1<G, kPair, 1>(grid, lds, stream, ma); break;
+        case 2: launch_stream1<G, kPair, 2>(grid, lds, stream, ma); break;
+        case 3: launch_stream1<G, kPair, 3>(grid, lds, stream, ma); break;
+        case 4: launch_stream1<G, kPair, 4>(grid, lds, stream, ma); break;
+        case 5: launch_stream1<G, kPair, 5>(grid, lds, stream, ma); break;
+        case 6: launch_stream1<G, kPair, 6>(grid, lds, stream, ma); break;
+        default: launch_stream1<G, kPair, 0>(grid, lds, stream, ma); break;
+    }
 }
 
 static int device_cus() {

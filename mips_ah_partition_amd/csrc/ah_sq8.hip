@@ -22,9 +22,12 @@
 // documents and B = 16 queries, each lane feeding the 16 bytes k = 16 g .. 16 g
 // + 15 of one row (g = lane / 16) to both operands (the same k map on both
 // sides, so the contraction is exact whatever the hardware's internal k order);
-// a workgroup computes 256 documents x 64 queries (four waves of 64 x 64), the
-// int32 dots are rescaled in the epilogue into a score block, and the best R of
-// each query's row come from the same selection kernels as the leaf choice.
+// a workgroup computes 256 documents x 64 queries (four waves of 64 x 64) and
+// rescales the int32 dots in the epilogue.  Top R: for small n or large R the
+// epilogue writes a score block that a row selection reduces; otherwise a bound
+// from sampled 64-row group maxima lets the epilogue append only the scores at
+// or above it to a per-query candidate list, which one wave selects (an exact
+// rescan redoes a query whose list overflowed).
 // Bound: int8 MFMA (2 n d FLOP-equivalents per query).
 #include "ah_device.hpp"
 #include "ah_kernels.hpp"
