@@ -198,15 +198,35 @@ __device__ __forceinline__ int nibble(const uint8_t* row, int b) { return (row[b
 // four banks.
 __host__ __device__ constexpr int32_t tstride(int32_t B) { return 4 * (((B + 3) / 4) | 1); }
 
-__device__ __forceinline__ void stage_table_cm(int8_t* dst, const int8_t* src, int32_t B, int t0, int nt) {
-    const int32_t S = tstride(B);
-    for (int e = t0; e < B * 16; e += nt) dst[(e & 15) * S + (e >> 4)] = src[e];
+// Copies a query's int8 [B][16] table (src 16-byte aligned) into dst center
+// major with stride tstride(Bp), Bp >= B, blocks B..Bp-1 zero: one 16-byte
+// block per thread and pass, the loads of four passes issued before any is
+// written.
+__device__ __forceinline__ void stage_table_cm(int8_t* dst, const int8_t* src, int32_t B, int32_t Bp, int t0,
+                                               int nt) {
+    const int32_t S = tstride(Bp);
+    for (int b0 = t0; b0 < Bp; b0 += 4 * nt) {
+        uint4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int b = b0 + k * nt;
+            v[k] = b < B ? *reinterpret_cast<const uint4*>(src + (int64_t)b * 16) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int b = b0 + k * nt;
+            if (b >= Bp) break;
+            const uint32_t wd[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+            for (int c = 0; c < 16; ++c) dst[c * S + b] = (int8_t)(wd[c >> 2] >> (8 * (c & 3)));
+        }
+    }
 }
 
-// Sum of one row's table entries; the table is int8, center major (tstride), in LDS.
-__device__ __forceinline__ int32_t row_sum(const int8_t* lut_s, int32_t B, const uint8_t* row, bool aligned4,
-                                           int32_t ss = 16) {
-    const int32_t S = tstride(B);
+// Sum of one row's table entries; the table is int8, center major with stride
+// S (at least tstride(B)), in LDS.
+__device__ __forceinline__ int32_t row_sum(const int8_t* lut_s, int32_t B, int32_t S, const uint8_t* row,
+                                           bool aligned4, int32_t ss = 16) {
     int32_t s = 0;
     if (aligned4) {  // dword k of the row: segment k / 4 (ss bytes apart), word k % 4
         for (int b0 = 0; b0 < B; b0 += 8) {
@@ -231,6 +251,64 @@ __global__ void leaf_count_kernel(const int32_t* __restrict__ leaves, int64_t pa
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < pairs; i += (int64_t)gridDim.x * blockDim.x) {
         const int32_t l = leaves[i];
         if (l >= 0 && l < L) atomicAdd(&lcnt[l], 1u);
+    }
+}
+
+// The same two steps with the pairs of a workgroup's chunk counted in LDS
+// first (L <= kLeafLds): one device atomic per (workgroup, leaf) instead of one
+// per pair.  Chunks of kLeafChunk pairs; dynamic LDS of L words.
+constexpr int kLeafLds = 16384;
+constexpr int kLeafThreads = 1024;
+constexpr int64_t kLeafChunk = 32768;
+
+__global__ __launch_bounds__(kLeafThreads) void leaf_count_lds_kernel(const int32_t* __restrict__ leaves, int64_t pairs,
+                                                                     int32_t L, uint32_t* __restrict__ lcnt) {
+    extern __shared__ uint32_t cnt_s[];
+    const int tid = threadIdx.x;
+    for (int l = tid; l < L; l += kLeafThreads) cnt_s[l] = 0;
+    __syncthreads();
+    const int64_t i0 = (int64_t)blockIdx.x * kLeafChunk;
+    const int64_t i1 = i0 + kLeafChunk < pairs ? i0 + kLeafChunk : pairs;
+    for (int64_t i = i0 + tid; i < i1; i += kLeafThreads) {
+        const int32_t l = leaves[i];
+        if (l >= 0 && l < L) atomicAdd(&cnt_s[l], 1u);
+    }
+    __syncthreads();
+    for (int l = tid; l < L; l += kLeafThreads)
+        if (cnt_s[l]) atomicAdd(&lcnt[l], cnt_s[l]);
+}
+
+__global__ __launch_bounds__(kLeafThreads) void leaf_scatter_lds_kernel(const int32_t* __restrict__ leaves, int64_t nq,
+                                                                       int32_t nl, int32_t L,
+                                                                       const int32_t* __restrict__ lqoff,
+                                                                       uint32_t* __restrict__ lcur,
+                                                                       int32_t* __restrict__ qlist,
+                                                                       const int32_t* __restrict__ bias, int32_t bound,
+                                                                       int32_t* __restrict__ qbias) {
+    extern __shared__ uint32_t pos_s[];
+    const int tid = threadIdx.x;
+    const int64_t pairs = nq * nl;
+    for (int l = tid; l < L; l += kLeafThreads) pos_s[l] = 0;
+    __syncthreads();
+    const int64_t i0 = (int64_t)blockIdx.x * kLeafChunk;
+    const int64_t i1 = i0 + kLeafChunk < pairs ? i0 + kLeafChunk : pairs;
+    for (int64_t i = i0 + tid; i < i1; i += kLeafThreads) {
+        const int32_t l = leaves[i];
+        if (l >= 0 && l < L) atomicAdd(&pos_s[l], 1u);
+    }
+    __syncthreads();
+    // the chunk's slots of each leaf: one reservation per leaf
+    for (int l = tid; l < L; l += kLeafThreads)
+        if (pos_s[l]) pos_s[l] = (uint32_t)lqoff[l] + atomicAdd(&lcur[l], pos_s[l]);
+    __syncthreads();
+    for (int64_t i = i0 + tid; i < i1; i += kLeafThreads) {
+        const int32_t l = leaves[i];
+        if (l < 0 || l >= L) continue;
+        const uint32_t at = atomicAdd(&pos_s[l], 1u);
+        qlist[at] = (int32_t)(i / nl);
+        int32_t v = bias ? bias[i] : 0;
+        v = v < -bound ? -bound : (v > bound ? bound : v);
+        qbias[at] = v;
     }
 }
 
@@ -308,7 +386,7 @@ __global__ __launch_bounds__(kSelThreads) void warmup_kernel(Problem p, ScanStat
     const int tid = threadIdx.x;
     int8_t* lut_s = reinterpret_cast<int8_t*>(smem);
     uint64_t* keys = reinterpret_cast<uint64_t*>(smem + (((size_t)tstride(p.B) * 16 + 15) & ~(size_t)15));
-    stage_table_cm(lut_s, p.lut + q * p.B * 16, p.B, tid, kSelThreads);
+    stage_table_cm(lut_s, p.lut + q * p.B * 16, p.B, p.B, tid, kSelThreads);
     for (int j = tid; j < kNB; j += kSelThreads) st.hist[q * kNB + j] = 0;
     if (tid == 0) {
         st.cnt[q] = 0;
@@ -337,7 +415,7 @@ __global__ __launch_bounds__(kSelThreads) void warmup_kernel(Problem p, ScanStat
         const int32_t off = p.leaves ? leaf_bias_at(p, q, j) : 0;
         for (int64_t t = tid; t < take; t += kSelThreads) {
             const int64_t row = a + t;
-            const int32_t s = row_sum(lut_s, p.B, code_row(p, row), al4, seg_step(p)) + off;
+            const int32_t s = row_sum(lut_s, p.B, tstride(p.B), code_row(p, row), al4, seg_step(p)) + off;
             keys[got + t] = int_key(s, p.ids ? p.ids[row] : (int32_t)row);
         }
         __syncthreads();
@@ -1498,6 +1576,8 @@ static size_t stream_lds(int G, bool pair, int32_t B) {
 // the query's threshold (others are deferred to the workgroup kernel).
 constexpr int kWaveKeys = 1024;
 constexpr int kWaveLut = 4096;
+constexpr int kFineShift = 8;                 // fine histogram of the final selection: 256 bins
+constexpr int kFineBins = 1 << kFineShift;
 
 // The warm-up threshold here is the lower edge of the histogram bin holding the
 // R-th best of the W sums (a valid bound, at most one bin below the exact R-th
@@ -1511,8 +1591,11 @@ __global__ __launch_bounds__(kSelThreads) void warmup_wave_kernel(Problem p, Sca
     if (q >= p.nq) return;
     int8_t* lut_s = lut_all[w];
     uint32_t* hw_s = hist_all[w];
-    stage_table_cm(lut_s, p.lut + q * p.B * 16, p.B, lane, kWave);
-    const int32_t S = tstride(p.B);
+    // blocks padded with zeros to whole 16-byte code segments (32 blocks), so a
+    // row's segments are summed without per-block tests
+    const int nseg = ((p.B + 1) / 2 + 15) / 16;
+    stage_table_cm(lut_s, p.lut + q * p.B * 16, p.B, 32 * nseg, lane, kWave);
+    const int32_t S = tstride(32 * nseg);
     for (int j = lane; j < kNB; j += kWave) st.hist[q * kNB + j] = 0;
     if (lane == 0) {
         st.cnt[q] = 0;
@@ -1521,7 +1604,6 @@ __global__ __launch_bounds__(kSelThreads) void warmup_wave_kernel(Problem p, Sca
     const bool al4 = (p.stride & 3) == 0 && (reinterpret_cast<uintptr_t>(p.codes) & 3) == 0;
     // 16-byte aligned rows (then the stride holds every 16-byte segment of the codes)
     const bool al16 = (p.stride & 15) == 0 && (reinterpret_cast<uintptr_t>(p.codes) & 15) == 0;
-    const int nseg = ((p.B + 1) / 2 + 15) / 16;
     for (int j = lane; j < kNB; j += kWave) hw_s[j] = 0;
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -1540,31 +1622,46 @@ __global__ __launch_bounds__(kSelThreads) void warmup_wave_kernel(Problem p, Sca
         }
         const int64_t take = b - a < W - got ? b - a : W - got;
         const int32_t off = p.leaves ? leaf_bias_at(p, q, j) : 0;
-        for (int64_t t = lane; t < take; t += kWave) {
-            const int64_t row = a + t;
-            const uint8_t* src = code_row(p, row);
-            const int32_t ss = seg_step(p);
-            int32_t sv = off;
-            if (al16) {
-                // the whole row's code bytes (at most 8 x 16) in one round trip
-                uint4 seg[kWaveLut / 512];
+        const int32_t ss = seg_step(p);
+        if (al16) {
+            // the whole row's code bytes (at most 8 x 16) in registers, the
+            // lane's next row loading while this one is summed (two buffers,
+            // alternating; rows past the range read its last row, unused)
+            constexpr int kS = kWaveLut / 512;
+            auto load = [&](int64_t t, uint4* r) {
+                const uint8_t* src = code_row(p, a + (t < take ? t : take - 1));
 #pragma unroll
-                for (int j = 0; j < kWaveLut / 512; ++j)
-                    if (j < nseg) seg[j] = *reinterpret_cast<const uint4*>(src + j * ss);
+                for (int j = 0; j < kS; ++j)
+                    if (j < nseg) r[j] = *reinterpret_cast<const uint4*>(src + j * ss);
+            };
+            auto sum = [&](int64_t t, const uint4* r, uint4* nr) {
+                load(t + kWave, nr);
+                if (t >= take) return;
+                int32_t sv = off;
 #pragma unroll
-                for (int j = 0; j < kWaveLut / 512; ++j) {
+                for (int j = 0; j < kS; ++j) {
                     if (j >= nseg) break;
-                    const uint32_t wd[4] = {seg[j].x, seg[j].y, seg[j].z, seg[j].w};
+                    const uint32_t wd[4] = {r[j].x, r[j].y, r[j].z, r[j].w};
 #pragma unroll
-                    for (int u = 0; u < 32; ++u) {
-                        const int blk = 32 * j + u;
-                        if (blk < p.B) sv += lut_s[(int)((wd[u >> 3] >> (4 * (u & 7))) & 15u) * S + blk];
-                    }
+                    for (int u = 0; u < 32; ++u)
+                        sv += lut_s[(int)((wd[u >> 3] >> (4 * (u & 7))) & 15u) * S + 32 * j + u];
                 }
-            } else {
-                sv += row_sum(lut_s, p.B, src, al4, ss);
+                atomicAdd(&hw_s[hist_bin(sv, st.hlo, st.hsh)], 1u);
+            };
+            if (take > 0) {
+                uint4 ra[kS], rb[kS];
+                load(lane, ra);
+                for (int64_t t0 = 0; t0 < take; t0 += 2 * kWave) {
+                    sum(t0 + lane, ra, rb);
+                    if (t0 + kWave >= take) break;
+                    sum(t0 + kWave + lane, rb, ra);
+                }
             }
-            atomicAdd(&hw_s[hist_bin(sv, st.hlo, st.hsh)], 1u);
+        } else {
+            for (int64_t t = lane; t < take; t += kWave) {
+                const int32_t sv = off + row_sum(lut_s, p.B, S, code_row(p, a + t), al4, ss);
+                atomicAdd(&hw_s[hist_bin(sv, st.hlo, st.hsh)], 1u);
+            }
         }
         got += take;
     }
@@ -1601,6 +1698,7 @@ __global__ __launch_bounds__(kSelThreads) void warmup_wave_kernel(Problem p, Sca
 
 __global__ __launch_bounds__(kSelThreads) void final_select_wave_kernel(Problem p, ScanState st) {
     __shared__ uint64_t stage_all[4][kWaveKeys];
+    __shared__ uint32_t fine_all[4][kFineBins];
     const int w = threadIdx.x / kWave, lane = lane_id();
     const int64_t q = (int64_t)blockIdx.x * 4 + w;
     if (q >= p.nq) return;
@@ -1609,22 +1707,111 @@ __global__ __launch_bounds__(kSelThreads) void final_select_wave_kernel(Problem 
         if (lane == 0) st.ovf[atomicAdd(&st.ctrl[1], 1u)] = (int32_t)q;
         return;
     }
-    const int32_t tau = st.tau[q];
+    // tau first raised to the highest edge of the query's histogram with at
+    // least R appended sums at or above it (items publish only their own)
+    refresh_tau(st, (int)q, p.R);
+    const int32_t tau = ld_coherent(st.tau + q);
     const uint64_t* list = st.cand + q * st.cap;
     uint64_t* stage = stage_all[w];
-    int n = 0;  // keys at or above tau, staged while they fit
-    for (uint32_t b0 = 0; b0 < total; b0 += kWave) {
-        const uint32_t i = b0 + lane;
-        const uint64_t k = i < total ? list[i] : 0;
-        const bool keep = k != 0 && key_int_score(k) >= tau;
+    uint32_t* fine = fine_all[w];
+    // The list's keys at or above tau are staged while they fit.  Alongside,
+    // the scores in [tau, tau + kFineBins * fw) go into a fine histogram (fw:
+    // the scan histogram's bin width / kFineBins, at least 1) and the keys
+    // above that range are counted, so that when too many keys reach tau a
+    // higher threshold t2 can be read off with at least R keys at or above it.
+    const int32_t fsh = st.hsh > kFineShift ? st.hsh - kFineShift : 0;
+    const int64_t ftop = (int64_t)tau + ((int64_t)kFineBins << fsh);
+    for (int j = lane; j < kFineBins; j += kWave) fine[j] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // the list is read in rounds of 8 keys per lane, all loads of a round
+    // issued before any key is used (every lane runs every call of f: f may
+    // take ballots)
+    auto for_keys = [&](auto f) {
+        for (uint32_t b0 = 0; b0 < total; b0 += 8 * kWave) {
+            uint64_t kk[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const uint32_t i = b0 + r * kWave + lane;
+                kk[r] = i < total ? list[i] : 0;
+            }
+#pragma unroll
+            for (int r = 0; r < 8; ++r) f(kk[r]);
+        }
+    };
+    int n = 0;        // keys at or above tau
+    int n_high = 0;   // keys at or above ftop
+    int32_t smax = INT_MIN;  // this lane's best score at or above tau
+    for_keys([&](const uint64_t k) {
+        const int32_t sc = key_int_score(k);
+        const bool keep = k != 0 && sc >= tau;
         const uint64_t mk = __ballot(keep);
         const int pos = n + __popcll(mk & lanemask_lt());
         if (keep && pos < kWaveKeys) stage[pos] = k;
         n += __popcll(mk);
-    }
+        const bool high = keep && (int64_t)sc >= ftop;
+        n_high += __popcll(__ballot(high));
+        if (keep && !high && tau != INT_MIN) atomicAdd(&fine[((int64_t)sc - tau) >> fsh], 1u);
+        if (keep && sc > smax) smax = sc;
+    });
     if (n > kWaveKeys) {
-        if (lane == 0) st.dfr[atomicAdd(&st.ctrl[3], 1u)] = (int32_t)q;
-        return;
+        // t2: the lower edge of the fine bin holding the R-th best key (n2
+        // keys at or above it), read from the fine histogram of [lo, lo +
+        // kFineBins << sh) with `above` keys above that range
+        auto pick = [&](int64_t lo, int32_t sh, int above, int& n2, int32_t& t2) {
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            n2 = -1;
+            int acc = above;
+            for (int top = kFineBins - 1; top >= 0 && n2 < 0; top -= kWave) {
+                const int j = top - lane;
+                const int c = j >= 0 ? (int)fine[j] : 0;
+                const int incl = acc + wave_inclusive_sum(c);
+                const uint64_t mk = __ballot(j >= 0 && incl >= p.R);
+                if (mk) {
+                    const int l = __ffsll((unsigned long long)mk) - 1;
+                    n2 = __shfl(incl, l);
+                    t2 = (int32_t)(lo + ((int64_t)(top - l) << sh));
+                }
+                acc = __shfl(incl, kWave - 1);
+            }
+        };
+        int n2 = -1;
+        int32_t t2 = tau;
+        if (tau != INT_MIN && n_high < p.R) {
+            pick(tau, fsh, n_high, n2, t2);
+        } else if (tau != INT_MIN) {
+            // at least R keys lie above the first fine range (the histogram
+            // that set tau counts some sums in lower bins than their own): a
+            // second fine histogram over [ftop, the best score]
+            for (int o = 1; o < kWave; o <<= 1) {
+                const int32_t v = __shfl_xor(smax, o);
+                smax = v > smax ? v : smax;
+            }
+            int32_t sh2 = 0;
+            while (((int64_t)kFineBins << sh2) < (int64_t)smax - ftop + 1) ++sh2;
+            for (int j = lane; j < kFineBins; j += kWave) fine[j] = 0;
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            for_keys([&](const uint64_t k) {
+                const int32_t sc = key_int_score(k);
+                if (k != 0 && (int64_t)sc >= ftop) atomicAdd(&fine[((int64_t)sc - ftop) >> sh2], 1u);
+            });
+            pick(ftop, sh2, 0, n2, t2);
+        }
+        if (n2 < 0 || n2 > kWaveKeys) {
+            if (lane == 0) st.dfr[atomicAdd(&st.ctrl[3], 1u)] = (int32_t)q;
+            return;
+        }
+        // stage again: the n2 keys at or above t2
+        n = 0;
+        for_keys([&](const uint64_t k) {
+            const bool keep = k != 0 && key_int_score(k) >= t2;
+            const uint64_t mk = __ballot(keep);
+            const int pos = n + __popcll(mk & lanemask_lt());
+            if (keep && pos < kWaveKeys) stage[pos] = k;
+            n += __popcll(mk);
+        });
     }
     const int P = next_pow2(n > 0 ? n : 1);
     for (int j = n + lane; j < P; j += kWave) stage[j] = 0;
@@ -1700,7 +1887,7 @@ __global__ __launch_bounds__(kSelThreads) void fallback_kernel(Problem p, ScanSt
         const uint32_t it = item;
         if (it >= ld_coherent(&st.ctrl[1])) break;
         const int64_t q = st.ovf[it];
-        stage_table_cm(lut_s, p.lut + q * p.B * 16, p.B, tid, kSelThreads);
+        stage_table_cm(lut_s, p.lut + q * p.B * 16, p.B, p.B, tid, kSelThreads);
         __syncthreads();
         int64_t m = 0;
         const int nsrc = p.leaves ? p.nl : 1;
@@ -1719,7 +1906,7 @@ __global__ __launch_bounds__(kSelThreads) void fallback_kernel(Problem p, ScanSt
             const int32_t off = p.leaves ? leaf_bias_at(p, q, j) : 0;
             for (int64_t t = tid; t < b - a; t += kSelThreads) {
                 const int64_t row = a + t;
-                scratch[m + t] = int_key(row_sum(lut_s, p.B, code_row(p, row), al4, seg_step(p)) + off,
+                scratch[m + t] = int_key(row_sum(lut_s, p.B, tstride(p.B), code_row(p, row), al4, seg_step(p)) + off,
                                          p.ids ? p.ids[row] : (int32_t)row);
             }
             m += b - a;
@@ -1853,11 +2040,25 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
         hipLaunchKernelGGL(zero_u32_kernel, dim3(64), dim3(256), 0, stream, lcur, (int64_t)sp.L);
         const int64_t pairs = sp.nq * sp.nl;
         const unsigned gb = (unsigned)((pairs + 255) / 256 < 4096 ? (pairs + 255) / 256 : 4096);
-        hipLaunchKernelGGL(leaf_count_kernel, dim3(gb), dim3(256), 0, stream, sp.leaves, pairs, sp.L, lcnt);
+        const bool lds = sp.L <= kLeafLds;
+        const unsigned gc = (unsigned)((pairs + kLeafChunk - 1) / kLeafChunk);
+        const size_t lbytes = (size_t)sp.L * 4;
+        if (lds) {
+            allow_lds(leaf_count_lds_kernel, lbytes);
+            allow_lds(leaf_scatter_lds_kernel, lbytes);
+            hipLaunchKernelGGL(leaf_count_lds_kernel, dim3(gc), dim3(kLeafThreads), lbytes, stream, sp.leaves, pairs,
+                               sp.L, lcnt);
+        } else {
+            hipLaunchKernelGGL(leaf_count_kernel, dim3(gb), dim3(256), 0, stream, sp.leaves, pairs, sp.L, lcnt);
+        }
         hipLaunchKernelGGL(leaf_scan_kernel, dim3(1), dim3(1024), 0, stream, lcnt, sp.leaf_offsets, sp.L, ma.qg,
                            ma.item_pts, lqoff, itemoff);
-        hipLaunchKernelGGL(leaf_scatter_kernel, dim3(gb), dim3(256), 0, stream, sp.leaves, sp.nq, sp.nl, sp.L, lqoff, lcur,
-                           qlist, p.leaf_bias, p.bias_bound, qbias);
+        if (lds)
+            hipLaunchKernelGGL(leaf_scatter_lds_kernel, dim3(gc), dim3(kLeafThreads), lbytes, stream, sp.leaves, sp.nq,
+                               sp.nl, sp.L, lqoff, lcur, qlist, p.leaf_bias, p.bias_bound, qbias);
+        else
+            hipLaunchKernelGGL(leaf_scatter_kernel, dim3(gb), dim3(256), 0, stream, sp.leaves, sp.nq, sp.nl, sp.L, lqoff,
+                               lcur, qlist, p.leaf_bias, p.bias_bound, qbias);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         ma.lqoff = lqoff;
         ma.qlist = qlist;
@@ -1871,7 +2072,8 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     if (streaming) W = 8192;  // a few queries: a tighter first bound is cheap and every workgroup starts from it
     if (W > 8192) W = 8192;
     const size_t lut_bytes = ((size_t)tstride(sp.B) * 16 + 15) & ~(size_t)15;
-    if ((size_t)tstride(sp.B) * 16 <= (size_t)kWaveLut) {
+    // (the one-wave warm-up pads its table to whole 32-block code segments)
+    if ((size_t)tstride(32 * (((sp.B + 1) / 2 + 15) / 16)) * 16 <= (size_t)kWaveLut) {
         hipLaunchKernelGGL(warmup_wave_kernel, dim3((unsigned)((sp.nq + 3) / 4)), dim3(kSelThreads), 0, stream, p, st, W);
     } else {
         allow_lds(warmup_kernel, lut_bytes + (size_t)W * 8);
