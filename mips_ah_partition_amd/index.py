@@ -326,8 +326,14 @@ def build_gpu(X, dpb: int, eta: float, num_leaves: int = 0, seed=0, sample_rows:
     cb, _ = train_codebooks_gpu(Xs, dpb, eta, iters, init_rows=rng.choice(m, 16, replace=False))
     del Xs
     t0 = mark("codebook_training", t0)
-    codes = ahlib.ah_encode(X if X.dtype in (torch.float32, torch.bfloat16) else X.to(torch.float32), cb, eta,
-                            sweeps=sweeps)
+    # rows padded with zero bytes to a multiple of 16 (the scan's aligned,
+    # one-load-per-segment code paths need it; 25-byte rows otherwise take
+    # byte-wise loads everywhere)
+    B = cb.shape[0]
+    stride = ((B + 1) // 2 + 15) // 16 * 16
+    codes = torch.zeros((n, stride), dtype=torch.uint8, device=dev)
+    ahlib.ah_encode(X if X.dtype in (torch.float32, torch.bfloat16) else X.to(torch.float32), cb, eta,
+                    sweeps=sweeps, codes_out=codes)
     t0 = mark("encode", t0)
     if num_leaves > 0:
         order = torch.sort(leaf, stable=True).indices
