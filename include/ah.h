@@ -398,7 +398,8 @@ int ah_scan_topk_residual(const int8_t* lut_i8, int64_t nq, int32_t B, const uin
  *   cand_ids  int32 [nq][R]  candidate ids, -1 = empty slot (skipped)
  *   ids_out   int32 [nq][k]  best k by exact score, best first
  *   scores_out float32 [nq][k] exact q.x (bf16 rows widened exactly to fp32,
- *             fp32 accumulation); empty slots (-1, -inf)
+ *             products and sum in fp64, rounded once to fp32); ranking by
+ *             (that fp32 score desc, id asc); empty slots (-1, -inf)
  * Errors: AH_ERR_NULL, AH_ERR_SHAPE (nq < 0, d < 1, n < 0, R < 1, k < 1,
  * k > R), AH_ERR_UNSUPPORTED (dtype, R > AH_MAX_R, d > AH_MAX_DIM).  Candidate
  * ids must lie in [-1, n).

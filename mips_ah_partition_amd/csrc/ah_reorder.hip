@@ -10,10 +10,16 @@
 // contiguous 400 B .. 3 KB run -- so it is bound by HBM bandwidth.  One
 // workgroup per query keeps the query in LDS; each wave streams candidate rows
 // with 16-byte loads, G lanes per row (G = rows' 16-byte chunks rounded up to a
-// power of two, at most 64) so short rows still fill the wave, and two rows per
-// lane group are in flight at once.  bf16 rows are widened exactly (bits << 16)
-// and accumulated in fp32.  The R scores become ranking keys and the
-// workgroup's exact top-k selection orders them.
+// power of two, at most 64) so short rows still fill the wave, and four rows
+// per lane group are in flight at once.  bf16 rows are widened exactly (bits
+// << 16); every product of two fp32 values is exact in fp64 and the dot
+// product is accumulated in fp64 (the gather leaves the ALUs mostly idle),
+// then rounded once to fp32: scores agree with an fp64 reference to the
+// rounding of the result, so near-ties at the k-th place are ordered as in
+// fp64 unless they round to the same fp32 value (then the lower id wins).  A
+// lane meets the same query elements in every row, so when a row takes one
+// pass it holds them in registers, widened once.  The R scores become ranking
+// keys and the workgroup's exact top-k selection orders them.
 #include "ah_device.hpp"
 #include "ah_kernels.hpp"
 
@@ -22,27 +28,27 @@ namespace ah {
 constexpr int kReorderThreads = 256;
 constexpr int kReorderWaves = kReorderThreads / kWave;
 
+// a += chunk x . qq (qq: the chunk's query elements, fp32 or already fp64)
 struct ChunkF32 {
     static constexpr int kElems = 4;
-    __device__ static float dot(const uint4 x, int j, const float* qs) {
-        const float* qq = qs + 4 * j;
-        float a = __uint_as_float(x.x) * qq[0];
-        a = __fmaf_rn(__uint_as_float(x.y), qq[1], a);
-        a = __fmaf_rn(__uint_as_float(x.z), qq[2], a);
-        a = __fmaf_rn(__uint_as_float(x.w), qq[3], a);
+    template <typename QT>
+    __device__ static double dot(const uint4 x, const QT* qq, double a) {
+        a = __fma_rn((double)__uint_as_float(x.x), (double)qq[0], a);
+        a = __fma_rn((double)__uint_as_float(x.y), (double)qq[1], a);
+        a = __fma_rn((double)__uint_as_float(x.z), (double)qq[2], a);
+        a = __fma_rn((double)__uint_as_float(x.w), (double)qq[3], a);
         return a;
     }
 };
 struct ChunkBF16 {
     static constexpr int kElems = 8;
-    __device__ static float dot(const uint4 x, int j, const float* qs) {
-        const float* qq = qs + 8 * j;
+    template <typename QT>
+    __device__ static double dot(const uint4 x, const QT* qq, double a) {
         const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-        float a = 0.0f;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            a = __fmaf_rn(__uint_as_float(w[t] << 16), qq[2 * t], a);
-            a = __fmaf_rn(__uint_as_float(w[t] & 0xFFFF0000u), qq[2 * t + 1], a);
+            a = __fma_rn((double)__uint_as_float(w[t] << 16), (double)qq[2 * t], a);
+            a = __fma_rn((double)__uint_as_float(w[t] & 0xFFFF0000u), (double)qq[2 * t + 1], a);
         }
         return a;
     }
@@ -54,8 +60,10 @@ __device__ __forceinline__ float load_elem(const void* base, int32_t dtype, int6
 }
 
 // G lanes per row, kNR rows per lane group in flight, each lane's (at most kCPL)
-// 16-byte chunks of all kNR rows loaded before any is used.
-template <typename Chunk, int kCPL>
+// 16-byte chunks of all kNR rows loaded before any is used.  kOnePass: a row
+// takes one pass (at most kCPL x G chunks), so the lane's query elements stay
+// in registers as fp64.
+template <typename Chunk, int kCPL, bool kOnePass>
 __device__ void score_rows_vec(const float* qs, int32_t d, const void* base, int64_t n, const int32_t* cand,
                                int32_t R, uint64_t* keys) {
     constexpr int kNR = 4;
@@ -67,6 +75,15 @@ __device__ void score_rows_vec(const float* qs, int32_t d, const void* base, int
     const int per = kWave / G;  // rows per wave pass
     const int sub = lane / G, gl = lane % G;
     const size_t row_bytes = (size_t)d * (Chunk::kElems == 4 ? 4 : 2);
+    double qv[kOnePass ? kCPL : 1][Chunk::kElems];
+    if (kOnePass) {
+#pragma unroll
+        for (int t = 0; t < kCPL; ++t) {
+            const int j = gl + t * G;
+#pragma unroll
+            for (int e = 0; e < Chunk::kElems; ++e) qv[t][e] = j < C ? (double)qs[Chunk::kElems * j + e] : 0.0;
+        }
+    }
     for (int r0 = w * per * kNR; r0 < R; r0 += kReorderWaves * per * kNR) {
         int id[kNR];
         const char* row[kNR];
@@ -77,7 +94,7 @@ __device__ void score_rows_vec(const float* qs, int32_t d, const void* base, int
             id[v] = x >= n ? -1 : x;
             row[v] = reinterpret_cast<const char*>(base) + (size_t)(id[v] < 0 ? 0 : id[v]) * row_bytes;
         }
-        float sc[kNR] = {};
+        double sc[kNR] = {};
         for (int jb = gl; jb < C; jb += kCPL * G) {  // one pass unless the row exceeds kCPL x 64 chunks
             uint4 raw[kNR][kCPL];
 #pragma unroll
@@ -92,22 +109,46 @@ __device__ void score_rows_vec(const float* qs, int32_t d, const void* base, int
 #pragma unroll
                 for (int t = 0; t < kCPL; ++t) {
                     const int j = jb + t * G;
-                    if (j < C) sc[v] += Chunk::dot(raw[v][t], j, qs);
+                    if (j < C) {
+                        if (kOnePass) sc[v] = Chunk::dot(raw[v][t], qv[t], sc[v]);
+                        else sc[v] = Chunk::dot(raw[v][t], qs + Chunk::kElems * j, sc[v]);
+                    }
                 }
         }
-#pragma unroll
-        for (int v = 0; v < kNR; ++v) {
-            float a = sc[v];
-#pragma unroll
-            for (int o = kWave / 2; o > 0; o >>= 1)
-                if (o < G) a += __shfl_xor(a, o, kWave);
-            sc[v] = a;
-        }
-        if (gl == 0) {
+        static_assert(kNR == 4, "the reduce-scatter below splits four rows");
+        if (G >= 4) {
+            // reduce-scatter over the G lanes: the two top exchange steps each
+            // halve the rows a lane carries (four rows, then two, then one), so
+            // a pass costs log2(G) + 1 exchanges of a double instead of 4 log2(G)
+            const int h = G >> 1, qb = G >> 2;
+            const bool b1 = (gl & h) != 0, b0 = (gl & qb) != 0;
+            double k0 = b1 ? sc[2] : sc[0], k1 = b1 ? sc[3] : sc[1];
+            const double s0 = b1 ? sc[0] : sc[2], s1 = b1 ? sc[1] : sc[3];
+            k0 += __shfl_xor(s0, h, kWave);
+            k1 += __shfl_xor(s1, h, kWave);
+            double a = b0 ? k1 : k0;
+            a += __shfl_xor(b0 ? k0 : k1, qb, kWave);
+            for (int o = qb >> 1; o > 0; o >>= 1) a += __shfl_xor(a, o, kWave);
+            // every lane of the group now holds the sum of row 2 b1 + b0
+            if ((gl & (qb - 1)) == 0) {
+                const int v = 2 * (int)b1 + (int)b0;
+                const int r = r0 + v * per + sub;
+                const int idv = v == 0 ? id[0] : (v == 1 ? id[1] : (v == 2 ? id[2] : id[3]));
+                if (r < R) keys[r] = idv >= 0 ? float_key(__double2float_rn(a), idv) : 0ull;
+            }
+        } else {
 #pragma unroll
             for (int v = 0; v < kNR; ++v) {
-                const int r = r0 + v * per + sub;
-                if (r < R) keys[r] = id[v] >= 0 ? float_key(sc[v], id[v]) : 0ull;
+                double a = sc[v];
+                for (int o = G >> 1; o > 0; o >>= 1) a += __shfl_xor(a, o, kWave);
+                sc[v] = a;
+            }
+            if (gl == 0) {
+#pragma unroll
+                for (int v = 0; v < kNR; ++v) {
+                    const int r = r0 + v * per + sub;
+                    if (r < R) keys[r] = id[v] >= 0 ? float_key(__double2float_rn(sc[v]), id[v]) : 0ull;
+                }
             }
         }
     }
@@ -119,17 +160,20 @@ __device__ void score_rows_scalar(const float* qs, int32_t d, const void* base, 
     const int w = threadIdx.x / kWave;
     for (int r = w; r < R; r += kReorderWaves) {
         const int id = cand[r] < n ? cand[r] : -1;
-        float s = 0.0f;
+        double s = 0.0;
         if (id >= 0)
-            for (int j = lane; j < d; j += kWave) s = __fmaf_rn(qs[j], load_elem(base, dtype, (int64_t)id * d + j), s);
-        s = wave_sum(s);
-        if (lane == 0) keys[r] = id >= 0 ? float_key(s, id) : 0ull;
+            for (int j = lane; j < d; j += kWave)
+                s = __fma_rn((double)qs[j], (double)load_elem(base, dtype, (int64_t)id * d + j), s);
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
+        if (lane == 0) keys[r] = id >= 0 ? float_key(__double2float_rn(s), id) : 0ull;
     }
 }
 
 // LDS: [R keys][next_pow2(k) selected][d query floats].  kPath: 0 = element-wise
-// (rows not in whole 16-byte chunks), else the chunk path with kCPL chunks per lane.
-template <int kPath, int kCPL>
+// (rows not in whole 16-byte chunks), else the chunk path with kCPL chunks per lane
+// (kOnePass: every row in one pass).
+template <int kPath, int kCPL, bool kOnePass>
 __global__ __launch_bounds__(kReorderThreads) void reorder_kernel(
     const float* __restrict__ q, int32_t d, const void* __restrict__ base, int32_t dtype,
     int64_t n, const int32_t* __restrict__ cand, int32_t R, int32_t k, int32_t* __restrict__ ids_out,
@@ -147,9 +191,9 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_kernel(
     if constexpr (kPath == 0) {
         score_rows_scalar(qs, d, base, dtype, n, c, R, keys);
     } else if (kPath == 1) {
-        score_rows_vec<ChunkF32, kCPL>(qs, d, base, n, c, R, keys);
+        score_rows_vec<ChunkF32, kCPL, kOnePass>(qs, d, base, n, c, R, keys);
     } else {
-        score_rows_vec<ChunkBF16, kCPL>(qs, d, base, n, c, R, keys);
+        score_rows_vec<ChunkBF16, kCPL, kOnePass>(qs, d, base, n, c, R, keys);
     }
     __syncthreads();
     const int m = wg_select_topk<kReorderThreads>(LdsKeys{keys}, R, k, sh, sel);
@@ -159,14 +203,14 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_kernel(
     }
 }
 
-template <int kPath, int kCPL>
+template <int kPath, int kCPL, bool kOnePass = true>
 static hipError_t launch_reorder1(size_t lds, const float* q, int64_t nq, int32_t d, const void* base, int32_t dtype,
                                   int64_t n, const int32_t* cand, int32_t R, int32_t k, int32_t* ids, float* scores,
                                   hipStream_t stream) {
     if (lds > 48 * 1024)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(reorder_kernel<kPath, kCPL>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(reorder_kernel<kPath, kCPL, kOnePass>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL((reorder_kernel<kPath, kCPL>), dim3((unsigned)nq), dim3(kReorderThreads), lds, stream, q, d,
+    hipLaunchKernelGGL((reorder_kernel<kPath, kCPL, kOnePass>), dim3((unsigned)nq), dim3(kReorderThreads), lds, stream, q, d,
                        base, dtype, n, cand, R, k, ids, scores);
     return hipGetLastError();
 }
@@ -188,7 +232,8 @@ hipError_t launch_reorder(const float* q, int64_t nq, int32_t d, const void* bas
     do {                                                                                                     \
         if (cpl <= 1) return launch_reorder1<P, 1>(lds, q, nq, d, base, dtype, n, cand, R, k, ids, scores, stream); \
         if (cpl <= 2) return launch_reorder1<P, 2>(lds, q, nq, d, base, dtype, n, cand, R, k, ids, scores, stream); \
-        return launch_reorder1<P, 4>(lds, q, nq, d, base, dtype, n, cand, R, k, ids, scores, stream);              \
+        if (cpl <= 4) return launch_reorder1<P, 4>(lds, q, nq, d, base, dtype, n, cand, R, k, ids, scores, stream); \
+        return launch_reorder1<P, 4, false>(lds, q, nq, d, base, dtype, n, cand, R, k, ids, scores, stream);       \
     } while (0)
     if (dtype == 0) AH_RO(1);
     AH_RO(2);

@@ -415,10 +415,12 @@ def _check_ranked(g_ids, g_sc, o_ids, o_sc, ref_fn, denom_fn):
 
 
 # Row lengths cover one, two and four 16-byte chunks per lane, rows longer than
-# 4 x 64 chunks (several passes), and rows not in whole chunks (element path).
+# 4 x 64 chunks (several passes; 12,288 dims: a dozen), and rows not in whole
+# chunks (element path).
 @pytest.mark.parametrize("dtype,d,R,k", [("f32", 128, 200, 10), ("f32", 100, 37, 37), ("bf16", 384, 300, 10),
                                          ("bf16", 1536, 64, 10), ("f32", 7, 10, 3), ("f32", 512, 50, 5),
-                                         ("bf16", 4096, 40, 8), ("f32", 2048, 30, 30), ("f32", 32, 4096, 4096)])
+                                         ("bf16", 4096, 40, 8), ("f32", 2048, 30, 30), ("f32", 32, 4096, 4096),
+                                         ("f32", 12288, 64, 10), ("bf16", 12288, 32, 8), ("f32", 12289, 16, 4)])
 def test_reorder_parity(gpu, dtype, d, R, k):
     torch, ah = gpu
     rng = np.random.default_rng(d + R)
