@@ -64,9 +64,13 @@ constexpr int kItemPts = 16384;                   // rows per item (row offsets 
 constexpr int kFbSlots = 4;                       // fallback workgroups
 constexpr int kSelThreads = 256;
 constexpr int kSelLds = 4096;                     // keys staged in LDS by the final select
+constexpr int kStreamMaxQ = 4;                    // batches scanned by the streaming kernel (VALU lookups)
+constexpr int kSpreadWG = 128;                    // spread warm-up: workgroups (partial histograms) per query
+constexpr int kSpreadThreads = 512;
+constexpr int32_t kSpreadRows = 131072;           // spread warm-up: rows per query
 
 struct ScanLayout {
-    size_t tau, cnt, hmax, hist, cand, ctrl, ovf, dfr, fb, lcnt, lqoff, lcur, qlist, qbias, itemoff, total;
+    size_t tau, cnt, hmax, hist, cand, ctrl, ovf, dfr, fb, lcnt, lqoff, lcur, qlist, qbias, itemoff, wpart, total;
     int64_t cap;
 };
 
@@ -99,6 +103,8 @@ static ScanLayout scan_layout(int64_t nq, int32_t B, int64_t n, int32_t L, int32
     s.qlist = o;   o = align_up(o + (part ? (size_t)nq * nl * 4 : 0));
     s.qbias = o;   o = align_up(o + (part ? (size_t)nq * nl * 4 : 0));
     s.itemoff = o; o = align_up(o + (part ? (size_t)(L + 1) * 8 : 0));
+    // partial histograms of the spread warm-up (full scans by a few queries)
+    s.wpart = o;   o = align_up(o + (!part && nq <= kStreamMaxQ ? (size_t)nq * kSpreadWG * kNB * 4 : 0));
     s.total = o;
     return s;
 }
@@ -426,6 +432,83 @@ __global__ __launch_bounds__(kSelThreads) void warmup_kernel(Problem p, ScanStat
     const uint64_t kth = wg_kth_largest<kSelThreads>(LdsKeys{keys}, W, p.R, sh, &nvalid);
     if (tid == 0) st.tau[q] = nvalid >= p.R ? key_int_score(kth) : INT_MIN;
     if (q == 0 && tid < 16) st.ctrl[tid] = 0;
+}
+
+// Warm-up of a full scan by a few queries, whose thresholds every workgroup of
+// the scan starts from: W rows evenly spaced over the whole array (distinct, as
+// W <= n), summed by kSpreadWG workgroups per query, each writing a histogram
+// of its share's sums; warmup_spread_finish_kernel adds the shares up.  Many
+// more rows than the one-workgroup warm-up reads, in less time.
+__global__ __launch_bounds__(kSpreadThreads) void warmup_spread_kernel(Problem p, ScanState st, int32_t W,
+                                                                       uint32_t* part) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ uint32_t h_s[kNB];
+    const int64_t q = blockIdx.y;
+    const int tid = threadIdx.x;
+    int8_t* lut_s = reinterpret_cast<int8_t*>(smem);
+    stage_table_cm(lut_s, p.lut + q * p.B * 16, p.B, p.B, tid, kSpreadThreads);
+    for (int j = tid; j < kNB; j += kSpreadThreads) h_s[j] = 0;
+    __syncthreads();
+    const bool al4 = (p.stride & 3) == 0 && (reinterpret_cast<uintptr_t>(p.codes) & 3) == 0;
+    const int32_t S = tstride(p.B), ss = seg_step(p);
+    for (int64_t i = (int64_t)blockIdx.x * kSpreadThreads + tid; i < W; i += (int64_t)kSpreadWG * kSpreadThreads) {
+        const int64_t row = i * p.n / W;
+        atomicAdd(&h_s[hist_bin(row_sum(lut_s, p.B, S, code_row(p, row), al4, ss), st.hlo, st.hsh)], 1u);
+    }
+    __syncthreads();
+    uint32_t* dst = part + (q * kSpreadWG + blockIdx.x) * kNB;
+    for (int j = tid; j < kNB; j += kSpreadThreads) dst[j] = h_s[j];
+}
+
+// One workgroup per query: adds up the spread warm-up's partial histograms,
+// sets tau to the lower edge of the bin holding the R-th best of the W sums (a
+// valid bound, at most one bin below the exact R-th best) and clears the
+// query's candidate count and histogram.
+__global__ __launch_bounds__(kNB) void warmup_spread_finish_kernel(Problem p, ScanState st, int32_t W,
+                                                                   const uint32_t* part) {
+    __shared__ uint32_t h_s[kNB];
+    const int64_t q = blockIdx.x;
+    const int j = threadIdx.x;  // one bin per thread
+    if (q == 0 && j < 16) st.ctrl[j] = 0;
+    const uint32_t* src = part + q * kSpreadWG * kNB + j;
+    uint32_t c = 0;
+#pragma unroll 16
+    for (int g = 0; g < kSpreadWG; ++g) c += src[(int64_t)g * kNB];
+    h_s[j] = c;
+    st.hist[q * kNB + j] = 0;
+    if (j == 0) {
+        st.cnt[q] = 0;
+        st.hmax[q] = 0;
+    }
+    __syncthreads();
+    if (j >= kWave) return;
+    const int lane = j;
+    if (W < p.R) {
+        if (lane == 0) st.tau[q] = INT_MIN;
+        return;
+    }
+    // lane l owns the 16 bins from the top 16 l down
+    int cb[16], tot = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        cb[k] = (int)h_s[kNB - 1 - 16 * lane - k];
+        tot += cb[k];
+    }
+    const int incl = wave_inclusive_sum(tot);
+    const uint64_t mk = __ballot(incl >= p.R);
+    const int l = __ffsll((unsigned long long)mk) - 1;  // W >= R sums, so some lane reaches R
+    if (lane == l) {
+        int cum = incl - tot, bin = kNB - 1 - 16 * lane;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            cum += cb[k];
+            if (cum >= p.R) {
+                bin = kNB - 1 - 16 * lane - k;
+                break;
+            }
+        }
+        st.tau[q] = (int32_t)(st.hlo + ((int64_t)bin << st.hsh));
+    }
 }
 
 // ------------------------------------------------------------------ main scan
@@ -1249,7 +1332,6 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
 // and flushes are those of the main kernel, with G queries per item; every
 // flush also merges into the global histograms and refreshes the global
 // thresholds, because every workgroup scans rows of the same few queries.
-constexpr int kStreamMaxQ = 4;
 constexpr size_t kStreamMaxTable = 120 * 1024;  // LDS bytes for the table
 constexpr int kStreamWaves = 12;               // one workgroup (and one table copy) per CU, 3 waves per SIMD
 constexpr int kStreamThreads = kStreamWaves * kWave;
@@ -2069,11 +2151,19 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     // thresholds tighten it within the first items
     int32_t W = 2 * sp.R;
     if (W < 1024) W = 1024;
-    if (streaming) W = 8192;  // a few queries: a tighter first bound is cheap and every workgroup starts from it
+    if (streaming) W = 8192;  // a few queries (partitioned): a tighter first bound is cheap and every workgroup starts from it
     if (W > 8192) W = 8192;
     const size_t lut_bytes = ((size_t)tstride(sp.B) * 16 + 15) & ~(size_t)15;
-    // (the one-wave warm-up pads its table to whole 32-block code segments)
-    if ((size_t)tstride(32 * (((sp.B + 1) / 2 + 15) / 16)) * 16 <= (size_t)kWaveLut) {
+    if (streaming && !part && sp.n > 0 && lut_bytes <= 64 * 1024) {
+        const int32_t Ws = sp.n < kSpreadRows ? (int32_t)sp.n : kSpreadRows;
+        uint32_t* wpart = reinterpret_cast<uint32_t*>(base + lay.wpart);
+        allow_lds(warmup_spread_kernel, lut_bytes);
+        hipLaunchKernelGGL(warmup_spread_kernel, dim3(kSpreadWG, (unsigned)sp.nq), dim3(kSpreadThreads), lut_bytes,
+                           stream, p, st, Ws, wpart);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(warmup_spread_finish_kernel, dim3((unsigned)sp.nq), dim3(kNB), 0, stream, p, st, Ws, wpart);
+    } else if ((size_t)tstride(32 * (((sp.B + 1) / 2 + 15) / 16)) * 16 <= (size_t)kWaveLut) {
+        // (the one-wave warm-up pads its table to whole 32-block code segments)
         hipLaunchKernelGGL(warmup_wave_kernel, dim3((unsigned)((sp.nq + 3) / 4)), dim3(kSelThreads), 0, stream, p, st, W);
     } else {
         allow_lds(warmup_kernel, lut_bytes + (size_t)W * 8);

@@ -259,6 +259,8 @@ def test_scan_partitioned_parity(gpu):
     (1001, 3000, 1, 64, 11),    # odd B in 512 B rows
     (1536, 2000, 1, 50, 0),     # 768 B rows
     (64, 9000, 3, 4096, 0),     # R at its maximum (AH_MAX_R)
+    (192, 300000, 1, 300, 0),   # warm-up sample spread over a longer array (every 2nd or 3rd row)
+    (768, 140000, 2, 400, 0),   # the same, packed pair table
 ])
 def test_scan_stream_parity(gpu, B, n, nq, R, stride_pad):
     torch, ah = gpu
