@@ -65,9 +65,10 @@ constexpr int kFbSlots = 4;                       // fallback workgroups
 constexpr int kSelThreads = 256;
 constexpr int kSelLds = 4096;                     // keys staged in LDS by the final select
 constexpr int kStreamMaxQ = 4;                    // batches scanned by the streaming kernel (VALU lookups)
-constexpr int kSpreadWG = 128;                    // spread warm-up: workgroups (partial histograms) per query
+constexpr int kSpreadWG = 256;                    // spread warm-up: most workgroups (partial histograms) per query
 constexpr int kSpreadThreads = 512;
-constexpr int32_t kSpreadRows = 131072;           // spread warm-up: rows per query
+constexpr int32_t kSpreadRows = 131072;           // spread warm-up: most rows per query
+constexpr int64_t kSpreadLookups = 1LL << 25;     // spread warm-up: rows x blocks per query, at most
 
 struct ScanLayout {
     size_t tau, cnt, hmax, hist, cand, ctrl, ovf, dfr, fb, lcnt, lqoff, lcur, qlist, qbias, itemoff, wpart, total;
@@ -436,9 +437,11 @@ __global__ __launch_bounds__(kSelThreads) void warmup_kernel(Problem p, ScanStat
 
 // Warm-up of a full scan by a few queries, whose thresholds every workgroup of
 // the scan starts from: W rows evenly spaced over the whole array (distinct, as
-// W <= n), summed by kSpreadWG workgroups per query, each writing a histogram
-// of its share's sums; warmup_spread_finish_kernel adds the shares up.  Many
-// more rows than the one-workgroup warm-up reads, in less time.
+// W <= n), one per thread of nwg workgroups per query, each workgroup writing a
+// histogram of its rows' sums; warmup_spread_finish_kernel adds them up.  Many
+// more rows than the one-workgroup warm-up reads, in less time.  Rows of whole
+// 16-byte segments load all their segments (up to 8) before any lookup, on a
+// table padded with zero blocks to whole segments.
 __global__ __launch_bounds__(kSpreadThreads) void warmup_spread_kernel(Problem p, ScanState st, int32_t W,
                                                                        uint32_t* part) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -446,17 +449,41 @@ __global__ __launch_bounds__(kSpreadThreads) void warmup_spread_kernel(Problem p
     const int64_t q = blockIdx.y;
     const int tid = threadIdx.x;
     int8_t* lut_s = reinterpret_cast<int8_t*>(smem);
-    stage_table_cm(lut_s, p.lut + q * p.B * 16, p.B, p.B, tid, kSpreadThreads);
+    const bool al4 = (p.stride & 3) == 0 && (reinterpret_cast<uintptr_t>(p.codes) & 3) == 0;
+    const bool al16 = (p.stride & 15) == 0 && (reinterpret_cast<uintptr_t>(p.codes) & 15) == 0;
+    const int nseg = ((p.B + 1) / 2 + 15) / 16;
+    const int32_t Bp = al16 ? 32 * nseg : p.B;
+    stage_table_cm(lut_s, p.lut + q * p.B * 16, p.B, Bp, tid, kSpreadThreads);
     for (int j = tid; j < kNB; j += kSpreadThreads) h_s[j] = 0;
     __syncthreads();
-    const bool al4 = (p.stride & 3) == 0 && (reinterpret_cast<uintptr_t>(p.codes) & 3) == 0;
-    const int32_t S = tstride(p.B), ss = seg_step(p);
-    for (int64_t i = (int64_t)blockIdx.x * kSpreadThreads + tid; i < W; i += (int64_t)kSpreadWG * kSpreadThreads) {
+    const int32_t S = tstride(Bp), ss = seg_step(p);
+    const int64_t i = (int64_t)blockIdx.x * kSpreadThreads + tid;
+    if (i < W) {
         const int64_t row = i * p.n / W;
-        atomicAdd(&h_s[hist_bin(row_sum(lut_s, p.B, S, code_row(p, row), al4, ss), st.hlo, st.hsh)], 1u);
+        const uint8_t* src = code_row(p, row);
+        int32_t sv = 0;
+        if (al16) {
+            for (int j0 = 0; j0 < nseg; j0 += 8) {
+                uint4 r[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (j0 + k < nseg) r[k] = *reinterpret_cast<const uint4*>(src + (j0 + k) * ss);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    if (j0 + k >= nseg) break;
+                    const uint32_t wd[4] = {r[k].x, r[k].y, r[k].z, r[k].w};
+#pragma unroll
+                    for (int u = 0; u < 32; ++u)
+                        sv += lut_s[(int)((wd[u >> 3] >> (4 * (u & 7))) & 15u) * S + 32 * (j0 + k) + u];
+                }
+            }
+        } else {
+            sv = row_sum(lut_s, p.B, S, src, al4, ss);
+        }
+        atomicAdd(&h_s[hist_bin(sv, st.hlo, st.hsh)], 1u);
     }
     __syncthreads();
-    uint32_t* dst = part + (q * kSpreadWG + blockIdx.x) * kNB;
+    uint32_t* dst = part + (q * gridDim.x + blockIdx.x) * kNB;
     for (int j = tid; j < kNB; j += kSpreadThreads) dst[j] = h_s[j];
 }
 
@@ -464,16 +491,16 @@ __global__ __launch_bounds__(kSpreadThreads) void warmup_spread_kernel(Problem p
 // sets tau to the lower edge of the bin holding the R-th best of the W sums (a
 // valid bound, at most one bin below the exact R-th best) and clears the
 // query's candidate count and histogram.
-__global__ __launch_bounds__(kNB) void warmup_spread_finish_kernel(Problem p, ScanState st, int32_t W,
+__global__ __launch_bounds__(kNB) void warmup_spread_finish_kernel(Problem p, ScanState st, int32_t W, int32_t nwg,
                                                                    const uint32_t* part) {
     __shared__ uint32_t h_s[kNB];
     const int64_t q = blockIdx.x;
     const int j = threadIdx.x;  // one bin per thread
     if (q == 0 && j < 16) st.ctrl[j] = 0;
-    const uint32_t* src = part + q * kSpreadWG * kNB + j;
+    const uint32_t* src = part + q * nwg * kNB + j;
     uint32_t c = 0;
 #pragma unroll 16
-    for (int g = 0; g < kSpreadWG; ++g) c += src[(int64_t)g * kNB];
+    for (int g = 0; g < nwg; ++g) c += src[(int64_t)g * kNB];
     h_s[j] = c;
     st.hist[q * kNB + j] = 0;
     if (j == 0) {
@@ -531,7 +558,7 @@ struct MainArgs {
     int32_t nkstep;   // k-steps of 4 blocks (blocks rounded up to 8)
     int32_t nchunk;   // 1: the table is resident (B <= 64); else staged chunks of 32 blocks
     int32_t qg;       // queries per item
-    int32_t item_pts; // rows per item (at most kItemPts)
+    int32_t item_pts; // rows per item (MFMA kernel: kItemPts; streaming kernel: at most 65536)
     int32_t nqg;      // query groups (full scan)
     int64_t n_items;  // items (full scan); partitioned: itemoff[L]
     const int32_t* lqoff;
@@ -1908,6 +1935,187 @@ __global__ __launch_bounds__(kSelThreads) void final_select_wave_kernel(Problem 
     }
 }
 
+// The same selection by one 16-wave workgroup per query, for batches of a few
+// queries: every workgroup of the scan appends to their lists, which grow long,
+// and reading a long list one wave at a time is a chain of round trips.  Here
+// the list is read by all 16 waves at once (8 keys per thread and round); the
+// staged keys are sorted by the whole workgroup.
+constexpr int kFewThreads = 1024;
+constexpr int kFewMaxQ = 64;  // batches up to this many queries take this kernel
+
+__global__ __launch_bounds__(kFewThreads) void final_select_few_kernel(Problem p, ScanState st) {
+    __shared__ uint64_t stage[kWaveKeys];
+    __shared__ uint32_t fine[kFineBins];
+    __shared__ int32_t tau_s, t2_s, smax_s;
+    __shared__ int n_s, nh_s, n2_s;
+    const int tid = threadIdx.x, lane = lane_id();
+    const int64_t q = blockIdx.x;
+    const uint32_t total = st.cnt[q];
+    if ((int64_t)total > st.cap) {
+        if (tid == 0) st.ovf[atomicAdd(&st.ctrl[1], 1u)] = (int32_t)q;
+        return;
+    }
+    if (tid < kWave) {
+        refresh_tau(st, (int)q, p.R);
+        const int32_t t = ld_coherent(st.tau + q);
+        if (lane == 0) {
+            tau_s = t;
+            n_s = 0;
+            nh_s = 0;
+            smax_s = INT_MIN;
+        }
+    }
+    for (int j = tid; j < kFineBins; j += kFewThreads) fine[j] = 0;
+    __syncthreads();
+    const int32_t tau = tau_s;
+    const uint64_t* list = st.cand + q * st.cap;
+    const int32_t fsh = st.hsh > kFineShift ? st.hsh - kFineShift : 0;
+    const int64_t ftop = (int64_t)tau + ((int64_t)kFineBins << fsh);
+    // rounds of 8 keys per thread, every load of a round issued before any key
+    // is used; the keys of a round that pass `keep` go to consecutive stage
+    // slots (one LDS atomic per wave and round)
+    auto for_keys = [&](auto keep, auto f) {
+        for (uint32_t b0 = 0; b0 < total; b0 += 8 * kFewThreads) {
+            uint64_t kk[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const uint32_t i = b0 + r * kFewThreads + tid;
+                kk[r] = i < total ? list[i] : 0;
+            }
+            uint64_t mk[8];
+            int cnt = 0;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                mk[r] = __ballot(keep(kk[r]));
+                cnt += __popcll(mk[r]);
+            }
+            if (cnt == 0) continue;  // wave-uniform
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&n_s, cnt);
+            base = __shfl(base, 0, kWave);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const bool kp = (mk[r] >> lane) & 1;
+                const int pos = base + __popcll(mk[r] & lanemask_lt());
+                if (kp && pos < kWaveKeys) stage[pos] = kk[r];
+                base += __popcll(mk[r]);
+                if (kp) f(kk[r]);
+            }
+        }
+    };
+    int n_high = 0;
+    int32_t smax = INT_MIN;
+    for_keys([&](uint64_t k) { return k != 0 && key_int_score(k) >= tau; },
+             [&](uint64_t k) {
+                 const int32_t sc = key_int_score(k);
+                 if ((int64_t)sc >= ftop) ++n_high;
+                 else if (tau != INT_MIN) atomicAdd(&fine[((int64_t)sc - tau) >> fsh], 1u);
+                 smax = sc > smax ? sc : smax;
+             });
+    if (n_high) atomicAdd(&nh_s, n_high);
+    if (smax != INT_MIN) atomicMax(&smax_s, smax);
+    __syncthreads();
+    int n = n_s;
+    if (n > kWaveKeys) {
+        // t2: the lower edge of the fine bin holding the R-th best key (n2
+        // keys at or above it), read by wave 0 from the fine histogram of
+        // [lo, lo + kFineBins << sh) with `above` keys above that range
+        auto pick = [&](int64_t lo, int32_t sh, int above) {
+            if (tid >= kWave) return;
+            int n2 = -1;
+            int32_t t2 = tau;
+            int acc = above;
+            for (int top = kFineBins - 1; top >= 0 && n2 < 0; top -= kWave) {
+                const int j = top - lane;
+                const int c = j >= 0 ? (int)fine[j] : 0;
+                const int incl = acc + wave_inclusive_sum(c);
+                const uint64_t mk = __ballot(j >= 0 && incl >= p.R);
+                if (mk) {
+                    const int l = __ffsll((unsigned long long)mk) - 1;
+                    n2 = __shfl(incl, l);
+                    t2 = (int32_t)(lo + ((int64_t)(top - l) << sh));
+                }
+                acc = __shfl(incl, kWave - 1);
+            }
+            if (lane == 0) {
+                n2_s = n2;
+                t2_s = t2;
+            }
+        };
+        const int nh = nh_s;
+        if (tid == 0) n2_s = -1;
+        __syncthreads();
+        if (tau != INT_MIN && nh < p.R) {
+            pick(tau, fsh, nh);
+        } else if (tau != INT_MIN) {
+            // at least R keys lie above the first fine range: a second fine
+            // histogram over [ftop, the best score]
+            const int32_t sm = smax_s;
+            int32_t sh2 = 0;
+            while (((int64_t)kFineBins << sh2) < (int64_t)sm - ftop + 1) ++sh2;
+            for (int j = tid; j < kFineBins; j += kFewThreads) fine[j] = 0;
+            __syncthreads();
+            for (uint32_t b0 = 0; b0 < total; b0 += 8 * kFewThreads) {
+                uint64_t kk[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const uint32_t i = b0 + r * kFewThreads + tid;
+                    kk[r] = i < total ? list[i] : 0;
+                }
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int32_t sc = key_int_score(kk[r]);
+                    if (kk[r] != 0 && (int64_t)sc >= ftop) atomicAdd(&fine[((int64_t)sc - ftop) >> sh2], 1u);
+                }
+            }
+            __syncthreads();
+            pick(ftop, sh2, 0);
+        }
+        __syncthreads();
+        const int n2 = n2_s;
+        const int32_t t2 = t2_s;
+        if (n2 < 0 || n2 > kWaveKeys) {
+            if (tid == 0) st.dfr[atomicAdd(&st.ctrl[3], 1u)] = (int32_t)q;
+            return;
+        }
+        // stage again: the n2 keys at or above t2
+        if (tid == 0) n_s = 0;
+        __syncthreads();
+        for_keys([&](uint64_t k) { return k != 0 && key_int_score(k) >= t2; }, [](uint64_t) {});
+        __syncthreads();
+        n = n_s;
+        if (n > kWaveKeys) {  // (the count n2 says it cannot happen)
+            if (tid == 0) st.dfr[atomicAdd(&st.ctrl[3], 1u)] = (int32_t)q;
+            return;
+        }
+    }
+    const int P = next_pow2(n > 0 ? n : 1);
+    for (int j = n + tid; j < P; j += kFewThreads) stage[j] = 0;
+    __syncthreads();
+    // bitonic sort, descending, one compare-exchange per thread and step
+    for (int size = 2; size <= P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = tid; i < (P >> 1); i += kFewThreads) {
+                const int lo = 2 * i - (i & (stride - 1));
+                const int hi = lo + stride;
+                const bool desc = (lo & size) == 0;
+                const uint64_t x = stage[lo], y = stage[hi];
+                if ((x < y) == desc) {
+                    stage[lo] = y;
+                    stage[hi] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    const int m = n < p.R ? n : p.R;
+    for (int r = tid; r < p.R; r += kFewThreads) {
+        const uint64_t k = r < m ? stage[r] : 0;
+        p.out_ids[q * p.R + r] = r < m ? key_id(k) : -1;
+        p.out_scores[q * p.R + r] = r < m ? key_int_score(k) : INT_MIN;
+    }
+}
+
 // ------------------------------------------------------------------ final selection
 // The workgroup selection, for the queries the one-wave kernel deferred
 // (workgroup i takes the i-th of them; the list has ctrl[3] entries).
@@ -2101,11 +2309,21 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     const bool streaming = sg != 0;
     ma.qg = streaming ? sg : kQG;
     ma.nqg = (int32_t)((sp.nq + ma.qg - 1) / ma.qg);
-    // the MFMA kernel's items are kItemPts rows; the streaming kernel's are cut
-    // so that every CU gets at least two of them
+    // the MFMA kernel's items are kItemPts rows.  A full streaming scan is cut
+    // into about three items per CU (fewer item ends, at which a workgroup's
+    // loads stop while its waves flush; still some balancing); a partitioned
+    // one into items small enough that every CU gets at least two.
     ma.item_pts = kItemPts;
-    if (streaming) {
-        const int64_t rows = part ? (sp.n * sp.nl + sp.L - 1) / (sp.L > 0 ? sp.L : 1) : sp.n;  // rows per query group, roughly
+    if (streaming && !part) {
+        const int64_t want = 3LL * device_cus();
+        const int64_t chunks = (want + ma.nqg - 1) / ma.nqg;
+        int64_t pts = (sp.n + chunks - 1) / chunks;
+        pts = (pts + 63) & ~(int64_t)63;  // whole 64-row tiles
+        if (pts < 1024) pts = 1024;
+        if (pts > 65536) pts = 65536;     // row offsets within an item fit the log's 16 bits
+        ma.item_pts = (int32_t)pts;
+    } else if (streaming) {
+        const int64_t rows = (sp.n * sp.nl + sp.L - 1) / (sp.L > 0 ? sp.L : 1);  // rows per query group, roughly
         while (ma.item_pts > 1024 && (int64_t)ma.nqg * ((rows + ma.item_pts - 1) / ma.item_pts) < 2LL * device_cus())
             ma.item_pts >>= 1;
     }
@@ -2154,14 +2372,20 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     if (streaming) W = 8192;  // a few queries (partitioned): a tighter first bound is cheap and every workgroup starts from it
     if (W > 8192) W = 8192;
     const size_t lut_bytes = ((size_t)tstride(sp.B) * 16 + 15) & ~(size_t)15;
-    if (streaming && !part && sp.n > 0 && lut_bytes <= 64 * 1024) {
-        const int32_t Ws = sp.n < kSpreadRows ? (int32_t)sp.n : kSpreadRows;
+    // (the spread warm-up may pad its table to whole 32-block code segments)
+    const size_t spread_lut = (size_t)tstride(32 * (((sp.B + 1) / 2 + 15) / 16)) * 16;
+    if (streaming && !part && sp.n > 0 && spread_lut <= 64 * 1024) {
+        int64_t Ws = sp.n < kSpreadRows ? sp.n : kSpreadRows;
+        const int64_t cap = kSpreadLookups / sp.B, floor_rows = sp.n < 8192 ? sp.n : 8192;
+        if (Ws > cap) Ws = cap > floor_rows ? cap : floor_rows;
+        const int nwg = (int)((Ws + kSpreadThreads - 1) / kSpreadThreads);  // at most kSpreadWG
         uint32_t* wpart = reinterpret_cast<uint32_t*>(base + lay.wpart);
-        allow_lds(warmup_spread_kernel, lut_bytes);
-        hipLaunchKernelGGL(warmup_spread_kernel, dim3(kSpreadWG, (unsigned)sp.nq), dim3(kSpreadThreads), lut_bytes,
-                           stream, p, st, Ws, wpart);
+        allow_lds(warmup_spread_kernel, spread_lut);
+        hipLaunchKernelGGL(warmup_spread_kernel, dim3((unsigned)nwg, (unsigned)sp.nq), dim3(kSpreadThreads), spread_lut,
+                           stream, p, st, (int32_t)Ws, wpart);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(warmup_spread_finish_kernel, dim3((unsigned)sp.nq), dim3(kNB), 0, stream, p, st, Ws, wpart);
+        hipLaunchKernelGGL(warmup_spread_finish_kernel, dim3((unsigned)sp.nq), dim3(kNB), 0, stream, p, st,
+                           (int32_t)Ws, nwg, wpart);
     } else if ((size_t)tstride(32 * (((sp.B + 1) / 2 + 15) / 16)) * 16 <= (size_t)kWaveLut) {
         // (the one-wave warm-up pads its table to whole 32-block code segments)
         hipLaunchKernelGGL(warmup_wave_kernel, dim3((unsigned)((sp.nq + 3) / 4)), dim3(kSelThreads), 0, stream, p, st, W);
@@ -2201,7 +2425,10 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     if (main_stop && (e = hipEventRecord(main_stop, stream)) != hipSuccess) return e;
     int Rp = 1;
     while (Rp < sp.R) Rp <<= 1;
-    hipLaunchKernelGGL(final_select_wave_kernel, dim3((unsigned)((sp.nq + 3) / 4)), dim3(kSelThreads), 0, stream, p, st);
+    if (sp.nq <= kFewMaxQ)
+        hipLaunchKernelGGL(final_select_few_kernel, dim3((unsigned)sp.nq), dim3(kFewThreads), 0, stream, p, st);
+    else
+        hipLaunchKernelGGL(final_select_wave_kernel, dim3((unsigned)((sp.nq + 3) / 4)), dim3(kSelThreads), 0, stream, p, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     allow_lds(final_select_kernel, (size_t)(kSelLds + Rp) * 8);
     hipLaunchKernelGGL(final_select_kernel, dim3((unsigned)sp.nq), dim3(kSelThreads), (size_t)(kSelLds + Rp) * 8, stream, p, st);
