@@ -248,6 +248,36 @@ __device__ __forceinline__ int32_t row_sum(const int8_t* lut_s, int32_t B, int32
     return s;
 }
 
+// Sum of one row's table entries for rows of whole 16-byte segments (nseg of
+// them, ss bytes apart): the segments of a batch of up to 8 are all loaded
+// before any lookup, so a row costs one memory round trip per batch rather
+// than one per word.  The table is center major in LDS with stride S, its
+// blocks zero from B up to 32 nseg (nibbles past B, in padding bytes, add 0).
+__device__ __forceinline__ int32_t row_sum_seg(const int8_t* lut_s, int32_t S, const uint8_t* src, int nseg,
+                                               int32_t ss) {
+    int32_t sv = 0;
+    for (int j0 = 0; j0 < nseg; j0 += 8) {
+        uint4 r[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (j0 + k < nseg) r[k] = *reinterpret_cast<const uint4*>(src + (j0 + k) * ss);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (j0 + k >= nseg) break;
+            const uint32_t wd[4] = {r[k].x, r[k].y, r[k].z, r[k].w};
+#pragma unroll
+            for (int u = 0; u < 32; ++u)
+                sv += lut_s[(int)((wd[u >> 3] >> (4 * (u & 7))) & 15u) * S + 32 * (j0 + k) + u];
+        }
+    }
+    return sv;
+}
+
+// LDS bytes of a query's center-major table padded to whole 32-block segments.
+__host__ __device__ inline size_t seg_lut_bytes(int32_t B) {
+    return ((size_t)tstride(32 * (((B + 1) / 2 + 15) / 16)) * 16 + 15) & ~(size_t)15;
+}
+
 // ------------------------------------------------------------------ leaf -> query inversion
 __global__ void zero_u32_kernel(uint32_t* p, int64_t count) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
@@ -392,8 +422,13 @@ __global__ __launch_bounds__(kSelThreads) void warmup_kernel(Problem p, ScanStat
     const int64_t q = blockIdx.x;
     const int tid = threadIdx.x;
     int8_t* lut_s = reinterpret_cast<int8_t*>(smem);
-    uint64_t* keys = reinterpret_cast<uint64_t*>(smem + (((size_t)tstride(p.B) * 16 + 15) & ~(size_t)15));
-    stage_table_cm(lut_s, p.lut + q * p.B * 16, p.B, p.B, tid, kSelThreads);
+    uint64_t* keys = reinterpret_cast<uint64_t*>(smem + seg_lut_bytes(p.B));
+    // rows of whole 16-byte segments are summed a segment batch at a time on a
+    // table padded to whole segments
+    const bool al16 = (p.stride & 15) == 0 && (reinterpret_cast<uintptr_t>(p.codes) & 15) == 0;
+    const int nseg = ((p.B + 1) / 2 + 15) / 16;
+    const int32_t Bp = al16 ? 32 * nseg : p.B, S = tstride(Bp);
+    stage_table_cm(lut_s, p.lut + q * p.B * 16, p.B, Bp, tid, kSelThreads);
     for (int j = tid; j < kNB; j += kSelThreads) st.hist[q * kNB + j] = 0;
     if (tid == 0) {
         st.cnt[q] = 0;
@@ -422,7 +457,9 @@ __global__ __launch_bounds__(kSelThreads) void warmup_kernel(Problem p, ScanStat
         const int32_t off = p.leaves ? leaf_bias_at(p, q, j) : 0;
         for (int64_t t = tid; t < take; t += kSelThreads) {
             const int64_t row = a + t;
-            const int32_t s = row_sum(lut_s, p.B, tstride(p.B), code_row(p, row), al4, seg_step(p)) + off;
+            const uint8_t* src = code_row(p, row);
+            const int32_t s = (al16 ? row_sum_seg(lut_s, S, src, nseg, seg_step(p))
+                                    : row_sum(lut_s, p.B, S, src, al4, seg_step(p))) + off;
             keys[got + t] = int_key(s, p.ids ? p.ids[row] : (int32_t)row);
         }
         __syncthreads();
@@ -461,25 +498,7 @@ __global__ __launch_bounds__(kSpreadThreads) void warmup_spread_kernel(Problem p
     if (i < W) {
         const int64_t row = i * p.n / W;
         const uint8_t* src = code_row(p, row);
-        int32_t sv = 0;
-        if (al16) {
-            for (int j0 = 0; j0 < nseg; j0 += 8) {
-                uint4 r[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    if (j0 + k < nseg) r[k] = *reinterpret_cast<const uint4*>(src + (j0 + k) * ss);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    if (j0 + k >= nseg) break;
-                    const uint32_t wd[4] = {r[k].x, r[k].y, r[k].z, r[k].w};
-#pragma unroll
-                    for (int u = 0; u < 32; ++u)
-                        sv += lut_s[(int)((wd[u >> 3] >> (4 * (u & 7))) & 15u) * S + 32 * (j0 + k) + u];
-                }
-            }
-        } else {
-            sv = row_sum(lut_s, p.B, S, src, al4, ss);
-        }
+        const int32_t sv = al16 ? row_sum_seg(lut_s, S, src, nseg, ss) : row_sum(lut_s, p.B, S, src, al4, ss);
         atomicAdd(&h_s[hist_bin(sv, st.hlo, st.hsh)], 1u);
     }
     __syncthreads();
@@ -2373,7 +2392,7 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
     if (W > 8192) W = 8192;
     const size_t lut_bytes = ((size_t)tstride(sp.B) * 16 + 15) & ~(size_t)15;
     // (the spread warm-up may pad its table to whole 32-block code segments)
-    const size_t spread_lut = (size_t)tstride(32 * (((sp.B + 1) / 2 + 15) / 16)) * 16;
+    const size_t spread_lut = seg_lut_bytes(sp.B);
     if (streaming && !part && sp.n > 0 && spread_lut <= 64 * 1024) {
         int64_t Ws = sp.n < kSpreadRows ? sp.n : kSpreadRows;
         const int64_t cap = kSpreadLookups / sp.B, floor_rows = sp.n < 8192 ? sp.n : 8192;
@@ -2390,8 +2409,8 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
         // (the one-wave warm-up pads its table to whole 32-block code segments)
         hipLaunchKernelGGL(warmup_wave_kernel, dim3((unsigned)((sp.nq + 3) / 4)), dim3(kSelThreads), 0, stream, p, st, W);
     } else {
-        allow_lds(warmup_kernel, lut_bytes + (size_t)W * 8);
-        hipLaunchKernelGGL(warmup_kernel, dim3((unsigned)sp.nq), dim3(kSelThreads), lut_bytes + (size_t)W * 8, stream, p,
+        allow_lds(warmup_kernel, seg_lut_bytes(sp.B) + (size_t)W * 8);
+        hipLaunchKernelGGL(warmup_kernel, dim3((unsigned)sp.nq), dim3(kSelThreads), seg_lut_bytes(sp.B) + (size_t)W * 8, stream, p,
                            st, W);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;

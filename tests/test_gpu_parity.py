@@ -232,6 +232,25 @@ def test_scan_partitioned_parity(gpu):
     _scan_check(torch, ah, lut, codes, R, ids=perm, offs=offs, leaves=leaves)
 
 
+@pytest.mark.parametrize("B,nq,stride_pad", [(768, 20, 0), (300, 9, 0), (200, 7, 12), (1001, 6, 11)])
+def test_scan_partitioned_large_tables(gpu, B, nq, stride_pad):
+    """Partitioned batches with tables past the one-wave warm-up's size: the
+    workgroup warm-up sums rows of whole 16-byte segments a batch of segments at
+    a time (384 B rows; 112 B rows whose 12 padding bytes hold random nibbles
+    that must add nothing) or word by word (150 B and 512 B rows, unaligned)."""
+    torch, ah = gpu
+    rng = np.random.default_rng(500 + B + nq)
+    n, L, nl, R = 6000, 12, 4, 100
+    sizes = synth.random_leaf_sizes(rng, n, L, skew=1.0)
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    lut = synth.random_lut_i8(rng, nq, B)
+    codes = synth.random_codes(rng, n, B)
+    if stride_pad:
+        codes = np.concatenate([codes, rng.integers(0, 256, size=(n, stride_pad), dtype=np.uint8)], axis=1)
+    leaves = synth.random_probe_lists(rng, nq, L, nl)
+    _scan_check(torch, ah, lut, codes, R, offs=offs, leaves=leaves)
+
+
 # Small batches (at most four queries) on rows aligned to 16 bytes take the
 # streaming kernel: byte-pair tables for one or two queries per item, nibble
 # tables (one query, or four packed) when pair tables would not fit.  Cases
