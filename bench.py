@@ -347,6 +347,7 @@ def code_scan_probe(torch, ahlib, ev, runs=5):
         tiled = ahlib.ah_tile_codes(codes, B)
         # plain-stream read of the same bytes, several launch widths; the best is the reference
         e0, e1 = ev.create(), ev.create()
+        c0, c1 = ev.create(), ev.create()  # around the whole top-R call (warm-up, scan, selection)
         best = 0.0
         for bpc in (2, 4, 8, 16):
             ts = []
@@ -362,12 +363,15 @@ def code_scan_probe(torch, ahlib, ev, runs=5):
             lut = torch.randint(-127, 128, (nq, B, 16), generator=g, device="cuda", dtype=torch.int8)
             ws = torch.empty(ahlib.ah_scan_workspace_bytes(nq, B, n, 0, 0, R), dtype=torch.uint8, device="cuda")
             for layout, src in (("", tiled), ("_rowmajor", codes)):
-                ts = []
+                ts, tc = [], []
                 for it in range(runs + 1):
+                    ev.record(c0, sh)
                     ahlib.ah_scan_topk(lut, src, R, workspace=ws, main_events=(e0, e1))
+                    ev.record(c1, sh)
                     torch.cuda.synchronize()
                     if it:
                         ts.append(ev.elapsed_ms(e0, e1))
+                        tc.append(ev.elapsed_ms(c0, c1))
                 ms = float(np.median(ts))
                 gbps = codes.numel() / (ms / 1e3) / 1e9
                 appended, _ = ahlib.scan_counters(ws, nq, B, n, 0, 0, R)
@@ -375,7 +379,8 @@ def code_scan_probe(torch, ahlib, ev, runs=5):
                                                 "layout": "tiled" if not layout else "row-major",
                                                 "scan_ms": ms, "GBps": gbps, "frac_of_8TBps": gbps / PEAK_HBM_GBPS,
                                                 "frac_of_plain_read": gbps / best,
-                                                "candidates_per_query": float(appended.mean())}
+                                                "candidates_per_query": float(appended.mean()),
+                                                "call_ms": float(np.median(tc))}
             del ws
         del codes, tiled
     torch.cuda.empty_cache()

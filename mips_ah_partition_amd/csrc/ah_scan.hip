@@ -513,14 +513,29 @@ __global__ __launch_bounds__(kSpreadThreads) void warmup_spread_kernel(Problem p
 __global__ __launch_bounds__(kNB) void warmup_spread_finish_kernel(Problem p, ScanState st, int32_t W, int32_t nwg,
                                                                    const uint32_t* part) {
     __shared__ uint32_t h_s[kNB];
+    __shared__ __align__(16) uint32_t h4_s[4][kNB];
     const int64_t q = blockIdx.x;
-    const int j = threadIdx.x;  // one bin per thread
+    const int j = threadIdx.x;
     if (q == 0 && j < 16) st.ctrl[j] = 0;
-    const uint32_t* src = part + q * nwg * kNB + j;
-    uint32_t c = 0;
+    {
+        // thread j adds bins 4 (j % 256) .. +3 of every fourth partial
+        // histogram from j / 256 (16-byte loads, 16 in flight), then the four
+        // groups are added in LDS
+        const int j4 = (j & 255) * 4, grp = j >> 8;
+        const uint32_t* src = part + q * nwg * kNB + j4;
+        uint4 c = make_uint4(0, 0, 0, 0);
 #pragma unroll 16
-    for (int g = 0; g < nwg; ++g) c += src[(int64_t)g * kNB];
-    h_s[j] = c;
+        for (int g = grp; g < nwg; g += 4) {
+            const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)g * kNB);
+            c.x += v.x;
+            c.y += v.y;
+            c.z += v.z;
+            c.w += v.w;
+        }
+        *reinterpret_cast<uint4*>(&h4_s[grp][j4]) = c;
+    }
+    __syncthreads();
+    h_s[j] = h4_s[0][j] + h4_s[1][j] + h4_s[2][j] + h4_s[3][j];
     st.hist[q * kNB + j] = 0;
     if (j == 0) {
         st.cnt[q] = 0;
