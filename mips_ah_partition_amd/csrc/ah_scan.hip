@@ -2400,9 +2400,15 @@ hipError_t launch_scan(const ScanProblem& sp, void* ws, size_t ws_bytes, hipStre
         ma.itemoff = itemoff;
     }
     // warm-up rows per query: enough for a first bound; the item-local
-    // thresholds tighten it within the first items
+    // thresholds tighten it within the first items.  Queries that scan about
+    // 2^19 rows or more take at least 2,048: their first bound holds for the
+    // whole first round of items (one per CU), which at 20M x 384 (1M rows per
+    // query) otherwise appended 2.4x the candidates; with fewer rows per query
+    // the larger warm-up costs more than it saves.
+    const int64_t rows_q = part ? sp.n * sp.nl / (sp.L > 0 ? sp.L : 1) : sp.n;
     int32_t W = 2 * sp.R;
-    if (W < 1024) W = 1024;
+    const int32_t wmin = rows_q >= (int64_t)1 << 19 ? 2048 : 1024;
+    if (W < wmin) W = wmin;
     if (streaming) W = 8192;  // a few queries (partitioned): a tighter first bound is cheap and every workgroup starts from it
     if (W > 8192) W = 8192;
     const size_t lut_bytes = ((size_t)tstride(sp.B) * 16 + 15) & ~(size_t)15;
