@@ -476,7 +476,7 @@ __global__ __launch_bounds__(kSelThreads) void warmup_kernel(Problem p, ScanStat
 // the scan starts from: W rows evenly spaced over the whole array (distinct, as
 // W <= n), one per thread of nwg workgroups per query, each workgroup writing a
 // histogram of its rows' sums; warmup_spread_finish_kernel adds them up.  Many
-// more rows than the one-workgroup warm-up reads, in less time.  Rows of whole
+// more rows than the one-wave warm-up reads, in less time.  Rows of whole
 // 16-byte segments load all their segments (up to 8) before any lookup, on a
 // table padded with zero blocks to whole segments.
 __global__ __launch_bounds__(kSpreadThreads) void warmup_spread_kernel(Problem p, ScanState st, int32_t W,
