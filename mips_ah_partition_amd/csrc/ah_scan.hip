@@ -985,16 +985,23 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
             }
         };
         // resident table (B <= 64): B operand layout [kstep][ntile][lane][16 bytes]
+        // (entries past the item's queries or past B read 16 zero bytes, so every
+        // load is unconditional and a thread's eight are in flight together)
         auto stage_lut = [&](int c) {
-            for (int e = tid; e < kKC * 4 * kWave; e += kScanThreads) {
+            constexpr int kPer = kKC * 4 * kWave / kScanThreads;
+            v4i v[kPer];
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+                const int e = tid + k * kScanThreads;
                 const int s = e >> 8, nt = (e >> 6) & 3, ln = e & 63;
                 const int ql = 16 * nt + (ln & 15);
                 const int blk = c * 64 + 4 * s + (ln >> 4);
-                v4i v = {0, 0, 0, 0};
-                if (ql < qn && blk < p.B)
-                    v = *reinterpret_cast<const v4i*>(p.lut + ((int64_t)qid_s[ql] * p.B + blk) * 16);
-                *reinterpret_cast<v4i*>(lut_s + e * 16) = v;
+                const int8_t* src =
+                    (ql < qn && blk < p.B) ? p.lut + ((int64_t)qid_s[ql] * p.B + blk) * 16 : g_zero16;
+                v[k] = *reinterpret_cast<const v4i*>(src);
             }
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) *reinterpret_cast<v4i*>(lut_s + (tid + k * kScanThreads) * 16) = v[k];
         };
         // code staging: lane l of a wave owns row rowbase + l, code bytes
         // [32c, 32c+32).  A staged pair of 16-byte words carries a keep mask
