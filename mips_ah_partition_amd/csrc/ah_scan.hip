@@ -634,6 +634,62 @@ __device__ __forceinline__ void decode_item(const MainArgs& a, int64_t item, int
     }
 }
 
+// decode_item by one whole wave (every lane gets the result): a partitioned
+// item's leaf is found in two rounds of 64 loads (every ceil(L/64)-th entry of
+// itemoff, then the entries of the chosen stride) instead of a binary search's
+// log2 L dependent loads, which every workgroup waited for at every item start.
+__device__ __forceinline__ void decode_item_wave(const MainArgs& a, int64_t item, int64_t& p0, int64_t& p1,
+                                                 int64_t& qbase, int& qn) {
+    const Problem& p = a.p;
+    if (!p.leaves || p.L > kWave * kWave) {
+        decode_item(a, item, p0, p1, qbase, qn);
+        return;
+    }
+    const int lane = lane_id();
+    const int64_t G = a.qg;
+    // largest l < L with itemoff[l] <= item (itemoff[0] = 0, non-decreasing)
+    const int step = (p.L + kWave - 1) / kWave;
+    const int i1 = lane * step;
+    const uint64_t m1 = __ballot(i1 < p.L && a.itemoff[i1] <= item);
+    const int l1 = (63 - __clzll((long long)m1)) * step;
+    const int i2 = l1 + lane;
+    const uint64_t m2 = __ballot(lane < step && i2 < p.L && a.itemoff[i2] <= item);
+    const int l = l1 + (63 - __clzll((long long)m2));
+    const int64_t nqL = a.lqoff[l + 1] - a.lqoff[l];
+    const int64_t ng = (nqL + G - 1) / G;
+    const int64_t loc = item - a.itemoff[l];
+    const int64_t chunk = loc / ng, grp = loc % ng;
+    const int64_t ra = p.leaf_offsets[l], rb = p.leaf_offsets[l + 1];
+    p0 = ra + chunk * a.item_pts;
+    p1 = p0 + a.item_pts < rb ? p0 + a.item_pts : rb;
+    qbase = a.lqoff[l] + grp * G;
+    qn = (int)(nqL - grp * G < G ? nqL - grp * G : G);
+}
+
+// The next item for a workgroup, by its wave 0 (lane 0 holds the claimed index
+// and claims the one after): the item and its rows and queries go to LDS.
+__device__ __forceinline__ void fetch_item(const MainArgs& a, int64_t& claimed, int64_t n_items, int64_t* item_s,
+                                           int64_t* p0_s, int64_t* p1_s, int64_t* qbase_s, int* qn_s,
+                                           uint32_t* slab_s) {
+    const int lane = lane_id();
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)claimed);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)claimed >> 32));
+    const int64_t item = (int64_t)(((uint64_t)hi << 32) | lo);
+    if (lane == 0) *item_s = item;
+    if (item >= n_items) return;
+    int64_t p0, p1, qbase;
+    int qn;
+    decode_item_wave(a, item, p0, p1, qbase, qn);
+    if (lane == 0) {
+        *p0_s = p0;
+        *p1_s = p1;
+        *qbase_s = qbase;
+        *qn_s = qn;
+        if (slab_s) *slab_s = 0;
+        claimed = (int64_t)atomicAdd(&a.st.ctrl[0], 1u);
+    }
+}
+
 __device__ __forceinline__ v4i onehot16(uint32_t x) {
     // x & 15 = center index; returns 16 bytes with a single 1 at that index
     const uint32_t sh8 = (x & 7u) << 3;
@@ -935,21 +991,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
     int64_t claimed = 0;  // thread 0: the next item, claimed while the current one computes
     if (tid == 0) claimed = (int64_t)atomicAdd(&st.ctrl[0], 1u);
     for (;;) {
-        if (tid == 0) {
-            const int64_t item = claimed;
-            item_s = item;
-            if (item < n_items) {
-                int64_t p0, p1, qbase;
-                int qn;
-                decode_item(a, item, p0, p1, qbase, qn);
-                p0_s = p0;
-                p1_s = p1;
-                qbase_s = qbase;
-                qn_s = qn;
-                slab_s = 0;
-                claimed = (int64_t)atomicAdd(&st.ctrl[0], 1u);
-            }
-        }
+        if (w == 0) fetch_item(a, claimed, n_items, &item_s, &p0_s, &p1_s, &qbase_s, &qn_s, &slab_s);
         __syncthreads();
         const int64_t item = item_s;
         if (item >= n_items) break;
@@ -1521,20 +1563,7 @@ __global__ __launch_bounds__(kStreamThreads) void scan_stream_kernel(MainArgs a)
     int staged_qn = 0;
     if (tid == 0) claimed = (int64_t)atomicAdd(&st.ctrl[0], 1u);
     for (;;) {
-        if (tid == 0) {
-            const int64_t item = claimed;
-            item_s = item;
-            if (item < n_items) {
-                int64_t p0, p1, qbase;
-                int qn;
-                decode_item(a, item, p0, p1, qbase, qn);
-                p0_s = p0;
-                p1_s = p1;
-                qbase_s = qbase;
-                qn_s = qn;
-                claimed = (int64_t)atomicAdd(&st.ctrl[0], 1u);
-            }
-        }
+        if (w == 0) fetch_item(a, claimed, n_items, &item_s, &p0_s, &p1_s, &qbase_s, &qn_s, nullptr);
         __syncthreads();
         const int64_t item = item_s;
         if (item >= n_items) break;
