@@ -954,9 +954,12 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
     __shared__ int32_t jb_s[kQG];      // global bin of the threshold at item start
     __shared__ int32_t off_s[kQG];     // residual variant: the item's leaf term per query (0 otherwise)
     __shared__ uint32_t fl_s[kScanWaves * 2 * kWave];  // per-wave flush scratch
-    __shared__ int64_t item_s, p0_s, p1_s, qbase_s;
-    __shared__ uint32_t slab_s;  // next 64-row slab of the item (one 64-block chunk)
-    __shared__ int32_t qn_s;
+    // the item's record (item, rows, queries, next 64-row slab with a resident
+    // table), two of them: with a resident table wave 0 decodes the next item
+    // into the other one while the rest of the workgroup starts on this one
+    __shared__ int64_t item_r[2], p0_r[2], p1_r[2], qbase_r[2];
+    __shared__ uint32_t slab_r[2];
+    __shared__ int32_t qn_r[2];
 
     const Problem& p = a.p;
     const ScanState& st = a.st;
@@ -990,19 +993,22 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
 
     int64_t claimed = 0;  // thread 0: the next item, claimed while the current one computes
     if (tid == 0) claimed = (int64_t)atomicAdd(&st.ctrl[0], 1u);
+    int par = 0;  // the record of the current item
+    if (dyn && w == 0) fetch_item(a, claimed, n_items, &item_r[0], &p0_r[0], &p1_r[0], &qbase_r[0], &qn_r[0], &slab_r[0]);
     for (;;) {
-        if (w == 0) fetch_item(a, claimed, n_items, &item_s, &p0_s, &p1_s, &qbase_s, &qn_s, &slab_s);
+        if (!dyn && w == 0)
+            fetch_item(a, claimed, n_items, &item_r[par], &p0_r[par], &p1_r[par], &qbase_r[par], &qn_r[par], &slab_r[par]);
         __syncthreads();
-        const int64_t item = item_s;
+        const int64_t item = item_r[par];
         if (item >= n_items) break;
-        const int64_t p0 = p0_s, p1 = p1_s;
-        const int qn = qn_s;
+        const int64_t p0 = p0_r[par], p1 = p1_r[par], qbase = qbase_r[par];
+        const int qn = qn_r[par];
         if (tid < kQG) {
             int32_t qq = 0;
-            if (tid < qn) qq = p.leaves ? a.qlist[qbase_s + tid] : (int32_t)(qbase_s + tid);
+            if (tid < qn) qq = p.leaves ? a.qlist[qbase + tid] : (int32_t)(qbase + tid);
             qid_s[tid] = qq;
             qapp_s[tid] = 0;
-            if (kBias) off_s[tid] = tid < qn ? a.qbias[qbase_s + tid] : 0;
+            if (kBias) off_s[tid] = tid < qn ? a.qbias[qbase + tid] : 0;
             const int32_t t = tid < qn ? ld_coherent(st.tau + qq) : INT_MAX;
             tau_s[tid] = t;
             jb_s[tid] = (t == INT_MIN || t == INT_MAX) ? 0 : hist_bin(t, st.hlo, st.hsh);
@@ -1128,7 +1134,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
         const int64_t nsteps = ((p1 - p0 + kTilePts - 1) / kTilePts) * a.nchunk;
         auto claim = [&]() -> int64_t {
             uint32_t v = 0;
-            if (lane == 0) v = atomicAdd(&slab_s, 1u);
+            if (lane == 0) v = atomicAdd(&slab_r[par], 1u);
             return (int64_t)__builtin_amdgcn_readfirstlane(v);
         };
         // (u, c): unit (slab, or tile) and chunk of a step; valid while u < nunits
@@ -1153,6 +1159,11 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
         if (nu < nunits) load_codes(rowbase_of(nu), nc, px0, px1, pkeep);
         if (dyn) stage_lut(0);
         __syncthreads();  // lut_s (its first chunk), qid_s and the first codes for this item are complete
+        // resident table (no workgroup barrier until the item ends): wave 0
+        // decodes the next item now, its loads overlapping the other waves' slabs
+        if (dyn && w == 0)
+            fetch_item(a, claimed, n_items, &item_r[par ^ 1], &p0_r[par ^ 1], &p1_r[par ^ 1], &qbase_r[par ^ 1],
+                       &qn_r[par ^ 1], &slab_r[par ^ 1]);
 
         v4i acc[4][4];
         int32_t tq[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
@@ -1419,6 +1430,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
         publish_item(st, tau_s, qid_s, qn, w);
         refresh_tau_wave(st, qid_s, qapp_s, qn, w, kScanWaves, p.R);
         __syncthreads();
+        par ^= 1;
     }
 }
 
