@@ -55,7 +55,6 @@ constexpr int kKCS = 8;                           // k-steps of one staged chunk
 // The one-hot contraction runs on the sparse int8 matrix instruction (2:4
 // structured sparsity, twice the k of the dense one per instruction); false
 // selects the dense instruction with one-hot operands from an LDS table.
-constexpr bool kSparseScan = true;
 constexpr int kCodeStride = 9;                    // LDS row stride (dwords) for a chunk's 8 code dwords
 constexpr int kNB = 1024;                         // histogram bins per query
 constexpr int kLB = 64;                           // an item's LDS histogram bins per query
@@ -690,20 +689,6 @@ __device__ __forceinline__ void fetch_item(const MainArgs& a, int64_t& claimed, 
     }
 }
 
-__device__ __forceinline__ v4i onehot16(uint32_t x) {
-    // x & 15 = center index; returns 16 bytes with a single 1 at that index
-    const uint32_t sh8 = (x & 7u) << 3;
-    const uint64_t t = 1ull << sh8;
-    const uint32_t m = 0u - ((x >> 3) & 1u);
-    const uint32_t tl = (uint32_t)t, th = (uint32_t)(t >> 32);
-    v4i r;
-    r.x = (int)(tl & ~m);
-    r.y = (int)(th & ~m);
-    r.z = (int)(tl & m);
-    r.w = (int)(th & m);
-    return r;
-}
-
 // Appends a wave's logged hits to the queries' candidate lists and counts them
 // (kGlobalHist: also in the global histograms, hit by hit; fh: also in the
 // wave's flush histogram, merged into the global ones after the flush) in the
@@ -944,7 +929,6 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
     __shared__ __align__(16) int8_t lut_t[kStaged ? kKCS * 4 * kWave * 16 : 16];
     __shared__ __align__(16) uint32_t code_s[2][kTilePts * kCodeStride];
     __shared__ uint64_t log_s[kScanWaves * kLogCap];
-    __shared__ __align__(16) uint32_t onehot_s[16 * 4];           // onehot_s[c] = 16 bytes, byte c = 1
     __shared__ __align__(16) uint32_t spv_s[16 * 4];  // sparse A values by (c0 >> 2) | (c1 >> 2) << 2
     __shared__ uint32_t spi_s[256];                   // sparse A index word by code byte
     __shared__ int32_t qid_s[kQG];
@@ -984,11 +968,6 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
         spv_s[tid * 4 + 1] = (uint32_t)(lo >> 32);
         spv_s[tid * 4 + 2] = (uint32_t)hi;
         spv_s[tid * 4 + 3] = (uint32_t)(hi >> 32);
-    }
-    if (tid < 16) {
-        // center c: dword c/4 holds 1 << 8*(c%4), the other three dwords are 0
-#pragma unroll
-        for (int j = 0; j < 4; ++j) onehot_s[tid * 4 + j] = (tid >> 2) == j ? 1u << (8 * (tid & 3)) : 0u;
     }
 
     int64_t claimed = 0;  // thread 0: the next item, claimed while the current one computes
@@ -1212,8 +1191,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
             // 16-query tiles past the item's last query inside the loop measured
             // slower: the branch breaks the loop's schedule.)
             const bool wlive = dyn || rowbase_of(cu) < p1;
-            if (!wlive) {
-            } else if constexpr (kSparseScan) {
+            if (wlive) {
                 // Sparse steps of 8 blocks (a code dword per row tile).  Lane group
                 // g's A operand is the one-hot of the code byte g of its row (blocks
                 // 2g and 2g+1 of the step) in the 2:4 sparse form: value slots 0-7
@@ -1268,69 +1246,6 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                     }
 #pragma unroll
                     for (int m = 0; m < 4; ++m) cw[m] = cwn[m];
-                }
-            } else {
-                // k-steps go in pairs sharing one code dword per row tile (blocks
-                // 8j..8j+7); each step's A and B fragments are fetched from LDS one
-                // step ahead into alternating registers.
-                v4i aA[4], aB[4], bA[4], bB[4];
-                uint32_t cw[4], cwn[4];
-    #pragma unroll
-                for (int m = 0; m < 4; ++m) cw[m] = crow[m * 16 * kCodeStride];
-    #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) bA[nt] = *reinterpret_cast<const v4i*>(lutw + nt * kWave * 16);
-    #pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    aA[m] = *reinterpret_cast<const v4i*>(onehot_s + __builtin_amdgcn_ubfe(cw[m], 4 * g, 4) * 4);
-                // LDS reads only (lgkmcnt 0; vmcnt and expcnt at their maxima, so the
-                // code loads in flight are not waited for): the loop is entered with
-                // no LDS read pending, and the waits inside it follow its own order
-                __builtin_amdgcn_s_waitcnt(0xC07F);
-                for (int j = 0; j < (ks >> 1); ++j) {
-                    const int s1 = 2 * j + 1;
-                    // the next pair's operands are fetched unconditionally (the last
-                    // pair re-reads its own: same addresses, unused), so the loop has
-                    // one path.  The reads are spread over the pair so that at most
-                    // 14 are in flight (the LDS counter holds 15): second-half B and
-                    // the next code words, first-half products m = 0-1, second-half
-                    // A, products m = 2-3, then the next pair's first-half operands.
-                    const int jn = j + 1 < (ks >> 1) ? j + 1 : j;
-    #pragma unroll
-                    for (int nt = 0; nt < 4; ++nt)
-                        bB[nt] = *reinterpret_cast<const v4i*>(lutw + (s1 * 4 + nt) * kWave * 16);
-    #pragma unroll
-                    for (int m = 0; m < 4; ++m) cwn[m] = crow[m * 16 * kCodeStride + jn];
-                    __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
-                    for (int m = 0; m < 2; ++m)
-    #pragma unroll
-                        for (int nt = 0; nt < 4; ++nt)
-                            acc[m][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aA[m], bA[nt], acc[m][nt], 0, 0, 0);
-                    __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
-                    for (int m = 0; m < 4; ++m)
-                        aB[m] = *reinterpret_cast<const v4i*>(onehot_s + __builtin_amdgcn_ubfe(cw[m], 16 + 4 * g, 4) * 4);
-                    __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
-                    for (int m = 2; m < 4; ++m)
-    #pragma unroll
-                        for (int nt = 0; nt < 4; ++nt)
-                            acc[m][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aA[m], bA[nt], acc[m][nt], 0, 0, 0);
-                    __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
-                    for (int nt = 0; nt < 4; ++nt)
-                        bA[nt] = *reinterpret_cast<const v4i*>(lutw + ((2 * jn) * 4 + nt) * kWave * 16);
-    #pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        cw[m] = cwn[m];
-                        aA[m] = *reinterpret_cast<const v4i*>(onehot_s + __builtin_amdgcn_ubfe(cw[m], 4 * g, 4) * 4);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
-                    for (int m = 0; m < 4; ++m)
-    #pragma unroll
-                        for (int nt = 0; nt < 4; ++nt)
-                            acc[m][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aB[m], bB[nt], acc[m][nt], 0, 0, 0);
                 }
             }
             if (wlive && c == a.nchunk - 1) {
