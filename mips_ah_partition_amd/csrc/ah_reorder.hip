@@ -19,7 +19,10 @@
 // fp64 unless they round to the same fp32 value (then the lower id wins).  A
 // lane meets the same query elements in every row, so when a row takes one
 // pass it holds them in registers, widened once.  The R scores become ranking
-// keys and the workgroup's exact top-k selection orders them.
+// keys; for k <= 64 of R <= 512 one wave takes the best k by k rounds of a wave
+// maximum (the workgroup selection's radix passes and barriers cost 28% of the
+// kernel at 1M x 100, R = 200, k = 10; this path 12%), otherwise the
+// workgroup's exact top-k selection orders them.
 #include "ah_device.hpp"
 #include "ah_kernels.hpp"
 
@@ -170,6 +173,46 @@ __device__ void score_rows_scalar(const float* qs, int32_t d, const void* base, 
     }
 }
 
+// The best k of the R keys in LDS (k <= 64, R <= 512), in descending order, into
+// sel, by wave 0: each lane holds up to eight keys, and k rounds each take the
+// wave's largest remaining key and clear one occurrence of it (the lowest lane,
+// then its first slot, holding it), stopping at the zero keys of invalid
+// candidates.  The same keys in the same order as the workgroup selection.
+// Returns the number selected (wave 0 only).
+__device__ __forceinline__ int wave_select_topk(const uint64_t* keys, int R, int k, uint64_t* sel) {
+    const int lane = lane_id();
+    uint64_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int r = lane + kWave * j;
+        v[j] = r < R ? keys[r] : 0ull;
+    }
+    int m = 0;
+    for (; m < k; ++m) {
+        uint64_t best = v[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) best = v[j] > best ? v[j] : best;
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1) {
+            const uint64_t other = __shfl_xor(best, o, kWave);
+            best = other > best ? other : best;
+        }
+        if (best == 0) break;
+        if (lane == 0) sel[m] = best;
+        int slot = -1;
+#pragma unroll
+        for (int j = 7; j >= 0; --j)
+            if (v[j] == best) slot = j;
+        const uint64_t mk = __ballot(slot >= 0);
+        if (lane == __ffsll((unsigned long long)mk) - 1) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (j == slot) v[j] = 0ull;
+        }
+    }
+    return m;
+}
+
 // LDS: [R keys][next_pow2(k) selected][d query floats].  kPath: 0 = element-wise
 // (rows not in whole 16-byte chunks), else the chunk path with kCPL chunks per lane
 // (kOnePass: every row in one pass).
@@ -180,6 +223,7 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_kernel(
     float* __restrict__ scores_out) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ SelectShared sh;
+    __shared__ int sel_m;
     const int64_t qi = blockIdx.x;
     const int Kp = next_pow2(k);
     uint64_t* keys = reinterpret_cast<uint64_t*>(smem);
@@ -196,7 +240,17 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_kernel(
         score_rows_vec<ChunkBF16, kCPL, kOnePass>(qs, d, base, n, c, R, keys);
     }
     __syncthreads();
-    const int m = wg_select_topk<kReorderThreads>(LdsKeys{keys}, R, k, sh, sel);
+    int m;
+    if (k <= kWave && R <= 8 * kWave) {
+        if (threadIdx.x < kWave) {
+            const int mw = wave_select_topk(keys, R, k, sel);
+            if (threadIdx.x == 0) sel_m = mw;
+        }
+        __syncthreads();
+        m = sel_m;
+    } else {
+        m = wg_select_topk<kReorderThreads>(LdsKeys{keys}, R, k, sh, sel);
+    }
     for (int r = threadIdx.x; r < k; r += kReorderThreads) {
         ids_out[qi * k + r] = r < m ? key_id(sel[r]) : -1;
         scores_out[qi * k + r] = r < m ? key_float_score(sel[r]) : -__builtin_huge_valf();

@@ -441,7 +441,8 @@ def _check_ranked(g_ids, g_sc, o_ids, o_sc, ref_fn, denom_fn):
 @pytest.mark.parametrize("dtype,d,R,k", [("f32", 128, 200, 10), ("f32", 100, 37, 37), ("bf16", 384, 300, 10),
                                          ("bf16", 1536, 64, 10), ("f32", 7, 10, 3), ("f32", 512, 50, 5),
                                          ("bf16", 4096, 40, 8), ("f32", 2048, 30, 30), ("f32", 32, 4096, 4096),
-                                         ("f32", 12288, 64, 10), ("bf16", 12288, 32, 8), ("f32", 12289, 16, 4)])
+                                         ("f32", 12288, 64, 10), ("bf16", 12288, 32, 8), ("f32", 12289, 16, 4),
+                                         ("f32", 64, 512, 64), ("f32", 64, 513, 64), ("bf16", 64, 512, 65)])
 def test_reorder_parity(gpu, dtype, d, R, k):
     torch, ah = gpu
     rng = np.random.default_rng(d + R)
@@ -465,6 +466,25 @@ def test_reorder_parity(gpu, dtype, d, R, k):
     _check_ranked(_np(g_ids), _np(g_sc), o_ids, o_sc,
                   lambda q, ids: Xr[ids] @ Qd[q], lambda q, ids: np.abs(Xr[ids]) @ np.abs(Qd[q]))
     assert (_np(g_ids)[4] == -1).all() and np.isneginf(_np(g_sc)[4]).all()
+
+
+# Scores that are small exact integers tie often: the best k, ties broken by
+# the lower id, is then unique and the ids must match the oracle exactly.  The
+# sizes straddle the one-wave selection (R <= 512, k <= 64) and the workgroup one.
+@pytest.mark.parametrize("R,k", [(512, 64), (513, 64), (512, 65), (64, 64), (300, 1)])
+def test_reorder_ties(gpu, R, k):
+    torch, ah = gpu
+    rng = np.random.default_rng(R * 100 + k)
+    n, nq, d = 4000, 33, 8
+    X = rng.integers(-1, 2, size=(n, d)).astype(np.float32)
+    Q = rng.integers(-1, 2, size=(nq, d)).astype(np.float32)
+    cand = np.stack([rng.permutation(n)[:R] for _ in range(nq)]).astype(np.int32)
+    cand[5, ::3] = -1
+    g_ids, g_sc = ah.ah_reorder_exact(_t(torch, Q), _t(torch, X), _t(torch, cand), k)
+    torch.cuda.synchronize()
+    o_ids, o_sc = oracle.reorder(Q, X, cand, k)
+    assert np.array_equal(_np(g_ids), o_ids)
+    assert np.array_equal(_np(g_sc), o_sc)
 
 
 # ----------------------------------------------------------------------------- partition
