@@ -929,7 +929,6 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
     __shared__ __align__(16) int8_t lut_t[kStaged ? kKCS * 4 * kWave * 16 : 16];
     __shared__ __align__(16) uint32_t code_s[2][kTilePts * kCodeStride];
     __shared__ uint64_t log_s[kScanWaves * kLogCap];
-    __shared__ __align__(16) uint32_t spv_s[16 * 4];  // sparse A values by (c0 >> 2) | (c1 >> 2) << 2
     __shared__ uint32_t spi_s[256];                   // sparse A index word by code byte
     __shared__ int32_t qid_s[kQG];
     __shared__ uint32_t qapp_s[kQG];
@@ -953,21 +952,12 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
     constexpr bool dyn = !kStaged;  // resident table; else staged 32-block chunks
     uint64_t* mylog = log_s + w * kLogCap;
     uint32_t* mywq = fl_s + w * 2 * kWave;
-    // sparse one-hot operands: pair indices (c & 3, (c & 3) ^ 1) of both blocks
-    // of a code byte in every pair of the block (nibble 4 ^ 5 (c & 3)), and the
-    // value patterns with a 1 in the first slot of pair c >> 2 of each block
+    // sparse one-hot index words: pair indices (c & 3, (c & 3) ^ 1) of both
+    // blocks of a code byte in every pair of the block (nibble 4 ^ 5 (c & 3))
     if (tid < 256) {
         const uint32_t x = (uint32_t)tid;
         const uint32_t u = (x & 3u) | (((x >> 4) & 3u) << 16);
         spi_s[tid] = (u * 0x5555u) ^ 0x44444444u;
-    }
-    if (tid < 16) {
-        const uint32_t k0 = (uint32_t)tid & 3u, k1 = (uint32_t)tid >> 2;
-        const uint64_t lo = 1ull << (16 * k0), hi = 1ull << (16 * k1);
-        spv_s[tid * 4 + 0] = (uint32_t)lo;
-        spv_s[tid * 4 + 1] = (uint32_t)(lo >> 32);
-        spv_s[tid * 4 + 2] = (uint32_t)hi;
-        spv_s[tid * 4 + 3] = (uint32_t)(hi >> 32);
     }
 
     int64_t claimed = 0;  // thread 0: the next item, claimed while the current one computes
@@ -1200,9 +1190,11 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
                 // group holds the center, and each slot's 2-bit index selects the
                 // center inside its group (every pair of a block carries the
                 // center's indices; only the pair with the 1 contributes).  The
-                // values come from spv_s (16 patterns, so lanes share entries
-                // instead of conflicting), the index word from spi_s (one per code
-                // byte).  The matching B fragment of lane group g is the table row
+                // values of each block are the 64-bit word 1 << 16 (c >> 2), built
+                // in registers (a 16-pattern LDS table read here was as fast or,
+                // on the 20M-row scan, 0.7% slower); the index word comes from
+                // spi_s (one per code byte; its closed form in registers measured
+                // 1-3% slower).  The matching B fragment of lane group g is the table row
                 // of block g (bytes 0-15) and of block 4 + g (bytes 16-31): the
                 // dense fragments of k-steps 2S and 2S+1.  (Fetching the next
                 // step's A operands a step ahead measured slower: the registers
@@ -1231,8 +1223,8 @@ __global__ __launch_bounds__(kScanThreads, 1) void scan_main_kernel(MainArgs a) 
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
                         const uint32_t x = __builtin_amdgcn_ubfe(cw[m], 8 * g, 8);
-                        const uint32_t va = ((x << 2) & 0x30u) | (x & 0xC0u);
-                        av[m] = *reinterpret_cast<const v4i*>(reinterpret_cast<const unsigned char*>(spv_s) + va);
+                        const uint64_t lo = 1ull << ((x << 2) & 0x30u), hi = 1ull << ((x >> 2) & 0x30u);
+                        av[m] = v4i{(int)(uint32_t)lo, (int)(uint32_t)(lo >> 32), (int)(uint32_t)hi, (int)(uint32_t)(hi >> 32)};
                         iv[m] = spi_s[x];
                     }
                     __builtin_amdgcn_sched_barrier(0);
@@ -1596,23 +1588,23 @@ __global__ __launch_bounds__(kStreamThreads) void scan_stream_kernel(MainArgs a)
 #pragma unroll
             for (int g = 0; g < G; ++g)
                 sum[g] = G == 1 ? acc.s[0] : acc.s[g] - (kPair ? 256 * cb : 128 * p.B);
-                if (log_n > kCap - G * kWave) {
-                    flush_publish(log_n);
-                    log_n = 0;
-                }
-                const uint32_t lr = (uint32_t)(row - p0);
+            if (log_n > kCap - G * kWave) {
+                flush_publish(log_n);
+                log_n = 0;
+            }
+            const uint32_t lr = (uint32_t)(row - p0);
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const bool hit = valid && sum[g] >= tq[g];
-                    const uint64_t mk = __ballot(hit);
-                    if (mk) {
-                        if (hit)
-                            mylog[log_n + __popcll(mk & lanemask_lt())] =
-                                ((uint64_t)(uint32_t)(sum[g] + (a.qbias ? off_s[g] : 0)) << 32) |
-                                ((uint64_t)g << 16) | (uint64_t)lr;
-                        log_n += __popcll(mk);
-                    }
+            for (int g = 0; g < G; ++g) {
+                const bool hit = valid && sum[g] >= tq[g];
+                const uint64_t mk = __ballot(hit);
+                if (mk) {
+                    if (hit)
+                        mylog[log_n + __popcll(mk & lanemask_lt())] =
+                            ((uint64_t)(uint32_t)(sum[g] + (a.qbias ? off_s[g] : 0)) << 32) |
+                            ((uint64_t)g << 16) | (uint64_t)lr;
+                    log_n += __popcll(mk);
                 }
+            }
         };
         const int64_t rb0 = p0 + w * kWave;
         const int32_t ss = seg_step(p);
