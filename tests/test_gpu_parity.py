@@ -435,14 +435,16 @@ def _check_ranked(g_ids, g_sc, o_ids, o_sc, ref_fn, denom_fn):
         assert len(set(gi.tolist())) == len(gi)
 
 
-# Row lengths cover one, two and four 16-byte chunks per lane, rows longer than
+# Row lengths cover one, two and four 16-byte chunks per lane (two on a 32-lane
+# group for bf16 rows of 33-63 chunks: 264, 384 and 504 dims), rows longer than
 # 4 x 64 chunks (several passes; 12,288 dims: a dozen), and rows not in whole
 # chunks (element path).
 @pytest.mark.parametrize("dtype,d,R,k", [("f32", 128, 200, 10), ("f32", 100, 37, 37), ("bf16", 384, 300, 10),
                                          ("bf16", 1536, 64, 10), ("f32", 7, 10, 3), ("f32", 512, 50, 5),
                                          ("bf16", 4096, 40, 8), ("f32", 2048, 30, 30), ("f32", 32, 4096, 4096),
                                          ("f32", 12288, 64, 10), ("bf16", 12288, 32, 8), ("f32", 12289, 16, 4),
-                                         ("f32", 64, 512, 64), ("f32", 64, 513, 64), ("bf16", 64, 512, 65)])
+                                         ("f32", 64, 512, 64), ("f32", 64, 513, 64), ("bf16", 64, 512, 65),
+                                         ("bf16", 264, 100, 10), ("bf16", 504, 70, 7)])
 def test_reorder_parity(gpu, dtype, d, R, k):
     torch, ah = gpu
     rng = np.random.default_rng(d + R)
